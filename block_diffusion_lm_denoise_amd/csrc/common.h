@@ -1,0 +1,125 @@
+// common.h -- device helpers shared by the libdgpass kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dg {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// scalar conversions
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// round-to-nearest-even fp32 -> bf16 (NaN stays NaN)
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t b = __float_as_uint(f);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((b >> 16) | 0x40u);
+  b += 0x7fffu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+// activation storage: float or bf16 bit patterns
+__device__ __forceinline__ float ldx(const float* p, size_t i) { return p[i]; }
+__device__ __forceinline__ float ldx(const uint16_t* p, size_t i) { return bf2f(p[i]); }
+__device__ __forceinline__ void stx(float* p, size_t i, float v) { p[i] = v; }
+__device__ __forceinline__ void stx(uint16_t* p, size_t i, float v) { p[i] = f2bf(v); }
+__device__ __forceinline__ float rnd(float v, const float*) { return v; }
+__device__ __forceinline__ float rnd(float v, const uint16_t*) { return bf2f(f2bf(v)); }
+
+// ---------------------------------------------------------------------------
+// MFMA fragments.  A fragment is 8 consecutive contraction-dim elements of one
+// matrix row held by one lane.  For a 16x16 output tile, lane l holds row
+// (l % 16) and contraction chunk (l / 16); both operands use the same chunk
+// assignment, so any consistent permutation of the contraction index is
+// harmless.  bf16: one v_mfma_f32_16x16x32_bf16 per fragment pair; fp32: eight
+// v_mfma_f32_16x16x4_f32, element j of each lane feeding the j-th.
+// The accumulator (4 floats) of lane l holds rows 4*(l/16)+i, column l%16.
+// ---------------------------------------------------------------------------
+struct FragBF {
+  bf16x8_t v;
+};
+struct FragF32 {
+  float v[8];
+};
+
+template <typename T> struct FragOf;
+template <> struct FragOf<uint16_t> { typedef FragBF type; };
+template <> struct FragOf<float> { typedef FragF32 type; };
+
+__device__ __forceinline__ void mma(f32x4_t& acc, const FragBF& a, const FragBF& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4_t& acc, const FragF32& a, const FragF32& b) {
+#pragma unroll
+  for (int j = 0; j < 8; j++) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], acc, 0, 0, 0);
+}
+
+// 8 elements from memory (global or LDS)
+__device__ __forceinline__ void load_frag(FragBF& f, const uint16_t* p) {
+  uint4 u = *reinterpret_cast<const uint4*>(p);
+  f.v = __builtin_bit_cast(bf16x8_t, u);
+}
+__device__ __forceinline__ void load_frag(FragF32& f, const float* p) {
+  float4 a = *reinterpret_cast<const float4*>(p);
+  float4 b = *reinterpret_cast<const float4*>(p + 4);
+  f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+  f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+__device__ __forceinline__ void zero_frag(FragBF& f) {
+  f.v = __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+}
+__device__ __forceinline__ void zero_frag(FragF32& f) {
+#pragma unroll
+  for (int j = 0; j < 8; j++) f.v[j] = 0.f;
+}
+
+// OCP e4m3 byte pair -> two floats (hardware conversion), then bf16 bits.
+// Every e4m3 value is exact in bf16 (4 significant bits, exponent range
+// 2^-9 .. 448), so taking the top half of the fp32 pattern is exact.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+  return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
+}
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 u) {
+  uint4 r;
+  r.x = fp8x2_to_bf16x2<false>(u.x);
+  r.y = fp8x2_to_bf16x2<true>(u.x);
+  r.z = fp8x2_to_bf16x2<false>(u.y);
+  r.w = fp8x2_to_bf16x2<true>(u.y);
+  return r;
+}
+__device__ __forceinline__ void load_frag_fp8(FragBF& f, const uint8_t* p) {
+  uint2 u = *reinterpret_cast<const uint2*>(p);
+  f.v = __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8(u));
+}
+
+// ---------------------------------------------------------------------------
+// wave / block reductions (wave64)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// deterministic block sum for blockDim.x == 256 (4 waves); red: >= 4 floats of LDS
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+}  // namespace dg

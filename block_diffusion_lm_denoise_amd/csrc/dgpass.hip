@@ -1,0 +1,366 @@
+// dgpass.hip -- the C ABI of libdgpass: validation, workspace carving and the
+// launch sequence of a prefill and of a denoising pass.  See include/dgpass.h.
+#include <string.h>
+
+#include "launch.h"
+
+using namespace dg;
+
+namespace {
+
+constexpr uint32_t MODEL_MAGIC = 0x44475041u;  // "DGPA"
+
+size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
+int esize(int dt) { return dt == DG_F32 ? 4 : dt == DG_BF16 ? 2 : 1; }
+
+constexpr int SKINNY_TILE = 32;   // row tile of the weight-streaming expert kernels
+constexpr int FAT_TILE = 128;     // row tile of the LDS-tiled expert kernels
+
+struct Layout {
+  size_t cov;       // [L][E] int32 expert counts of the last pass (offset 0)
+  size_t x, u, qkv, o, x1, u2, rl, ids, gates, counts, offsets, perm, inv, tiles, ntiles, H, Y;
+  size_t po, pml, lpm, lpi, lps, total;
+  long part_cap;
+  int max_tiles;
+};
+
+Layout layout(const dg_config& c, int rows) {
+  Layout L{};
+  const size_t a = esize(c.act_dtype);
+  const size_t R = rows > 0 ? rows : 1;
+  const size_t QKV = (size_t)(c.Hq + 2 * c.Hkv) * c.hd, QD = (size_t)c.Hq * c.hd;
+  const size_t slots = R * c.k;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += al(bytes);
+    return o;
+  };
+  L.cov = take((size_t)c.L * c.E * 4);
+  L.x = take(R * c.D * a);
+  L.u = take(R * c.D * a);
+  L.qkv = take(R * QKV * a);
+  L.o = take(R * QD * a);
+  L.x1 = take(R * c.D * a);
+  L.u2 = take(R * c.D * a);
+  L.rl = take(R * c.E * 4);
+  L.ids = take(slots * 4);
+  L.gates = take(slots * 4);
+  L.counts = take((size_t)c.E * 4);
+  L.offsets = take((size_t)(c.E + 1) * 4);
+  L.perm = take(slots * 4);
+  L.inv = take(slots * 4);
+  L.max_tiles = (int)((slots + SKINNY_TILE - 1) / SKINNY_TILE) + c.E;
+  L.tiles = take((size_t)L.max_tiles * 16);
+  L.ntiles = take(4);
+  L.H = take(slots * c.F * a);
+  L.Y = take(slots * c.D * a);
+  L.part_cap = attn_partial_entries((int)R, c.Hq);
+  L.po = take((size_t)L.part_cap * c.hd * 4);
+  L.pml = take((size_t)L.part_cap * 2 * 4);
+  const size_t nt = lm_tiles(c.V);
+  L.lpm = take(R * nt * 4);
+  L.lpi = take(R * nt * 4);
+  L.lps = take(R * nt * 4);
+  L.total = off;
+  return L;
+}
+
+bool valid_cfg(const dg_config* c) {
+  if (!c) return false;
+  if (c->L < 1 || c->L > DG_MAX_LAYERS || c->D < 1 || c->Hq < 1 || c->Hkv < 1 || c->E < 1 ||
+      c->k < 1 || c->F < 1 || c->V < 1 || !(c->eps >= 0.f))
+    return false;
+  return true;
+}
+
+dg_status supported_cfg(const dg_config* c) {
+  if (c->D % 128 || c->F % 64) return DG_ERR_UNSUPPORTED;
+  if (c->hd != 64 && c->hd != 128) return DG_ERR_UNSUPPORTED;
+  if (c->Hq % c->Hkv) return DG_ERR_UNSUPPORTED;
+  const int G = c->Hq / c->Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return DG_ERR_UNSUPPORTED;
+  if ((c->Hq * c->hd) % 64) return DG_ERR_UNSUPPORTED;
+  if (c->k > 8 || c->k > c->E || c->E > 256) return DG_ERR_UNSUPPORTED;
+  if (c->act_dtype == DG_F32) {
+    if (c->expert_dtype != DG_F32) return DG_ERR_UNSUPPORTED;
+  } else if (c->act_dtype == DG_BF16) {
+    if (c->expert_dtype != DG_BF16 && c->expert_dtype != DG_FP8E4M3) return DG_ERR_UNSUPPORTED;
+  } else {
+    return DG_ERR_UNSUPPORTED;
+  }
+  return DG_OK;
+}
+
+bool model_ok(const dg_model* m) { return m && m->magic == MODEL_MAGIC; }
+
+// everything after the attention of one layer: Wo + residual, norm, router,
+// top-k, permutation, experts, combine + the next norm
+struct Ctx {
+  const dg_model* m;
+  char* ws;
+  Layout L;
+  int R;          // token rows
+  const dg_taps* taps;
+  hipStream_t s;
+  bool pass;      // denoising pass (writes coverage counts)
+};
+
+template <typename T>
+T* at(const Ctx& c, size_t off) {
+  return reinterpret_cast<T*>(c.ws + off);
+}
+
+void tap_copy(void* dst, const void* src, size_t bytes, hipStream_t s) {
+  if (dst && bytes) (void)hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);
+}
+
+void moe_block(const Ctx& c, int l, const float* gnext) {
+  const dg_config& cf = c.m->cfg;
+  const dg_layer_weights& w = c.m->w.layers[l];
+  const int act = cf.act_dtype == DG_BF16 ? ACT_BF16 : ACT_F32;
+  const size_t a = esize(cf.act_dtype);
+  const size_t R = c.R, D = cf.D, QD = (size_t)cf.Hq * cf.hd, E = cf.E, k = cf.k;
+  const dg_taps* t = c.taps;
+  hipStream_t s = c.s;
+
+  // x1 = x + o Wo^T
+  launch_gemm(act, GEMM_RESID, at<void>(c, c.L.o), c.R, (int)QD, w.wo, cf.D, nullptr, 0, nullptr,
+              cf.D, at<void>(c, c.L.x1), cf.D, at<void>(c, c.L.x), nullptr, s);
+  if (t) tap_copy(t->x1 ? (char*)t->x1 + l * R * D * a : nullptr, at<void>(c, c.L.x1), R * D * a, s);
+  launch_rmsnorm(act, at<void>(c, c.L.x1), w.g2, c.R, cf.D, cf.eps, at<void>(c, c.L.u2), s);
+  if (t) tap_copy(t->u2 ? (char*)t->u2 + l * R * D * a : nullptr, at<void>(c, c.L.u2), R * D * a, s);
+
+  // router logits (fp32) and top-k
+  const float* rl = at<float>(c, c.L.rl);
+  if (t && t->inject_router) {
+    rl = t->inject_router + (size_t)l * R * E;
+  } else {
+    launch_gemm(act, GEMM_F32, at<void>(c, c.L.u2), c.R, cf.D, w.wr, cf.E, nullptr, 0, nullptr, cf.E,
+                at<void>(c, c.L.rl), cf.E, nullptr, nullptr, s);
+  }
+  if (t) tap_copy(t->router ? t->router + l * R * E : nullptr, rl, R * E * 4, s);
+  launch_topk(rl, c.R, cf.E, cf.k, at<int32_t>(c, c.L.ids), at<float>(c, c.L.gates), s);
+  if (t) {
+    tap_copy(t->ids ? t->ids + l * R * k : nullptr, at<void>(c, c.L.ids), R * k * 4, s);
+    tap_copy(t->gates ? t->gates + l * R * k : nullptr, at<void>(c, c.L.gates), R * k * 4, s);
+  }
+
+  // permutation and row tiles
+  const int avg = (int)(R * k / E);
+  const bool skinny = avg <= 48;
+  const int tile_rows = skinny ? SKINNY_TILE : FAT_TILE;
+  const int max_tiles = (int)((R * k + tile_rows - 1) / tile_rows) + (int)E;
+  int32_t* counts = c.pass ? at<int32_t>(c, c.L.cov) + l * E : at<int32_t>(c, c.L.counts);
+  launch_plan(at<int32_t>(c, c.L.ids), c.R, cf.k, cf.E, tile_rows, counts, at<int32_t>(c, c.L.offsets),
+              at<int32_t>(c, c.L.perm), at<int32_t>(c, c.L.inv), at<int4>(c, c.L.tiles),
+              at<int32_t>(c, c.L.ntiles), s);
+  if (t) {
+    tap_copy(t->counts ? t->counts + l * E : nullptr, counts, E * 4, s);
+    tap_copy(t->offsets ? t->offsets + l * (E + 1) : nullptr, at<void>(c, c.L.offsets), (E + 1) * 4, s);
+    tap_copy(t->perm ? t->perm + l * R * k : nullptr, at<void>(c, c.L.perm), R * k * 4, s);
+  }
+
+  // experts over the union of the selected ones
+  MoeW mw{w.wg, w.wu, w.wd, w.escale, cf.expert_dtype};
+  if (t && t->ev_gateup && t->ev_gateup[2 * l]) (void)hipEventRecord((hipEvent_t)t->ev_gateup[2 * l], s);
+  if (skinny)
+    launch_gateup_stream(act, at<void>(c, c.L.u2), at<int32_t>(c, c.L.perm), cf.k, mw,
+                         at<int4>(c, c.L.tiles), at<int32_t>(c, c.L.ntiles), max_tiles, cf.D, cf.F,
+                         at<void>(c, c.L.H), s);
+  else
+    launch_gateup_lds(act, at<void>(c, c.L.u2), at<int32_t>(c, c.L.perm), cf.k, mw,
+                      at<int4>(c, c.L.tiles), at<int32_t>(c, c.L.ntiles), max_tiles, cf.D, cf.F,
+                      at<void>(c, c.L.H), s);
+  if (t && t->ev_gateup && t->ev_gateup[2 * l + 1])
+    (void)hipEventRecord((hipEvent_t)t->ev_gateup[2 * l + 1], s);
+  if (t && t->hmid)
+    launch_unpermute(act, at<void>(c, c.L.H), at<int32_t>(c, c.L.inv), (int)(R * k), cf.F,
+                     (char*)t->hmid + l * R * k * cf.F * a, s);
+  if (skinny)
+    launch_down_stream(act, at<void>(c, c.L.H), mw, at<int4>(c, c.L.tiles), at<int32_t>(c, c.L.ntiles),
+                       max_tiles, cf.D, cf.F, at<void>(c, c.L.Y), s);
+  else
+    launch_down_lds(act, at<void>(c, c.L.H), mw, at<int4>(c, c.L.tiles), at<int32_t>(c, c.L.ntiles),
+                    max_tiles, cf.D, cf.F, at<void>(c, c.L.Y), s);
+  if (t && t->yexp)
+    launch_unpermute(act, at<void>(c, c.L.Y), at<int32_t>(c, c.L.inv), (int)(R * k), cf.D,
+                     (char*)t->yexp + l * R * k * D * a, s);
+
+  // x = x1 + sum_j g_j y_j; u = next norm
+  launch_combine_norm(act, at<void>(c, c.L.x1), at<void>(c, c.L.Y), at<float>(c, c.L.gates),
+                      at<int32_t>(c, c.L.inv), c.R, cf.k, cf.D, gnext, cf.eps, at<void>(c, c.L.x),
+                      at<void>(c, c.L.u), s);
+  if (t) tap_copy(t->xout ? (char*)t->xout + l * R * D * a : nullptr, at<void>(c, c.L.x), R * D * a, s);
+}
+
+dg_status check_hip() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? DG_OK : DG_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dg_status_str(dg_status s) {
+  switch (s) {
+    case DG_OK: return "ok";
+    case DG_ERR_INVALID: return "invalid argument";
+    case DG_ERR_CAPACITY: return "KV cache capacity exceeded";
+    case DG_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case DG_ERR_WORKSPACE: return "workspace too small";
+    case DG_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+dg_status dg_model_init(dg_model* m, const dg_config* cfg, const dg_weights* w) {
+  if (!m || !valid_cfg(cfg) || !w) return DG_ERR_INVALID;
+  dg_status st = supported_cfg(cfg);
+  if (st != DG_OK) return st;
+  if (!w->emb || !w->gf || !w->lm) return DG_ERR_INVALID;
+  for (int l = 0; l < cfg->L; l++) {
+    const dg_layer_weights& x = w->layers[l];
+    if (!x.g1 || !x.wq || !x.wk || !x.wv || !x.wo || !x.g2 || !x.wr || !x.wg || !x.wu || !x.wd)
+      return DG_ERR_INVALID;
+    if ((cfg->expert_dtype == DG_FP8E4M3) != (x.escale != nullptr)) return DG_ERR_INVALID;
+  }
+  memset(m, 0, sizeof(*m));
+  m->cfg = *cfg;
+  m->w = *w;
+  m->magic = MODEL_MAGIC;
+  return DG_OK;
+}
+
+size_t dg_workspace_bytes(const dg_config* cfg, int32_t max_rows, int32_t max_keys) {
+  if (!valid_cfg(cfg) || max_rows < 1 || max_keys < 0) return 0;
+  return layout(*cfg, max_rows).total;
+}
+
+dg_status dg_kv_prefill(const dg_model* m, dg_kv* kv, const int32_t* tokens, int32_t B, int32_t T,
+                        const dg_taps* taps, void* ws, size_t ws_bytes, void* stream) {
+  if (!model_ok(m) || !kv || !kv->len || !tokens || !ws) return DG_ERR_INVALID;
+  if (B < 1 || B > DG_MAX_BATCH || T < 1 || kv->cap < 1) return DG_ERR_INVALID;
+  const dg_config& cf = m->cfg;
+  for (int l = 0; l < cf.L; l++)
+    if (!kv->k[l] || !kv->v[l]) return DG_ERR_INVALID;
+  Lens lens{};
+  for (int b = 0; b < B; b++) {
+    if (kv->len[b] < 0 || kv->len[b] > kv->cap) return DG_ERR_INVALID;
+    if ((long)kv->len[b] + T > kv->cap) return DG_ERR_CAPACITY;
+    lens.v[b] = kv->len[b];
+  }
+  if ((long)B * T > (1L << 20)) return DG_ERR_UNSUPPORTED;
+  const int R = B * T;
+  Ctx c{m, (char*)ws, layout(cf, R), R, taps, (hipStream_t)stream, false};
+  if (c.L.total > ws_bytes) return DG_ERR_WORKSPACE;
+
+  (void)hipGetLastError();  // clear a stale error so the status below is ours
+  const int act = cf.act_dtype == DG_BF16 ? ACT_BF16 : ACT_F32;
+  const size_t a = esize(cf.act_dtype);
+  const int QD = cf.Hq * cf.hd, KD = cf.Hkv * cf.hd, QKV = QD + 2 * KD;
+  hipStream_t s = c.s;
+  launch_embed_norm(act, tokens, m->w.emb, m->w.layers[0].g1, R, cf.D, cf.V, cf.eps, at<void>(c, c.L.x),
+                    at<void>(c, c.L.u), s);
+  for (int l = 0; l < cf.L; l++) {
+    const dg_layer_weights& w = m->w.layers[l];
+    CacheDst cd{kv->k[l], kv->v[l], kv->cap, T, QD, KD, cf.hd, cf.Hkv, lens};
+    launch_gemm(act, GEMM_QKV_CACHE, at<void>(c, c.L.u), R, cf.D, w.wq, QD, w.wk, KD, w.wv, QKV,
+                at<void>(c, c.L.qkv), QKV, nullptr, &cd, s);
+    if (taps) tap_copy(taps->qkv ? (char*)taps->qkv + (size_t)l * R * QKV * a : nullptr,
+                       at<void>(c, c.L.qkv), (size_t)R * QKV * a, s);
+    if (l == cf.L - 1) break;  // nothing downstream reads the last layer's output
+    AttnArgsHost ah{act, at<void>(c, c.L.qkv), QKV, kv->k[l], kv->v[l], kv->cap, nullptr, nullptr,
+                    B, T, cf.Hq, cf.Hkv, cf.hd, 1, lens, at<void>(c, c.L.o), at<float>(c, c.L.po),
+                    at<float>(c, c.L.pml), c.L.part_cap};
+    launch_attention(ah, s);
+    if (taps) tap_copy(taps->attn ? (char*)taps->attn + (size_t)l * R * QD * a : nullptr,
+                       at<void>(c, c.L.o), (size_t)R * QD * a, s);
+    moe_block(c, l, m->w.layers[l + 1].g1);
+  }
+  dg_status st = check_hip();
+  if (st != DG_OK) return st;
+  for (int b = 0; b < B; b++) kv->len[b] += T;
+  return DG_OK;
+}
+
+dg_status dg_denoise_pass(const dg_model* m, const dg_kv* kv, const int32_t* canvas, int32_t B,
+                          int32_t N, int32_t* argmax, float* conf, const dg_taps* taps, void* ws,
+                          size_t ws_bytes, void* stream) {
+  if (!model_ok(m) || !kv || !kv->len || !canvas || !argmax || !conf || !ws) return DG_ERR_INVALID;
+  if (B < 1 || B > DG_MAX_BATCH || N < 1) return DG_ERR_INVALID;
+  const dg_config& cf = m->cfg;
+  Lens lens{};
+  bool any_prefix = false;
+  for (int b = 0; b < B; b++) {
+    if (kv->len[b] < 0 || (kv->len[b] > 0 && kv->len[b] > kv->cap)) return DG_ERR_INVALID;
+    lens.v[b] = kv->len[b];
+    any_prefix |= kv->len[b] > 0;
+  }
+  if (any_prefix)
+    for (int l = 0; l < cf.L; l++)
+      if (!kv->k[l] || !kv->v[l]) return DG_ERR_INVALID;
+  if ((long)B * N > (1L << 20)) return DG_ERR_UNSUPPORTED;
+  const int R = B * N;
+  Ctx c{m, (char*)ws, layout(cf, R), R, taps, (hipStream_t)stream, true};
+  if (c.L.total > ws_bytes) return DG_ERR_WORKSPACE;
+
+  (void)hipGetLastError();
+  const int act = cf.act_dtype == DG_BF16 ? ACT_BF16 : ACT_F32;
+  const size_t a = esize(cf.act_dtype);
+  const int QD = cf.Hq * cf.hd, KD = cf.Hkv * cf.hd, QKV = QD + 2 * KD;
+  hipStream_t s = c.s;
+  launch_embed_norm(act, canvas, m->w.emb, m->w.layers[0].g1, R, cf.D, cf.V, cf.eps, at<void>(c, c.L.x),
+                    at<void>(c, c.L.u), s);
+  for (int l = 0; l < cf.L; l++) {
+    const dg_layer_weights& w = m->w.layers[l];
+    launch_gemm(act, GEMM_STORE, at<void>(c, c.L.u), R, cf.D, w.wq, QD, w.wk, KD, w.wv, QKV,
+                at<void>(c, c.L.qkv), QKV, nullptr, nullptr, s);
+    if (taps) tap_copy(taps->qkv ? (char*)taps->qkv + (size_t)l * R * QKV * a : nullptr,
+                       at<void>(c, c.L.qkv), (size_t)R * QKV * a, s);
+    const char* qkv = at<char>(c, c.L.qkv);
+    AttnArgsHost ah{act, qkv, QKV, kv->k[l], kv->v[l], kv->cap, qkv + QD * a, qkv + (QD + KD) * a,
+                    B, N, cf.Hq, cf.Hkv, cf.hd, 0, lens, at<void>(c, c.L.o), at<float>(c, c.L.po),
+                    at<float>(c, c.L.pml), c.L.part_cap};
+    launch_attention(ah, s);
+    if (taps) tap_copy(taps->attn ? (char*)taps->attn + (size_t)l * R * QD * a : nullptr,
+                       at<void>(c, c.L.o), (size_t)R * QD * a, s);
+    moe_block(c, l, l + 1 < cf.L ? m->w.layers[l + 1].g1 : m->w.gf);
+  }
+  // head: logits tiles reduced to (max, argmax, sum exp), merged per row
+  launch_lmhead(act, at<void>(c, c.L.u), R, cf.D, m->w.lm, cf.V, at<float>(c, c.L.lpm),
+                at<int32_t>(c, c.L.lpi), at<float>(c, c.L.lps), taps ? taps->logits : nullptr, s);
+  if (taps) tap_copy(taps->uf, at<void>(c, c.L.u), (size_t)R * cf.D * a, s);
+  launch_lm_merge(at<float>(c, c.L.lpm), at<int32_t>(c, c.L.lpi), at<float>(c, c.L.lps), R,
+                  lm_tiles(cf.V), argmax, conf, s);
+  return check_hip();
+}
+
+dg_status dg_renoise(int32_t* canvas, const int32_t* argmax, const float* conf, float tau,
+                     uint64_t seed, uint32_t pass_tag, const int32_t* pos0, const uint32_t* req_id,
+                     int32_t B, int32_t N, int32_t V, void* stream) {
+  if (!canvas || !pos0 || B < 1 || B > DG_MAX_BATCH || N < 1 || V < 1) return DG_ERR_INVALID;
+  if (conf && !argmax) return DG_ERR_INVALID;
+  Lens p{};
+  ReqIds r{};
+  for (int b = 0; b < B; b++) {
+    if (pos0[b] < 0) return DG_ERR_INVALID;
+    p.v[b] = pos0[b];
+    r.v[b] = req_id ? req_id[b] : (uint32_t)b;
+  }
+  (void)hipGetLastError();
+  launch_renoise(canvas, argmax, conf, tau, seed, pass_tag, p, r, B, N, V, (hipStream_t)stream);
+  return check_hip();
+}
+
+dg_status dg_expert_coverage(const dg_model* m, const void* ws, size_t ws_bytes, int32_t* touched,
+                             int32_t* counts, void* stream) {
+  if (!model_ok(m) || !ws || !touched) return DG_ERR_INVALID;
+  if ((size_t)m->cfg.L * m->cfg.E * 4 > ws_bytes) return DG_ERR_WORKSPACE;
+  (void)hipGetLastError();
+  launch_coverage((const int32_t*)ws, m->cfg.L, m->cfg.E, touched, counts, (hipStream_t)stream);
+  return check_hip();
+}
+
+}  // extern "C"

@@ -1,0 +1,260 @@
+// kern_elem.hip -- embedding + RMSNorm, combine + RMSNorm, re-noise, coverage,
+// tap un-permute and the LM-head partial merge.
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace dg {
+
+// x[row] = emb[tok[row]] (copied), u[row] = round(x * rsqrt(mean(x^2)+eps) * g)
+// (token ids outside [0, V) are clamped into range rather than read out of bounds)
+template <typename TA>
+__global__ __launch_bounds__(256) void embed_norm_k(const int32_t* __restrict__ tok,
+                                                    const TA* __restrict__ emb,
+                                                    const float* __restrict__ g, int D, int V,
+                                                    float eps, TA* __restrict__ x,
+                                                    TA* __restrict__ u) {
+  __shared__ float red[4];
+  const size_t row = blockIdx.x;
+  const int tk = min(max(tok[row], 0), V - 1);
+  const TA* src = emb + (size_t)tk * D;
+  float ss = 0.f;
+  for (int d = threadIdx.x; d < D; d += 256) {
+    float v = ldx(src, d);
+    ss += v * v;
+    x[row * D + d] = src[d];
+  }
+  ss = block_sum256(ss, red);
+  const float r = rsqrtf(ss / (float)D + eps);
+  for (int d = threadIdx.x; d < D; d += 256) stx(u, row * D + d, ldx(src, d) * r * g[d]);
+}
+
+template <typename TA>
+__global__ __launch_bounds__(256) void rmsnorm_k(const TA* __restrict__ x, const float* __restrict__ g,
+                                                 int D, float eps, TA* __restrict__ u) {
+  __shared__ float red[4];
+  const size_t row = blockIdx.x;
+  float ss = 0.f;
+  for (int d = threadIdx.x; d < D; d += 256) {
+    float v = ldx(x, row * D + d);
+    ss += v * v;
+  }
+  ss = block_sum256(ss, red);
+  const float r = rsqrtf(ss / (float)D + eps);
+  for (int d = threadIdx.x; d < D; d += 256) stx(u, row * D + d, ldx(x, row * D + d) * r * g[d]);
+}
+
+// x = round(x1 + sum_j g_j y_j) in slot order j; u = round(rmsnorm(x) * gnext)
+template <typename TA>
+__global__ __launch_bounds__(256) void combine_norm_k(const TA* __restrict__ x1,
+                                                      const TA* __restrict__ Y,
+                                                      const float* __restrict__ gates,
+                                                      const int32_t* __restrict__ inv, int k, int D,
+                                                      const float* __restrict__ gnext, float eps,
+                                                      TA* __restrict__ x, TA* __restrict__ u) {
+  __shared__ float red[4];
+  __shared__ float gs[8];
+  __shared__ int32_t rs[8];
+  const size_t row = blockIdx.x;
+  if (threadIdx.x < k) {
+    gs[threadIdx.x] = gates[row * k + threadIdx.x];
+    rs[threadIdx.x] = inv[row * k + threadIdx.x];
+  }
+  __syncthreads();
+  float ss = 0.f;
+  for (int d = threadIdx.x; d < D; d += 256) {
+    float mix = 0.f;
+    for (int j = 0; j < k; j++) mix += gs[j] * ldx(Y, (size_t)rs[j] * D + d);
+    float v = rnd(ldx(x1, row * D + d) + mix, x);
+    stx(x, row * D + d, v);
+    ss += v * v;
+  }
+  ss = block_sum256(ss, red);
+  const float r = rsqrtf(ss / (float)D + eps);
+  for (int d = threadIdx.x; d < D; d += 256) stx(u, row * D + d, ldx(x, row * D + d) * r * gnext[d]);
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC'11): per round the counter
+// words 0 and 2 are multiplied by the round constants; high halves are xored
+// with the other words and the key, which is bumped by two Weyl constants.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; r++) {
+    if (r) {
+      k0 += W0;
+      k1 += W1;
+    }
+    const uint64_t hi0 = __umul64hi(M0, c[0]), lo0 = M0 * c[0];
+    const uint64_t hi1 = __umul64hi(M1, c[2]), lo1 = M1 * c[2];
+    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+  }
+}
+
+struct RenoiseArgs {
+  int32_t* canvas;
+  const int32_t* argmax;
+  const float* conf;
+  float tau;
+  uint64_t seed;
+  uint32_t tag;
+  int B, N;
+  uint32_t V;
+  Lens pos0;
+  ReqIds req;
+};
+
+__global__ __launch_bounds__(256) void renoise_k(RenoiseArgs a) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= a.B * a.N) return;
+  const int b = idx / a.N, i = idx % a.N;
+  if (a.conf && a.conf[idx] >= a.tau) {  // NaN compares false: noised
+    a.canvas[idx] = a.argmax[idx];
+    return;
+  }
+  uint64_t c[4] = {(uint64_t)(int64_t)(a.pos0.v[b] + i), (uint64_t)a.tag, (uint64_t)a.req.v[b], 0};
+  philox4x64_10(c, a.seed, 0);
+  a.canvas[idx] = (int32_t)__umul64hi(c[0], (uint64_t)a.V);  // floor(r * V / 2^64)
+}
+
+__global__ __launch_bounds__(256) void coverage_k(const int32_t* __restrict__ counts, int E,
+                                                  int32_t* __restrict__ touched,
+                                                  int32_t* __restrict__ counts_out) {
+  __shared__ int red[4];
+  const int l = blockIdx.x;
+  int t = 0;
+  for (int e = threadIdx.x; e < E; e += 256) {
+    int c = counts[l * E + e];
+    t += c > 0;
+    if (counts_out) counts_out[l * E + e] = c;
+  }
+  for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = t;
+  __syncthreads();
+  if (threadIdx.x == 0) touched[l] = red[0] + red[1] + red[2] + red[3];
+}
+
+// dst[slot][c] = src[inv[slot]][c]
+template <typename TA>
+__global__ __launch_bounds__(256) void unpermute_k(const TA* __restrict__ src,
+                                                   const int32_t* __restrict__ inv, int C,
+                                                   TA* __restrict__ dst) {
+  const size_t slot = blockIdx.x;
+  const size_t r = inv[slot];
+  for (int c = threadIdx.x; c < C; c += 256) dst[slot * C + c] = src[r * C + c];
+}
+
+// Merge per-tile (max, argmax, sum exp(l - max)) in vocabulary order: the
+// global maximum, the lowest index attaining it, conf = 1 / sum exp(l - max).
+__device__ __forceinline__ void merge3(float& m, int& i, float& s, float m2, int i2, float s2) {
+  if (m2 == -INFINITY) return;  // empty partial
+  if (m2 > m || (m2 == m && i2 < i)) {
+    s = s * __expf(m - m2) + s2;
+    m = m2;
+    i = i2;
+  } else {
+    s = s + s2 * __expf(m2 - m);
+  }
+}
+
+__global__ __launch_bounds__(256) void lm_merge_k(const float* __restrict__ pmax,
+                                                  const int32_t* __restrict__ pidx,
+                                                  const float* __restrict__ psum, int ntiles,
+                                                  int32_t* __restrict__ argmax,
+                                                  float* __restrict__ conf) {
+  __shared__ float sm[4], ss[4];
+  __shared__ int si[4];
+  const size_t row = blockIdx.x;
+  float m = -INFINITY, s = 0.f;
+  int i = 0x7fffffff;
+  for (int t = threadIdx.x; t < ntiles; t += 256)
+    merge3(m, i, s, pmax[row * ntiles + t], pidx[row * ntiles + t], psum[row * ntiles + t]);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+    int i2 = __shfl_xor(i, o, 64);
+    merge3(m, i, s, m2, i2, s2);
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sm[w] = m;
+    ss[w] = s;
+    si[w] = i;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = sm[0];
+    s = ss[0];
+    i = si[0];
+    for (int q = 1; q < 4; q++) merge3(m, i, s, sm[q], si[q], ss[q]);
+    argmax[row] = i;
+    conf[row] = 1.f / s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+void launch_embed_norm(int act, const int32_t* tok, const void* emb, const float* g, int rows, int D,
+                       int V, float eps, void* x, void* u, hipStream_t s) {
+  if (act == ACT_BF16)
+    embed_norm_k<uint16_t><<<rows, 256, 0, s>>>(tok, (const uint16_t*)emb, g, D, V, eps,
+                                                 (uint16_t*)x, (uint16_t*)u);
+  else
+    embed_norm_k<float><<<rows, 256, 0, s>>>(tok, (const float*)emb, g, D, V, eps, (float*)x,
+                                              (float*)u);
+}
+
+void launch_rmsnorm(int act, const void* x, const float* g, int rows, int D, float eps, void* u,
+                    hipStream_t s) {
+  if (act == ACT_BF16)
+    rmsnorm_k<uint16_t><<<rows, 256, 0, s>>>((const uint16_t*)x, g, D, eps, (uint16_t*)u);
+  else
+    rmsnorm_k<float><<<rows, 256, 0, s>>>((const float*)x, g, D, eps, (float*)u);
+}
+
+void launch_combine_norm(int act, const void* x1, const void* Y, const float* gates,
+                         const int32_t* inv, int rows, int k, int D, const float* gnext, float eps,
+                         void* x, void* u, hipStream_t s) {
+  if (act == ACT_BF16)
+    combine_norm_k<uint16_t><<<rows, 256, 0, s>>>((const uint16_t*)x1, (const uint16_t*)Y, gates,
+                                                   inv, k, D, gnext, eps, (uint16_t*)x, (uint16_t*)u);
+  else
+    combine_norm_k<float><<<rows, 256, 0, s>>>((const float*)x1, (const float*)Y, gates, inv, k, D,
+                                                gnext, eps, (float*)x, (float*)u);
+}
+
+void launch_renoise(int32_t* canvas, const int32_t* argmax, const float* conf, float tau,
+                    uint64_t seed, uint32_t tag, const Lens& pos0, const ReqIds& req, int B, int N,
+                    int V, hipStream_t s) {
+  RenoiseArgs a{canvas, argmax, conf, tau, seed, tag, B, N, (uint32_t)V, pos0, req};
+  const int n = B * N;
+  if (n == 0) return;
+  renoise_k<<<(n + 255) / 256, 256, 0, s>>>(a);
+}
+
+void launch_coverage(const int32_t* counts, int L, int E, int32_t* touched, int32_t* counts_out,
+                     hipStream_t s) {
+  coverage_k<<<L, 256, 0, s>>>(counts, E, touched, counts_out);
+}
+
+void launch_unpermute(int act, const void* src, const int32_t* inv, int slots, int C, void* dst,
+                      hipStream_t s) {
+  if (act == ACT_BF16)
+    unpermute_k<uint16_t><<<slots, 256, 0, s>>>((const uint16_t*)src, inv, C, (uint16_t*)dst);
+  else
+    unpermute_k<float><<<slots, 256, 0, s>>>((const float*)src, inv, C, (float*)dst);
+}
+
+void launch_lm_merge(const float* pmax, const int32_t* pidx, const float* psum, int rows,
+                     int ntiles, int32_t* argmax, float* conf, hipStream_t s) {
+  lm_merge_k<<<rows, 256, 0, s>>>(pmax, pidx, psum, ntiles, argmax, conf);
+}
+
+}  // namespace dg

@@ -1,0 +1,431 @@
+// kern_gemm.hip -- LDS-tiled MFMA GEMM C = A . B^T for the dense projections,
+// the grouped expert GEMMs when many rows route to each expert, and the LM
+// head with a fused per-row (max, argmax, sum exp) epilogue.
+//
+// Block: 256 threads = 4 waves in a 2 x 2 grid over a BM x BN output tile.
+// Contraction tiles of 128 bytes per row (64 bf16 or 32 fp32 elements) are
+// staged through LDS with a register prefetch of the next tile (double
+// buffer); fp8 weights are decoded to bf16 on the way into LDS.  LDS rows are
+// padded to 144 bytes so the 16 rows a fragment read touches fall in distinct
+// banks.
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace dg {
+
+template <typename TA, typename TW, int BM, int BN>
+struct Mainloop {
+  static constexpr int BK = 128 / (int)sizeof(TA);            // elements per staged row
+  static constexpr int LDK = 144 / (int)sizeof(TA);           // padded LDS row (elements)
+  static constexpr bool FP8 = sizeof(TW) == 1;
+  static constexpr int A_LD = BM / 32;                         // 16-byte A chunks per thread
+  static constexpr int B_ROWS_PER_PASS = FP8 ? 64 : 32;        // rows covered by 256 threads
+  static constexpr int B_LD = BN / B_ROWS_PER_PASS;
+  static constexpr int RT = BM / 32, CT = BN / 32;             // 16x16 tiles per wave
+  static constexpr int SMEM = 2 * (BM + BN) * LDK;             // elements of TA
+  typedef typename FragOf<TA>::type Frag;
+
+  // thread -> chunk assignment
+  static __device__ __forceinline__ int a_row(int p) { return (threadIdx.x >> 3) + 32 * p; }
+  static __device__ __forceinline__ int a_col() { return (threadIdx.x & 7) * (16 / (int)sizeof(TA)); }
+  static __device__ __forceinline__ int b_row(int p) {
+    return FP8 ? (threadIdx.x >> 2) + 64 * p : (threadIdx.x >> 3) + 32 * p;
+  }
+  static __device__ __forceinline__ int b_col() {
+    return FP8 ? (threadIdx.x & 3) * 16 : (threadIdx.x & 7) * (16 / (int)sizeof(TA));
+  }
+
+  // ap[p] / bp[p]: row pointers of the rows this thread stages (nullptr = zero row)
+  static __device__ __forceinline__ void run(const TA* const (&ap)[A_LD], const TW* const (&bp)[B_LD],
+                                             int K, TA* smem, f32x4_t (&acc)[RT][CT]) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int wm = w >> 1, wn = w & 1, l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+      for (int ct = 0; ct < CT; ct++) acc[rt][ct] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+    uint4 ra[A_LD], rb[B_LD];
+    const int nk = K / BK;
+    auto gload = [&](int kt) {
+      const int k0 = kt * BK;
+#pragma unroll
+      for (int p = 0; p < A_LD; p++)
+        ra[p] = ap[p] ? *reinterpret_cast<const uint4*>(ap[p] + k0 + a_col()) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int p = 0; p < B_LD; p++)
+        rb[p] = bp[p] ? *reinterpret_cast<const uint4*>(bp[p] + k0 + b_col()) : make_uint4(0, 0, 0, 0);
+    };
+    auto sstore = [&](int buf) {
+      TA* sa = smem + buf * (BM + BN) * LDK;
+      TA* sb = sa + BM * LDK;
+#pragma unroll
+      for (int p = 0; p < A_LD; p++) *reinterpret_cast<uint4*>(sa + a_row(p) * LDK + a_col()) = ra[p];
+#pragma unroll
+      for (int p = 0; p < B_LD; p++) {
+        if (FP8) {
+          uint4 lo = fp8x8_to_bf16x8(make_uint2(rb[p].x, rb[p].y));
+          uint4 hi = fp8x8_to_bf16x8(make_uint2(rb[p].z, rb[p].w));
+          *reinterpret_cast<uint4*>(sb + b_row(p) * LDK + b_col()) = lo;
+          *reinterpret_cast<uint4*>(sb + b_row(p) * LDK + b_col() + 8) = hi;
+        } else {
+          *reinterpret_cast<uint4*>(sb + b_row(p) * LDK + b_col()) = rb[p];
+        }
+      }
+    };
+
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt++) {
+      if (kt + 1 < nk) gload(kt + 1);
+      const TA* sa = smem + (kt & 1) * (BM + BN) * LDK;
+      const TA* sb = sa + BM * LDK;
+#pragma unroll
+      for (int ks = 0; ks < BK / 32; ks++) {
+        Frag af[RT], bf[CT];
+#pragma unroll
+        for (int rt = 0; rt < RT; rt++)
+          load_frag(af[rt], sa + (wm * (BM / 2) + 16 * rt + l16) * LDK + 32 * ks + 8 * g);
+#pragma unroll
+        for (int ct = 0; ct < CT; ct++)
+          load_frag(bf[ct], sb + (wn * (BN / 2) + 16 * ct + l16) * LDK + 32 * ks + 8 * g);
+#pragma unroll
+        for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+          for (int ct = 0; ct < CT; ct++) mma(acc[rt][ct], af[rt], bf[ct]);
+      }
+      if (kt + 1 < nk) sstore((kt + 1) & 1);
+      __syncthreads();
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// dense GEMM with epilogues
+// ---------------------------------------------------------------------------
+struct DenseArgs {
+  const void* A;
+  int M, K;
+  const void* B0;
+  int n1;
+  const void* B1;
+  int n2;
+  const void* B2;
+  int N;
+  void* C;
+  int ldc;
+  const void* R;
+  int mode;
+  CacheDst cache;
+};
+
+template <typename TA, int BM, int BN>
+__global__ __launch_bounds__(256) void gemm_dense_k(DenseArgs a) {
+  typedef Mainloop<TA, TA, BM, BN> ML;
+  __shared__ __attribute__((aligned(16))) TA smem[ML::SMEM];
+  const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
+  const TA* ap[ML::A_LD];
+  const TA* bp[ML::B_LD];
+#pragma unroll
+  for (int p = 0; p < ML::A_LD; p++) {
+    const int r = m0 + ML::a_row(p);
+    ap[p] = r < a.M ? (const TA*)a.A + (size_t)r * a.K : nullptr;
+  }
+#pragma unroll
+  for (int p = 0; p < ML::B_LD; p++) {
+    const int n = n0 + ML::b_row(p);
+    const TA* q = nullptr;
+    if (n < a.n1) q = (const TA*)a.B0 + (size_t)n * a.K;
+    else if (n < a.n1 + a.n2) q = (const TA*)a.B1 + (size_t)(n - a.n1) * a.K;
+    else if (n < a.N) q = (const TA*)a.B2 + (size_t)(n - a.n1 - a.n2) * a.K;
+    bp[p] = q;
+  }
+  f32x4_t acc[ML::RT][ML::CT];
+  ML::run(ap, bp, a.K, smem, acc);
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w >> 1, wn = w & 1, l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int rt = 0; rt < ML::RT; rt++)
+#pragma unroll
+    for (int ct = 0; ct < ML::CT; ct++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int r = m0 + wm * (BM / 2) + 16 * rt + 4 * g + i;
+        const int n = n0 + wn * (BN / 2) + 16 * ct + l16;
+        if (r >= a.M || n >= a.N) continue;
+        float v = acc[rt][ct][i];
+        const size_t o = (size_t)r * a.ldc + n;
+        if (a.mode == GEMM_F32) {
+          ((float*)a.C)[o] = v;
+          continue;
+        }
+        if (a.mode == GEMM_RESID) v += ldx((const TA*)a.R, o);
+        stx((TA*)a.C, o, v);
+        if (a.mode == GEMM_QKV_CACHE && n >= a.cache.QD) {
+          // new key / value of token (b, i) goes to cache position len[b] + i
+          const int c = n - a.cache.QD;
+          const bool isv = c >= a.cache.KD;
+          const int cc = isv ? c - a.cache.KD : c;
+          const int gh = cc / a.cache.hd, d = cc % a.cache.hd;
+          const int b = r / a.cache.T, t = r % a.cache.T;
+          const size_t co = (((size_t)b * a.cache.Hkv + gh) * a.cache.cap + a.cache.len.v[b] + t) *
+                                a.cache.hd + d;
+          stx((TA*)(isv ? a.cache.v : a.cache.k), co, v);
+        }
+      }
+}
+
+// ---------------------------------------------------------------------------
+// grouped expert GEMMs over row tiles (expert, first permuted row, rows)
+// ---------------------------------------------------------------------------
+struct GroupArgs {
+  const void* A;
+  const int32_t* perm;
+  int k;
+  const void* W1;
+  const void* W2;
+  const float* escale;
+  const int4* tiles;
+  const int32_t* ntiles;
+  int K, NW, ldo;
+  void* out;
+};
+
+// gate/up: BN weight rows = BN/2 SwiGLU outputs, rows ordered in 32-row
+// groups [gate f..f+15, up f..f+15] so each wave holds matching gate and up tiles.
+template <typename TA, typename TW, int BM, int BN>
+__global__ __launch_bounds__(256) void gateup_lds_k(GroupArgs a) {
+  typedef Mainloop<TA, TW, BM, BN> ML;
+  __shared__ __attribute__((aligned(16))) TA smem[ML::SMEM];
+  const int tile_id = blockIdx.x;
+  if (tile_id >= *a.ntiles) return;
+  const int4 tl = a.tiles[tile_id];
+  const int e = tl.x, row0 = tl.y, nrows = tl.z;
+  const int f0 = blockIdx.y * (BN / 2);
+  const TA* ap[ML::A_LD];
+  const TW* bp[ML::B_LD];
+#pragma unroll
+  for (int p = 0; p < ML::A_LD; p++) {
+    const int r = ML::a_row(p);
+    ap[p] = r < nrows ? (const TA*)a.A + (size_t)(a.perm[row0 + r] / a.k) * a.K : nullptr;
+  }
+#pragma unroll
+  for (int p = 0; p < ML::B_LD; p++) {
+    const int n = ML::b_row(p);
+    const int f = f0 + 16 * (n >> 5) + (n & 15);
+    const TW* base = (const TW*)(((n >> 4) & 1) ? a.W2 : a.W1);
+    bp[p] = base + ((size_t)e * a.NW + f) * a.K;
+  }
+  f32x4_t acc[ML::RT][ML::CT];
+  ML::run(ap, bp, a.K, smem, acc);
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w >> 1, wn = w & 1, l16 = lane & 15, g = lane >> 4;
+  float sg = 1.f, su = 1.f;
+  if (a.escale) {
+    sg = a.escale[e * 3 + 0];
+    su = a.escale[e * 3 + 1];
+  }
+#pragma unroll
+  for (int rt = 0; rt < ML::RT; rt++)
+#pragma unroll
+    for (int p = 0; p < ML::CT / 2; p++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int r = wm * (BM / 2) + 16 * rt + 4 * g + i;
+        if (r >= nrows) continue;
+        const float gv = acc[rt][2 * p][i] * sg, uv = acc[rt][2 * p + 1][i] * su;
+        const int f = f0 + wn * (BN / 4) + 16 * p + l16;
+        stx((TA*)a.out, (size_t)(row0 + r) * a.ldo + f, gv / (1.f + expf(-gv)) * uv);
+      }
+}
+
+template <typename TA, typename TW, int BM, int BN>
+__global__ __launch_bounds__(256) void down_lds_k(GroupArgs a) {
+  typedef Mainloop<TA, TW, BM, BN> ML;
+  __shared__ __attribute__((aligned(16))) TA smem[ML::SMEM];
+  const int tile_id = blockIdx.x;
+  if (tile_id >= *a.ntiles) return;
+  const int4 tl = a.tiles[tile_id];
+  const int e = tl.x, row0 = tl.y, nrows = tl.z;
+  const int n0 = blockIdx.y * BN;
+  const TA* ap[ML::A_LD];
+  const TW* bp[ML::B_LD];
+#pragma unroll
+  for (int p = 0; p < ML::A_LD; p++) {
+    const int r = ML::a_row(p);
+    ap[p] = r < nrows ? (const TA*)a.A + (size_t)(row0 + r) * a.K : nullptr;
+  }
+#pragma unroll
+  for (int p = 0; p < ML::B_LD; p++)
+    bp[p] = (const TW*)a.W1 + ((size_t)e * a.NW + n0 + ML::b_row(p)) * a.K;
+  f32x4_t acc[ML::RT][ML::CT];
+  ML::run(ap, bp, a.K, smem, acc);
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w >> 1, wn = w & 1, l16 = lane & 15, g = lane >> 4;
+  const float sd = a.escale ? a.escale[e * 3 + 2] : 1.f;
+#pragma unroll
+  for (int rt = 0; rt < ML::RT; rt++)
+#pragma unroll
+    for (int ct = 0; ct < ML::CT; ct++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int r = wm * (BM / 2) + 16 * rt + 4 * g + i;
+        if (r >= nrows) continue;
+        const int n = n0 + wn * (BN / 2) + 16 * ct + l16;
+        stx((TA*)a.out, (size_t)(row0 + r) * a.ldo + n, acc[rt][ct][i] * sd);
+      }
+}
+
+// ---------------------------------------------------------------------------
+// LM head: logits tile [BM rows x 128 vocabulary], reduced per row to
+// (max, lowest index attaining it, sum exp(l - max)); logits never stored
+// unless the debug tap asks for them.
+// ---------------------------------------------------------------------------
+struct HeadArgs {
+  const void* A;
+  int M, K;
+  const void* B;
+  int V;
+  float* pmax;
+  int32_t* pidx;
+  float* psum;
+  float* logits;
+  int ntiles;
+};
+
+__device__ __forceinline__ void mrg(float& m, int& i, float& s, float m2, int i2, float s2) {
+  if (m2 == -INFINITY) return;
+  if (m2 > m || (m2 == m && i2 < i)) {
+    s = s * __expf(m - m2) + s2;
+    m = m2;
+    i = i2;
+  } else {
+    s = s + s2 * __expf(m2 - m);
+  }
+}
+
+template <typename TA, int BM>
+__global__ __launch_bounds__(256) void lmhead_k(HeadArgs a) {
+  constexpr int BN = 128;
+  typedef Mainloop<TA, TA, BM, BN> ML;
+  __shared__ __attribute__((aligned(16))) TA smem[ML::SMEM];
+  __shared__ float xm[2][BM], xs[2][BM];
+  __shared__ int xi[2][BM];
+  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+  const TA* ap[ML::A_LD];
+  const TA* bp[ML::B_LD];
+#pragma unroll
+  for (int p = 0; p < ML::A_LD; p++) {
+    const int r = m0 + ML::a_row(p);
+    ap[p] = r < a.M ? (const TA*)a.A + (size_t)r * a.K : nullptr;
+  }
+#pragma unroll
+  for (int p = 0; p < ML::B_LD; p++) {
+    const int n = n0 + ML::b_row(p);
+    bp[p] = n < a.V ? (const TA*)a.B + (size_t)n * a.K : nullptr;
+  }
+  f32x4_t acc[ML::RT][ML::CT];
+  ML::run(ap, bp, a.K, smem, acc);
+
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w >> 1, wn = w & 1, l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int rt = 0; rt < ML::RT; rt++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int rl = wm * (BM / 2) + 16 * rt + 4 * g + i;
+      const int r = m0 + rl;
+      float m = -INFINITY, s = 0.f;
+      int idx = 0x7fffffff;
+#pragma unroll
+      for (int ct = 0; ct < ML::CT; ct++) {
+        const int n = n0 + wn * (BN / 2) + 16 * ct + l16;
+        const float v = n < a.V ? acc[rt][ct][i] : -INFINITY;
+        if (a.logits && r < a.M && n < a.V) a.logits[(size_t)r * a.V + n] = v;
+        mrg(m, idx, s, v, n, 1.f);
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+        const int i2 = __shfl_xor(idx, o, 64);
+        mrg(m, idx, s, m2, i2, s2);
+      }
+      if (l16 == 0) {
+        xm[wn][rl] = m;
+        xs[wn][rl] = s;
+        xi[wn][rl] = idx;
+      }
+    }
+  __syncthreads();
+  for (int rl = threadIdx.x; rl < BM; rl += 256) {
+    const int r = m0 + rl;
+    if (r >= a.M) continue;
+    float m = xm[0][rl], s = xs[0][rl];
+    int idx = xi[0][rl];
+    mrg(m, idx, s, xm[1][rl], xi[1][rl], xs[1][rl]);
+    const size_t o = (size_t)r * a.ntiles + blockIdx.x;
+    a.pmax[o] = m;
+    a.pidx[o] = idx;
+    a.psum[o] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+void launch_gemm(int act, int mode, const void* A, int M, int K, const void* B0, int n1,
+                 const void* B1, int n2, const void* B2, int N, void* C, int ldc, const void* R,
+                 const CacheDst* cache, hipStream_t s) {
+  DenseArgs a{A, M, K, B0, n1, B1, n2, B2, N, C, ldc, R, mode, CacheDst{}};
+  if (cache) a.cache = *cache;
+  if (M > 1024) {
+    dim3 grid((M + 127) / 128, (N + 127) / 128);
+    if (act == ACT_BF16) gemm_dense_k<uint16_t, 128, 128><<<grid, 256, 0, s>>>(a);
+    else gemm_dense_k<float, 128, 128><<<grid, 256, 0, s>>>(a);
+  } else {
+    dim3 grid((M + 63) / 64, (N + 63) / 64);
+    if (act == ACT_BF16) gemm_dense_k<uint16_t, 64, 64><<<grid, 256, 0, s>>>(a);
+    else gemm_dense_k<float, 64, 64><<<grid, 256, 0, s>>>(a);
+  }
+}
+
+void launch_gateup_lds(int act, const void* u2, const int32_t* perm, int k, const MoeW& w,
+                       const int4* tiles, const int32_t* ntiles, int max_tiles, int D, int F,
+                       void* H, hipStream_t s) {
+  GroupArgs a{u2, perm, k, w.wg, w.wu, w.escale, tiles, ntiles, D, F, F, H};
+  dim3 grid(max_tiles, F / 64);   // 128 weight rows = 64 SwiGLU outputs per block
+  if (act == ACT_F32) gateup_lds_k<float, float, 128, 128><<<grid, 256, 0, s>>>(a);
+  else if (w.wdt == DG_FP8E4M3) gateup_lds_k<uint16_t, uint8_t, 128, 128><<<grid, 256, 0, s>>>(a);
+  else gateup_lds_k<uint16_t, uint16_t, 128, 128><<<grid, 256, 0, s>>>(a);
+}
+
+void launch_down_lds(int act, const void* H, const MoeW& w, const int4* tiles,
+                     const int32_t* ntiles, int max_tiles, int D, int F, void* Y, hipStream_t s) {
+  GroupArgs a{H, nullptr, 0, w.wd, nullptr, w.escale, tiles, ntiles, F, D, D, Y};
+  dim3 grid(max_tiles, D / 128);
+  if (act == ACT_F32) down_lds_k<float, float, 128, 128><<<grid, 256, 0, s>>>(a);
+  else if (w.wdt == DG_FP8E4M3) down_lds_k<uint16_t, uint8_t, 128, 128><<<grid, 256, 0, s>>>(a);
+  else down_lds_k<uint16_t, uint16_t, 128, 128><<<grid, 256, 0, s>>>(a);
+}
+
+int lm_tiles(int V) { return (V + 127) / 128; }
+
+void launch_lmhead(int act, const void* uf, int M, int D, const void* lm, int V, float* pmax,
+                   int32_t* pidx, float* psum, float* logits, hipStream_t s) {
+  HeadArgs a{uf, M, D, lm, V, pmax, pidx, psum, logits, lm_tiles(V)};
+  if (M > 128) {
+    dim3 grid(lm_tiles(V), (M + 255) / 256);
+    if (act == ACT_BF16) lmhead_k<uint16_t, 256><<<grid, 256, 0, s>>>(a);
+    else lmhead_k<float, 256><<<grid, 256, 0, s>>>(a);
+  } else {
+    dim3 grid(lm_tiles(V), (M + 63) / 64);
+    if (act == ACT_BF16) lmhead_k<uint16_t, 64><<<grid, 256, 0, s>>>(a);
+    else lmhead_k<float, 64><<<grid, 256, 0, s>>>(a);
+  }
+}
+
+}  // namespace dg

@@ -1,0 +1,105 @@
+// launch.h -- host-side launchers of the libdgpass kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dgpass.h"
+
+namespace dg {
+
+// activation storage selector
+enum Act { ACT_F32 = 0, ACT_BF16 = 1 };
+
+struct Lens {
+  int32_t v[DG_MAX_BATCH];
+};
+struct ReqIds {
+  uint32_t v[DG_MAX_BATCH];
+};
+
+// ---- elementwise / reductions (kern_elem.hip) ----
+void launch_embed_norm(int act, const int32_t* tok, const void* emb, const float* g, int rows, int D,
+                       int V, float eps, void* x, void* u, hipStream_t s);
+void launch_rmsnorm(int act, const void* x, const float* g, int rows, int D, float eps, void* u,
+                    hipStream_t s);
+void launch_combine_norm(int act, const void* x1, const void* Y, const float* gates,
+                         const int32_t* inv, int rows, int k, int D, const float* gnext, float eps,
+                         void* x, void* u, hipStream_t s);
+void launch_renoise(int32_t* canvas, const int32_t* argmax, const float* conf, float tau,
+                    uint64_t seed, uint32_t tag, const Lens& pos0, const ReqIds& req, int B, int N,
+                    int V, hipStream_t s);
+void launch_coverage(const int32_t* counts, int L, int E, int32_t* touched, int32_t* counts_out,
+                     hipStream_t s);
+void launch_unpermute(int act, const void* src, const int32_t* inv, int slots, int C, void* dst,
+                      hipStream_t s);
+void launch_lm_merge(const float* pmax, const int32_t* pidx, const float* psum, int rows,
+                     int ntiles, int32_t* argmax, float* conf, hipStream_t s);
+
+// ---- MoE routing (kern_moe.hip) ----
+void launch_topk(const float* logits, int rows, int E, int k, int32_t* ids, float* gates,
+                 hipStream_t s);
+// counts/offsets/perm/inv + row tiles of at most tile_rows rows per expert
+void launch_plan(const int32_t* ids, int rows, int k, int E, int tile_rows, int32_t* counts,
+                 int32_t* offsets, int32_t* perm, int32_t* inv, int4* tiles, int32_t* ntiles,
+                 hipStream_t s);
+
+struct MoeW {
+  const void* wg;
+  const void* wu;
+  const void* wd;
+  const float* escale;  // [E][3] or null
+  int wdt;              // DG_F32 / DG_BF16 / DG_FP8E4M3
+};
+// skinny grouped GEMMs (row tiles of <= 32 rows, weights streamed, split-K in the block)
+void launch_gateup_stream(int act, const void* u2, const int32_t* perm, int k, const MoeW& w,
+                          const int4* tiles, const int32_t* ntiles, int max_tiles, int D, int F,
+                          void* H, hipStream_t s);
+void launch_down_stream(int act, const void* H, const MoeW& w, const int4* tiles,
+                        const int32_t* ntiles, int max_tiles, int D, int F, void* Y, hipStream_t s);
+
+// ---- LDS-tiled MFMA GEMMs (kern_gemm.hip) ----
+enum GemmMode { GEMM_STORE = 0, GEMM_RESID = 1, GEMM_F32 = 2, GEMM_QKV_CACHE = 3 };
+struct CacheDst {
+  void* k;
+  void* v;
+  int cap, T, QD, KD, hd, Hkv;
+  Lens len;
+};
+// C[M][N] = A[M][K] . B^T where B rows n come from up to three stacked matrices
+// (rows [0,n1) from B0, [n1,n1+n2) from B1, the rest from B2).
+void launch_gemm(int act, int mode, const void* A, int M, int K, const void* B0, int n1,
+                 const void* B1, int n2, const void* B2, int N, void* C, int ldc, const void* R,
+                 const CacheDst* cache, hipStream_t s);
+void launch_gateup_lds(int act, const void* u2, const int32_t* perm, int k, const MoeW& w,
+                       const int4* tiles, const int32_t* ntiles, int max_tiles, int D, int F,
+                       void* H, hipStream_t s);
+void launch_down_lds(int act, const void* H, const MoeW& w, const int4* tiles,
+                     const int32_t* ntiles, int max_tiles, int D, int F, void* Y, hipStream_t s);
+// LM head: per-row partial (max, argmax, sum exp) over vocabulary tiles of 128
+int lm_tiles(int V);
+void launch_lmhead(int act, const void* uf, int M, int D, const void* lm, int V, float* pmax,
+                   int32_t* pidx, float* psum, float* logits, hipStream_t s);
+
+// ---- attention (kern_attn.hip) ----
+struct AttnArgsHost {
+  int act;
+  const void* q;   // qkv buffer (q at column h*hd), row stride ldq
+  int ldq;
+  const void* kc;  // cache of this layer [B][Hkv][cap][hd]
+  const void* vc;
+  int cap;
+  const void* kn;  // canvas k/v (mode 0): rows of the qkv buffer
+  const void* vn;
+  int B, T, Hq, Hkv, hd;
+  int mode;        // 0 = canvas (bidirectional over cache + canvas), 1 = causal over cache
+  Lens len;
+  void* out;       // [B*T][Hq*hd]
+  float* po;       // split partials
+  float* pml;
+  long part_cap;   // capacity of the partial buffers in (row, head) entries
+};
+void launch_attention(const AttnArgsHost& a, hipStream_t s);
+long attn_partial_entries(int rows, int Hq);
+
+}  // namespace dg

@@ -1,0 +1,245 @@
+"""ctypes binding of libdgpass (include/dgpass.h), same names as the C ABI.
+
+Argument marshalling only: every step of the pass runs in the HIP kernels of
+libdgpass.so.  PyTorch provides device memory and the current stream.  There
+is no fallback: if the library is not built the import of `lib()` raises.
+"""
+import ctypes as C
+import os
+
+import numpy as np
+import torch
+
+from .configs import ModelConfig
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdgpass.so")
+MAX_LAYERS = 64
+MAX_BATCH = 64
+
+DG_F32, DG_BF16, DG_FP8E4M3 = 0, 1, 2
+_DT = {"f32": DG_F32, "bf16": DG_BF16, "fp8": DG_FP8E4M3}
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
+
+TAP_FIELDS = ("qkv", "attn", "x1", "u2", "router", "ids", "gates", "counts", "offsets", "perm",
+              "hmid", "yexp", "xout", "uf", "logits")
+STATUS = {0: "ok", -1: "invalid argument", -2: "KV cache capacity exceeded",
+          -3: "unsupported shape or dtype", -4: "workspace too small", -5: "HIP launch error"}
+
+
+class DgError(RuntimeError):
+    def __init__(self, status, where):
+        super().__init__(f"{where}: {STATUS.get(status, 'unknown')} ({status})")
+        self.status = status
+
+
+class dg_config(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("L", "D", "Hq", "Hkv", "hd", "E", "k", "F", "V")] + [
+        ("eps", C.c_float), ("act_dtype", C.c_int32), ("expert_dtype", C.c_int32)]
+
+
+class dg_layer_weights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in ("g1", "wq", "wk", "wv", "wo", "g2", "wr", "wg", "wu",
+                                          "wd", "escale")]
+
+
+class dg_weights(C.Structure):
+    _fields_ = [("emb", C.c_void_p), ("gf", C.c_void_p), ("lm", C.c_void_p),
+                ("layers", dg_layer_weights * MAX_LAYERS)]
+
+
+class dg_model(C.Structure):
+    _fields_ = [("cfg", dg_config), ("w", dg_weights), ("magic", C.c_uint32)]
+
+
+class dg_kv(C.Structure):
+    _fields_ = [("k", C.c_void_p * MAX_LAYERS), ("v", C.c_void_p * MAX_LAYERS), ("cap", C.c_int32),
+                ("len", C.POINTER(C.c_int32))]
+
+
+class dg_taps(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in TAP_FIELDS] + [("inject_router", C.c_void_p),
+                                                         ("ev_gateup", C.c_void_p)]
+
+
+EXPORTS = ("dg_model_init", "dg_workspace_bytes", "dg_kv_prefill", "dg_denoise_pass", "dg_renoise",
+           "dg_expert_coverage", "dg_status_str")
+
+_lib = None
+
+
+def lib():
+    """Load libdgpass.so (built in-tree); raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run __graft_entry__.build() (hipcc, gfx950)")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
+        L.dg_model_init.argtypes = [vp, vp, vp]
+        L.dg_model_init.restype = i32
+        L.dg_workspace_bytes.argtypes = [vp, i32, i32]
+        L.dg_workspace_bytes.restype = sz
+        L.dg_kv_prefill.argtypes = [vp, vp, vp, i32, i32, vp, vp, sz, vp]
+        L.dg_kv_prefill.restype = i32
+        L.dg_denoise_pass.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.dg_denoise_pass.restype = i32
+        L.dg_renoise.argtypes = [vp, vp, vp, C.c_float, C.c_uint64, C.c_uint32, vp, vp, i32, i32, i32,
+                                 vp]
+        L.dg_renoise.restype = i32
+        L.dg_expert_coverage.argtypes = [vp, vp, sz, vp, vp, vp]
+        L.dg_expert_coverage.restype = i32
+        L.dg_status_str.argtypes = [i32]
+        L.dg_status_str.restype = C.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(st, where):
+    if st != 0:
+        raise DgError(st, where)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def make_config(cfg: ModelConfig) -> dg_config:
+    return dg_config(cfg.L, cfg.D, cfg.Hq, cfg.Hkv, cfg.hd, cfg.E, cfg.k, cfg.F, cfg.V, float(cfg.eps),
+                     _DT[cfg.act], _DT[cfg.expert])
+
+
+def workspace_bytes(cfg: ModelConfig, max_rows: int, max_keys: int = 0) -> int:
+    c = make_config(cfg)
+    return lib().dg_workspace_bytes(C.byref(c), int(max_rows), int(max_keys))
+
+
+class KVCache:
+    """Per-layer K/V device tensors [B][Hkv][cap][hd] plus host lengths."""
+
+    def __init__(self, cfg: ModelConfig, B: int, cap: int, device="cuda", k=None, v=None):
+        self.cfg, self.B, self.cap = cfg, B, cap
+        dt = TORCH_DT[cfg.act]
+        self.k = k if k is not None else [torch.zeros(B, cfg.Hkv, cap, cfg.hd, dtype=dt, device=device)
+                                          for _ in range(cfg.L)]
+        self.v = v if v is not None else [torch.zeros(B, cfg.Hkv, cap, cfg.hd, dtype=dt, device=device)
+                                          for _ in range(cfg.L)]
+        self.lens = np.zeros(B, dtype=np.int32)
+
+    def struct(self) -> dg_kv:
+        s = dg_kv()
+        for l in range(self.cfg.L):
+            s.k[l] = self.k[l].data_ptr()
+            s.v[l] = self.v[l].data_ptr()
+        s.cap = self.cap
+        s.len = self.lens.ctypes.data_as(C.POINTER(C.c_int32))
+        return s
+
+
+def make_taps(cfg: ModelConfig, rows: int, names, device="cuda") -> dict:
+    """Device tensors for the requested taps of a call over `rows` token rows."""
+    a = TORCH_DT[cfg.act]
+    shapes = {
+        "qkv": ((cfg.L, rows, cfg.qkv_dim), a), "attn": ((cfg.L, rows, cfg.Hq * cfg.hd), a),
+        "x1": ((cfg.L, rows, cfg.D), a), "u2": ((cfg.L, rows, cfg.D), a),
+        "router": ((cfg.L, rows, cfg.E), torch.float32), "ids": ((cfg.L, rows, cfg.k), torch.int32),
+        "gates": ((cfg.L, rows, cfg.k), torch.float32), "counts": ((cfg.L, cfg.E), torch.int32),
+        "offsets": ((cfg.L, cfg.E + 1), torch.int32), "perm": ((cfg.L, rows * cfg.k), torch.int32),
+        "hmid": ((cfg.L, rows, cfg.k, cfg.F), a), "yexp": ((cfg.L, rows, cfg.k, cfg.D), a),
+        "xout": ((cfg.L, rows, cfg.D), a), "uf": ((rows, cfg.D), a),
+        "logits": ((rows, cfg.V), torch.float32),
+    }
+    return {n: torch.zeros(*shapes[n][0], dtype=shapes[n][1], device=device) for n in names}
+
+
+def _taps_struct(taps, inject_router=None, events=None):
+    if not taps and inject_router is None and events is None:
+        return None, None
+    t = dg_taps()
+    for n, v in (taps or {}).items():
+        setattr(t, n, v.data_ptr())
+    if inject_router is not None:
+        t.inject_router = inject_router.data_ptr()
+    keep = None
+    if events is not None:
+        keep = (C.c_void_p * len(events))(*[e.cuda_event for e in events])
+        t.ev_gateup = C.cast(keep, C.c_void_p)
+    return t, keep
+
+
+class Model:
+    """A model on the device: config + weight tensors (kept alive here)."""
+
+    def __init__(self, cfg: ModelConfig, weights: dict):
+        if cfg.L > MAX_LAYERS:
+            raise ValueError("too many layers")
+        self.cfg = cfg
+        self.weights = weights
+        w = dg_weights()
+        w.emb = weights["emb"].data_ptr()
+        w.gf = weights["gf"].data_ptr()
+        w.lm = weights["lm"].data_ptr()
+        for l, lw in enumerate(weights["layers"]):
+            L = w.layers[l]
+            for n in ("g1", "wq", "wk", "wv", "wo", "g2", "wr", "wg", "wu", "wd"):
+                setattr(L, n, lw[n].data_ptr())
+            L.escale = _ptr(lw.get("escale"))
+        self._c = make_config(cfg)
+        self._m = dg_model()
+        _check(lib().dg_model_init(C.byref(self._m), C.byref(self._c), C.byref(w)), "dg_model_init")
+
+    def workspace(self, max_rows: int, max_keys: int = 0, device="cuda") -> torch.Tensor:
+        n = lib().dg_workspace_bytes(C.byref(self._c), int(max_rows), int(max_keys))
+        if n == 0:
+            raise DgError(-1, "dg_workspace_bytes")
+        return torch.empty(n, dtype=torch.uint8, device=device)
+
+    def kv_cache(self, B: int, cap: int, device="cuda") -> KVCache:
+        return KVCache(self.cfg, B, cap, device)
+
+    def kv_prefill(self, kv: KVCache, tokens: torch.Tensor, ws: torch.Tensor, taps=None,
+                   inject_router=None, stream=None):
+        B, T = tokens.shape
+        s = kv.struct()
+        ts, _ = _taps_struct(taps, inject_router)
+        st = lib().dg_kv_prefill(C.byref(self._m), C.byref(s), tokens.data_ptr(), B, T,
+                                 None if ts is None else C.byref(ts), ws.data_ptr(), ws.numel(),
+                                 _stream(stream))
+        _check(st, "dg_kv_prefill")
+
+    def denoise_pass(self, kv: KVCache, canvas: torch.Tensor, argmax: torch.Tensor, conf: torch.Tensor,
+                     ws: torch.Tensor, taps=None, inject_router=None, events=None, stream=None):
+        B, N = canvas.shape
+        s = kv.struct()
+        ts, keep = _taps_struct(taps, inject_router, events)
+        st = lib().dg_denoise_pass(C.byref(self._m), C.byref(s), canvas.data_ptr(), B, N,
+                                   argmax.data_ptr(), conf.data_ptr(),
+                                   None if ts is None else C.byref(ts), ws.data_ptr(), ws.numel(),
+                                   _stream(stream))
+        del keep
+        _check(st, "dg_denoise_pass")
+
+    def expert_coverage(self, ws: torch.Tensor, touched: torch.Tensor, counts=None, stream=None):
+        st = lib().dg_expert_coverage(C.byref(self._m), ws.data_ptr(), ws.numel(), touched.data_ptr(),
+                                      _ptr(counts), _stream(stream))
+        _check(st, "dg_expert_coverage")
+
+
+def renoise(canvas: torch.Tensor, argmax, conf, tau: float, seed: int, pass_tag: int, pos0, V: int,
+            req_id=None, stream=None):
+    """Re-noise device canvases [B][N] in place (conf None: noise every slot)."""
+    B, N = canvas.shape
+    p0 = np.ascontiguousarray(pos0, dtype=np.int32)
+    rq = None if req_id is None else np.ascontiguousarray(req_id, dtype=np.uint32)
+    st = lib().dg_renoise(canvas.data_ptr(), _ptr(argmax), _ptr(conf), float(tau),
+                          int(seed) & (2**64 - 1), int(pass_tag) & 0xFFFFFFFF,
+                          p0.ctypes.data_as(C.c_void_p),
+                          None if rq is None else rq.ctypes.data_as(C.c_void_p), B, N, V,
+                          _stream(stream))
+    _check(st, "dg_renoise")

@@ -1,0 +1,194 @@
+/*
+ * dgpass.h -- C ABI of libdgpass: one block-diffusion denoising pass over a
+ * canvas of vocabulary tokens, on an MI355X (gfx950).
+ *
+ * The method (pages cited by title and section):
+ *  - explainer "DiffusionGemma", "Two modes, one model": a causal prefill
+ *    writes the KV cache; a denoising pass attends bidirectionally over the
+ *    canvas and the cache.  "Uniform State Diffusion": noise is random
+ *    vocabulary tokens, every position is updated in parallel each pass and
+ *    low-confidence positions are replaced by fresh random tokens.  "Long-form
+ *    text: chaining canvases": each finished canvas is appended to the cache
+ *    by a prefill step and a fresh canvas is opened.
+ *  - course page "Module 12. Diffusion Language Models", block-mask exercise:
+ *    prefix rows causal, block rows see prefix and block; prefix K/V are
+ *    reused across denoising steps, block states are recomputed every pass.
+ *  - newsletter comment under "A Visual Guide to DiffusionGemma": every canvas
+ *    token goes through the MoE router, so a pass reads the union of the
+ *    selected experts; the comment asks for the expert coverage per step.
+ *
+ * Layer (pre-norm; plain readings where the pages are silent: no positional
+ * terms, attention scale 1/sqrt(hd), RMSNorm with gain, no shared expert):
+ *   u  = rmsnorm(x) * g1;  q,k,v = u Wq^T, u Wk^T, u Wv^T
+ *   o  = softmax(q k^T / sqrt(hd)) v  over the keys the block mask allows
+ *   x1 = x + o Wo^T;  u2 = rmsnorm(x1) * g2;  r = u2 Wr^T (fp32)
+ *   top-k experts by (r descending, index ascending); gates = softmax of the
+ *   k selected logits;  x = x1 + sum_j g_j * (silu(u2 Wg_e^T) * (u2 Wu_e^T)) Wd_e^T
+ * Head: uf = rmsnorm(x) * gf;  logits = uf W_lm^T (fp32); argmax = lowest
+ * index of the maximum; conf = softmax probability of the maximum.
+ * Stored tensors are rounded (RNE) to the activation type: u, q, k, v (hence
+ * the cache), o, x1, u2, SwiGLU output, expert outputs, x, uf.  Router and
+ * head logits stay fp32.
+ *
+ * Conventions of every call:
+ *  - Device pointers are HIP device memory owned by the caller.  Host pointers
+ *    are marked "host".  The library allocates nothing and keeps no global
+ *    state; every call enqueues on `stream` (a hipStream_t, NULL = the null
+ *    stream) and returns without synchronising.
+ *  - Matrices are row-major [rows][cols] with the contraction dimension
+ *    contiguous (weights are [out][in]).
+ *  - Arguments are validated before the first launch; a call that returns an
+ *    error has enqueued nothing and changed nothing.  Device faults surface at
+ *    the caller's next synchronisation.  No C++ exception crosses the ABI.
+ *  - Two calls that share a workspace must be ordered (same stream).
+ */
+#ifndef DGPASS_H
+#define DGPASS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t dg_status;
+#define DG_OK 0
+#define DG_ERR_INVALID (-1)      /* null pointer, bad shape or value */
+#define DG_ERR_CAPACITY (-2)     /* len[b] + T exceeds the cache capacity */
+#define DG_ERR_UNSUPPORTED (-3)  /* shape or dtype outside what the kernels implement */
+#define DG_ERR_WORKSPACE (-4)    /* workspace too small */
+#define DG_ERR_HIP (-5)          /* a launch failed (hipGetLastError) */
+
+/* storage types */
+#define DG_F32 0
+#define DG_BF16 1
+#define DG_FP8E4M3 2   /* OCP e4m3 (max 448, no infinities), expert weights only */
+
+#define DG_MAX_LAYERS 64
+#define DG_MAX_BATCH 64
+
+/* Model shape.  Supported: act_dtype F32 with expert_dtype F32, or act_dtype
+ * BF16 with expert_dtype BF16 or FP8E4M3; hd in {64, 128}; Hq/Hkv in
+ * {1, 2, 4, 8, 16}; D, F and Hq*hd multiples of 64; 1 <= k <= 8; k <= E <= 256. */
+typedef struct dg_config {
+  int32_t L, D, Hq, Hkv, hd, E, k, F, V;
+  float eps;               /* RMSNorm epsilon */
+  int32_t act_dtype;       /* embeddings, attention/router/head weights, activations, KV cache */
+  int32_t expert_dtype;    /* expert weights */
+} dg_config;
+
+/* Device pointers of one layer. */
+typedef struct dg_layer_weights {
+  const float* g1;     /* [D] f32 */
+  const void* wq;      /* [Hq*hd][D] act */
+  const void* wk;      /* [Hkv*hd][D] act */
+  const void* wv;      /* [Hkv*hd][D] act */
+  const void* wo;      /* [D][Hq*hd] act */
+  const float* g2;     /* [D] f32 */
+  const void* wr;      /* [E][D] act */
+  const void* wg;      /* [E][F][D] expert dtype */
+  const void* wu;      /* [E][F][D] expert dtype */
+  const void* wd;      /* [E][D][F] expert dtype */
+  const float* escale; /* [E][3] f32 (gate, up, down) multipliers of the
+                          accumulated fp8 products; NULL unless FP8E4M3 */
+} dg_layer_weights;
+
+typedef struct dg_weights {
+  const void* emb;     /* [V][D] act */
+  const float* gf;     /* [D] f32 final norm gain */
+  const void* lm;      /* [V][D] act (may alias emb) */
+  dg_layer_weights layers[DG_MAX_LAYERS];
+} dg_weights;
+
+/* Immutable description of a model; a host struct the caller owns. */
+typedef struct dg_model {
+  dg_config cfg;
+  dg_weights w;
+  uint32_t magic;
+} dg_model;
+
+/* KV cache: per layer K and V, device [B][Hkv][cap][hd] act.  len is a host
+ * array [B] of valid prefix lengths; kv_prefill advances it. */
+typedef struct dg_kv {
+  void* k[DG_MAX_LAYERS];
+  void* v[DG_MAX_LAYERS];
+  int32_t cap;
+  int32_t* len;
+} dg_kv;
+
+/* Optional device outputs (debug taps) of a pass or prefill; every field may
+ * be NULL.  BN = B*N (or B*T for a prefill).  Token-major, slots in top-k
+ * order.  Writing taps adds work; leave them NULL when timing. */
+typedef struct dg_taps {
+  void* qkv;                 /* [L][BN][(Hq+2Hkv)*hd] act */
+  void* attn;                /* [L][BN][Hq*hd] act: attention output before Wo */
+  void* x1;                  /* [L][BN][D] act */
+  void* u2;                  /* [L][BN][D] act */
+  float* router;             /* [L][BN][E] f32 (the logits routing used) */
+  int32_t* ids;              /* [L][BN][k] */
+  float* gates;              /* [L][BN][k] */
+  int32_t* counts;           /* [L][E] */
+  int32_t* offsets;          /* [L][E+1] */
+  int32_t* perm;             /* [L][BN*k]: entries t*k+j sorted by (expert, t, j) */
+  void* hmid;                /* [L][BN][k][F] act: SwiGLU output per slot */
+  void* yexp;                /* [L][BN][k][D] act: expert output per slot */
+  void* xout;                /* [L][BN][D] act: layer output */
+  void* uf;                  /* [BN][D] act (pass only) */
+  float* logits;             /* [BN][V] f32 (pass only) */
+  const float* inject_router;/* input [L][BN][E] f32: route on these logits instead */
+  void* const* ev_gateup;    /* host array of 2*L hipEvent_t: recorded on `stream`
+                                just before and after each layer's gate/up expert
+                                launch (for timing that kernel); NULL = none */
+} dg_taps;
+
+/* Fill *m after validating cfg and the weight pointers.  No device work. */
+dg_status dg_model_init(dg_model* m, const dg_config* cfg, const dg_weights* w);
+
+/* Bytes of workspace a call needs for up to max_rows token rows (B*N of a
+ * pass or B*T of a prefill) and up to max_keys keys per request (prefix +
+ * rows of that request).  0 when cfg is invalid.  Host arithmetic only. */
+size_t dg_workspace_bytes(const dg_config* cfg, int32_t max_rows, int32_t max_keys);
+
+/* Causal prefill ("Prefill mode"): appends T tokens per request (device
+ * tokens [B][T] int32 in [0, V)) to every layer's cache at positions
+ * [len[b], len[b]+T) and, on success, advances kv->len[b] by T (host).  Query
+ * i sees keys 0 .. len[b]+i.  The last layer stops after its cache write.
+ * Errors: INVALID, CAPACITY (len[b]+T > cap), UNSUPPORTED, WORKSPACE, HIP. */
+dg_status dg_kv_prefill(const dg_model* m, dg_kv* kv, const int32_t* tokens, int32_t B, int32_t T,
+                        const dg_taps* taps, void* ws, size_t ws_bytes, void* stream);
+
+/* One denoising pass ("Denoising mode") over device canvases [B][N] int32.
+ * Request b's canvas queries see its whole cached prefix kv->len[b] and its
+ * whole canvas (bidirectional).  The cache is only read.  Outputs device
+ * argmax [B][N] int32 and conf [B][N] f32.  The per-layer expert counts of
+ * this pass stay in the workspace for dg_expert_coverage until the workspace
+ * is used again. */
+dg_status dg_denoise_pass(const dg_model* m, const dg_kv* kv, const int32_t* canvas, int32_t B,
+                          int32_t N, int32_t* argmax, float* conf, const dg_taps* taps, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/* Uniform-state re-noise of device canvases [B][N] in place.  conf == NULL
+ * noises every slot (canvas initialisation; argmax may be NULL).  Otherwise
+ * slot i of request b keeps argmax[b][i] when conf[b][i] >= tau and else takes
+ * a uniform token floor(r * V / 2^64), r = word 0 of Philox4x64-10 with
+ * counter (pos0[b] + i, pass_tag, req_id[b], 0) and key (seed, 0) (Salmon et
+ * al., "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11).  A NaN conf is
+ * noised.  pos0: host [B] absolute position of slot 0; req_id: host [B] or
+ * NULL for b.  B <= DG_MAX_BATCH. */
+dg_status dg_renoise(int32_t* canvas, const int32_t* argmax, const float* conf, float tau,
+                     uint64_t seed, uint32_t pass_tag, const int32_t* pos0,
+                     const uint32_t* req_id, int32_t B, int32_t N, int32_t V, void* stream);
+
+/* Experts touched per layer by the last pass run with this workspace: device
+ * touched [L] int32 = #{e : count[l][e] > 0} (the union over the batch), and
+ * optionally device counts [L][E] int32. */
+dg_status dg_expert_coverage(const dg_model* m, const void* ws, size_t ws_bytes, int32_t* touched,
+                             int32_t* counts, void* stream);
+
+const char* dg_status_str(dg_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,165 @@
+"""Denoising pass on the GPU (through the C ABI) against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_lm_denoise_amd import synth
+from block_diffusion_lm_denoise_amd.configs import WORKLOADS, ModelConfig
+from gpu_helpers import ALL_TAPS, DEV, Pair, compare_pass, host
+
+pytestmark = pytest.mark.gpu
+
+
+def _cfg(**kw):
+    base = dict(L=1, D=256, Hq=4, Hkv=2, hd=128, E=16, k=4, F=128, V=640, act="bf16", expert="bf16")
+    base.update(kw)
+    return ModelConfig(**base)
+
+
+def _run(pair, B, lens, N, seed, synthetic=False, inject=True, scale_note="", head_scale=1.0):
+    cap = max(lens) + N + 3
+    oks, ovs, oln, kv = pair.caches(B, cap, lens, seed, synthetic=synthetic)
+    if not synthetic:
+        for l in range(pair.cfg.L):
+            assert np.array_equal(oln, kv.lens)
+            # prefilled caches agree within the storage tolerance
+            from gpu_helpers import f64, max_rel, TOL
+            for b in range(B):
+                n = lens[b]
+                if n:
+                    assert max_rel(f64(host(kv.k[l][b, :, :n]), pair.cfg.act),
+                                   f64(oks[l][b, :, :n], pair.cfg.act)) < TOL[pair.cfg.act]
+                    assert max_rel(f64(host(kv.v[l][b, :, :n]), pair.cfg.act),
+                                   f64(ovs[l][b, :, :n], pair.cfg.act)) < TOL[pair.cfg.act]
+    canvas = synth.tokens(pair.cfg.V, (B, N), seed, "canvas").numpy()
+    o = pair.om.denoise_pass(oks, ovs, oln, canvas, taps=ALL_TAPS)
+    reps = {}
+    if inject:
+        g = pair.gpu_pass(kv, canvas, inject=o[2]["router"])
+        reps["inject"] = compare_pass(pair.cfg, o, g[:3], True, "inject", head_scale)
+    g = pair.gpu_pass(kv, canvas)
+    reps["free"] = compare_pass(pair.cfg, o, g[:3], False, "free", head_scale)
+    # the pass never writes the cache
+    if synthetic:
+        for l in range(pair.cfg.L):
+            np.testing.assert_array_equal(host(kv.k[l]), oks[l])
+            np.testing.assert_array_equal(host(kv.v[l]), ovs[l])
+    print(scale_note, reps)
+    return reps, g
+
+
+def test_tiny_fp32_workload():
+    wl = WORKLOADS["tiny_fp32"]
+    pair = Pair(wl.model, wl.seed, gain="ones")
+    _run(pair, 1, [wl.P], wl.N, wl.seed)
+
+
+@pytest.mark.parametrize("act,hd,G", [("f32", 64, 1), ("f32", 128, 2), ("bf16", 128, 2), ("bf16", 64, 4)])
+def test_small_layers_ragged_batch(act, hd, G):
+    cfg = _cfg(L=2, act=act, expert=act, hd=hd, Hkv=8 // G, Hq=8)
+    pair = Pair(cfg, 11, scale_lm=10.0)
+    _run(pair, 3, [50, 0, 13], 37, 11, head_scale=10.0)
+
+
+def test_single_slot_canvas_and_empty_prefix():
+    pair = Pair(_cfg(), 12)
+    _run(pair, 1, [0], 1, 12)
+    _run(pair, 2, [1, 0], 1, 13)
+
+
+def test_fp8_experts_small():
+    pair = Pair(_cfg(expert="fp8", L=2), 14, scale_lm=10.0)
+    _run(pair, 2, [20, 9], 33, 14, head_scale=10.0)
+
+
+@pytest.mark.parametrize("act,expert", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "fp8")])
+def test_many_rows_per_expert_uses_tiled_expert_path(act, expert):
+    # 4 experts, top-2, 200 tokens: ~100 rows per expert (LDS-tiled grouped GEMM)
+    cfg = _cfg(E=4, k=2, act=act, expert=expert, V=384)
+    pair = Pair(cfg, 15)
+    _run(pair, 2, [30, 5], 100, 15)
+
+
+def test_injected_router_ties_are_bit_exact():
+    cfg = _cfg(E=8, k=3)
+    pair = Pair(cfg, 16)
+    N = 4
+    oks, ovs, oln, kv = pair.caches(1, 8, [3], 16)
+    inj = np.zeros((1, N, 8), np.float32)
+    inj[0, 0] = [1, 2, 2, 0, 2, -1, 5, 0]
+    inj[0, 1] = 0
+    inj[0, 2] = [3, 1, 3, 1, 3, 9, 3, 1]
+    inj[0, 3] = [-1, -1, -2, -1, 7, -1, 7, 7]
+    canvas = synth.tokens(cfg.V, (1, N), 16, "canvas").numpy()
+    g = pair.gpu_pass(kv, canvas, inject=inj)
+    np.testing.assert_array_equal(g[2]["ids"][0], [[6, 1, 2], [0, 1, 2], [5, 0, 2], [4, 6, 7]])
+    o = pair.om.denoise_pass(oks, ovs, oln, canvas, taps=ALL_TAPS, inject_router=inj)
+    compare_pass(cfg, o, g[:3], True, "ties")
+
+
+def test_moe_layer_prefix1024_full_size():
+    """One bf16 MoE layer, 1024-token prefix prefilled on both sides, 256-token canvas."""
+    wl = WORKLOADS["layer_p1024"]
+    pair = Pair(wl.model, wl.seed, gain="ones")
+    reps, g = _run(pair, 1, [wl.P], wl.N, wl.seed, scale_note="layer_p1024")
+    # expert coverage of the pass (union of the selected experts)
+    touched = torch.zeros(1, dtype=torch.int32, device=DEV)
+    pair.gm.expert_coverage(g[3], touched)
+    assert int(touched.item()) == int((g[2]["counts"][0] > 0).sum())
+    assert int(touched.item()) >= 96   # most of the 128 experts are touched by one pass
+
+
+def test_moe_layer_prefix8192_full_size_synthetic_cache():
+    wl = WORKLOADS["layer_p8192"]
+    pair = Pair(wl.model, wl.seed, gain="ones")
+    _run(pair, 1, [wl.P], wl.N, wl.seed, synthetic=True, inject=False, scale_note="layer_p8192")
+
+
+def test_batch8_fp8_full_size_sampled_requests():
+    """Eight requests in one pass on the GPU; requests are independent, so the
+    oracle checks a sample of them one at a time."""
+    wl = WORKLOADS["batch8_fp8"]
+    cfg = wl.model
+    pair = Pair(cfg, wl.seed, gain="ones")
+    B, N, P = wl.B, wl.N, wl.P
+    cap = P + N
+    ks, vs = synth.kv_cache_values(cfg, B, cap, P, wl.seed)
+    kv = pair.gm.kv_cache(B, cap, device=DEV)
+    for l in range(cfg.L):
+        kv.k[l].copy_(ks[l])
+        kv.v[l].copy_(vs[l])
+    kv.lens[:] = P
+    canvas = synth.tokens(cfg.V, (B, N), wl.seed, "canvas").numpy()
+    gam, gcf, gt, ws = pair.gpu_pass(kv, canvas, taps=("router", "ids", "logits", "counts"))
+    touched = torch.zeros(1, dtype=torch.int32, device=DEV)
+    pair.gm.expert_coverage(ws, touched)
+    assert int(touched.item()) == int((gt["counts"][0] > 0).sum()) >= 120
+    for b in (0, 5):
+        o = pair.om.denoise_pass([host(k[b:b + 1]) for k in ks], [host(v[b:b + 1]) for v in vs],
+                                 np.array([P], np.int32), canvas[b:b + 1], taps=("router", "ids", "logits"))
+        sl = slice(b * N, (b + 1) * N)
+        g = (gam[b:b + 1], gcf[b:b + 1], {"router": gt["router"][:, sl], "ids": gt["ids"][:, sl],
+                                          "logits": gt["logits"][sl]})
+        print("batch8_fp8 request", b, compare_pass(cfg, o, g, False, f"req{b}"))
+
+
+def test_pass_is_deterministic_and_reads_cache_only():
+    wl = WORKLOADS["layer_p1024"]
+    cfg = wl.model
+    w = synth.make_weights(cfg, 5, device=DEV)
+    from block_diffusion_lm_denoise_amd import dgpass
+    gm = dgpass.Model(cfg, w)
+    kv = gm.kv_cache(1, 1280, device=DEV)
+    ws = gm.workspace(1024, 1280, device=DEV)
+    gm.kv_prefill(kv, synth.tokens(cfg.V, (1, 1024), 5, device=DEV), ws)
+    k0, v0 = kv.k[0].clone(), kv.v[0].clone()
+    canvas = synth.tokens(cfg.V, (1, 256), 5, "canvas", device=DEV)
+    outs = []
+    for _ in range(2):
+        am = torch.empty(1, 256, dtype=torch.int32, device=DEV)
+        cf = torch.empty(1, 256, dtype=torch.float32, device=DEV)
+        gm.denoise_pass(kv, canvas, am, cf, ws)
+        outs.append((am, cf))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    assert torch.equal(kv.k[0], k0) and torch.equal(kv.v[0], v0)
