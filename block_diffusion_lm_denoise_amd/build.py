@@ -12,7 +12,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdgpass.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["dgpass.hip", "kern_elem.hip", "kern_moe.hip", "kern_gemm.hip", "kern_attn.hip"]
+SOURCES = ["dgpass.hip", "kern_elem.hip", "kern_moe.hip", "kern_gemm.hip", "kern_attn.hip",
+           "kern_stream.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-Wall", "-Wno-unused-result",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics"]

@@ -77,6 +77,20 @@ __device__ __forceinline__ void zero_frag(FragF32& f) {
   for (int j = 0; j < 8; j++) f.v[j] = 0.f;
 }
 
+// keep f when ok, else zero it, without a branch (a select per register)
+__device__ __forceinline__ void mask_frag(FragBF& f, bool ok) {
+  uint4 u = __builtin_bit_cast(uint4, f.v);
+  u.x = ok ? u.x : 0u;
+  u.y = ok ? u.y : 0u;
+  u.z = ok ? u.z : 0u;
+  u.w = ok ? u.w : 0u;
+  f.v = __builtin_bit_cast(bf16x8_t, u);
+}
+__device__ __forceinline__ void mask_frag(FragF32& f, bool ok) {
+#pragma unroll
+  for (int j = 0; j < 8; j++) f.v[j] = ok ? f.v[j] : 0.f;
+}
+
 // OCP e4m3 byte pair -> two floats (hardware conversion), then bf16 bits.
 // Every e4m3 value is exact in bf16 (4 significant bits, exponent range
 // 2^-9 .. 448), so taking the top half of the fp32 pattern is exact.
@@ -96,6 +110,35 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 u) {
 __device__ __forceinline__ void load_frag_fp8(FragBF& f, const uint8_t* p) {
   uint2 u = *reinterpret_cast<const uint2*>(p);
   f.v = __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8(u));
+}
+
+// 8 consecutive activations <-> 8 floats (16 bytes bf16, 32 bytes fp32)
+__device__ __forceinline__ void ld8(const uint16_t* p, float (&v)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void ld8(const float* p, float (&v)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void st8(uint16_t* p, const float (&v)[8]) {
+  uint4 u;
+  u.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+  u.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  u.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
+  u.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+  *reinterpret_cast<uint4*>(p) = u;
+}
+__device__ __forceinline__ void st8(float* p, const float (&v)[8]) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
 // ---------------------------------------------------------------------------

@@ -13,8 +13,11 @@ constexpr uint32_t MODEL_MAGIC = 0x44475041u;  // "DGPA"
 size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 int esize(int dt) { return dt == DG_F32 ? 4 : dt == DG_BF16 ? 2 : 1; }
 
-constexpr int SKINNY_TILE = 32;   // row tile of the weight-streaming expert kernels
+constexpr int MIN_TILE = 32;      // smallest expert row tile (sizes the tile list)
+constexpr int STREAM_TILE = 32;   // row tile of the weight-streaming kernels
 constexpr int FAT_TILE = 128;     // row tile of the LDS-tiled expert kernels
+constexpr int STREAM_MAX_ROWS = 1024;  // dense projections: weight streaming up to this many rows
+constexpr int HEAD_STREAM_MAX_ROWS = 0;  // the LDS-tiled head kernel wins at 256 rows
 
 struct Layout {
   size_t cov;       // [L][E] int32 expert counts of the last pass (offset 0)
@@ -50,7 +53,7 @@ Layout layout(const dg_config& c, int rows) {
   L.offsets = take((size_t)(c.E + 1) * 4);
   L.perm = take(slots * 4);
   L.inv = take(slots * 4);
-  L.max_tiles = (int)((slots + SKINNY_TILE - 1) / SKINNY_TILE) + c.E;
+  L.max_tiles = (int)((slots + MIN_TILE - 1) / MIN_TILE) + c.E;
   L.tiles = take((size_t)L.max_tiles * 16);
   L.ntiles = take(4);
   L.H = take(slots * c.F * a);
@@ -58,7 +61,7 @@ Layout layout(const dg_config& c, int rows) {
   L.part_cap = attn_partial_entries((int)R, c.Hq);
   L.po = take((size_t)L.part_cap * c.hd * 4);
   L.pml = take((size_t)L.part_cap * 2 * 4);
-  const size_t nt = lm_tiles(c.V);
+  const size_t nt = (c.V + 63) / 64;  // LM-head partials per row (64-column chunks)
   L.lpm = take(R * nt * 4);
   L.lpi = take(R * nt * 4);
   L.lps = take(R * nt * 4);
@@ -115,6 +118,37 @@ void tap_copy(void* dst, const void* src, size_t bytes, hipStream_t s) {
   if (dst && bytes) (void)hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);
 }
 
+// dense projection C = A W^T (W rows stacked from up to three matrices):
+// weight streaming for few rows, LDS-tiled MFMA GEMM for many
+void dense_gemm(const Ctx& c, int mode, const void* A, int M, int K, const void* B0, int n1,
+                const void* B1, int n2, const void* B2, int N, void* C, int ldc, const void* R,
+                const CacheDst* cache) {
+  const dg_config& cf = c.m->cfg;
+  const int act = cf.act_dtype == DG_BF16 ? ACT_BF16 : ACT_F32;
+  if (M <= STREAM_MAX_ROWS) {
+    StreamGemm g{};
+    g.A = A;
+    g.M = M;
+    g.K = K;
+    g.W0 = B0;
+    g.W1 = B1;
+    g.W2 = B2;
+    g.n1 = n1;
+    g.n2 = n2;
+    g.N = N;
+    g.nchunks = (N + 63) / 64;
+    g.out = C;
+    g.ldo = ldc;
+    g.R = R;
+    if (cache) g.cache = *cache;
+    const int sm = mode == GEMM_STORE ? SG_STORE : mode == GEMM_RESID ? SG_RESID
+                 : mode == GEMM_F32 ? SG_F32 : SG_QKV_CACHE;
+    launch_stream_gemm(act, cf.act_dtype, sm, g, (M + STREAM_TILE - 1) / STREAM_TILE, c.s);
+  } else {
+    launch_gemm(act, mode, A, M, K, B0, n1, B1, n2, B2, N, C, ldc, R, cache, c.s);
+  }
+}
+
 void moe_block(const Ctx& c, int l, const float* gnext) {
   const dg_config& cf = c.m->cfg;
   const dg_layer_weights& w = c.m->w.layers[l];
@@ -125,31 +159,35 @@ void moe_block(const Ctx& c, int l, const float* gnext) {
   hipStream_t s = c.s;
 
   // x1 = x + o Wo^T
-  launch_gemm(act, GEMM_RESID, at<void>(c, c.L.o), c.R, (int)QD, w.wo, cf.D, nullptr, 0, nullptr,
-              cf.D, at<void>(c, c.L.x1), cf.D, at<void>(c, c.L.x), nullptr, s);
+  dense_gemm(c, GEMM_RESID, at<void>(c, c.L.o), c.R, (int)QD, w.wo, cf.D, nullptr, 0, nullptr, cf.D,
+             at<void>(c, c.L.x1), cf.D, at<void>(c, c.L.x), nullptr);
   if (t) tap_copy(t->x1 ? (char*)t->x1 + l * R * D * a : nullptr, at<void>(c, c.L.x1), R * D * a, s);
-  launch_rmsnorm(act, at<void>(c, c.L.x1), w.g2, c.R, cf.D, cf.eps, at<void>(c, c.L.u2), s);
-  if (t) tap_copy(t->u2 ? (char*)t->u2 + l * R * D * a : nullptr, at<void>(c, c.L.u2), R * D * a, s);
-
-  // router logits (fp32) and top-k
+  // RMSNorm + router logits (fp32) + top-k
   const float* rl = at<float>(c, c.L.rl);
-  if (t && t->inject_router) {
-    rl = t->inject_router + (size_t)l * R * E;
-  } else {
-    launch_gemm(act, GEMM_F32, at<void>(c, c.L.u2), c.R, cf.D, w.wr, cf.E, nullptr, 0, nullptr, cf.E,
-                at<void>(c, c.L.rl), cf.E, nullptr, nullptr, s);
+  if (t && t->inject_router) rl = t->inject_router + (size_t)l * R * E;
+  RouteArgs ra{at<void>(c, c.L.x1), w.g2, w.wr, c.R, cf.D, cf.E, cf.k, cf.eps,
+               (t && t->inject_router) ? rl : nullptr, at<void>(c, c.L.u2),
+               (t && t->router && !t->inject_router) ? at<float>(c, c.L.rl) : nullptr,
+               at<int32_t>(c, c.L.ids), at<float>(c, c.L.gates)};
+  // the fused kernel works on 16-token tiles: worth it only with many tiles
+  if (c.R < 2048 || !launch_route(act, ra, s)) {
+    launch_rmsnorm(act, at<void>(c, c.L.x1), w.g2, c.R, cf.D, cf.eps, at<void>(c, c.L.u2), s);
+    if (!(t && t->inject_router))
+      dense_gemm(c, GEMM_F32, at<void>(c, c.L.u2), c.R, cf.D, w.wr, cf.E, nullptr, 0, nullptr, cf.E,
+                 at<void>(c, c.L.rl), cf.E, nullptr, nullptr);
+    launch_topk(rl, c.R, cf.E, cf.k, at<int32_t>(c, c.L.ids), at<float>(c, c.L.gates), s);
   }
-  if (t) tap_copy(t->router ? t->router + l * R * E : nullptr, rl, R * E * 4, s);
-  launch_topk(rl, c.R, cf.E, cf.k, at<int32_t>(c, c.L.ids), at<float>(c, c.L.gates), s);
   if (t) {
+    tap_copy(t->u2 ? (char*)t->u2 + l * R * D * a : nullptr, at<void>(c, c.L.u2), R * D * a, s);
+    tap_copy(t->router ? t->router + l * R * E : nullptr, rl, R * E * 4, s);
     tap_copy(t->ids ? t->ids + l * R * k : nullptr, at<void>(c, c.L.ids), R * k * 4, s);
     tap_copy(t->gates ? t->gates + l * R * k : nullptr, at<void>(c, c.L.gates), R * k * 4, s);
   }
 
   // permutation and row tiles
   const int avg = (int)(R * k / E);
-  const bool skinny = avg <= 48;
-  const int tile_rows = skinny ? SKINNY_TILE : FAT_TILE;
+  const bool stream = avg <= 64;
+  const int tile_rows = stream ? STREAM_TILE : FAT_TILE;
   const int max_tiles = (int)((R * k + tile_rows - 1) / tile_rows) + (int)E;
   int32_t* counts = c.pass ? at<int32_t>(c, c.L.cov) + l * E : at<int32_t>(c, c.L.counts);
   launch_plan(at<int32_t>(c, c.L.ids), c.R, cf.k, cf.E, tile_rows, counts, at<int32_t>(c, c.L.offsets),
@@ -163,26 +201,48 @@ void moe_block(const Ctx& c, int l, const float* gnext) {
 
   // experts over the union of the selected ones
   MoeW mw{w.wg, w.wu, w.wd, w.escale, cf.expert_dtype};
+  StreamGemm g{};
+  g.perm = at<int32_t>(c, c.L.perm);
+  g.k = cf.k;
+  g.escale = w.escale;
+  g.tiles = at<int4>(c, c.L.tiles);
+  g.ntiles = at<int32_t>(c, c.L.ntiles);
   if (t && t->ev_gateup && t->ev_gateup[2 * l]) (void)hipEventRecord((hipEvent_t)t->ev_gateup[2 * l], s);
-  if (skinny)
-    launch_gateup_stream(act, at<void>(c, c.L.u2), at<int32_t>(c, c.L.perm), cf.k, mw,
-                         at<int4>(c, c.L.tiles), at<int32_t>(c, c.L.ntiles), max_tiles, cf.D, cf.F,
-                         at<void>(c, c.L.H), s);
-  else
+  if (stream) {
+    g.A = at<void>(c, c.L.u2);
+    g.K = cf.D;
+    g.W0 = w.wg;
+    g.W1 = w.wu;
+    g.NW = cf.F;
+    g.nchunks = cf.F / 32;
+    g.out = at<void>(c, c.L.H);
+    g.ldo = cf.F;
+    launch_stream_gemm(act, cf.expert_dtype, SG_GATEUP, g, max_tiles, s);
+  } else {
     launch_gateup_lds(act, at<void>(c, c.L.u2), at<int32_t>(c, c.L.perm), cf.k, mw,
                       at<int4>(c, c.L.tiles), at<int32_t>(c, c.L.ntiles), max_tiles, cf.D, cf.F,
                       at<void>(c, c.L.H), s);
+  }
   if (t && t->ev_gateup && t->ev_gateup[2 * l + 1])
     (void)hipEventRecord((hipEvent_t)t->ev_gateup[2 * l + 1], s);
   if (t && t->hmid)
     launch_unpermute(act, at<void>(c, c.L.H), at<int32_t>(c, c.L.inv), (int)(R * k), cf.F,
                      (char*)t->hmid + l * R * k * cf.F * a, s);
-  if (skinny)
-    launch_down_stream(act, at<void>(c, c.L.H), mw, at<int4>(c, c.L.tiles), at<int32_t>(c, c.L.ntiles),
-                       max_tiles, cf.D, cf.F, at<void>(c, c.L.Y), s);
-  else
+  if (stream) {
+    g.A = at<void>(c, c.L.H);
+    g.K = cf.F;
+    g.W0 = w.wd;
+    g.W1 = nullptr;
+    g.NW = cf.D;
+    g.N = cf.D;
+    g.nchunks = cf.D / 64;
+    g.out = at<void>(c, c.L.Y);
+    g.ldo = cf.D;
+    launch_stream_gemm(act, cf.expert_dtype, SG_DOWN, g, max_tiles, s);
+  } else {
     launch_down_lds(act, at<void>(c, c.L.H), mw, at<int4>(c, c.L.tiles), at<int32_t>(c, c.L.ntiles),
                     max_tiles, cf.D, cf.F, at<void>(c, c.L.Y), s);
+  }
   if (t && t->yexp)
     launch_unpermute(act, at<void>(c, c.L.Y), at<int32_t>(c, c.L.inv), (int)(R * k), cf.D,
                      (char*)t->yexp + l * R * k * D * a, s);
@@ -266,8 +326,8 @@ dg_status dg_kv_prefill(const dg_model* m, dg_kv* kv, const int32_t* tokens, int
   for (int l = 0; l < cf.L; l++) {
     const dg_layer_weights& w = m->w.layers[l];
     CacheDst cd{kv->k[l], kv->v[l], kv->cap, T, QD, KD, cf.hd, cf.Hkv, lens};
-    launch_gemm(act, GEMM_QKV_CACHE, at<void>(c, c.L.u), R, cf.D, w.wq, QD, w.wk, KD, w.wv, QKV,
-                at<void>(c, c.L.qkv), QKV, nullptr, &cd, s);
+    dense_gemm(c, GEMM_QKV_CACHE, at<void>(c, c.L.u), R, cf.D, w.wq, QD, w.wk, KD, w.wv, QKV,
+               at<void>(c, c.L.qkv), QKV, nullptr, &cd);
     if (taps) tap_copy(taps->qkv ? (char*)taps->qkv + (size_t)l * R * QKV * a : nullptr,
                        at<void>(c, c.L.qkv), (size_t)R * QKV * a, s);
     if (l == cf.L - 1) break;  // nothing downstream reads the last layer's output
@@ -315,8 +375,8 @@ dg_status dg_denoise_pass(const dg_model* m, const dg_kv* kv, const int32_t* can
                     at<void>(c, c.L.u), s);
   for (int l = 0; l < cf.L; l++) {
     const dg_layer_weights& w = m->w.layers[l];
-    launch_gemm(act, GEMM_STORE, at<void>(c, c.L.u), R, cf.D, w.wq, QD, w.wk, KD, w.wv, QKV,
-                at<void>(c, c.L.qkv), QKV, nullptr, nullptr, s);
+    dense_gemm(c, GEMM_STORE, at<void>(c, c.L.u), R, cf.D, w.wq, QD, w.wk, KD, w.wv, QKV,
+               at<void>(c, c.L.qkv), QKV, nullptr, nullptr);
     if (taps) tap_copy(taps->qkv ? (char*)taps->qkv + (size_t)l * R * QKV * a : nullptr,
                        at<void>(c, c.L.qkv), (size_t)R * QKV * a, s);
     const char* qkv = at<char>(c, c.L.qkv);
@@ -329,11 +389,30 @@ dg_status dg_denoise_pass(const dg_model* m, const dg_kv* kv, const int32_t* can
     moe_block(c, l, l + 1 < cf.L ? m->w.layers[l + 1].g1 : m->w.gf);
   }
   // head: logits tiles reduced to (max, argmax, sum exp), merged per row
-  launch_lmhead(act, at<void>(c, c.L.u), R, cf.D, m->w.lm, cf.V, at<float>(c, c.L.lpm),
-                at<int32_t>(c, c.L.lpi), at<float>(c, c.L.lps), taps ? taps->logits : nullptr, s);
+  int nparts;
+  if (R <= HEAD_STREAM_MAX_ROWS) {
+    StreamGemm g{};
+    g.A = at<void>(c, c.L.u);
+    g.M = R;
+    g.K = cf.D;
+    g.W0 = m->w.lm;
+    g.n1 = cf.V;
+    g.N = cf.V;
+    g.nchunks = (cf.V + 63) / 64;
+    g.pmax = at<float>(c, c.L.lpm);
+    g.pidx = at<int32_t>(c, c.L.lpi);
+    g.psum = at<float>(c, c.L.lps);
+    g.logits = taps ? taps->logits : nullptr;
+    launch_stream_gemm(act, cf.act_dtype, SG_LMHEAD, g, (R + STREAM_TILE - 1) / STREAM_TILE, s);
+    nparts = g.nchunks;
+  } else {
+    launch_lmhead(act, at<void>(c, c.L.u), R, cf.D, m->w.lm, cf.V, at<float>(c, c.L.lpm),
+                  at<int32_t>(c, c.L.lpi), at<float>(c, c.L.lps), taps ? taps->logits : nullptr, s);
+    nparts = lm_tiles(cf.V);
+  }
   if (taps) tap_copy(taps->uf, at<void>(c, c.L.u), (size_t)R * cf.D * a, s);
-  launch_lm_merge(at<float>(c, c.L.lpm), at<int32_t>(c, c.L.lpi), at<float>(c, c.L.lps), R,
-                  lm_tiles(cf.V), argmax, conf, s);
+  launch_lm_merge(at<float>(c, c.L.lpm), at<int32_t>(c, c.L.lpi), at<float>(c, c.L.lps), R, nparts,
+                  argmax, conf, s);
   return check_hip();
 }
 

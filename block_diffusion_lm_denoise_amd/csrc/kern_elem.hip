@@ -7,6 +7,9 @@
 
 namespace dg {
 
+// Row kernels: one block of 256 threads per token row, 8 consecutive elements
+// per thread and step (D is a multiple of 128).
+
 // x[row] = emb[tok[row]] (copied), u[row] = round(x * rsqrt(mean(x^2)+eps) * g)
 // (token ids outside [0, V) are clamped into range rather than read out of bounds)
 template <typename TA>
@@ -20,14 +23,22 @@ __global__ __launch_bounds__(256) void embed_norm_k(const int32_t* __restrict__ 
   const int tk = min(max(tok[row], 0), V - 1);
   const TA* src = emb + (size_t)tk * D;
   float ss = 0.f;
-  for (int d = threadIdx.x; d < D; d += 256) {
-    float v = ldx(src, d);
-    ss += v * v;
-    x[row * D + d] = src[d];
+  for (int c = threadIdx.x * 8; c < D; c += 2048) {
+    float v[8];
+    ld8(src + c, v);
+    st8(x + row * D + c, v);
+#pragma unroll
+    for (int i = 0; i < 8; i++) ss += v[i] * v[i];
   }
   ss = block_sum256(ss, red);
   const float r = rsqrtf(ss / (float)D + eps);
-  for (int d = threadIdx.x; d < D; d += 256) stx(u, row * D + d, ldx(src, d) * r * g[d]);
+  for (int c = threadIdx.x * 8; c < D; c += 2048) {
+    float v[8];
+    ld8(src + c, v);
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = v[i] * r * g[c + i];
+    st8(u + row * D + c, v);
+  }
 }
 
 template <typename TA>
@@ -36,13 +47,21 @@ __global__ __launch_bounds__(256) void rmsnorm_k(const TA* __restrict__ x, const
   __shared__ float red[4];
   const size_t row = blockIdx.x;
   float ss = 0.f;
-  for (int d = threadIdx.x; d < D; d += 256) {
-    float v = ldx(x, row * D + d);
-    ss += v * v;
+  for (int c = threadIdx.x * 8; c < D; c += 2048) {
+    float v[8];
+    ld8(x + row * D + c, v);
+#pragma unroll
+    for (int i = 0; i < 8; i++) ss += v[i] * v[i];
   }
   ss = block_sum256(ss, red);
   const float r = rsqrtf(ss / (float)D + eps);
-  for (int d = threadIdx.x; d < D; d += 256) stx(u, row * D + d, ldx(x, row * D + d) * r * g[d]);
+  for (int c = threadIdx.x * 8; c < D; c += 2048) {
+    float v[8];
+    ld8(x + row * D + c, v);
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = v[i] * r * g[c + i];
+    st8(u + row * D + c, v);
+  }
 }
 
 // x = round(x1 + sum_j g_j y_j) in slot order j; u = round(rmsnorm(x) * gnext)
@@ -63,16 +82,33 @@ __global__ __launch_bounds__(256) void combine_norm_k(const TA* __restrict__ x1,
   }
   __syncthreads();
   float ss = 0.f;
-  for (int d = threadIdx.x; d < D; d += 256) {
-    float mix = 0.f;
-    for (int j = 0; j < k; j++) mix += gs[j] * ldx(Y, (size_t)rs[j] * D + d);
-    float v = rnd(ldx(x1, row * D + d) + mix, x);
-    stx(x, row * D + d, v);
-    ss += v * v;
+  for (int c = threadIdx.x * 8; c < D; c += 2048) {
+    float acc[8], mix[8], y[8];
+    ld8(x1 + row * D + c, acc);
+#pragma unroll
+    for (int i = 0; i < 8; i++) mix[i] = 0.f;
+    for (int j = 0; j < k; j++) {
+      ld8(Y + (size_t)rs[j] * D + c, y);
+      const float gj = gs[j];
+#pragma unroll
+      for (int i = 0; i < 8; i++) mix[i] += gj * y[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      acc[i] = rnd(acc[i] + mix[i], x);
+      ss += acc[i] * acc[i];
+    }
+    st8(x + row * D + c, acc);
   }
   ss = block_sum256(ss, red);
   const float r = rsqrtf(ss / (float)D + eps);
-  for (int d = threadIdx.x; d < D; d += 256) stx(u, row * D + d, ldx(x, row * D + d) * r * gnext[d]);
+  for (int c = threadIdx.x * 8; c < D; c += 2048) {
+    float v[8];
+    ld8(x + row * D + c, v);
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = v[i] * r * gnext[c + i];
+    st8(u + row * D + c, v);
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -1,5 +1,5 @@
-// kern_moe.hip -- MoE routing (top-k, permutation) and the weight-streaming
-// grouped expert GEMMs used when few rows route to each expert.
+// kern_moe.hip -- MoE routing: top-k selection with gates, and the permutation
+// that groups the (token, slot) entries by expert into row tiles.
 //
 // Every canvas token goes through the router and selects k experts; a pass
 // therefore reads the union of the selected experts (newsletter comment under
@@ -144,163 +144,154 @@ __global__ __launch_bounds__(256) void plan_k(const int32_t* __restrict__ ids, i
     tiles[tst[e] + i] = make_int4(e, off[e] + i * tile_rows, min(tile_rows, ce - i * tile_rows), 0);
 }
 
-// ---------------------------------------------------------------------------
-// Weight-streaming grouped GEMM.  One block = one row tile (<= 32 rows routed
-// to one expert) x 64 weight rows.  The four waves split the contraction in
-// 64-element chunks (wave w takes chunks w, w+4, ...), load A and B fragments
-// straight from memory (no LDS for the weights: each weight byte is used by
-// one block only), and reduce their partial tiles through LDS at the end.
-//   gate/up: weight rows = [gate f0..f0+15, up f0.., gate f0+16.., up f0+16..]
-//            for 32 SwiGLU outputs; A rows gathered through perm.
-//   down:    64 output columns; A rows are the permuted SwiGLU rows.
-// ---------------------------------------------------------------------------
-template <typename TA, typename TW>
-__device__ __forceinline__ void load_wfrag(typename FragOf<TA>::type& f, const TW* p);
-template <>
-__device__ __forceinline__ void load_wfrag<uint16_t, uint16_t>(FragBF& f, const uint16_t* p) {
-  load_frag(f, p);
-}
-template <>
-__device__ __forceinline__ void load_wfrag<uint16_t, uint8_t>(FragBF& f, const uint8_t* p) {
-  load_frag_fp8(f, p);
-}
-template <>
-__device__ __forceinline__ void load_wfrag<float, float>(FragF32& f, const float* p) {
-  load_frag(f, p);
-}
 
-struct StreamArgs {
-  const void* A;          // gate/up: u2 [tokens][D]; down: H [slots][F]
-  const int32_t* perm;    // gate/up only
-  int k;
-  const void* W1;         // gate/up: wg; down: wd
-  const void* W2;         // gate/up: wu
-  const float* escale;
-  const int4* tiles;
-  const int32_t* ntiles;
-  int K;                  // contraction length (D or F)
-  int NW;                 // rows per expert of W1 (F for gate/up, D for down)
-  int ldo;                // output row length (F or D)
-  void* out;
-};
-
-template <typename TA, typename TW, bool GATEUP>
-__global__ __launch_bounds__(256) void moe_stream_k(StreamArgs a) {
+// ---------------------------------------------------------------------------
+// route_k: RMSNorm of x1, router logits and top-k in one kernel for a tile of
+// 16 tokens.  The normalised rows stay in LDS as the A operand of the router
+// MFMAs (waves split the experts in 16-column tiles, W_r fragments come from
+// L2); the logits go to LDS and each wave then ranks 4 of the tokens.
+// ---------------------------------------------------------------------------
+template <typename TA>
+__global__ __launch_bounds__(256) void route_k(RouteArgs a) {
   typedef typename FragOf<TA>::type Frag;
-  __shared__ float red[4][8][64][4];  // [wave][rt*4+ct][lane][i]  32 KB
-  const int tile_id = blockIdx.x;
-  if (tile_id >= *a.ntiles) return;
-  const int4 tl = a.tiles[tile_id];
-  const int e = tl.x, row0 = tl.y, nrows = tl.z;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int l16 = lane & 15, g = lane >> 4;
-  const int K = a.K;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+  const int D = a.D, E = a.E;
+  const int LDA = D + 16 / (int)sizeof(TA);            // padded A row (elements)
+  TA* sa = reinterpret_cast<TA*>(smem_raw);             // [16][LDA]
+  float* sl = reinterpret_cast<float*>(smem_raw + (size_t)16 * LDA * sizeof(TA));  // [16][E]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
+  const int row0 = blockIdx.x * 16;
+  const int nrows = min(16, a.rows - row0);
 
-  // A row pointers (2 row tiles) and weight row pointers (4 column tiles)
-  const TA* arow[2];
-#pragma unroll
-  for (int rt = 0; rt < 2; rt++) {
-    const int r = rt * 16 + l16;
-    if (r < nrows) {
-      const int slot = row0 + r;
-      const size_t src = GATEUP ? (size_t)(a.perm[slot] / a.k) : (size_t)slot;
-      arow[rt] = (const TA*)a.A + src * K;
-    } else {
-      arow[rt] = nullptr;
+  // ---- RMSNorm: wave w normalises rows w, w+4, w+8, w+12 ----
+  for (int rr = w; rr < 16; rr += 4) {
+    TA* dst = sa + rr * LDA;
+    if (rr >= nrows) {
+      for (int d = lane; d < D; d += 64) dst[d] = 0;
+      continue;
+    }
+    const TA* src = (const TA*)a.x1 + (size_t)(row0 + rr) * D;
+    float ss = 0.f;
+    for (int d = lane; d < D; d += 64) {
+      const float v = ldx(src, d);
+      ss += v * v;
+    }
+    ss = wave_sum(ss);
+    const float r = rsqrtf(ss / (float)D + a.eps);
+    for (int d = lane; d < D; d += 64) {
+      const float v = ldx(src, d) * r * a.g2[d];
+      stx(dst, d, v);
+      stx((TA*)a.u2, (size_t)(row0 + rr) * D + d, v);
     }
   }
-  const TW* wrow[4];
-  int f0 = 0;
-  if (GATEUP) {
-    f0 = blockIdx.y * 32;
-#pragma unroll
-    for (int ct = 0; ct < 4; ct++) {
-      const int f = f0 + 16 * (ct >> 1) + l16;
-      const TW* base = (const TW*)((ct & 1) ? a.W2 : a.W1);
-      wrow[ct] = base + ((size_t)e * a.NW + f) * K;
-    }
-  } else {
-    f0 = blockIdx.y * 64;
-#pragma unroll
-    for (int ct = 0; ct < 4; ct++)
-      wrow[ct] = (const TW*)a.W1 + ((size_t)e * a.NW + f0 + 16 * ct + l16) * K;
-  }
-
-  f32x4_t acc[2][4];
-#pragma unroll
-  for (int rt = 0; rt < 2; rt++)
-#pragma unroll
-    for (int ct = 0; ct < 4; ct++) acc[rt][ct] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-
-  const int nch = K / 64;
-
-  for (int ch = w; ch < nch; ch += 4) {
-#pragma unroll
-    for (int s = 0; s < 2; s++) {
-      const int kk = ch * 64 + s * 32 + 8 * g;
-      Frag af[2], bf[4];
-#pragma unroll
-      for (int ct = 0; ct < 4; ct++) load_wfrag<TA, TW>(bf[ct], wrow[ct] + kk);
-#pragma unroll
-      for (int rt = 0; rt < 2; rt++) {
-        if (arow[rt]) load_frag(af[rt], arow[rt] + kk);
-        else zero_frag(af[rt]);
-      }
-#pragma unroll
-      for (int rt = 0; rt < 2; rt++)
-#pragma unroll
-        for (int ct = 0; ct < 4; ct++) mma(acc[rt][ct], af[rt], bf[ct]);
-    }
-  }
-
-#pragma unroll
-  for (int rt = 0; rt < 2; rt++)
-#pragma unroll
-    for (int ct = 0; ct < 4; ct++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) red[w][rt * 4 + ct][lane][i] = acc[rt][ct][i];
   __syncthreads();
 
-  TA* out = (TA*)a.out;
-  if (GATEUP) {
-    // thread -> (row tile, f half); combines gate tile 2*fh and up tile 2*fh+1
-    const int combo = threadIdx.x >> 6, rt = combo >> 1, fh = combo & 1;
-    float sg = 1.f, su = 1.f;
-    if (a.escale) {
-      sg = a.escale[e * 3 + 0];
-      su = a.escale[e * 3 + 1];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      float gv = 0.f, uv = 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; q++) {
-        gv += red[q][rt * 4 + 2 * fh][lane][i];
-        uv += red[q][rt * 4 + 2 * fh + 1][lane][i];
-      }
-      const int r = rt * 16 + 4 * g + i;
-      if (r < nrows) {
-        gv *= sg;
-        uv *= su;
-        const float h = gv / (1.f + expf(-gv)) * uv;
-        stx(out, (size_t)(row0 + r) * a.ldo + f0 + 16 * fh + l16, h);
-      }
+  // ---- router logits: column tiles of 16 experts split over the waves ----
+  if (a.inject) {
+    for (int i = threadIdx.x; i < 16 * E; i += 256) {
+      const int rr = i / E, e = i % E;
+      sl[i] = rr < nrows ? a.inject[(size_t)(row0 + rr) * E + e] : 0.f;
     }
   } else {
-    const float sd = a.escale ? a.escale[e * 3 + 2] : 1.f;
+    const int nct = (E + 15) / 16;
+    for (int ct = w; ct < nct; ct += 4) {
+      const int e = ct * 16 + l16;
+      const TA* wr = e < E ? (const TA*)a.wr + (size_t)e * D : nullptr;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < D; k0 += 128) {   // D is a multiple of 128
+        Frag af[4], bf[4];
 #pragma unroll
-    for (int pass = 0; pass < 2; pass++) {
-      const int combo = pass * 4 + (threadIdx.x >> 6), rt = combo >> 2, ct = combo & 3;
+        for (int u = 0; u < 4; u++) {
+          load_frag(af[u], sa + l16 * LDA + k0 + 32 * u + 8 * g);
+          if (wr) load_frag(bf[u], wr + k0 + 32 * u + 8 * g);
+          else zero_frag(bf[u]);
+        }
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        float v = 0.f;
+        for (int u = 0; u < 4; u++) mma(acc, af[u], bf[u]);
+      }
 #pragma unroll
-        for (int q = 0; q < 4; q++) v += red[q][rt * 4 + ct][lane][i];
-        const int r = rt * 16 + 4 * g + i;
-        if (r < nrows) stx(out, (size_t)(row0 + r) * a.ldo + f0 + 16 * ct + l16, v * sd);
+      for (int i = 0; i < 4; i++)
+        if (e < E) sl[(4 * g + i) * E + e] = acc[i];
+    }
+  }
+  __syncthreads();
+  if (a.logits)
+    for (int i = threadIdx.x; i < nrows * E; i += 256)
+      a.logits[(size_t)row0 * E + i] = sl[i];
+
+  // ---- top-k: wave w ranks rows w, w+4, w+8, w+12 ----
+  for (int rr = w; rr < nrows; rr += 4) {
+    float v[4];
+    bool taken[4];
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      const int e = lane + 64 * c;
+      const float x = e < E ? sl[rr * E + e] : -INFINITY;
+      v[c] = x != x ? -INFINITY : x;
+      taken[c] = e >= E;
+    }
+    float sel_v[8];
+    int sel_i[8];
+    for (int j = 0; j < a.k; j++) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int c = 0; c < 4; c++)
+        if (!taken[c] && better(v[c], lane + 64 * c, bv, bi)) {
+          bv = v[c];
+          bi = lane + 64 * c;
+        }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bi, o, 64);
+        if (better(ov, oi, bv, bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      sel_v[j] = bv;
+      sel_i[j] = bi;
+#pragma unroll
+      for (int c = 0; c < 4; c++)
+        if (lane + 64 * c == bi) taken[c] = true;
+    }
+    if (lane == 0) {
+      float den = 0.f;
+      for (int j = 0; j < a.k; j++) den += expf(sel_v[j] - sel_v[0]);
+      const size_t row = (size_t)(row0 + rr);
+      for (int j = 0; j < a.k; j++) {
+        a.ids[row * a.k + j] = sel_i[j];
+        a.gates[row * a.k + j] = expf(sel_v[j] - sel_v[0]) / den;
       }
     }
   }
+}
+
+size_t route_smem_bytes(int act, int D, int E) {
+  const size_t esz = act == ACT_BF16 ? 2 : 4;
+  return (size_t)16 * (D + 16 / esz) * esz + (size_t)16 * E * 4;
+}
+
+bool launch_route(int act, const RouteArgs& a, hipStream_t s) {
+  constexpr size_t kMaxSmem = 96 * 1024;
+  const size_t smem = route_smem_bytes(act, a.D, a.E);
+  if (smem > kMaxSmem) return false;
+  // allow more than the default 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU)
+  static const bool attr_set = [] {
+    hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_k<uint16_t>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxSmem);
+    hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_k<float>),
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxSmem);
+    return e1 == hipSuccess && e2 == hipSuccess;
+  }();
+  if (!attr_set && smem > 64 * 1024) return false;
+  const int blocks = (a.rows + 15) / 16;
+  if (act == ACT_BF16)
+    route_k<uint16_t><<<blocks, 256, smem, s>>>(a);
+  else
+    route_k<float><<<blocks, 256, smem, s>>>(a);
+  return true;
 }
 
 // ---------------------------------------------------------------------------
@@ -313,29 +304,6 @@ void launch_plan(const int32_t* ids, int rows, int k, int E, int tile_rows, int3
                  int32_t* offsets, int32_t* perm, int32_t* inv, int4* tiles, int32_t* ntiles,
                  hipStream_t s) {
   plan_k<<<E, 256, 0, s>>>(ids, rows, k, E, tile_rows, counts, offsets, perm, inv, tiles, ntiles);
-}
-
-template <bool GATEUP>
-static void stream_dispatch(int act, int wdt, const StreamArgs& a, dim3 grid, hipStream_t s) {
-  if (act == ACT_F32)
-    moe_stream_k<float, float, GATEUP><<<grid, 256, 0, s>>>(a);
-  else if (wdt == DG_FP8E4M3)
-    moe_stream_k<uint16_t, uint8_t, GATEUP><<<grid, 256, 0, s>>>(a);
-  else
-    moe_stream_k<uint16_t, uint16_t, GATEUP><<<grid, 256, 0, s>>>(a);
-}
-
-void launch_gateup_stream(int act, const void* u2, const int32_t* perm, int k, const MoeW& w,
-                          const int4* tiles, const int32_t* ntiles, int max_tiles, int D, int F,
-                          void* H, hipStream_t s) {
-  StreamArgs a{u2, perm, k, w.wg, w.wu, w.escale, tiles, ntiles, D, F, F, H};
-  stream_dispatch<true>(act, w.wdt, a, dim3(max_tiles, F / 32), s);
-}
-
-void launch_down_stream(int act, const void* H, const MoeW& w, const int4* tiles,
-                        const int32_t* ntiles, int max_tiles, int D, int F, void* Y, hipStream_t s) {
-  StreamArgs a{H, nullptr, 0, w.wd, nullptr, w.escale, tiles, ntiles, F, D, D, Y};
-  stream_dispatch<false>(act, w.wdt, a, dim3(max_tiles, D / 64), s);
 }
 
 }  // namespace dg

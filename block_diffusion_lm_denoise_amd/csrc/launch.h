@@ -39,6 +39,20 @@ void launch_lm_merge(const float* pmax, const int32_t* pidx, const float* psum, 
 // ---- MoE routing (kern_moe.hip) ----
 void launch_topk(const float* logits, int rows, int E, int k, int32_t* ids, float* gates,
                  hipStream_t s);
+// fused RMSNorm + router logits + top-k (false if D does not fit the LDS tile)
+struct RouteArgs {
+  const void* x1;
+  const float* g2;
+  const void* wr;
+  int rows, D, E, k;
+  float eps;
+  const float* inject;  // optional [rows][E] logits to route on
+  void* u2;             // out [rows][D]
+  float* logits;        // optional out [rows][E]
+  int32_t* ids;
+  float* gates;
+};
+bool launch_route(int act, const RouteArgs& a, hipStream_t s);
 // counts/offsets/perm/inv + row tiles of at most tile_rows rows per expert
 void launch_plan(const int32_t* ids, int rows, int k, int E, int tile_rows, int32_t* counts,
                  int32_t* offsets, int32_t* perm, int32_t* inv, int4* tiles, int32_t* ntiles,
@@ -51,12 +65,6 @@ struct MoeW {
   const float* escale;  // [E][3] or null
   int wdt;              // DG_F32 / DG_BF16 / DG_FP8E4M3
 };
-// skinny grouped GEMMs (row tiles of <= 32 rows, weights streamed, split-K in the block)
-void launch_gateup_stream(int act, const void* u2, const int32_t* perm, int k, const MoeW& w,
-                          const int4* tiles, const int32_t* ntiles, int max_tiles, int D, int F,
-                          void* H, hipStream_t s);
-void launch_down_stream(int act, const void* H, const MoeW& w, const int4* tiles,
-                        const int32_t* ntiles, int max_tiles, int D, int F, void* Y, hipStream_t s);
 
 // ---- LDS-tiled MFMA GEMMs (kern_gemm.hip) ----
 enum GemmMode { GEMM_STORE = 0, GEMM_RESID = 1, GEMM_F32 = 2, GEMM_QKV_CACHE = 3 };
@@ -80,6 +88,35 @@ void launch_down_lds(int act, const void* H, const MoeW& w, const int4* tiles,
 int lm_tiles(int V);
 void launch_lmhead(int act, const void* uf, int M, int D, const void* lm, int V, float* pmax,
                    int32_t* pidx, float* psum, float* logits, hipStream_t s);
+
+// ---- weight-streaming MFMA GEMM for few rows (kern_stream.hip) ----
+enum StreamMode { SG_STORE = 0, SG_RESID = 1, SG_F32 = 2, SG_QKV_CACHE = 3, SG_GATEUP = 4,
+                  SG_DOWN = 5, SG_LMHEAD = 6 };
+struct StreamGemm {
+  const void* A;          // activations [rows][K] (gate/up: gathered through perm)
+  int M, K;
+  const int32_t* perm;    // gate/up: slot -> token*k + j
+  int k;
+  const void* W0;         // weights: dense rows [0,n1) / gate / down / head
+  const void* W1;         // dense rows [n1,n1+n2) / up
+  const void* W2;         // dense rows [n1+n2,N)
+  int n1, n2, N;          // dense / head output columns
+  int NW;                 // grouped: rows per expert of W0
+  const float* escale;    // grouped fp8: [E][3]
+  const int4* tiles;      // grouped: (expert, first row, rows)
+  const int32_t* ntiles;
+  int nchunks;            // 64-weight-row chunks per row tile (gate/up: F/32)
+  void* out;
+  int ldo;
+  const void* R;          // residual (SG_RESID)
+  CacheDst cache;         // SG_QKV_CACHE
+  float* pmax;            // SG_LMHEAD partials [rows][nchunks]
+  int32_t* pidx;
+  float* psum;
+  float* logits;          // SG_LMHEAD optional tap [rows][N]
+};
+void launch_stream_gemm(int act, int wdt, int mode, const StreamGemm& a, int ntiles_max,
+                        hipStream_t s);
 
 // ---- attention (kern_attn.hip) ----
 struct AttnArgsHost {
