@@ -118,6 +118,13 @@ void tap_copy(void* dst, const void* src, size_t bytes, hipStream_t s) {
   if (dst && bytes) (void)hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);
 }
 
+// waves splitting the contraction: 4, or 2 when 4 would leave each wave an odd
+// number of 64-element pieces (the pipeline works on pairs)
+int stream_kw(int K) {
+  const int nch = K / 64, per4 = (nch + 3) / 4;
+  return (per4 % 2 == 1 && nch % 2 == 0) ? 2 : 4;
+}
+
 // dense projection C = A W^T (W rows stacked from up to three matrices):
 // weight streaming for few rows, LDS-tiled MFMA GEMM for many
 void dense_gemm(const Ctx& c, int mode, const void* A, int M, int K, const void* B0, int n1,
@@ -136,14 +143,15 @@ void dense_gemm(const Ctx& c, int mode, const void* A, int M, int K, const void*
     g.n1 = n1;
     g.n2 = n2;
     g.N = N;
-    g.nchunks = (N + 63) / 64;
+    const int kw = stream_kw(K);
+    g.nchunks = (N + 64 * (4 / kw) - 1) / (64 * (4 / kw));
     g.out = C;
     g.ldo = ldc;
     g.R = R;
     if (cache) g.cache = *cache;
     const int sm = mode == GEMM_STORE ? SG_STORE : mode == GEMM_RESID ? SG_RESID
                  : mode == GEMM_F32 ? SG_F32 : SG_QKV_CACHE;
-    launch_stream_gemm(act, cf.act_dtype, sm, g, (M + STREAM_TILE - 1) / STREAM_TILE, c.s);
+    launch_stream_gemm(act, cf.act_dtype, sm, kw, g, (M + STREAM_TILE - 1) / STREAM_TILE, c.s);
   } else {
     launch_gemm(act, mode, A, M, K, B0, n1, B1, n2, B2, N, C, ldc, R, cache, c.s);
   }
@@ -214,10 +222,11 @@ void moe_block(const Ctx& c, int l, const float* gnext) {
     g.W0 = w.wg;
     g.W1 = w.wu;
     g.NW = cf.F;
-    g.nchunks = cf.F / 32;
+    const int kw = stream_kw(cf.D);
+    g.nchunks = cf.F / (32 * (4 / kw));
     g.out = at<void>(c, c.L.H);
     g.ldo = cf.F;
-    launch_stream_gemm(act, cf.expert_dtype, SG_GATEUP, g, max_tiles, s);
+    launch_stream_gemm(act, cf.expert_dtype, SG_GATEUP, kw, g, max_tiles, s);
   } else {
     launch_gateup_lds(act, at<void>(c, c.L.u2), at<int32_t>(c, c.L.perm), cf.k, mw,
                       at<int4>(c, c.L.tiles), at<int32_t>(c, c.L.ntiles), max_tiles, cf.D, cf.F,
@@ -235,10 +244,11 @@ void moe_block(const Ctx& c, int l, const float* gnext) {
     g.W1 = nullptr;
     g.NW = cf.D;
     g.N = cf.D;
-    g.nchunks = cf.D / 64;
+    const int kw = stream_kw(cf.F);
+    g.nchunks = cf.D / (64 * (4 / kw));
     g.out = at<void>(c, c.L.Y);
     g.ldo = cf.D;
-    launch_stream_gemm(act, cf.expert_dtype, SG_DOWN, g, max_tiles, s);
+    launch_stream_gemm(act, cf.expert_dtype, SG_DOWN, kw, g, max_tiles, s);
   } else {
     launch_down_lds(act, at<void>(c, c.L.H), mw, at<int4>(c, c.L.tiles), at<int32_t>(c, c.L.ntiles),
                     max_tiles, cf.D, cf.F, at<void>(c, c.L.Y), s);
@@ -403,7 +413,7 @@ dg_status dg_denoise_pass(const dg_model* m, const dg_kv* kv, const int32_t* can
     g.pidx = at<int32_t>(c, c.L.lpi);
     g.psum = at<float>(c, c.L.lps);
     g.logits = taps ? taps->logits : nullptr;
-    launch_stream_gemm(act, cf.act_dtype, SG_LMHEAD, g, (R + STREAM_TILE - 1) / STREAM_TILE, s);
+    launch_stream_gemm(act, cf.act_dtype, SG_LMHEAD, 4, g, (R + STREAM_TILE - 1) / STREAM_TILE, s);
     nparts = g.nchunks;
   } else {
     launch_lmhead(act, at<void>(c, c.L.u), R, cf.D, m->w.lm, cf.V, at<float>(c, c.L.lpm),

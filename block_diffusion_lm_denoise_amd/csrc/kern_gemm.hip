@@ -37,8 +37,11 @@ struct Mainloop {
     return FP8 ? (threadIdx.x & 3) * 16 : (threadIdx.x & 7) * (16 / (int)sizeof(TA));
   }
 
-  // ap[p] / bp[p]: row pointers of the rows this thread stages (nullptr = zero row)
-  static __device__ __forceinline__ void run(const TA* const (&ap)[A_LD], const TW* const (&bp)[B_LD],
+  // ap[p] / bp[p]: row pointers of the rows this thread stages; rows with
+  // aok/bok false point at a valid row and are zeroed by a select, so the load
+  // path has no branches (the prefetch of the next tile stays in flight)
+  static __device__ __forceinline__ void run(const TA* const (&ap)[A_LD], const bool (&aok)[A_LD],
+                                             const TW* const (&bp)[B_LD], const bool (&bok)[B_LD],
                                              int K, TA* smem, f32x4_t (&acc)[RT][CT]) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int wm = w >> 1, wn = w & 1, l16 = lane & 15, g = lane >> 4;
@@ -52,15 +55,23 @@ struct Mainloop {
     auto gload = [&](int kt) {
       const int k0 = kt * BK;
 #pragma unroll
-      for (int p = 0; p < A_LD; p++)
-        ra[p] = ap[p] ? *reinterpret_cast<const uint4*>(ap[p] + k0 + a_col()) : make_uint4(0, 0, 0, 0);
+      for (int p = 0; p < A_LD; p++) ra[p] = *reinterpret_cast<const uint4*>(ap[p] + k0 + a_col());
 #pragma unroll
-      for (int p = 0; p < B_LD; p++)
-        rb[p] = bp[p] ? *reinterpret_cast<const uint4*>(bp[p] + k0 + b_col()) : make_uint4(0, 0, 0, 0);
+      for (int p = 0; p < B_LD; p++) rb[p] = *reinterpret_cast<const uint4*>(bp[p] + k0 + b_col());
+    };
+    auto zero_if = [](uint4& u, bool ok) {
+      u.x = ok ? u.x : 0u;
+      u.y = ok ? u.y : 0u;
+      u.z = ok ? u.z : 0u;
+      u.w = ok ? u.w : 0u;
     };
     auto sstore = [&](int buf) {
       TA* sa = smem + buf * (BM + BN) * LDK;
       TA* sb = sa + BM * LDK;
+#pragma unroll
+      for (int p = 0; p < A_LD; p++) zero_if(ra[p], aok[p]);
+#pragma unroll
+      for (int p = 0; p < B_LD; p++) zero_if(rb[p], bok[p]);
 #pragma unroll
       for (int p = 0; p < A_LD; p++) *reinterpret_cast<uint4*>(sa + a_row(p) * LDK + a_col()) = ra[p];
 #pragma unroll
@@ -76,26 +87,41 @@ struct Mainloop {
       }
     };
 
+    // fragments of one 32-wide contraction step, double-buffered so the LDS
+    // reads of step ks+1 are in flight while the MFMAs of step ks run
+    constexpr int KS = BK / 32;
+    Frag af[2][RT], bf[2][CT];
+    auto lload = [&](int buf, int ks, int fb) {
+      const TA* sa = smem + buf * (BM + BN) * LDK;
+      const TA* sb = sa + BM * LDK;
+#pragma unroll
+      for (int rt = 0; rt < RT; rt++)
+        load_frag(af[fb][rt], sa + (wm * (BM / 2) + 16 * rt + l16) * LDK + 32 * ks + 8 * g);
+#pragma unroll
+      for (int ct = 0; ct < CT; ct++)
+        load_frag(bf[fb][ct], sb + (wn * (BN / 2) + 16 * ct + l16) * LDK + 32 * ks + 8 * g);
+    };
+    auto mmas = [&](int fb) {
+#pragma unroll
+      for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+        for (int ct = 0; ct < CT; ct++) mma(acc[rt][ct], af[fb][rt], bf[fb][ct]);
+    };
+
     gload(0);
     sstore(0);
     __syncthreads();
     for (int kt = 0; kt < nk; kt++) {
-      if (kt + 1 < nk) gload(kt + 1);
-      const TA* sa = smem + (kt & 1) * (BM + BN) * LDK;
-      const TA* sb = sa + BM * LDK;
+      gload(kt + 1 < nk ? kt + 1 : kt);   // clamped: always issue, stays in flight
+      __builtin_amdgcn_sched_barrier(0);
+      lload(kt & 1, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < BK / 32; ks++) {
-        Frag af[RT], bf[CT];
-#pragma unroll
-        for (int rt = 0; rt < RT; rt++)
-          load_frag(af[rt], sa + (wm * (BM / 2) + 16 * rt + l16) * LDK + 32 * ks + 8 * g);
-#pragma unroll
-        for (int ct = 0; ct < CT; ct++)
-          load_frag(bf[ct], sb + (wn * (BN / 2) + 16 * ct + l16) * LDK + 32 * ks + 8 * g);
-#pragma unroll
-        for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-          for (int ct = 0; ct < CT; ct++) mma(acc[rt][ct], af[rt], bf[ct]);
+      for (int ks = 0; ks < KS; ks++) {
+        if (ks + 1 < KS) lload(kt & 1, ks + 1, (ks + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mmas(ks & 1);
+        __builtin_amdgcn_sched_barrier(0);
       }
       if (kt + 1 < nk) sstore((kt + 1) & 1);
       __syncthreads();
@@ -129,22 +155,26 @@ __global__ __launch_bounds__(256) void gemm_dense_k(DenseArgs a) {
   const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
   const TA* ap[ML::A_LD];
   const TA* bp[ML::B_LD];
+  bool aok[ML::A_LD], bok[ML::B_LD];
 #pragma unroll
   for (int p = 0; p < ML::A_LD; p++) {
     const int r = m0 + ML::a_row(p);
-    ap[p] = r < a.M ? (const TA*)a.A + (size_t)r * a.K : nullptr;
+    aok[p] = r < a.M;
+    ap[p] = (const TA*)a.A + (size_t)(aok[p] ? r : 0) * a.K;
   }
 #pragma unroll
   for (int p = 0; p < ML::B_LD; p++) {
     const int n = n0 + ML::b_row(p);
-    const TA* q = nullptr;
-    if (n < a.n1) q = (const TA*)a.B0 + (size_t)n * a.K;
-    else if (n < a.n1 + a.n2) q = (const TA*)a.B1 + (size_t)(n - a.n1) * a.K;
-    else if (n < a.N) q = (const TA*)a.B2 + (size_t)(n - a.n1 - a.n2) * a.K;
+    bok[p] = n < a.N;
+    const int nn = bok[p] ? n : 0;
+    const TA* q;
+    if (nn < a.n1) q = (const TA*)a.B0 + (size_t)nn * a.K;
+    else if (nn < a.n1 + a.n2) q = (const TA*)a.B1 + (size_t)(nn - a.n1) * a.K;
+    else q = (const TA*)a.B2 + (size_t)(nn - a.n1 - a.n2) * a.K;
     bp[p] = q;
   }
   f32x4_t acc[ML::RT][ML::CT];
-  ML::run(ap, bp, a.K, smem, acc);
+  ML::run(ap, aok, bp, bok, a.K, smem, acc);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1, l16 = lane & 15, g = lane >> 4;
@@ -208,10 +238,12 @@ __global__ __launch_bounds__(256) void gateup_lds_k(GroupArgs a) {
   const int f0 = blockIdx.y * (BN / 2);
   const TA* ap[ML::A_LD];
   const TW* bp[ML::B_LD];
+  bool aok[ML::A_LD], bok[ML::B_LD];
 #pragma unroll
   for (int p = 0; p < ML::A_LD; p++) {
     const int r = ML::a_row(p);
-    ap[p] = r < nrows ? (const TA*)a.A + (size_t)(a.perm[row0 + r] / a.k) * a.K : nullptr;
+    aok[p] = r < nrows;
+    ap[p] = (const TA*)a.A + (size_t)(a.perm[row0 + (aok[p] ? r : 0)] / a.k) * a.K;
   }
 #pragma unroll
   for (int p = 0; p < ML::B_LD; p++) {
@@ -219,9 +251,10 @@ __global__ __launch_bounds__(256) void gateup_lds_k(GroupArgs a) {
     const int f = f0 + 16 * (n >> 5) + (n & 15);
     const TW* base = (const TW*)(((n >> 4) & 1) ? a.W2 : a.W1);
     bp[p] = base + ((size_t)e * a.NW + f) * a.K;
+    bok[p] = true;
   }
   f32x4_t acc[ML::RT][ML::CT];
-  ML::run(ap, bp, a.K, smem, acc);
+  ML::run(ap, aok, bp, bok, a.K, smem, acc);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1, l16 = lane & 15, g = lane >> 4;
@@ -255,16 +288,20 @@ __global__ __launch_bounds__(256) void down_lds_k(GroupArgs a) {
   const int n0 = blockIdx.y * BN;
   const TA* ap[ML::A_LD];
   const TW* bp[ML::B_LD];
+  bool aok[ML::A_LD], bok[ML::B_LD];
 #pragma unroll
   for (int p = 0; p < ML::A_LD; p++) {
     const int r = ML::a_row(p);
-    ap[p] = r < nrows ? (const TA*)a.A + (size_t)(row0 + r) * a.K : nullptr;
+    aok[p] = r < nrows;
+    ap[p] = (const TA*)a.A + (size_t)(row0 + (aok[p] ? r : 0)) * a.K;
   }
 #pragma unroll
-  for (int p = 0; p < ML::B_LD; p++)
+  for (int p = 0; p < ML::B_LD; p++) {
     bp[p] = (const TW*)a.W1 + ((size_t)e * a.NW + n0 + ML::b_row(p)) * a.K;
+    bok[p] = true;
+  }
   f32x4_t acc[ML::RT][ML::CT];
-  ML::run(ap, bp, a.K, smem, acc);
+  ML::run(ap, aok, bp, bok, a.K, smem, acc);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1, l16 = lane & 15, g = lane >> 4;
@@ -296,7 +333,7 @@ struct HeadArgs {
   int32_t* pidx;
   float* psum;
   float* logits;
-  int ntiles;
+  int ntiles, mtiles;
 };
 
 __device__ __forceinline__ void mrg(float& m, int& i, float& s, float m2, int i2, float s2) {
@@ -317,21 +354,29 @@ __global__ __launch_bounds__(256) void lmhead_k(HeadArgs a) {
   __shared__ __attribute__((aligned(16))) TA smem[ML::SMEM];
   __shared__ float xm[2][BM], xs[2][BM];
   __shared__ int xi[2][BM];
-  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+  // 1-D grid; the row tiles of one column tile are 8 block ids apart, so
+  // they run on the same XCD and share its L2 copy of the weight tile
+  const int b8 = blockIdx.x >> 3, mtiles = a.mtiles;
+  const int nt = (b8 / mtiles) * 8 + (blockIdx.x & 7), mt = b8 % mtiles;
+  if (nt >= a.ntiles) return;
+  const int n0 = nt * BN, m0 = mt * BM;
   const TA* ap[ML::A_LD];
   const TA* bp[ML::B_LD];
+  bool aok[ML::A_LD], bok[ML::B_LD];
 #pragma unroll
   for (int p = 0; p < ML::A_LD; p++) {
     const int r = m0 + ML::a_row(p);
-    ap[p] = r < a.M ? (const TA*)a.A + (size_t)r * a.K : nullptr;
+    aok[p] = r < a.M;
+    ap[p] = (const TA*)a.A + (size_t)(aok[p] ? r : 0) * a.K;
   }
 #pragma unroll
   for (int p = 0; p < ML::B_LD; p++) {
     const int n = n0 + ML::b_row(p);
-    bp[p] = n < a.V ? (const TA*)a.B + (size_t)n * a.K : nullptr;
+    bok[p] = n < a.V;
+    bp[p] = (const TA*)a.B + (size_t)(bok[p] ? n : 0) * a.K;
   }
   f32x4_t acc[ML::RT][ML::CT];
-  ML::run(ap, bp, a.K, smem, acc);
+  ML::run(ap, aok, bp, bok, a.K, smem, acc);
 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1, l16 = lane & 15, g = lane >> 4;
@@ -369,7 +414,7 @@ __global__ __launch_bounds__(256) void lmhead_k(HeadArgs a) {
     float m = xm[0][rl], s = xs[0][rl];
     int idx = xi[0][rl];
     mrg(m, idx, s, xm[1][rl], xi[1][rl], xs[1][rl]);
-    const size_t o = (size_t)r * a.ntiles + blockIdx.x;
+    const size_t o = (size_t)r * a.ntiles + nt;
     a.pmax[o] = m;
     a.pidx[o] = idx;
     a.psum[o] = s;
@@ -412,17 +457,26 @@ void launch_down_lds(int act, const void* H, const MoeW& w, const int4* tiles,
   else down_lds_k<uint16_t, uint16_t, 128, 128><<<grid, 256, 0, s>>>(a);
 }
 
+// row-tile height of the LM head for more than 64 rows
+#ifndef LMHEAD_BM
+#define LMHEAD_BM 128
+#endif
+static_assert(LMHEAD_BM == 128 || LMHEAD_BM == 256, "LM head row tile");
+
 int lm_tiles(int V) { return (V + 127) / 128; }
 
 void launch_lmhead(int act, const void* uf, int M, int D, const void* lm, int V, float* pmax,
                    int32_t* pidx, float* psum, float* logits, hipStream_t s) {
-  HeadArgs a{uf, M, D, lm, V, pmax, pidx, psum, logits, lm_tiles(V)};
-  if (M > 128) {
-    dim3 grid(lm_tiles(V), (M + 255) / 256);
+  const int nt = lm_tiles(V), bm = M > 64 ? LMHEAD_BM : 64;
+  HeadArgs a{uf, M, D, lm, V, pmax, pidx, psum, logits, nt, (M + bm - 1) / bm};
+  const dim3 grid(((nt + 7) / 8) * 8 * a.mtiles);
+  if (bm == 256) {
     if (act == ACT_BF16) lmhead_k<uint16_t, 256><<<grid, 256, 0, s>>>(a);
     else lmhead_k<float, 256><<<grid, 256, 0, s>>>(a);
+  } else if (bm == 128) {
+    if (act == ACT_BF16) lmhead_k<uint16_t, 128><<<grid, 256, 0, s>>>(a);
+    else lmhead_k<float, 128><<<grid, 256, 0, s>>>(a);
   } else {
-    dim3 grid(lm_tiles(V), (M + 63) / 64);
     if (act == ACT_BF16) lmhead_k<uint16_t, 64><<<grid, 256, 0, s>>>(a);
     else lmhead_k<float, 64><<<grid, 256, 0, s>>>(a);
   }

@@ -47,9 +47,12 @@ __device__ __forceinline__ void mrg3(float& m, int& i, float& s, float m2, int i
   }
 }
 
-template <typename TA, typename TW, int MODE>
+// KW waves split the contraction; the 4/KW wave groups take different 64-row
+// weight column groups (a block covers 64 * 4/KW weight rows).
+template <typename TA, typename TW, int MODE, int KW>
 __global__ __launch_bounds__(256) void wstream_k(StreamGemm a) {
   typedef typename FragOf<TA>::type Frag;
+  constexpr int CWG = 4 / KW;          // column groups per block
   __shared__ float red[4][4][64][4];   // [wave][col tile][lane][i], one 16-row tile at a time
   __shared__ float hm[4][16], hs[4][16];
   __shared__ int hi[4][16];
@@ -70,6 +73,7 @@ __global__ __launch_bounds__(256) void wstream_k(StreamGemm a) {
   }
   const int nrt = (nrows + 15) >> 4;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
+  const int kw = w % KW, cg = w / KW;  // contraction share, column group of this wave
   const int K = a.K;
 
   // A row pointers of this lane (row l16 of each 16-row tile).  Rows past the
@@ -88,14 +92,14 @@ __global__ __launch_bounds__(256) void wstream_k(StreamGemm a) {
   // W row pointers of this lane (row l16 of each 16-row column tile)
   const TW* wrow[4];
   bool wok[4];
-  const int n0 = chunk * 64;
+  const int n0 = (chunk * CWG + cg) * 64;   // first weight row (dense/down) of this wave
 #pragma unroll
   for (int ct = 0; ct < 4; ct++) {
     const TW* p;
     bool ok = true;
     if (MODE == SG_GATEUP) {
-      // 32 SwiGLU outputs per chunk: tiles [gate f, up f, gate f+16, up f+16]
-      const int f = chunk * 32 + 16 * (ct >> 1) + l16;
+      // 32 SwiGLU outputs per column group: tiles [gate f, up f, gate f+16, up f+16]
+      const int f = (chunk * CWG + cg) * 32 + 16 * (ct >> 1) + l16;
       p = (const TW*)((ct & 1) ? a.W1 : a.W0) + ((size_t)e * a.NW + f) * K;
     } else if (MODE == SG_DOWN) {
       p = (const TW*)a.W0 + ((size_t)e * a.NW + n0 + 16 * ct + l16) * K;
@@ -143,14 +147,14 @@ __global__ __launch_bounds__(256) void wstream_k(StreamGemm a) {
     }
   };
 
-  // wave w takes pieces w, w+4, w+8, ...; two register buffers, straight-line
+  // wave takes pieces kw, kw+KW, ...; two register buffers, straight-line
   // code (indices past the end are clamped and masked) so that the waits
   // before each MFMA group cover only the older buffer's loads
   const int nch = K / 64;
-  const int per = (nch + 3) / 4;
+  const int per = (nch + KW - 1) / KW;
   const int npairs = (per + 1) / 2;
-  auto cidx = [&](int i) { const int c = w + 4 * i; return c < nch ? c : nch - 1; };
-  auto cok = [&](int i) { return w + 4 * i < nch; };
+  auto cidx = [&](int i) { const int c = kw + KW * i; return c < nch ? c : nch - 1; };
+  auto cok = [&](int i) { return kw + KW * i < nch; };
   // sched_barrier pins each buffer's loads ahead of the other buffer's MFMAs
   // (otherwise the scheduler sinks them to save registers)
   load(wa, aa, cidx(0));
@@ -184,28 +188,34 @@ __global__ __launch_bounds__(256) void wstream_k(StreamGemm a) {
 #pragma unroll
       for (int i = 0; i < 4; i++) red[w][ct][lane][i] = acc[rt][ct][i];
     __syncthreads();
-    // thread (q = wave index, lane) takes column tile q
+    // thread (q = wave index, lane) takes column tile q of column group cq
+    // (KW == 4: the block's 4 tiles; KW == 2: tiles q of both groups, below)
     const int q = w;
+    auto sumk = [&](int grp, int tile, int i) {
+      float v = 0.f;
+#pragma unroll
+      for (int j = 0; j < KW; j++) v += red[grp * KW + j][tile][lane][i];
+      return v;
+    };
     float v[4];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
-      v[i] = (red[0][q][lane][i] + red[1][q][lane][i]) + (red[2][q][lane][i] + red[3][q][lane][i]);
+    for (int i = 0; i < 4; i++) v[i] = sumk(0, q, i);
     if (MODE == SG_GATEUP) {
-      // waves 0,1 own SwiGLU pairs (gate tile 2q, up tile 2q+1)
-      if (q < 2) {
+      // thread q < 2*CWG owns SwiGLU pair (group q/2, gate tile 2*(q%2), up tile 2*(q%2)+1)
+      if (q < 2 * CWG) {
+        const int grp = q >> 1, pp = q & 1;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          const float gv = ((red[0][2 * q][lane][i] + red[1][2 * q][lane][i]) +
-                            (red[2][2 * q][lane][i] + red[3][2 * q][lane][i])) * sg;
-          const float uv = ((red[0][2 * q + 1][lane][i] + red[1][2 * q + 1][lane][i]) +
-                            (red[2][2 * q + 1][lane][i] + red[3][2 * q + 1][lane][i])) * su;
+          const float gv = sumk(grp, 2 * pp, i) * sg;
+          const float uv = sumk(grp, 2 * pp + 1, i) * su;
           const int r = rt * 16 + 4 * g + i;
           if (r < nrows)
-            stx((TA*)a.out, (size_t)(row0 + r) * a.ldo + chunk * 32 + 16 * q + l16,
+            stx((TA*)a.out, (size_t)(row0 + r) * a.ldo + (chunk * CWG + grp) * 32 + 16 * pp + l16,
                 gv / (1.f + expf(-gv)) * uv);
         }
       }
     } else if (MODE == SG_LMHEAD) {
+      static_assert(MODE != SG_LMHEAD || KW == 4, "the head epilogue reduces one 64-column group");
       // per row: (max, lowest index attaining it, sum exp(l - max)) over the 64 columns
 #pragma unroll
       for (int i = 0; i < 4; i++) {
@@ -244,29 +254,32 @@ __global__ __launch_bounds__(256) void wstream_k(StreamGemm a) {
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int r = rt * 16 + 4 * g + i;
-        const int n = n0 + 16 * q + l16;
-        if (r >= nrows || n >= a.N) continue;
-        const size_t row = (size_t)(row0 + r);
-        const size_t o = row * a.ldo + n;
-        float val = v[i];
-        if (MODE == SG_DOWN) {
-          stx((TA*)a.out, o, val * sd);
-        } else if (MODE == SG_F32) {
-          ((float*)a.out)[o] = val;
-        } else {
-          if (MODE == SG_RESID) val += ldx((const TA*)a.R, o);
-          stx((TA*)a.out, o, val);
-          if (MODE == SG_QKV_CACHE && n >= a.cache.QD) {
-            const int c = n - a.cache.QD;
-            const bool isv = c >= a.cache.KD;
-            const int cc = isv ? c - a.cache.KD : c;
-            const int gh = cc / a.cache.hd, d = cc % a.cache.hd;
-            const int b = (int)(row / a.cache.T), t = (int)(row % a.cache.T);
-            const size_t co =
-                (((size_t)b * a.cache.Hkv + gh) * a.cache.cap + a.cache.len.v[b] + t) * a.cache.hd + d;
-            stx((TA*)(isv ? a.cache.v : a.cache.k), co, val);
+      for (int grp = 0; grp < CWG; grp++) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int r = rt * 16 + 4 * g + i;
+          const int n = (chunk * CWG + grp) * 64 + 16 * q + l16;
+          if (r >= nrows || n >= a.N) continue;
+          const size_t row = (size_t)(row0 + r);
+          const size_t o = row * a.ldo + n;
+          float val = grp == 0 ? v[i] : sumk(grp, q, i);
+          if (MODE == SG_DOWN) {
+            stx((TA*)a.out, o, val * sd);
+          } else if (MODE == SG_F32) {
+            ((float*)a.out)[o] = val;
+          } else {
+            if (MODE == SG_RESID) val += ldx((const TA*)a.R, o);
+            stx((TA*)a.out, o, val);
+            if (MODE == SG_QKV_CACHE && n >= a.cache.QD) {
+              const int c = n - a.cache.QD;
+              const bool isv = c >= a.cache.KD;
+              const int cc = isv ? c - a.cache.KD : c;
+              const int gh = cc / a.cache.hd, d = cc % a.cache.hd;
+              const int b = (int)(row / a.cache.T), t = (int)(row % a.cache.T);
+              const size_t co = (((size_t)b * a.cache.Hkv + gh) * a.cache.cap + a.cache.len.v[b] + t) *
+                                    a.cache.hd + d;
+              stx((TA*)(isv ? a.cache.v : a.cache.k), co, val);
+            }
           }
         }
       }
@@ -275,28 +288,42 @@ __global__ __launch_bounds__(256) void wstream_k(StreamGemm a) {
   }
 }
 
-template <int MODE>
+template <int MODE, int KW>
 static void dispatch(int act, int wdt, const StreamGemm& a, int nblocks, hipStream_t s) {
   if (nblocks <= 0) return;
   if (act == ACT_F32)
-    wstream_k<float, float, MODE><<<nblocks, 256, 0, s>>>(a);
+    wstream_k<float, float, MODE, KW><<<nblocks, 256, 0, s>>>(a);
   else if (wdt == DG_FP8E4M3)
-    wstream_k<uint16_t, uint8_t, MODE><<<nblocks, 256, 0, s>>>(a);
+    wstream_k<uint16_t, uint8_t, MODE, KW><<<nblocks, 256, 0, s>>>(a);
   else
-    wstream_k<uint16_t, uint16_t, MODE><<<nblocks, 256, 0, s>>>(a);
+    wstream_k<uint16_t, uint16_t, MODE, KW><<<nblocks, 256, 0, s>>>(a);
 }
 
-void launch_stream_gemm(int act, int wdt, int mode, const StreamGemm& a, int ntiles_max,
+// kw: waves splitting the contraction (4, or 2 when the block should cover 128
+// weight rows, e.g. a short contraction); a.nchunks counts blocks per row tile
+void launch_stream_gemm(int act, int wdt, int mode, int kw, const StreamGemm& a, int ntiles_max,
                         hipStream_t s) {
   const int nb = a.nchunks * ntiles_max;
+  if (kw == 2) {
+    switch (mode) {
+      case SG_STORE: dispatch<SG_STORE, 2>(act, wdt, a, nb, s); break;
+      case SG_RESID: dispatch<SG_RESID, 2>(act, wdt, a, nb, s); break;
+      case SG_F32: dispatch<SG_F32, 2>(act, wdt, a, nb, s); break;
+      case SG_QKV_CACHE: dispatch<SG_QKV_CACHE, 2>(act, wdt, a, nb, s); break;
+      case SG_GATEUP: dispatch<SG_GATEUP, 2>(act, wdt, a, nb, s); break;
+      case SG_DOWN: dispatch<SG_DOWN, 2>(act, wdt, a, nb, s); break;
+      default: break;
+    }
+    return;
+  }
   switch (mode) {
-    case SG_STORE: dispatch<SG_STORE>(act, wdt, a, nb, s); break;
-    case SG_RESID: dispatch<SG_RESID>(act, wdt, a, nb, s); break;
-    case SG_F32: dispatch<SG_F32>(act, wdt, a, nb, s); break;
-    case SG_QKV_CACHE: dispatch<SG_QKV_CACHE>(act, wdt, a, nb, s); break;
-    case SG_GATEUP: dispatch<SG_GATEUP>(act, wdt, a, nb, s); break;
-    case SG_DOWN: dispatch<SG_DOWN>(act, wdt, a, nb, s); break;
-    case SG_LMHEAD: dispatch<SG_LMHEAD>(act, wdt, a, nb, s); break;
+    case SG_STORE: dispatch<SG_STORE, 4>(act, wdt, a, nb, s); break;
+    case SG_RESID: dispatch<SG_RESID, 4>(act, wdt, a, nb, s); break;
+    case SG_F32: dispatch<SG_F32, 4>(act, wdt, a, nb, s); break;
+    case SG_QKV_CACHE: dispatch<SG_QKV_CACHE, 4>(act, wdt, a, nb, s); break;
+    case SG_GATEUP: dispatch<SG_GATEUP, 4>(act, wdt, a, nb, s); break;
+    case SG_DOWN: dispatch<SG_DOWN, 4>(act, wdt, a, nb, s); break;
+    case SG_LMHEAD: dispatch<SG_LMHEAD, 4>(act, wdt, a, nb, s); break;
   }
 }
 

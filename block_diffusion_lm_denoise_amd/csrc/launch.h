@@ -115,7 +115,7 @@ struct StreamGemm {
   float* psum;
   float* logits;          // SG_LMHEAD optional tap [rows][N]
 };
-void launch_stream_gemm(int act, int wdt, int mode, const StreamGemm& a, int ntiles_max,
+void launch_stream_gemm(int act, int wdt, int mode, int kw, const StreamGemm& a, int ntiles_max,
                         hipStream_t s);
 
 // ---- attention (kern_attn.hip) ----

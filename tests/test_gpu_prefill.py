@@ -116,3 +116,23 @@ def test_prefill_capacity_error_changes_nothing():
     assert e.value.status == -2
     torch.cuda.synchronize()
     assert kv.lens[0] == 8 and torch.equal(kv.k[0], k0)
+
+
+@pytest.mark.parametrize("act,expert", [("bf16", "bf16"), ("f32", "f32"), ("bf16", "fp8")])
+def test_large_prefill_uses_tiled_dense_gemm(act, expert):
+    # 3 x 400 = 1200 rows: above the weight-streaming row limit, so the dense
+    # projections take the LDS-tiled GEMM, and ~300 rows per expert the tiled
+    # grouped expert GEMMs; a ragged 1200 = 9 x 128 + 48 row tail
+    cfg = _cfg(L=2, act=act, expert=expert)
+    pair = Pair(cfg, 25)
+    B, T = 3, 400
+    toks = synth.tokens(cfg.V, (B, T), 25, "big")
+    oks, ovs = pair.om.new_cache(B, T)
+    oln = np.zeros(B, np.int32)
+    ro = pair.om.kv_prefill(oks, ovs, oln, toks.numpy(), taps=("router",))["router"]
+    kv = pair.gm.kv_cache(B, T, device=DEV)
+    ws = pair.gm.workspace(B * T, T, device=DEV)
+    pair.gm.kv_prefill(kv, toks.to(DEV), ws, inject_router=torch.from_numpy(ro).to(DEV))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(kv.lens, oln)
+    print(act, expert, "cache max-rel", _compare_caches(cfg, kv, oks, ovs, oln, "large"))
