@@ -16,7 +16,8 @@ SOURCES = ["dgpass.hip", "kern_elem.hip", "kern_moe.hip", "kern_gemm.hip", "kern
            "kern_stream.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-Wall", "-Wno-unused-result",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics",
+         "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _compile(src: str) -> str:

@@ -155,6 +155,37 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// reductions over the 16 lanes of a DPP row (lanes 16j .. 16j+15) with DPP
+// moves: two quad permutations, then the half-row and row mirrors.  Max and
+// min are exact; each lane's sum may round differently, so a sum is read from
+// one lane only.
+template <int CTRL> __device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+constexpr int DPP_QUAD_1032 = 0xB1, DPP_QUAD_2301 = 0x4E, DPP_ROW_HALF_MIRROR = 0x141,
+              DPP_ROW_MIRROR = 0x140;
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<DPP_QUAD_1032>(v));
+  v = fmaxf(v, dpp_f<DPP_QUAD_2301>(v));
+  v = fmaxf(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
+  return fmaxf(v, dpp_f<DPP_ROW_MIRROR>(v));
+}
+__device__ __forceinline__ int row16_min(int v) {
+  v = min(v, dpp_i<DPP_QUAD_1032>(v));
+  v = min(v, dpp_i<DPP_QUAD_2301>(v));
+  v = min(v, dpp_i<DPP_ROW_HALF_MIRROR>(v));
+  return min(v, dpp_i<DPP_ROW_MIRROR>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<DPP_QUAD_1032>(v);
+  v += dpp_f<DPP_QUAD_2301>(v);
+  v += dpp_f<DPP_ROW_HALF_MIRROR>(v);
+  return v + dpp_f<DPP_ROW_MIRROR>(v);
+}
+
 // deterministic block sum for blockDim.x == 256 (4 waves); red: >= 4 floats of LDS
 __device__ __forceinline__ float block_sum256(float v, float* red) {
   v = wave_sum(v);

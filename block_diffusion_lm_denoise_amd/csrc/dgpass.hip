@@ -416,9 +416,9 @@ dg_status dg_denoise_pass(const dg_model* m, const dg_kv* kv, const int32_t* can
     launch_stream_gemm(act, cf.act_dtype, SG_LMHEAD, 4, g, (R + STREAM_TILE - 1) / STREAM_TILE, s);
     nparts = g.nchunks;
   } else {
-    launch_lmhead(act, at<void>(c, c.L.u), R, cf.D, m->w.lm, cf.V, at<float>(c, c.L.lpm),
-                  at<int32_t>(c, c.L.lpi), at<float>(c, c.L.lps), taps ? taps->logits : nullptr, s);
-    nparts = lm_tiles(cf.V);
+    nparts = launch_lmhead(act, at<void>(c, c.L.u), R, cf.D, m->w.lm, cf.V, at<float>(c, c.L.lpm),
+                           at<int32_t>(c, c.L.lpi), at<float>(c, c.L.lps),
+                           taps ? taps->logits : nullptr, s);
   }
   if (taps) tap_copy(taps->uf, at<void>(c, c.L.u), (size_t)R * cf.D * a, s);
   launch_lm_merge(at<float>(c, c.L.lpm), at<int32_t>(c, c.L.lpi), at<float>(c, c.L.lps), R, nparts,

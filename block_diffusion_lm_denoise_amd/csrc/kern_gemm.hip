@@ -15,7 +15,7 @@
 
 namespace dg {
 
-template <typename TA, typename TW, int BM, int BN>
+template <typename TA, typename TW, int BM, int BN, int P = 1>
 struct Mainloop {
   static constexpr int BK = 128 / (int)sizeof(TA);            // elements per staged row
   static constexpr int LDK = 144 / (int)sizeof(TA);           // padded LDS row (elements)
@@ -39,7 +39,9 @@ struct Mainloop {
 
   // ap[p] / bp[p]: row pointers of the rows this thread stages; rows with
   // aok/bok false point at a valid row and are zeroed by a select, so the load
-  // path has no branches (the prefetch of the next tile stays in flight)
+  // path has no branches.  P contraction tiles are in flight in registers
+  // (a ring of P stages) while the MFMAs consume the LDS copy of an older
+  // one; the tile count is padded to a multiple of P with zero tiles.
   static __device__ __forceinline__ void run(const TA* const (&ap)[A_LD], const bool (&aok)[A_LD],
                                              const TW* const (&bp)[B_LD], const bool (&bok)[B_LD],
                                              int K, TA* smem, f32x4_t (&acc)[RT][CT]) {
@@ -50,14 +52,15 @@ struct Mainloop {
 #pragma unroll
       for (int ct = 0; ct < CT; ct++) acc[rt][ct] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-    uint4 ra[A_LD], rb[B_LD];
+    uint4 ra[P][A_LD], rb[P][B_LD];
     const int nk = K / BK;
-    auto gload = [&](int kt) {
-      const int k0 = kt * BK;
+    const int nkp = (nk + P - 1) / P * P;
+    auto gload = [&](int st, int kt) {
+      const int k0 = (kt < nk ? kt : nk - 1) * BK;   // clamped: always issued
 #pragma unroll
-      for (int p = 0; p < A_LD; p++) ra[p] = *reinterpret_cast<const uint4*>(ap[p] + k0 + a_col());
+      for (int p = 0; p < A_LD; p++) ra[st][p] = *reinterpret_cast<const uint4*>(ap[p] + k0 + a_col());
 #pragma unroll
-      for (int p = 0; p < B_LD; p++) rb[p] = *reinterpret_cast<const uint4*>(bp[p] + k0 + b_col());
+      for (int p = 0; p < B_LD; p++) rb[st][p] = *reinterpret_cast<const uint4*>(bp[p] + k0 + b_col());
     };
     auto zero_if = [](uint4& u, bool ok) {
       u.x = ok ? u.x : 0u;
@@ -65,24 +68,24 @@ struct Mainloop {
       u.z = ok ? u.z : 0u;
       u.w = ok ? u.w : 0u;
     };
-    auto sstore = [&](int buf) {
+    auto sstore = [&](int st, int buf, bool ok) {
       TA* sa = smem + buf * (BM + BN) * LDK;
       TA* sb = sa + BM * LDK;
 #pragma unroll
-      for (int p = 0; p < A_LD; p++) zero_if(ra[p], aok[p]);
+      for (int p = 0; p < A_LD; p++) zero_if(ra[st][p], aok[p] && ok);
 #pragma unroll
-      for (int p = 0; p < B_LD; p++) zero_if(rb[p], bok[p]);
+      for (int p = 0; p < B_LD; p++) zero_if(rb[st][p], bok[p] && ok);
 #pragma unroll
-      for (int p = 0; p < A_LD; p++) *reinterpret_cast<uint4*>(sa + a_row(p) * LDK + a_col()) = ra[p];
+      for (int p = 0; p < A_LD; p++) *reinterpret_cast<uint4*>(sa + a_row(p) * LDK + a_col()) = ra[st][p];
 #pragma unroll
       for (int p = 0; p < B_LD; p++) {
         if (FP8) {
-          uint4 lo = fp8x8_to_bf16x8(make_uint2(rb[p].x, rb[p].y));
-          uint4 hi = fp8x8_to_bf16x8(make_uint2(rb[p].z, rb[p].w));
+          uint4 lo = fp8x8_to_bf16x8(make_uint2(rb[st][p].x, rb[st][p].y));
+          uint4 hi = fp8x8_to_bf16x8(make_uint2(rb[st][p].z, rb[st][p].w));
           *reinterpret_cast<uint4*>(sb + b_row(p) * LDK + b_col()) = lo;
           *reinterpret_cast<uint4*>(sb + b_row(p) * LDK + b_col() + 8) = hi;
         } else {
-          *reinterpret_cast<uint4*>(sb + b_row(p) * LDK + b_col()) = rb[p];
+          *reinterpret_cast<uint4*>(sb + b_row(p) * LDK + b_col()) = rb[st][p];
         }
       }
     };
@@ -108,23 +111,28 @@ struct Mainloop {
         for (int ct = 0; ct < CT; ct++) mma(acc[rt][ct], af[fb][rt], bf[fb][ct]);
     };
 
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; kt++) {
-      gload(kt + 1 < nk ? kt + 1 : kt);   // clamped: always issue, stays in flight
-      __builtin_amdgcn_sched_barrier(0);
-      lload(kt & 1, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < KS; ks++) {
-        if (ks + 1 < KS) lload(kt & 1, ks + 1, (ks + 1) & 1);
+    for (int st = 0; st < P; st++) gload(st, st);
+    sstore(0, 0, true);
+    __syncthreads();
+    for (int kb = 0; kb < nkp; kb += P) {
+#pragma unroll
+      for (int st = 0; st < P; st++) {
+        const int kt = kb + st;
+        gload(st, kt + P);   // stage st was stored to LDS in the previous step
         __builtin_amdgcn_sched_barrier(0);
-        mmas(ks & 1);
+        lload(kt & 1, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) {
+          if (ks + 1 < KS) lload(kt & 1, ks + 1, (ks + 1) & 1);
+          __builtin_amdgcn_sched_barrier(0);
+          mmas(ks & 1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        sstore((st + 1) % P, (kt + 1) & 1, kt + 1 < nk);
+        __syncthreads();
       }
-      if (kt + 1 < nk) sstore((kt + 1) & 1);
-      __syncthreads();
     }
   }
 };
@@ -347,10 +355,10 @@ __device__ __forceinline__ void mrg(float& m, int& i, float& s, float m2, int i2
   }
 }
 
-template <typename TA, int BM>
+template <typename TA, int BM, int P>
 __global__ __launch_bounds__(256) void lmhead_k(HeadArgs a) {
   constexpr int BN = 128;
-  typedef Mainloop<TA, TA, BM, BN> ML;
+  typedef Mainloop<TA, TA, BM, BN, P> ML;
   __shared__ __attribute__((aligned(16))) TA smem[ML::SMEM];
   __shared__ float xm[2][BM], xs[2][BM];
   __shared__ int xi[2][BM];
@@ -422,6 +430,183 @@ __global__ __launch_bounds__(256) void lmhead_k(HeadArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// LM head for bf16 activations and more than 64 rows.  Block tile: 128 rows x
+// 256 vocabulary entries; the 4 waves sit side by side (128 x 64 each).  Every
+// weight byte is used by exactly one wave, so the weight rows stream from HBM
+// straight into MFMA fragments; only the activation tile, which all 4 waves
+// share, goes through LDS (a ring of P contraction tiles in flight in
+// registers, LDS double buffer).  Staging both operands through LDS would make
+// the LDS write port the bottleneck.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void mrg_bf(float& m, int& i, float& s, float m2, int i2, float s2) {
+  // branch-free merge of two (max, lowest argmax, sum exp(x - max)) triples;
+  // an empty triple has max -inf and sum 0
+  const float M = fmaxf(m, m2);
+  const float e1 = m == -INFINITY ? 0.f : __expf(m - M);
+  const float e2 = m2 == -INFINITY ? 0.f : __expf(m2 - M);
+  const int id = m > m2 ? i : (m2 > m ? i2 : min(i, i2));
+  s = s * e1 + s2 * e2;
+  m = M;
+  i = id;
+}
+
+template <int P>
+__global__ __launch_bounds__(256, 1) void lmhead_direct_k(HeadArgs a) {
+  constexpr int BM = 128, BN = 256, BK = 64, LDK = 72, RT = 8, CT = 4;
+  // three LDS buffers: while tile kt is consumed, tile kt+1 is readable (its
+  // first fragments are prefetched) and tile kt+2 is being written
+  __shared__ __attribute__((aligned(16))) uint16_t sA[3][BM * LDK];
+  __shared__ float xm[4][BM], xs[4][BM];
+  __shared__ int xi[4][BM];
+  const int b8 = blockIdx.x >> 3, mtiles = a.mtiles;
+  const int nt = (b8 / mtiles) * 8 + (blockIdx.x & 7), mt = b8 % mtiles;
+  if (nt >= a.ntiles) return;
+  const int n0 = nt * BN, m0 = mt * BM;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, l16 = lane & 15, g = lane >> 4;
+  const uint16_t* A = (const uint16_t*)a.A;
+  const uint16_t* W = (const uint16_t*)a.B;
+  const int K = a.K, nk = K / BK, nkp = (nk + P - 1) / P * P;
+
+  const uint16_t* ap[4];
+  bool aok[4];
+#pragma unroll
+  for (int p = 0; p < 4; p++) {
+    const int r = m0 + (t >> 3) + 32 * p;
+    aok[p] = r < a.M;
+    ap[p] = A + (size_t)(aok[p] ? r : 0) * K + (t & 7) * 8;
+  }
+  const uint16_t* bp[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ct++) {
+    const int n = n0 + 64 * w + 16 * ct + l16;
+    bp[ct] = W + (size_t)(n < a.V ? n : 0) * K + 8 * g;   // rows past V: masked in the epilogue
+  }
+
+  f32x4_t acc[RT][CT];
+#pragma unroll
+  for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+    for (int ct = 0; ct < CT; ct++) acc[rt][ct] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+  uint4 ra[P][4];
+  FragBF rb[P][2][CT];
+  auto gload = [&](int st, int kt) {
+    const int k0 = (kt < nk ? kt : nk - 1) * BK;   // clamped: always issued
+#pragma unroll
+    for (int p = 0; p < 4; p++) ra[st][p] = *reinterpret_cast<const uint4*>(ap[p] + k0);
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+      for (int ct = 0; ct < CT; ct++) load_frag(rb[st][ks][ct], bp[ct] + k0 + 32 * ks);
+  };
+  // tiles past the end are stored as zeros, so their MFMAs add nothing
+  auto astore = [&](int st, int buf, bool ok) {
+#pragma unroll
+    for (int p = 0; p < 4; p++) {
+      uint4 u = ra[st][p];
+      const bool z = aok[p] && ok;
+      u.x = z ? u.x : 0u;
+      u.y = z ? u.y : 0u;
+      u.z = z ? u.z : 0u;
+      u.w = z ? u.w : 0u;
+      *reinterpret_cast<uint4*>(&sA[buf][((t >> 3) + 32 * p) * LDK + (t & 7) * 8]) = u;
+    }
+  };
+  FragBF af[2][RT];
+  auto lload = [&](int buf, int ks) {
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++) load_frag(af[ks][rt], &sA[buf][(16 * rt + l16) * LDK + 32 * ks + 8 * g]);
+  };
+  auto mmas = [&](int st, int ks) {
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+      for (int ct = 0; ct < CT; ct++) mma(acc[rt][ct], af[ks][rt], rb[st][ks][ct]);
+  };
+
+#pragma unroll
+  for (int st = 0; st < P; st++) gload(st, st);
+  astore(0, 0, true);
+  astore(1 % P, 1, 1 < nk);
+  __syncthreads();
+  lload(0, 0);
+  int cur = 0;   // LDS buffer of tile kt
+  for (int kb = 0; kb < nkp; kb += P) {
+#pragma unroll
+    for (int st = 0; st < P; st++) {
+      const int kt = kb + st;
+      const int nxt = cur == 2 ? 0 : cur + 1, nn = nxt == 2 ? 0 : nxt + 1;
+      lload(cur, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mmas(st, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      lload(nxt, 0);   // tile kt+1: written one step ago, behind the last barrier
+      __builtin_amdgcn_sched_barrier(0);
+      mmas(st, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      gload(st, kt + P);   // stage st: its A tile is in LDS, its B fragments consumed
+      __builtin_amdgcn_sched_barrier(0);
+      astore((st + 2) % P, nn, kt + 2 < nk);
+      __syncthreads();
+      cur = nxt;
+    }
+  }
+
+  if (a.logits) {   // debug tap: raw logits
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int ct = 0; ct < CT; ct++) {
+          const int r = m0 + 16 * rt + 4 * g + i, n = n0 + 64 * w + 16 * ct + l16;
+          if (r < a.M && n < a.V) a.logits[(size_t)r * a.V + n] = acc[rt][ct][i];
+        }
+  }
+  // epilogue: per row, (max, lowest argmax, sum exp) over this wave's 64
+  // columns: a lane folds its 4 columns, then DPP reductions over the 16
+  // lanes that share the row
+#pragma unroll
+  for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int rl = 16 * rt + 4 * g + i;
+      float v[CT];
+      float lm = -INFINITY;
+      int li = 0x7fffffff;
+#pragma unroll
+      for (int ct = 0; ct < CT; ct++) {
+        const int n = n0 + 64 * w + 16 * ct + l16;
+        v[ct] = n < a.V ? acc[rt][ct][i] : -INFINITY;
+        li = v[ct] > lm ? n : li;   // columns ascend with ct: the lowest index wins ties
+        lm = fmaxf(lm, v[ct]);
+      }
+      const float m = row16_max(lm);
+      const int idx = row16_min(lm == m ? li : 0x7fffffff);
+      float s = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < CT; ct++) s += m == -INFINITY ? 0.f : __expf(v[ct] - m);
+      s = row16_sum(s);
+      if (l16 == 0) {
+        xm[w][rl] = m;
+        xs[w][rl] = s;
+        xi[w][rl] = idx;
+      }
+    }
+  __syncthreads();
+  if (t < BM && m0 + t < a.M) {
+    float m = xm[0][t], s = xs[0][t];
+    int idx = xi[0][t];
+#pragma unroll
+    for (int q = 1; q < 4; q++) mrg_bf(m, idx, s, xm[q][t], xi[q][t], xs[q][t]);
+    const size_t o = (size_t)(m0 + t) * a.ntiles + nt;
+    a.pmax[o] = m;
+    a.pidx[o] = idx;
+    a.psum[o] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
 void launch_gemm(int act, int mode, const void* A, int M, int K, const void* B0, int n1,
                  const void* B1, int n2, const void* B2, int N, void* C, int ldc, const void* R,
                  const CacheDst* cache, hipStream_t s) {
@@ -457,29 +642,30 @@ void launch_down_lds(int act, const void* H, const MoeW& w, const int4* tiles,
   else down_lds_k<uint16_t, uint16_t, 128, 128><<<grid, 256, 0, s>>>(a);
 }
 
-// row-tile height of the LM head for more than 64 rows
-#ifndef LMHEAD_BM
-#define LMHEAD_BM 128
+// contraction tiles in flight in the bf16 LM head
+#ifndef LMHEAD_P
+#define LMHEAD_P 3
 #endif
-static_assert(LMHEAD_BM == 128 || LMHEAD_BM == 256, "LM head row tile");
 
-int lm_tiles(int V) { return (V + 127) / 128; }
-
-void launch_lmhead(int act, const void* uf, int M, int D, const void* lm, int V, float* pmax,
-                   int32_t* pidx, float* psum, float* logits, hipStream_t s) {
-  const int nt = lm_tiles(V), bm = M > 64 ? LMHEAD_BM : 64;
+int launch_lmhead(int act, const void* uf, int M, int D, const void* lm, int V, float* pmax,
+                  int32_t* pidx, float* psum, float* logits, hipStream_t s) {
+  if (act == ACT_BF16 && M > 64) {
+    const int nt = (V + 255) / 256;
+    HeadArgs a{uf, M, D, lm, V, pmax, pidx, psum, logits, nt, (M + 127) / 128};
+    lmhead_direct_k<LMHEAD_P><<<((nt + 7) / 8) * 8 * a.mtiles, 256, 0, s>>>(a);
+    return nt;
+  }
+  const int nt = (V + 127) / 128, bm = M > 64 ? 128 : 64;
   HeadArgs a{uf, M, D, lm, V, pmax, pidx, psum, logits, nt, (M + bm - 1) / bm};
   const dim3 grid(((nt + 7) / 8) * 8 * a.mtiles);
-  if (bm == 256) {
-    if (act == ACT_BF16) lmhead_k<uint16_t, 256><<<grid, 256, 0, s>>>(a);
-    else lmhead_k<float, 256><<<grid, 256, 0, s>>>(a);
-  } else if (bm == 128) {
-    if (act == ACT_BF16) lmhead_k<uint16_t, 128><<<grid, 256, 0, s>>>(a);
-    else lmhead_k<float, 128><<<grid, 256, 0, s>>>(a);
+  if (bm == 128) {
+    if (act == ACT_BF16) lmhead_k<uint16_t, 128, 1><<<grid, 256, 0, s>>>(a);
+    else lmhead_k<float, 128, 1><<<grid, 256, 0, s>>>(a);
   } else {
-    if (act == ACT_BF16) lmhead_k<uint16_t, 64><<<grid, 256, 0, s>>>(a);
-    else lmhead_k<float, 64><<<grid, 256, 0, s>>>(a);
+    if (act == ACT_BF16) lmhead_k<uint16_t, 64, 1><<<grid, 256, 0, s>>>(a);
+    else lmhead_k<float, 64, 1><<<grid, 256, 0, s>>>(a);
   }
+  return nt;
 }
 
 }  // namespace dg

@@ -85,9 +85,9 @@ void launch_gateup_lds(int act, const void* u2, const int32_t* perm, int k, cons
 void launch_down_lds(int act, const void* H, const MoeW& w, const int4* tiles,
                      const int32_t* ntiles, int max_tiles, int D, int F, void* Y, hipStream_t s);
 // LM head: per-row partial (max, argmax, sum exp) over vocabulary tiles of 128
-int lm_tiles(int V);
-void launch_lmhead(int act, const void* uf, int M, int D, const void* lm, int V, float* pmax,
-                   int32_t* pidx, float* psum, float* logits, hipStream_t s);
+// returns the number of per-row partials written (one per vocabulary tile)
+int launch_lmhead(int act, const void* uf, int M, int D, const void* lm, int V, float* pmax,
+                  int32_t* pidx, float* psum, float* logits, hipStream_t s);
 
 // ---- weight-streaming MFMA GEMM for few rows (kern_stream.hip) ----
 enum StreamMode { SG_STORE = 0, SG_RESID = 1, SG_F32 = 2, SG_QKV_CACHE = 3, SG_GATEUP = 4,
