@@ -1,5 +1,6 @@
 // dgpass.hip -- the C ABI of libdgpass: validation, workspace carving and the
 // launch sequence of a prefill and of a denoising pass.  See include/dgpass.h.
+#include <stdint.h>
 #include <string.h>
 
 #include "launch.h"
@@ -17,7 +18,6 @@ constexpr int MIN_TILE = 32;      // smallest expert row tile (sizes the tile li
 constexpr int STREAM_TILE = 32;   // row tile of the weight-streaming kernels
 constexpr int FAT_TILE = 128;     // row tile of the LDS-tiled expert kernels
 constexpr int STREAM_MAX_ROWS = 1024;  // dense projections: weight streaming up to this many rows
-constexpr int HEAD_STREAM_MAX_ROWS = 0;  // the LDS-tiled head kernel wins at 256 rows
 
 struct Layout {
   size_t cov;       // [L][E] int32 expert counts of the last pass (offset 0)
@@ -79,6 +79,7 @@ bool valid_cfg(const dg_config* c) {
 
 dg_status supported_cfg(const dg_config* c) {
   if (c->D % 128 || c->F % 64) return DG_ERR_UNSUPPORTED;
+  if (c->expert_dtype == DG_FP8E4M3 && c->F % 128) return DG_ERR_UNSUPPORTED;   // packed fp8 rows
   if (c->hd != 64 && c->hd != 128) return DG_ERR_UNSUPPORTED;
   if (c->Hq % c->Hkv) return DG_ERR_UNSUPPORTED;
   const int G = c->Hq / c->Hkv;
@@ -119,9 +120,9 @@ void tap_copy(void* dst, const void* src, size_t bytes, hipStream_t s) {
 }
 
 // waves splitting the contraction: 4, or 2 when 4 would leave each wave an odd
-// number of 64-element pieces (the pipeline works on pairs)
-int stream_kw(int K) {
-  const int nch = K / 64, per4 = (nch + 3) / 4;
+// number of pieces (128 bytes of each weight row; the pipeline works on pairs)
+int stream_kw(int K, int wdt) {
+  const int nch = K * esize(wdt) / 128, per4 = (nch + 3) / 4;
   return (per4 % 2 == 1 && nch % 2 == 0) ? 2 : 4;
 }
 
@@ -143,7 +144,7 @@ void dense_gemm(const Ctx& c, int mode, const void* A, int M, int K, const void*
     g.n1 = n1;
     g.n2 = n2;
     g.N = N;
-    const int kw = stream_kw(K);
+    const int kw = stream_kw(K, cf.act_dtype);
     g.nchunks = (N + 64 * (4 / kw) - 1) / (64 * (4 / kw));
     g.out = C;
     g.ldo = ldc;
@@ -222,7 +223,7 @@ void moe_block(const Ctx& c, int l, const float* gnext) {
     g.W0 = w.wg;
     g.W1 = w.wu;
     g.NW = cf.F;
-    const int kw = stream_kw(cf.D);
+    const int kw = stream_kw(cf.D, cf.expert_dtype);
     g.nchunks = cf.F / (32 * (4 / kw));
     g.out = at<void>(c, c.L.H);
     g.ldo = cf.F;
@@ -244,7 +245,7 @@ void moe_block(const Ctx& c, int l, const float* gnext) {
     g.W1 = nullptr;
     g.NW = cf.D;
     g.N = cf.D;
-    const int kw = stream_kw(cf.F);
+    const int kw = stream_kw(cf.F, cf.expert_dtype);
     g.nchunks = cf.D / (64 * (4 / kw));
     g.out = at<void>(c, c.L.Y);
     g.ldo = cf.D;
@@ -399,27 +400,9 @@ dg_status dg_denoise_pass(const dg_model* m, const dg_kv* kv, const int32_t* can
     moe_block(c, l, l + 1 < cf.L ? m->w.layers[l + 1].g1 : m->w.gf);
   }
   // head: logits tiles reduced to (max, argmax, sum exp), merged per row
-  int nparts;
-  if (R <= HEAD_STREAM_MAX_ROWS) {
-    StreamGemm g{};
-    g.A = at<void>(c, c.L.u);
-    g.M = R;
-    g.K = cf.D;
-    g.W0 = m->w.lm;
-    g.n1 = cf.V;
-    g.N = cf.V;
-    g.nchunks = (cf.V + 63) / 64;
-    g.pmax = at<float>(c, c.L.lpm);
-    g.pidx = at<int32_t>(c, c.L.lpi);
-    g.psum = at<float>(c, c.L.lps);
-    g.logits = taps ? taps->logits : nullptr;
-    launch_stream_gemm(act, cf.act_dtype, SG_LMHEAD, 4, g, (R + STREAM_TILE - 1) / STREAM_TILE, s);
-    nparts = g.nchunks;
-  } else {
-    nparts = launch_lmhead(act, at<void>(c, c.L.u), R, cf.D, m->w.lm, cf.V, at<float>(c, c.L.lpm),
-                           at<int32_t>(c, c.L.lpi), at<float>(c, c.L.lps),
-                           taps ? taps->logits : nullptr, s);
-  }
+  const int nparts = launch_lmhead(act, at<void>(c, c.L.u), R, cf.D, m->w.lm, cf.V, at<float>(c, c.L.lpm),
+                                   at<int32_t>(c, c.L.lpi), at<float>(c, c.L.lps),
+                                   taps ? taps->logits : nullptr, s);
   if (taps) tap_copy(taps->uf, at<void>(c, c.L.u), (size_t)R * cf.D * a, s);
   launch_lm_merge(at<float>(c, c.L.lpm), at<int32_t>(c, c.L.lpi), at<float>(c, c.L.lps), R, nparts,
                   argmax, conf, s);
@@ -440,6 +423,23 @@ dg_status dg_renoise(int32_t* canvas, const int32_t* argmax, const float* conf, 
   }
   (void)hipGetLastError();
   launch_renoise(canvas, argmax, conf, tau, seed, pass_tag, p, r, B, N, V, (hipStream_t)stream);
+  return check_hip();
+}
+
+size_t dg_packed_bytes(int32_t rows, int32_t cols, int32_t dtype) {
+  if (rows < 1 || cols < 1 || (dtype != DG_F32 && dtype != DG_BF16 && dtype != DG_FP8E4M3)) return 0;
+  const size_t rowbytes = (size_t)cols * esize(dtype);
+  if (rowbytes % 128) return 0;
+  return (size_t)((rows + 15) / 16) * 16 * rowbytes;
+}
+
+dg_status dg_pack_weight(const void* src, void* dst, int32_t rows, int32_t cols, int32_t dtype,
+                         void* stream) {
+  if (!src || !dst || src == dst) return DG_ERR_INVALID;
+  if (dg_packed_bytes(rows, cols, dtype) == 0) return DG_ERR_INVALID;
+  if ((size_t)cols * esize(dtype) > (size_t)INT32_MAX) return DG_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  launch_pack(src, dst, rows, cols * esize(dtype), (hipStream_t)stream);
   return check_hip();
 }
 

@@ -237,6 +237,27 @@ __global__ __launch_bounds__(256) void lm_merge_k(const float* __restrict__ pmax
 }
 
 // ---------------------------------------------------------------------------
+// weight packing: 16-byte chunk q of the packed matrix is tile q/128 (row
+// group rg, 128-byte column block kb, tiles row-group-major), half h, lane l;
+// it holds row 16 rg + l%16, bytes 128 kb + 64 h + 16 (l/16) of the row-major
+// source; rows past the source are zero.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pack_k(const uint8_t* __restrict__ src, uint4* __restrict__ dst,
+                                              int rows, int rowbytes, size_t nchunks) {
+  const int nkb = rowbytes / 128;
+  for (size_t q = (size_t)blockIdx.x * 256 + threadIdx.x; q < nchunks; q += (size_t)gridDim.x * 256) {
+    const size_t tile = q >> 7;
+    const int h = (int)(q >> 6) & 1, l = (int)q & 63;
+    const size_t rg = tile / nkb;
+    const int kb = (int)(tile % nkb);
+    const size_t row = rg * 16 + (l & 15);
+    const size_t col = (size_t)kb * 128 + 64 * h + 16 * (l >> 4);
+    dst[q] = row < (size_t)rows ? *reinterpret_cast<const uint4*>(src + row * rowbytes + col)
+                                : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// ---------------------------------------------------------------------------
 void launch_embed_norm(int act, const int32_t* tok, const void* emb, const float* g, int rows, int D,
                        int V, float eps, void* x, void* u, hipStream_t s) {
   if (act == ACT_BF16)
@@ -291,6 +312,13 @@ void launch_unpermute(int act, const void* src, const int32_t* inv, int slots, i
 void launch_lm_merge(const float* pmax, const int32_t* pidx, const float* psum, int rows,
                      int ntiles, int32_t* argmax, float* conf, hipStream_t s) {
   lm_merge_k<<<rows, 256, 0, s>>>(pmax, pidx, psum, ntiles, argmax, conf);
+}
+
+void launch_pack(const void* src, void* dst, int rows, int rowbytes, hipStream_t s) {
+  const size_t nchunks = (size_t)((rows + 15) / 16) * 16 * rowbytes / 16;
+  const size_t blocks = (nchunks + 255) / 256;
+  pack_k<<<(unsigned)(blocks < 65536 ? blocks : 65536), 256, 0, s>>>((const uint8_t*)src, (uint4*)dst, rows,
+                                                                  rowbytes, nchunks);
 }
 
 }  // namespace dg

@@ -15,6 +15,12 @@
 
 namespace dg {
 
+// byte address of row group (row / 16) of a packed matrix with nkb 128-byte
+// pieces per row
+__device__ __forceinline__ const char* packed_group(const void* base, size_t row, int nkb) {
+  return (const char*)base + (row >> 4) * (size_t)nkb * 2048;
+}
+
 template <typename TA, typename TW, int BM, int BN, int P = 1>
 struct Mainloop {
   static constexpr int BK = 128 / (int)sizeof(TA);            // elements per staged row
@@ -30,20 +36,37 @@ struct Mainloop {
   // thread -> chunk assignment
   static __device__ __forceinline__ int a_row(int p) { return (threadIdx.x >> 3) + 32 * p; }
   static __device__ __forceinline__ int a_col() { return (threadIdx.x & 7) * (16 / (int)sizeof(TA)); }
+  // B comes from the packed weight layout (tiles of 16 rows x 128 bytes, two
+  // 1 KB halves; lane l of a half holds row l%16, bytes 64h + 16(l/16)): a
+  // pass of the 256 threads stages 2 row groups x both halves (32 rows of one
+  // 128-byte piece) or, for fp8, 4 row groups x the half that holds this
+  // 64-element k-tile.  Each wave load is 1 KB of contiguous memory.
   static __device__ __forceinline__ int b_row(int p) {
-    return FP8 ? (threadIdx.x >> 2) + 64 * p : (threadIdx.x >> 3) + 32 * p;
+    const int t = threadIdx.x;
+    return FP8 ? 64 * p + 16 * (t >> 6) + (t & 15) : 32 * p + 16 * (t >> 7) + (t & 15);
   }
-  static __device__ __forceinline__ int b_col() {
-    return FP8 ? (threadIdx.x & 3) * 16 : (threadIdx.x & 7) * (16 / (int)sizeof(TA));
+  static __device__ __forceinline__ int b_col() {   // TW elements into the k-tile
+    const int t = threadIdx.x;
+    return FP8 ? 16 * ((t & 63) >> 4) : (64 * ((t >> 6) & 1) + 16 * ((t & 63) >> 4)) / (int)sizeof(TW);
+  }
+  // byte offset of this thread's 16 bytes inside a row group's piece
+  static __device__ __forceinline__ int b_lane() {
+    const int t = threadIdx.x;
+    return (FP8 ? 0 : ((t >> 6) & 1) * 1024) + (t & 63) * 16;
+  }
+  // byte offset of k-tile kt inside a row group's packed rows
+  static __device__ __forceinline__ size_t b_koff(int kt) {
+    return FP8 ? (size_t)(kt >> 1) * 2048 + (kt & 1) * 1024 : (size_t)kt * 2048;
   }
 
-  // ap[p] / bp[p]: row pointers of the rows this thread stages; rows with
-  // aok/bok false point at a valid row and are zeroed by a select, so the load
-  // path has no branches.  P contraction tiles are in flight in registers
+  // ap[p]: row pointers of the A rows this thread stages; bp[p]: byte address
+  // of this thread's 16 bytes in k-tile 0 of its packed B row group (b_lane
+  // included).  Rows with aok/bok false point at valid memory and are zeroed
+  // by a select, so the load path has no branches.  P contraction tiles are in flight in registers
   // (a ring of P stages) while the MFMAs consume the LDS copy of an older
   // one; the tile count is padded to a multiple of P with zero tiles.
   static __device__ __forceinline__ void run(const TA* const (&ap)[A_LD], const bool (&aok)[A_LD],
-                                             const TW* const (&bp)[B_LD], const bool (&bok)[B_LD],
+                                             const char* const (&bp)[B_LD], const bool (&bok)[B_LD],
                                              int K, TA* smem, f32x4_t (&acc)[RT][CT]) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int wm = w >> 1, wn = w & 1, l16 = lane & 15, g = lane >> 4;
@@ -56,11 +79,12 @@ struct Mainloop {
     const int nk = K / BK;
     const int nkp = (nk + P - 1) / P * P;
     auto gload = [&](int st, int kt) {
-      const int k0 = (kt < nk ? kt : nk - 1) * BK;   // clamped: always issued
+      const int kc = kt < nk ? kt : nk - 1;   // clamped: always issued
+      const int k0 = kc * BK;
 #pragma unroll
       for (int p = 0; p < A_LD; p++) ra[st][p] = *reinterpret_cast<const uint4*>(ap[p] + k0 + a_col());
 #pragma unroll
-      for (int p = 0; p < B_LD; p++) rb[st][p] = *reinterpret_cast<const uint4*>(bp[p] + k0 + b_col());
+      for (int p = 0; p < B_LD; p++) rb[st][p] = *reinterpret_cast<const uint4*>(bp[p] + b_koff(kc));
     };
     auto zero_if = [](uint4& u, bool ok) {
       u.x = ok ? u.x : 0u;
@@ -162,8 +186,9 @@ __global__ __launch_bounds__(256) void gemm_dense_k(DenseArgs a) {
   __shared__ __attribute__((aligned(16))) TA smem[ML::SMEM];
   const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
   const TA* ap[ML::A_LD];
-  const TA* bp[ML::B_LD];
+  const char* bp[ML::B_LD];
   bool aok[ML::A_LD], bok[ML::B_LD];
+  const int nkb = a.K * (int)sizeof(TA) / 128;
 #pragma unroll
   for (int p = 0; p < ML::A_LD; p++) {
     const int r = m0 + ML::a_row(p);
@@ -175,11 +200,11 @@ __global__ __launch_bounds__(256) void gemm_dense_k(DenseArgs a) {
     const int n = n0 + ML::b_row(p);
     bok[p] = n < a.N;
     const int nn = bok[p] ? n : 0;
-    const TA* q;
-    if (nn < a.n1) q = (const TA*)a.B0 + (size_t)nn * a.K;
-    else if (nn < a.n1 + a.n2) q = (const TA*)a.B1 + (size_t)(nn - a.n1) * a.K;
-    else q = (const TA*)a.B2 + (size_t)(nn - a.n1 - a.n2) * a.K;
-    bp[p] = q;
+    const char* q;
+    if (nn < a.n1) q = packed_group(a.B0, nn, nkb);
+    else if (nn < a.n1 + a.n2) q = packed_group(a.B1, nn - a.n1, nkb);
+    else q = packed_group(a.B2, nn - a.n1 - a.n2, nkb);
+    bp[p] = q + ML::b_lane();
   }
   f32x4_t acc[ML::RT][ML::CT];
   ML::run(ap, aok, bp, bok, a.K, smem, acc);
@@ -245,8 +270,9 @@ __global__ __launch_bounds__(256) void gateup_lds_k(GroupArgs a) {
   const int e = tl.x, row0 = tl.y, nrows = tl.z;
   const int f0 = blockIdx.y * (BN / 2);
   const TA* ap[ML::A_LD];
-  const TW* bp[ML::B_LD];
+  const char* bp[ML::B_LD];
   bool aok[ML::A_LD], bok[ML::B_LD];
+  const int nkb = a.K * (int)sizeof(TW) / 128;
 #pragma unroll
   for (int p = 0; p < ML::A_LD; p++) {
     const int r = ML::a_row(p);
@@ -257,8 +283,7 @@ __global__ __launch_bounds__(256) void gateup_lds_k(GroupArgs a) {
   for (int p = 0; p < ML::B_LD; p++) {
     const int n = ML::b_row(p);
     const int f = f0 + 16 * (n >> 5) + (n & 15);
-    const TW* base = (const TW*)(((n >> 4) & 1) ? a.W2 : a.W1);
-    bp[p] = base + ((size_t)e * a.NW + f) * a.K;
+    bp[p] = packed_group(((n >> 4) & 1) ? a.W2 : a.W1, (size_t)e * a.NW + f, nkb) + ML::b_lane();
     bok[p] = true;
   }
   f32x4_t acc[ML::RT][ML::CT];
@@ -295,8 +320,9 @@ __global__ __launch_bounds__(256) void down_lds_k(GroupArgs a) {
   const int e = tl.x, row0 = tl.y, nrows = tl.z;
   const int n0 = blockIdx.y * BN;
   const TA* ap[ML::A_LD];
-  const TW* bp[ML::B_LD];
+  const char* bp[ML::B_LD];
   bool aok[ML::A_LD], bok[ML::B_LD];
+  const int nkb = a.K * (int)sizeof(TW) / 128;
 #pragma unroll
   for (int p = 0; p < ML::A_LD; p++) {
     const int r = ML::a_row(p);
@@ -305,7 +331,7 @@ __global__ __launch_bounds__(256) void down_lds_k(GroupArgs a) {
   }
 #pragma unroll
   for (int p = 0; p < ML::B_LD; p++) {
-    bp[p] = (const TW*)a.W1 + ((size_t)e * a.NW + n0 + ML::b_row(p)) * a.K;
+    bp[p] = packed_group(a.W1, (size_t)e * a.NW + n0 + ML::b_row(p), nkb) + ML::b_lane();
     bok[p] = true;
   }
   f32x4_t acc[ML::RT][ML::CT];
@@ -369,8 +395,9 @@ __global__ __launch_bounds__(256) void lmhead_k(HeadArgs a) {
   if (nt >= a.ntiles) return;
   const int n0 = nt * BN, m0 = mt * BM;
   const TA* ap[ML::A_LD];
-  const TA* bp[ML::B_LD];
+  const char* bp[ML::B_LD];
   bool aok[ML::A_LD], bok[ML::B_LD];
+  const int nkb = a.K * (int)sizeof(TA) / 128;
 #pragma unroll
   for (int p = 0; p < ML::A_LD; p++) {
     const int r = m0 + ML::a_row(p);
@@ -381,7 +408,7 @@ __global__ __launch_bounds__(256) void lmhead_k(HeadArgs a) {
   for (int p = 0; p < ML::B_LD; p++) {
     const int n = n0 + ML::b_row(p);
     bok[p] = n < a.V;
-    bp[p] = (const TA*)a.B + (size_t)(bok[p] ? n : 0) * a.K;
+    bp[p] = packed_group(a.B, bok[p] ? n : 0, nkb) + ML::b_lane();
   }
   f32x4_t acc[ML::RT][ML::CT];
   ML::run(ap, aok, bp, bok, a.K, smem, acc);
@@ -475,11 +502,12 @@ __global__ __launch_bounds__(256, 1) void lmhead_direct_k(HeadArgs a) {
     aok[p] = r < a.M;
     ap[p] = A + (size_t)(aok[p] ? r : 0) * K + (t & 7) * 8;
   }
-  const uint16_t* bp[CT];
+  // packed weights: one 1 KB wave load per (column tile, k-tile, half)
+  const char* bp[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ct++) {
-    const int n = n0 + 64 * w + 16 * ct + l16;
-    bp[ct] = W + (size_t)(n < a.V ? n : 0) * K + 8 * g;   // rows past V: masked in the epilogue
+    const int n = n0 + 64 * w + 16 * ct;
+    bp[ct] = packed_group(W, n < a.V ? n : 0, nk) + 16 * lane;   // groups past V: masked in the epilogue
   }
 
   f32x4_t acc[RT][CT];
@@ -497,7 +525,8 @@ __global__ __launch_bounds__(256, 1) void lmhead_direct_k(HeadArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 2; ks++)
 #pragma unroll
-      for (int ct = 0; ct < CT; ct++) load_frag(rb[st][ks][ct], bp[ct] + k0 + 32 * ks);
+      for (int ct = 0; ct < CT; ct++)
+        rb[st][ks][ct].v = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(bp[ct] + (size_t)(k0 / BK) * 2048 + ks * 1024));
   };
   // tiles past the end are stored as zeros, so their MFMAs add nothing
   auto astore = [&](int st, int buf, bool ok) {

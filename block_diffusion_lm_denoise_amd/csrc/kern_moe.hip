@@ -148,8 +148,8 @@ __global__ __launch_bounds__(256) void plan_k(const int32_t* __restrict__ ids, i
 // ---------------------------------------------------------------------------
 // route_k: RMSNorm of x1, router logits and top-k in one kernel for a tile of
 // 16 tokens.  The normalised rows stay in LDS as the A operand of the router
-// MFMAs (waves split the experts in 16-column tiles, W_r fragments come from
-// L2); the logits go to LDS and each wave then ranks 4 of the tokens.
+// MFMAs (waves split the experts in 16-column tiles, packed W_r fragments
+// come from L2); the logits go to LDS and each wave then ranks 4 of the tokens.
 // ---------------------------------------------------------------------------
 template <typename TA>
 __global__ __launch_bounds__(256) void route_k(RouteArgs a) {
@@ -194,17 +194,37 @@ __global__ __launch_bounds__(256) void route_k(RouteArgs a) {
     }
   } else {
     const int nct = (E + 15) / 16;
+    const int nkb = D * (int)sizeof(TA) / 128;   // packed pieces per router row
     for (int ct = w; ct < nct; ct += 4) {
       const int e = ct * 16 + l16;
-      const TA* wr = e < E ? (const TA*)a.wr + (size_t)e * D : nullptr;
+      // packed W_r: row group ct (rows past E are zero), this lane's 16 bytes
+      const char* wg = (const char*)a.wr + (size_t)ct * nkb * 2048 + 16 * lane;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
       for (int k0 = 0; k0 < D; k0 += 128) {   // D is a multiple of 128
         Frag af[4], bf[4];
 #pragma unroll
         for (int u = 0; u < 4; u++) {
-          load_frag(af[u], sa + l16 * LDA + k0 + 32 * u + 8 * g);
-          if (wr) load_frag(bf[u], wr + k0 + 32 * u + 8 * g);
-          else zero_frag(bf[u]);
+          if constexpr (sizeof(TA) == 2) {
+            // piece of 64 elements; half u&1 holds elements 32(u&1) + 8g of it
+            const int piece = k0 / 64 + (u >> 1);
+            load_frag(af[u], sa + l16 * LDA + k0 + 32 * u + 8 * g);
+            bf[u].v = __builtin_bit_cast(bf16x8_t,
+                                         *reinterpret_cast<const uint4*>(wg + (size_t)piece * 2048 + (u & 1) * 1024));
+          } else {
+            // piece of 32 floats; lane g holds floats 4g.. and 16+4g.. of it
+            const int piece = k0 / 32 + u;
+            const float* ar = reinterpret_cast<const float*>(sa) + l16 * LDA + k0 + 32 * u + 4 * g;
+            const float4 a0 = *reinterpret_cast<const float4*>(ar);
+            const float4 a1 = *reinterpret_cast<const float4*>(ar + 16);
+            const float4 w0 = *reinterpret_cast<const float4*>(wg + (size_t)piece * 2048);
+            const float4 w1 = *reinterpret_cast<const float4*>(wg + (size_t)piece * 2048 + 1024);
+            float* fa = reinterpret_cast<float*>(&af[u]);
+            float* fb = reinterpret_cast<float*>(&bf[u]);
+            fa[0] = a0.x; fa[1] = a0.y; fa[2] = a0.z; fa[3] = a0.w;
+            fa[4] = a1.x; fa[5] = a1.y; fa[6] = a1.z; fa[7] = a1.w;
+            fb[0] = w0.x; fb[1] = w0.y; fb[2] = w0.z; fb[3] = w0.w;
+            fb[4] = w1.x; fb[5] = w1.y; fb[6] = w1.z; fb[7] = w1.w;
+          }
         }
 #pragma unroll
         for (int u = 0; u < 4; u++) mma(acc, af[u], bf[u]);

@@ -1,13 +1,15 @@
 // kern_stream.hip -- weight-streaming MFMA GEMM for few rows against large
-// weight matrices: the grouped expert GEMMs of a pass, the dense projections
-// and the LM head.
+// weight matrices: the grouped expert GEMMs of a pass and the dense
+// projections.
 //
 // One block = (row tile of at most 32 rows, chunk of 64 weight rows).  The
-// four waves split the contraction in 64-element pieces (wave w takes pieces
-// w, w+4, ...), load MFMA fragments of A and W straight from memory with a
-// register double buffer (the next piece is in flight while the current one
-// is multiplied), and reduce their partial tiles through LDS one 16-row tile
-// at a time.  Each weight byte is used by the row tiles of its rows only.
+// four waves split the contraction in pieces of 128 bytes per weight row
+// (wave w takes pieces w, w+4, ...), load the weights from the packed layout
+// (every wave load is 1 KB of contiguous memory: whole cache lines) and the
+// activation fragments straight from memory, with a register double buffer
+// (the next piece is in flight while the current one is multiplied), and
+// reduce their partial tiles through LDS one 16-row tile at a time.  Each
+// weight byte is used by the row tiles of its rows only.
 //
 // Block ids run chunk-fastest (id = chunk + C * tile): blocks of one row tile
 // are consecutive, and the row tiles that share a weight chunk are C ids
@@ -21,41 +23,95 @@
 
 namespace dg {
 
-template <typename TA, typename TW>
-__device__ __forceinline__ void load_w(typename FragOf<TA>::type& f, const TW* p);
-template <>
-__device__ __forceinline__ void load_w<uint16_t, uint16_t>(FragBF& f, const uint16_t* p) {
-  load_frag(f, p);
-}
-template <>
-__device__ __forceinline__ void load_w<uint16_t, uint8_t>(FragBF& f, const uint8_t* p) {
-  load_frag_fp8(f, p);
-}
-template <>
-__device__ __forceinline__ void load_w<float, float>(FragF32& f, const float* p) {
-  load_frag(f, p);
+// A piece is one 128-byte column block of the packed weights (16 rows x 128
+// bytes, two 1 KB wave loads h = 0, 1; lane l gets row l%16, bytes
+// 64h + 16(l/16)): 64 bf16, 128 fp8 or 32 fp32 contraction elements.  The
+// activation fragments take the same elements in the same lane order, which
+// is a consistent permutation of the contraction inside the piece.
+template <typename TA, typename TW> struct Piece;
+template <> struct Piece<uint16_t, uint16_t> {
+  static constexpr int EP = 64, NA = 2;   // elements per piece, 16-byte A loads per row tile
+  static __device__ __forceinline__ int a_off(int j, int g) { return 32 * j + 8 * g; }
+};
+template <> struct Piece<uint16_t, uint8_t> {
+  static constexpr int EP = 128, NA = 4;
+  static __device__ __forceinline__ int a_off(int j, int g) { return 64 * (j >> 1) + 16 * g + 8 * (j & 1); }
+};
+template <> struct Piece<float, float> {
+  static constexpr int EP = 32, NA = 2;
+  static __device__ __forceinline__ int a_off(int j, int g) { return 16 * j + 4 * g; }
+};
+
+__device__ __forceinline__ void zero_unless(uint4& u, bool ok) {
+  u.x = ok ? u.x : 0u;
+  u.y = ok ? u.y : 0u;
+  u.z = ok ? u.z : 0u;
+  u.w = ok ? u.w : 0u;
 }
 
-__device__ __forceinline__ void mrg3(float& m, int& i, float& s, float m2, int i2, float s2) {
-  if (m2 == -INFINITY) return;
-  if (m2 > m || (m2 == m && i2 < i)) {
-    s = s * __expf(m - m2) + s2;
-    m = m2;
-    i = i2;
-  } else {
-    s = s + s2 * __expf(m2 - m);
-  }
+// acc[rt][ct] += A[rt] . W[ct] over one piece, from raw 16-byte registers
+__device__ __forceinline__ void piece_mma(f32x4_t (&acc)[2][4], const uint4 (&wr)[4][2],
+                                          const uint4 (&ar)[2][2], uint16_t*, uint16_t*) {
+#pragma unroll
+  for (int j = 0; j < 2; j++)
+#pragma unroll
+    for (int rt = 0; rt < 2; rt++)
+#pragma unroll
+      for (int ct = 0; ct < 4; ct++) {
+        FragBF x, y;
+        x.v = __builtin_bit_cast(bf16x8_t, ar[rt][j]);
+        y.v = __builtin_bit_cast(bf16x8_t, wr[ct][j]);
+        mma(acc[rt][ct], x, y);
+      }
+}
+__device__ __forceinline__ void piece_mma(f32x4_t (&acc)[2][4], const uint4 (&wr)[4][2],
+                                          const uint4 (&ar)[2][4], uint16_t*, uint8_t*) {
+#pragma unroll
+  for (int j = 0; j < 4; j++)
+#pragma unroll
+    for (int ct = 0; ct < 4; ct++) {
+      const uint4 u = wr[ct][j >> 1];
+      FragBF y;
+      y.v = __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8((j & 1) ? make_uint2(u.z, u.w) : make_uint2(u.x, u.y)));
+#pragma unroll
+      for (int rt = 0; rt < 2; rt++) {
+        FragBF x;
+        x.v = __builtin_bit_cast(bf16x8_t, ar[rt][j]);
+        mma(acc[rt][ct], x, y);
+      }
+    }
+}
+__device__ __forceinline__ void piece_mma(f32x4_t (&acc)[2][4], const uint4 (&wr)[4][2],
+                                          const uint4 (&ar)[2][2], float*, float*) {
+#pragma unroll
+  for (int rt = 0; rt < 2; rt++)
+#pragma unroll
+    for (int ct = 0; ct < 4; ct++) {
+      FragF32 x, y;
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        const uint4 ua = ar[rt][j], uw = wr[ct][j];
+        x.v[4 * j + 0] = __uint_as_float(ua.x);
+        x.v[4 * j + 1] = __uint_as_float(ua.y);
+        x.v[4 * j + 2] = __uint_as_float(ua.z);
+        x.v[4 * j + 3] = __uint_as_float(ua.w);
+        y.v[4 * j + 0] = __uint_as_float(uw.x);
+        y.v[4 * j + 1] = __uint_as_float(uw.y);
+        y.v[4 * j + 2] = __uint_as_float(uw.z);
+        y.v[4 * j + 3] = __uint_as_float(uw.w);
+      }
+      mma(acc[rt][ct], x, y);
+    }
 }
 
 // KW waves split the contraction; the 4/KW wave groups take different 64-row
 // weight column groups (a block covers 64 * 4/KW weight rows).
 template <typename TA, typename TW, int MODE, int KW>
 __global__ __launch_bounds__(256) void wstream_k(StreamGemm a) {
-  typedef typename FragOf<TA>::type Frag;
+  typedef Piece<TA, TW> PC;
+  constexpr int NA = PC::NA;
   constexpr int CWG = 4 / KW;          // column groups per block
   __shared__ float red[4][4][64][4];   // [wave][col tile][lane][i], one 16-row tile at a time
-  __shared__ float hm[4][16], hs[4][16];
-  __shared__ int hi[4][16];
   constexpr bool GROUPED = MODE == SG_GATEUP || MODE == SG_DOWN;
   const int C = a.nchunks;
   const int chunk = blockIdx.x % C, tile = blockIdx.x / C;
@@ -75,6 +131,7 @@ __global__ __launch_bounds__(256) void wstream_k(StreamGemm a) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
   const int kw = w % KW, cg = w / KW;  // contraction share, column group of this wave
   const int K = a.K;
+  const int nch = K / PC::EP;          // pieces (packed column blocks) per weight row
 
   // A row pointers of this lane (row l16 of each 16-row tile).  Rows past the
   // tile read a valid row and are zeroed by a select, so the load path has no
@@ -89,30 +146,33 @@ __global__ __launch_bounds__(256) void wstream_k(StreamGemm a) {
     const size_t src = MODE == SG_GATEUP ? (size_t)(a.perm[slot] / a.k) : (size_t)slot;
     arow[rt] = (const TA*)a.A + src * K;
   }
-  // W row pointers of this lane (row l16 of each 16-row column tile)
-  const TW* wrow[4];
+  // packed weight tiles of this wave's 4 column tiles: byte address of row
+  // group rg, piece c, load h, this lane = base + (rg * nch + c) * 2048 + h * 1024 + 16 * lane
+  const char* wtile[4];
   bool wok[4];
   const int n0 = (chunk * CWG + cg) * 64;   // first weight row (dense/down) of this wave
 #pragma unroll
   for (int ct = 0; ct < 4; ct++) {
-    const TW* p;
+    const char* base;
+    size_t row;   // first row of the 16-row group in its matrix
     bool ok = true;
     if (MODE == SG_GATEUP) {
       // 32 SwiGLU outputs per column group: tiles [gate f, up f, gate f+16, up f+16]
-      const int f = (chunk * CWG + cg) * 32 + 16 * (ct >> 1) + l16;
-      p = (const TW*)((ct & 1) ? a.W1 : a.W0) + ((size_t)e * a.NW + f) * K;
+      row = (size_t)e * a.NW + (chunk * CWG + cg) * 32 + 16 * (ct >> 1);
+      base = (const char*)((ct & 1) ? a.W1 : a.W0);
     } else if (MODE == SG_DOWN) {
-      p = (const TW*)a.W0 + ((size_t)e * a.NW + n0 + 16 * ct + l16) * K;
+      row = (size_t)e * a.NW + n0 + 16 * ct;
+      base = (const char*)a.W0;
     } else {
-      const int n = n0 + 16 * ct + l16;
+      const int n = n0 + 16 * ct;
       ok = n < a.N;
       const int nn = ok ? n : 0;
-      if (nn < a.n1) p = (const TW*)a.W0 + (size_t)nn * K;
-      else if (nn < a.n1 + a.n2) p = (const TW*)a.W1 + (size_t)(nn - a.n1) * K;
-      else p = (const TW*)a.W2 + (size_t)(nn - a.n1 - a.n2) * K;
+      if (nn < a.n1) { base = (const char*)a.W0; row = nn; }
+      else if (nn < a.n1 + a.n2) { base = (const char*)a.W1; row = nn - a.n1; }
+      else { base = (const char*)a.W2; row = nn - a.n1 - a.n2; }
     }
-    wrow[ct] = p;
-    wok[ct] = ok;
+    wtile[ct] = base + (row / 16) * nch * 2048 + 16 * lane;
+    wok[ct] = ok;   // per 16-row group: rows past N within a valid group are masked at the store
   }
 
   f32x4_t acc[2][4];
@@ -121,36 +181,35 @@ __global__ __launch_bounds__(256) void wstream_k(StreamGemm a) {
 #pragma unroll
     for (int ct = 0; ct < 4; ct++) acc[rt][ct] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-  Frag wa[4][2], aa[2][2], wb[4][2], ab[2][2];
-  auto load = [&](Frag(&wf)[4][2], Frag(&af)[2][2], int ch) {
+  uint4 wa[4][2], aa[2][NA], wb[4][2], ab[2][NA];
+  auto load = [&](uint4(&wr)[4][2], uint4(&ar)[2][NA], int c) {
 #pragma unroll
-    for (int s = 0; s < 2; s++) {
-      const int kk = ch * 64 + 32 * s + 8 * g;
+    for (int h = 0; h < 2; h++)
 #pragma unroll
-      for (int ct = 0; ct < 4; ct++) load_w<TA, TW>(wf[ct][s], wrow[ct] + kk);
+      for (int ct = 0; ct < 4; ct++)
+        wr[ct][h] = *reinterpret_cast<const uint4*>(wtile[ct] + (size_t)c * 2048 + h * 1024);
 #pragma unroll
-      for (int rt = 0; rt < 2; rt++) load_frag(af[rt][s], arow[rt] + kk);
-    }
-  };
-  // ok = false: the piece is past the contraction (clamped load), zero its A
-  auto comp = [&](Frag(&wf)[4][2], Frag(&af)[2][2], bool ok) {
-#pragma unroll
-    for (int s = 0; s < 2; s++) {
-#pragma unroll
-      for (int ct = 0; ct < 4; ct++) mask_frag(wf[ct][s], wok[ct]);
-#pragma unroll
-      for (int rt = 0; rt < 2; rt++) mask_frag(af[rt][s], aok[rt] && ok);
+    for (int j = 0; j < NA; j++)
 #pragma unroll
       for (int rt = 0; rt < 2; rt++)
+        ar[rt][j] = *reinterpret_cast<const uint4*>(arow[rt] + c * PC::EP + PC::a_off(j, g));
+  };
+  // ok = false: the piece is past the contraction (clamped load), zero its A
+  auto comp = [&](uint4(&wr)[4][2], uint4(&ar)[2][NA], bool ok) {
 #pragma unroll
-        for (int ct = 0; ct < 4; ct++) mma(acc[rt][ct], af[rt][s], wf[ct][s]);
-    }
+    for (int ct = 0; ct < 4; ct++)
+#pragma unroll
+      for (int h = 0; h < 2; h++) zero_unless(wr[ct][h], wok[ct]);
+#pragma unroll
+    for (int rt = 0; rt < 2; rt++)
+#pragma unroll
+      for (int j = 0; j < NA; j++) zero_unless(ar[rt][j], aok[rt] && ok);
+    piece_mma(acc, wr, ar, (TA*)nullptr, (TW*)nullptr);
   };
 
   // wave takes pieces kw, kw+KW, ...; two register buffers, straight-line
   // code (indices past the end are clamped and masked) so that the waits
   // before each MFMA group cover only the older buffer's loads
-  const int nch = K / 64;
   const int per = (nch + KW - 1) / KW;
   const int npairs = (per + 1) / 2;
   auto cidx = [&](int i) { const int c = kw + KW * i; return c < nch ? c : nch - 1; };
@@ -212,44 +271,6 @@ __global__ __launch_bounds__(256) void wstream_k(StreamGemm a) {
           if (r < nrows)
             stx((TA*)a.out, (size_t)(row0 + r) * a.ldo + (chunk * CWG + grp) * 32 + 16 * pp + l16,
                 gv / (1.f + expf(-gv)) * uv);
-        }
-      }
-    } else if (MODE == SG_LMHEAD) {
-      static_assert(MODE != SG_LMHEAD || KW == 4, "the head epilogue reduces one 64-column group");
-      // per row: (max, lowest index attaining it, sum exp(l - max)) over the 64 columns
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int r = rt * 16 + 4 * g + i;
-        const int n = n0 + 16 * q + l16;
-        const float val = n < a.N ? v[i] : -INFINITY;
-        if (a.logits && r < nrows && n < a.N) a.logits[(size_t)(row0 + r) * a.N + n] = val;
-        float m = -INFINITY, s = 0.f;
-        int idx = 0x7fffffff;
-        mrg3(m, idx, s, val, n, 1.f);
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-          const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
-          const int i2 = __shfl_xor(idx, o, 64);
-          mrg3(m, idx, s, m2, i2, s2);
-        }
-        if (l16 == 0) {
-          hm[q][4 * g + i] = m;
-          hs[q][4 * g + i] = s;
-          hi[q][4 * g + i] = idx;
-        }
-      }
-      __syncthreads();
-      if (threadIdx.x < 16) {
-        const int rr = threadIdx.x;
-        float m = hm[0][rr], s = hs[0][rr];
-        int idx = hi[0][rr];
-        for (int qq = 1; qq < 4; qq++) mrg3(m, idx, s, hm[qq][rr], hi[qq][rr], hs[qq][rr]);
-        const int r = rt * 16 + rr;
-        if (r < nrows) {
-          const size_t o = (size_t)(row0 + r) * C + chunk;
-          a.pmax[o] = m;
-          a.pidx[o] = idx;
-          a.psum[o] = s;
         }
       }
     } else {
@@ -323,7 +344,6 @@ void launch_stream_gemm(int act, int wdt, int mode, int kw, const StreamGemm& a,
     case SG_QKV_CACHE: dispatch<SG_QKV_CACHE, 4>(act, wdt, a, nb, s); break;
     case SG_GATEUP: dispatch<SG_GATEUP, 4>(act, wdt, a, nb, s); break;
     case SG_DOWN: dispatch<SG_DOWN, 4>(act, wdt, a, nb, s); break;
-    case SG_LMHEAD: dispatch<SG_LMHEAD, 4>(act, wdt, a, nb, s); break;
   }
 }
 

@@ -85,19 +85,23 @@ void launch_gateup_lds(int act, const void* u2, const int32_t* perm, int k, cons
 void launch_down_lds(int act, const void* H, const MoeW& w, const int4* tiles,
                      const int32_t* ntiles, int max_tiles, int D, int F, void* Y, hipStream_t s);
 // LM head: per-row partial (max, argmax, sum exp) over vocabulary tiles of 128
+// row-major [rows][rowbytes] -> packed weight layout (rowbytes % 128 == 0,
+// rows padded to a multiple of 16 with zeros)
+void launch_pack(const void* src, void* dst, int rows, int rowbytes, hipStream_t s);
+
 // returns the number of per-row partials written (one per vocabulary tile)
 int launch_lmhead(int act, const void* uf, int M, int D, const void* lm, int V, float* pmax,
                   int32_t* pidx, float* psum, float* logits, hipStream_t s);
 
 // ---- weight-streaming MFMA GEMM for few rows (kern_stream.hip) ----
 enum StreamMode { SG_STORE = 0, SG_RESID = 1, SG_F32 = 2, SG_QKV_CACHE = 3, SG_GATEUP = 4,
-                  SG_DOWN = 5, SG_LMHEAD = 6 };
+                  SG_DOWN = 5 };
 struct StreamGemm {
   const void* A;          // activations [rows][K] (gate/up: gathered through perm)
   int M, K;
   const int32_t* perm;    // gate/up: slot -> token*k + j
   int k;
-  const void* W0;         // weights: dense rows [0,n1) / gate / down / head
+  const void* W0;         // packed weights: dense rows [0,n1) / gate / down
   const void* W1;         // dense rows [n1,n1+n2) / up
   const void* W2;         // dense rows [n1+n2,N)
   int n1, n2, N;          // dense / head output columns
@@ -110,10 +114,6 @@ struct StreamGemm {
   int ldo;
   const void* R;          // residual (SG_RESID)
   CacheDst cache;         // SG_QKV_CACHE
-  float* pmax;            // SG_LMHEAD partials [rows][nchunks]
-  int32_t* pidx;
-  float* psum;
-  float* logits;          // SG_LMHEAD optional tap [rows][N]
 };
 void launch_stream_gemm(int act, int wdt, int mode, int kw, const StreamGemm& a, int ntiles_max,
                         hipStream_t s);

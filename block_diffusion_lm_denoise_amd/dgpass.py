@@ -63,7 +63,7 @@ class dg_taps(C.Structure):
 
 
 EXPORTS = ("dg_model_init", "dg_workspace_bytes", "dg_kv_prefill", "dg_denoise_pass", "dg_renoise",
-           "dg_expert_coverage", "dg_status_str")
+           "dg_expert_coverage", "dg_packed_bytes", "dg_pack_weight", "dg_status_str")
 
 _lib = None
 
@@ -89,6 +89,10 @@ def lib():
         L.dg_renoise.restype = i32
         L.dg_expert_coverage.argtypes = [vp, vp, sz, vp, vp, vp]
         L.dg_expert_coverage.restype = i32
+        L.dg_packed_bytes.argtypes = [i32, i32, i32]
+        L.dg_packed_bytes.restype = sz
+        L.dg_pack_weight.argtypes = [vp, vp, i32, i32, i32, vp]
+        L.dg_pack_weight.restype = i32
         L.dg_status_str.argtypes = [i32]
         L.dg_status_str.restype = C.c_char_p
         _lib = L
@@ -173,22 +177,54 @@ def _taps_struct(taps, inject_router=None, events=None):
     return t, keep
 
 
+def packed_bytes(rows: int, cols: int, dtype: str) -> int:
+    return lib().dg_packed_bytes(int(rows), int(cols), _DT[dtype])
+
+
+def pack_weight(src: torch.Tensor, rows: int, cols: int, dtype: str, stream=None) -> torch.Tensor:
+    """Packed copy (a new uint8 device tensor) of the row-major device matrix src [rows][cols]."""
+    n = packed_bytes(rows, cols, dtype)
+    if n == 0:
+        raise DgError(-1, "dg_packed_bytes")
+    dst = torch.empty(n, dtype=torch.uint8, device=src.device)
+    _check(lib().dg_pack_weight(src.data_ptr(), dst.data_ptr(), int(rows), int(cols), _DT[dtype],
+                                _stream(stream)), "dg_pack_weight")
+    return dst
+
+
+# streamed weight matrices: name -> (rows, cols, dtype field of the config)
+def _packed_shapes(cfg: ModelConfig):
+    QD, KD = cfg.Hq * cfg.hd, cfg.Hkv * cfg.hd
+    return {"wq": (QD, cfg.D, cfg.act), "wk": (KD, cfg.D, cfg.act), "wv": (KD, cfg.D, cfg.act),
+            "wo": (cfg.D, QD, cfg.act), "wr": (cfg.E, cfg.D, cfg.act),
+            "wg": (cfg.E * cfg.F, cfg.D, cfg.expert), "wu": (cfg.E * cfg.F, cfg.D, cfg.expert),
+            "wd": (cfg.E * cfg.D, cfg.F, cfg.expert)}
+
+
 class Model:
-    """A model on the device: config + weight tensors (kept alive here)."""
+    """A model on the device: config + weight tensors.  The streamed weight
+    matrices are packed once here (new device tensors, kept alive with the
+    caller's row-major weights)."""
 
     def __init__(self, cfg: ModelConfig, weights: dict):
         if cfg.L > MAX_LAYERS:
             raise ValueError("too many layers")
         self.cfg = cfg
         self.weights = weights
+        shapes = _packed_shapes(cfg)
+        self.packed = {"lm": pack_weight(weights["lm"], cfg.V, cfg.D, cfg.act), "layers": []}
         w = dg_weights()
         w.emb = weights["emb"].data_ptr()
         w.gf = weights["gf"].data_ptr()
-        w.lm = weights["lm"].data_ptr()
+        w.lm = self.packed["lm"].data_ptr()
         for l, lw in enumerate(weights["layers"]):
             L = w.layers[l]
-            for n in ("g1", "wq", "wk", "wv", "wo", "g2", "wr", "wg", "wu", "wd"):
+            pk = {n: pack_weight(lw[n], *shapes[n]) for n in shapes}
+            self.packed["layers"].append(pk)
+            for n in ("g1", "g2"):
                 setattr(L, n, lw[n].data_ptr())
+            for n in shapes:
+                setattr(L, n, pk[n].data_ptr())
             L.escale = _ptr(lw.get("escale"))
         self._c = make_config(cfg)
         self._m = dg_model()

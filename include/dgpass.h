@@ -35,8 +35,10 @@
  *    are marked "host".  The library allocates nothing and keeps no global
  *    state; every call enqueues on `stream` (a hipStream_t, NULL = the null
  *    stream) and returns without synchronising.
- *  - Matrices are row-major [rows][cols] with the contraction dimension
- *    contiguous (weights are [out][in]).
+ *  - Activations, caches and the embedding table are row-major [rows][cols].
+ *    The weight matrices a GEMM streams (wq, wk, wv, wo, wr, wg, wu, wd, lm;
+ *    logically [out][in]) are passed in the packed layout below, written by
+ *    dg_pack_weight from the row-major matrix.
  *  - Arguments are validated before the first launch; a call that returns an
  *    error has enqueued nothing and changed nothing.  Device faults surface at
  *    the caller's next synchronisation.  No C++ exception crosses the ABI.
@@ -70,7 +72,8 @@ typedef int32_t dg_status;
 
 /* Model shape.  Supported: act_dtype F32 with expert_dtype F32, or act_dtype
  * BF16 with expert_dtype BF16 or FP8E4M3; hd in {64, 128}; Hq/Hkv in
- * {1, 2, 4, 8, 16}; D, F and Hq*hd multiples of 64; 1 <= k <= 8; k <= E <= 256. */
+ * {1, 2, 4, 8, 16}; D a multiple of 128; F and Hq*hd multiples of 64 (F of
+ * 128 with FP8E4M3 experts); 1 <= k <= 8; k <= E <= 256. */
 typedef struct dg_config {
   int32_t L, D, Hq, Hkv, hd, E, k, F, V;
   float eps;               /* RMSNorm epsilon */
@@ -78,26 +81,38 @@ typedef struct dg_config {
   int32_t expert_dtype;    /* expert weights */
 } dg_config;
 
+/* Packed weight layout.  A logical row-major matrix [rows][cols] whose rows
+ * hold rb = cols * (element bytes) bytes, rb a multiple of 128, is stored as
+ * tiles of 16 rows x 128 bytes: tile (rg, kb) -- row group rg = 0 ..
+ * ceil(rows/16)-1, column block kb = 0 .. rb/128-1 -- occupies the 2048 bytes
+ * at offset (rg * rb/128 + kb) * 2048.  Inside a tile, the 16 bytes at offset
+ * 1024 h + 16 l (h in {0, 1}, l in 0..63) hold row 16 rg + l % 16, bytes
+ * 128 kb + 64 h + 16 (l / 16) .. +15 of that row; rows past the matrix are
+ * zero.  One 64-lane load of 16 bytes per lane then reads 1 KB of contiguous
+ * memory and leaves every lane with its matrix-core operand fragment.  An
+ * expert tensor [E][F][D] is packed as one [E*F][D] matrix (F is a multiple
+ * of 16, so no tile straddles two experts). */
+
 /* Device pointers of one layer. */
 typedef struct dg_layer_weights {
   const float* g1;     /* [D] f32 */
-  const void* wq;      /* [Hq*hd][D] act */
-  const void* wk;      /* [Hkv*hd][D] act */
-  const void* wv;      /* [Hkv*hd][D] act */
-  const void* wo;      /* [D][Hq*hd] act */
+  const void* wq;      /* [Hq*hd][D] act, packed */
+  const void* wk;      /* [Hkv*hd][D] act, packed */
+  const void* wv;      /* [Hkv*hd][D] act, packed */
+  const void* wo;      /* [D][Hq*hd] act, packed */
   const float* g2;     /* [D] f32 */
-  const void* wr;      /* [E][D] act */
-  const void* wg;      /* [E][F][D] expert dtype */
-  const void* wu;      /* [E][F][D] expert dtype */
-  const void* wd;      /* [E][D][F] expert dtype */
+  const void* wr;      /* [E][D] act, packed (rows padded to 16) */
+  const void* wg;      /* [E][F][D] expert dtype, packed as [E*F][D] */
+  const void* wu;      /* [E][F][D] expert dtype, packed as [E*F][D] */
+  const void* wd;      /* [E][D][F] expert dtype, packed as [E*D][F] */
   const float* escale; /* [E][3] f32 (gate, up, down) multipliers of the
                           accumulated fp8 products; NULL unless FP8E4M3 */
 } dg_layer_weights;
 
 typedef struct dg_weights {
-  const void* emb;     /* [V][D] act */
+  const void* emb;     /* [V][D] act, row-major (rows are gathered by token) */
   const float* gf;     /* [D] f32 final norm gain */
-  const void* lm;      /* [V][D] act (may alias emb) */
+  const void* lm;      /* [V][D] act, packed (rows padded to 16) */
   dg_layer_weights layers[DG_MAX_LAYERS];
 } dg_weights;
 
@@ -185,6 +200,19 @@ dg_status dg_renoise(int32_t* canvas, const int32_t* argmax, const float* conf, 
  * optionally device counts [L][E] int32. */
 dg_status dg_expert_coverage(const dg_model* m, const void* ws, size_t ws_bytes, int32_t* touched,
                              int32_t* counts, void* stream);
+
+/* Bytes of a packed weight matrix: ceil(rows/16)*16 * cols * element bytes;
+ * 0 when rows or cols < 1, dtype is not a storage type or the row bytes are
+ * not a multiple of 128.  Host arithmetic only. */
+size_t dg_packed_bytes(int32_t rows, int32_t cols, int32_t dtype);
+
+/* Write the packed layout of the row-major device matrix src [rows][cols]
+ * (dtype) to device dst (dg_packed_bytes(rows, cols, dtype) bytes, not
+ * overlapping src).  Enqueued on stream; a one-time step when a model is
+ * loaded.  Errors: INVALID (null or equal pointers, a shape dg_packed_bytes
+ * rejects), UNSUPPORTED, HIP. */
+dg_status dg_pack_weight(const void* src, void* dst, int32_t rows, int32_t cols, int32_t dtype,
+                         void* stream);
 
 const char* dg_status_str(dg_status s);
 

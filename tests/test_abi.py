@@ -124,3 +124,28 @@ def test_calls_reject_bad_arguments_before_launching():
     assert L.dg_renoise(dev, None, None, 0.5, 1, 0, p0, None, 65, 4, 512, None) == -1
     assert L.dg_expert_coverage(C.byref(m), dev, 4, dev, None, None) == -4
     assert L.dg_expert_coverage(C.byref(m), dev, 1 << 20, None, None, None) == -1
+
+
+def test_packed_bytes_pads_rows_and_requires_128_byte_rows():
+    L = dgpass.lib()
+    F32, BF16, FP8 = 0, 1, 2
+    assert L.dg_packed_bytes(32, 64, BF16) == 32 * 128
+    assert L.dg_packed_bytes(8, 64, BF16) == 16 * 128           # rows padded to 16
+    assert L.dg_packed_bytes(17, 2048, BF16) == 32 * 4096
+    assert L.dg_packed_bytes(16, 128, FP8) == 16 * 128
+    assert L.dg_packed_bytes(16, 32, F32) == 16 * 128
+    assert L.dg_packed_bytes(16, 96, BF16) == 0                 # 192-byte rows
+    assert L.dg_packed_bytes(16, 64, FP8) == 0                  # 64-byte rows
+    assert L.dg_packed_bytes(0, 64, BF16) == 0
+    assert L.dg_packed_bytes(16, 64, 7) == 0
+
+
+def test_pack_weight_rejects_bad_arguments_before_launch():
+    L = dgpass.lib()
+    a = C.c_void_p(0x1000)
+    b = C.c_void_p(0x2000)
+    assert L.dg_pack_weight(None, b, 16, 64, 1, None) == -1
+    assert L.dg_pack_weight(a, None, 16, 64, 1, None) == -1
+    assert L.dg_pack_weight(a, a, 16, 64, 1, None) == -1
+    assert L.dg_pack_weight(a, b, 16, 96, 1, None) == -1
+    assert L.dg_pack_weight(a, b, 0, 64, 1, None) == -1
