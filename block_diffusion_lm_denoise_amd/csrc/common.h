@@ -14,12 +14,15 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// round-to-nearest-even fp32 -> bf16 (NaN stays NaN)
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t b = __float_as_uint(f);
-  if ((b & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((b >> 16) | 0x40u);
-  b += 0x7fffu + ((b >> 16) & 1u);
-  return (uint16_t)(b >> 16);
+// round-to-nearest-even fp32 -> bf16 (NaN stays NaN): the gfx950 hardware
+// conversion (v_cvt_pk_bf16_f32)
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// two values -> packed bf16 pair (lo = a, hi = b), one instruction
+__device__ __forceinline__ uint32_t f2bf2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // activation storage: float or bf16 bit patterns
@@ -130,10 +133,10 @@ __device__ __forceinline__ void ld8(const float* p, float (&v)[8]) {
 }
 __device__ __forceinline__ void st8(uint16_t* p, const float (&v)[8]) {
   uint4 u;
-  u.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-  u.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-  u.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
-  u.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+  u.x = f2bf2(v[0], v[1]);
+  u.y = f2bf2(v[2], v[3]);
+  u.z = f2bf2(v[4], v[5]);
+  u.w = f2bf2(v[6], v[7]);
   *reinterpret_cast<uint4*>(p) = u;
 }
 __device__ __forceinline__ void st8(float* p, const float (&v)[8]) {

@@ -12,9 +12,11 @@
 // staged K/V tile serves every head of the group.  Each wave owns 16 rows and
 // computes S^T = K Q^T (keys on the MFMA row axis, queries on the column
 // axis), so a lane's softmax statistics belong to one query row; then
-// O^T += V^T P^T with V staged transposed in LDS (bf16: P as hi + lo bf16).  Online softmax in fp32
-// (base-2 exponent with the scale folded in).  Key splits write unnormalised
-// partials (O, m, l) that a merge kernel combines in split order.
+// O^T += V^T P^T with V staged transposed in LDS (bf16: P as hi + lo bf16).
+// Online softmax in fp32 (base-2 exponent with the scale folded in).  The
+// next K/V tile is loaded into registers while the current one is used.
+// Key splits write unnormalised partials (O, m, l) that a merge kernel
+// combines in split order.
 #include <math.h>
 
 #include "common.h"
@@ -47,13 +49,20 @@ struct AttnArgs {
 template <typename TA, int HD>
 __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
   typedef typename FragOf<TA>::type Frag;
-  constexpr int KLD = HD + 16 / (int)sizeof(TA);   // padded row of the K tile
-  constexpr int VLD = KT + 16 / (int)sizeof(TA);   // padded row of the transposed V tile
+  constexpr int ES = (int)sizeof(TA);
+  constexpr int EPC = 16 / ES;                  // elements per 16-byte chunk
+  constexpr int CPR = HD / EPC;                 // chunks per key row
+  constexpr int KLD = HD + EPC;                 // padded row of the K tile
+  constexpr int VLD = KT + EPC;                 // padded row of the transposed V tile
+  constexpr int KCH = KT * CPR / 256;           // K chunks staged per thread
+  constexpr int NVG = (KT / 4) * CPR;           // V groups (4 keys x 1 chunk)
+  constexpr int VCH = (NVG + 255) / 256;        // V groups per thread
+  static_assert(KT * CPR % 256 == 0, "K staging");
   __shared__ __attribute__((aligned(16))) TA ks[KT * KLD];
   __shared__ __attribute__((aligned(16))) TA vt[HD * VLD];
 
   const int qt = blockIdx.x, b = blockIdx.y / a.Hkv, gh = blockIdx.y % a.Hkv, split = blockIdx.z;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l16 = lane & 15, g4 = lane >> 4;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, l16 = lane & 15, g4 = lane >> 4;
   const int P = a.len.v[b];
 
   // this lane's query row
@@ -79,49 +88,76 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
   }
   f32x4_t o[HD / 16];
 #pragma unroll
-  for (int t = 0; t < HD / 16; t++) o[t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < HD / 16; u++) o[u] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   float mrow = -INFINITY, lsum = 0.f;
 
-  for (int k0 = kbeg; k0 < kend; k0 += KT) {
-    __syncthreads();
-    // ---- stage K [KT][HD] ----
-    constexpr int CPR = HD * (int)sizeof(TA) / 16;   // 16-byte chunks per key row
-    for (int c = threadIdx.x; c < KT * CPR; c += 256) {
-      const int j = c / CPR, q = c % CPR;
-      const int kk = k0 + j;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (kk < kend) {
-        const TA* src = (a.mode == 0 && kk >= P)
-                            ? (const TA*)a.kn + (size_t)(b * a.T + kk - P) * a.ldq + gh * HD
-                            : (const TA*)a.kc + (((size_t)b * a.Hkv + gh) * a.cap + kk) * HD;
-        v = *reinterpret_cast<const uint4*>(src + q * (16 / (int)sizeof(TA)));
-      }
-      *reinterpret_cast<uint4*>(ks + j * KLD + q * (16 / (int)sizeof(TA))) = v;
-    }
-    // ---- stage V transposed: vt[d][j] ----
-    constexpr int EPC = 16 / (int)sizeof(TA);        // elements per 16-byte chunk
-    for (int c = threadIdx.x; c < (KT / 4) * (HD / EPC); c += 256) {
-      const int jg = c / (HD / EPC), dq = c % (HD / EPC);
-      TA vals[4][EPC];
+  // K/V of key kk: the cache, or in mode 0 the canvas rows of the qkv buffer
+  // for kk >= P.  Keys past the split end read key kbeg (a valid key, so the
+  // data is finite): their scores are masked to -inf, so they add nothing.
+  // Straight-line selects keep the loads of the next tile in flight.
+  const TA* const kc = (const TA*)a.kc + ((size_t)b * a.Hkv + gh) * a.cap * HD;
+  const TA* const vc = (const TA*)a.vc + ((size_t)b * a.Hkv + gh) * a.cap * HD;
+  const TA* const kn = a.mode == 0 ? (const TA*)a.kn + (size_t)b * a.T * a.ldq + gh * HD : kc;
+  const TA* const vn = a.mode == 0 ? (const TA*)a.vn + (size_t)b * a.T * a.ldq + gh * HD : vc;
+  const int fresh0 = a.mode == 0 ? P : 0x7fffffff;   // first key read from the qkv rows
+  auto kptr = [&](int kk, const TA* cache, const TA* fresh) -> const TA* {
+    const int k = kk < kend ? kk : kbeg;
+    return k >= fresh0 ? fresh + (size_t)(k - fresh0) * a.ldq : cache + (size_t)k * HD;
+  };
+  // register copy of the next tile: K chunks and V 4-key groups (a native
+  // vector type: plain loads and stores, no struct copies through memory)
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 rk[KCH], rv[VCH][4];
+  auto gload = [&](int k0) {
 #pragma unroll
-      for (int jj = 0; jj < 4; jj++) {
-        const int kk = k0 + 4 * jg + jj;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (kk < kend) {
-          const TA* src = (a.mode == 0 && kk >= P)
-                              ? (const TA*)a.vn + (size_t)(b * a.T + kk - P) * a.ldq + gh * HD
-                              : (const TA*)a.vc + (((size_t)b * a.Hkv + gh) * a.cap + kk) * HD;
-          v = *reinterpret_cast<const uint4*>(src + dq * EPC);
+    for (int u = 0; u < KCH; u++) {
+      const int id = t + 256 * u, j = id / CPR, q = id % CPR;
+      rk[u] = *reinterpret_cast<const u32x4*>(kptr(k0 + j, kc, kn) + q * EPC);
+    }
+#pragma unroll
+    for (int u = 0; u < VCH; u++) {
+      const int id = t + 256 * u;
+      const int jg = (id < NVG ? id : 0) / CPR, dq = (id < NVG ? id : 0) % CPR;
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++)
+        rv[u][jj] = *reinterpret_cast<const u32x4*>(kptr(k0 + 4 * jg + jj, vc, vn) + dq * EPC);
+    }
+  };
+  auto word = [](u32x4 v, int k) -> uint32_t { return v[k]; };
+  // LDS: K row-major; V transposed (vt[d][key]), 4 keys of one d per store
+  auto sstore = [&]() {
+#pragma unroll
+    for (int u = 0; u < KCH; u++) {
+      const int id = t + 256 * u, j = id / CPR, q = id % CPR;
+      *reinterpret_cast<u32x4*>(ks + j * KLD + q * EPC) = rk[u];
+    }
+#pragma unroll
+    for (int u = 0; u < VCH; u++) {
+      const int id = t + 256 * u;
+      if (NVG % 256 != 0 && id >= NVG) continue;
+      const int jg = id / CPR, dq = id % CPR;
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        const uint32_t a0 = word(rv[u][0], k), a1 = word(rv[u][1], k);
+        const uint32_t a2 = word(rv[u][2], k), a3 = word(rv[u][3], k);
+        if constexpr (ES == 2) {
+          // elements 2k (low halves) and 2k+1 (high halves) of the chunk
+          const uint2 lo = make_uint2((a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16));
+          const uint2 hi = make_uint2((a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u));
+          *reinterpret_cast<uint2*>(vt + (dq * EPC + 2 * k) * VLD + 4 * jg) = lo;
+          *reinterpret_cast<uint2*>(vt + (dq * EPC + 2 * k + 1) * VLD + 4 * jg) = hi;
+        } else {
+          *reinterpret_cast<u32x4*>(vt + (dq * EPC + k) * VLD + 4 * jg) = (u32x4){a0, a1, a2, a3};
         }
-        *reinterpret_cast<uint4*>(vals[jj]) = v;
-      }
-#pragma unroll
-      for (int d = 0; d < EPC; d++) {
-        TA* dst = vt + (dq * EPC + d) * VLD + 4 * jg;
-#pragma unroll
-        for (int jj = 0; jj < 4; jj++) dst[jj] = vals[jj][d];
       }
     }
+  };
+
+  if (kbeg < kend) gload(kbeg);
+  for (int k0 = kbeg; k0 < kend; k0 += KT) {
+    __syncthreads();   // the previous tile's readers are done with LDS
+    sstore();
+    if (k0 + KT < kend) gload(k0 + KT);   // next tile in flight during this one
     __syncthreads();
 
     // ---- S^T = K Q^T: lane holds keys 16*mt + 4*g4 + i for query row l16 ----
@@ -142,28 +178,28 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int kk = k0 + 16 * mt + 4 * g4 + i;
-        float v = s[mt][i] * a.scale_log2;
-        if (kk >= kend || kk > qlimit || !qvalid) v = -INFINITY;
+        const bool ok = (kk < kend) & (kk <= qlimit) & qvalid;
+        const float v = ok ? s[mt][i] * a.scale_log2 : -INFINITY;
         s[mt][i] = v;
         tmax = fmaxf(tmax, v);
       }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const float mnew = fmaxf(mrow, tmax);
-    const float alpha = mnew == -INFINITY ? 1.f : exp2f(mrow - mnew);
+    const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mrow - mnew);
     float psum = 0.f;
 #pragma unroll
     for (int mt = 0; mt < KT / 16; mt++)
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        const float p = mnew == -INFINITY ? 0.f : exp2f(s[mt][i] - mnew);
+        const float p = mnew == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[mt][i] - mnew);
         s[mt][i] = p;
         psum += p;
       }
     lsum = lsum * alpha + psum;
     mrow = mnew;
 #pragma unroll
-    for (int t = 0; t < HD / 16; t++) o[t] *= alpha;
+    for (int u = 0; u < HD / 16; u++) o[u] *= alpha;
 
     // ---- O^T += V^T P^T: key slot 8*g4 + 4*t + i <-> key 32*c + 16*t + 4*g4 + i ----
     // bf16: P is split into hi + lo bf16 parts (two MFMAs), so the products
@@ -171,30 +207,30 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
 #pragma unroll
     for (int c = 0; c < KT / 32; c++) {
       Frag pf, pl;
-      if constexpr (sizeof(TA) == 2) {
-        uint16_t ph[8], plo[8];
+      if constexpr (ES == 2) {
+        uint32_t ph[4], plo[4];
 #pragma unroll
-        for (int t = 0; t < 2; t++)
+        for (int tt = 0; tt < 2; tt++)
 #pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const float p = s[2 * c + t][i];
-            const uint16_t h = f2bf(p);
-            ph[4 * t + i] = h;
-            plo[4 * t + i] = f2bf(p - bf2f(h));
+          for (int i = 0; i < 4; i += 2) {
+            const float p0 = s[2 * c + tt][i], p1 = s[2 * c + tt][i + 1];
+            const uint32_t h = f2bf2(p0, p1);
+            ph[2 * tt + i / 2] = h;
+            plo[2 * tt + i / 2] = f2bf2(p0 - __uint_as_float(h << 16), p1 - __uint_as_float(h & 0xffff0000u));
           }
-        pf.v = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<uint4*>(ph));
-        pl.v = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<uint4*>(plo));
+        pf.v = __builtin_bit_cast(bf16x8_t, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+        pl.v = __builtin_bit_cast(bf16x8_t, make_uint4(plo[0], plo[1], plo[2], plo[3]));
       } else {
 #pragma unroll
-        for (int t = 0; t < 2; t++)
+        for (int tt = 0; tt < 2; tt++)
 #pragma unroll
-          for (int i = 0; i < 4; i++) pf.v[4 * t + i] = s[2 * c + t][i];
+          for (int i = 0; i < 4; i++) pf.v[4 * tt + i] = s[2 * c + tt][i];
       }
 #pragma unroll
       for (int ht = 0; ht < HD / 16; ht++) {
         const TA* vrow = vt + (16 * ht + l16) * VLD + 32 * c + 4 * g4;
         Frag vf;
-        if constexpr (sizeof(TA) == 2) {
+        if constexpr (ES == 2) {
           uint2 lo = *reinterpret_cast<const uint2*>(vrow);
           uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
           vf.v = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
@@ -213,52 +249,83 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
 
   lsum += __shfl_xor(lsum, 16, 64);
   lsum += __shfl_xor(lsum, 32, 64);
-  if (!qvalid) return;
-  const size_t row = (size_t)b * a.T + qi;
+  const size_t row = (size_t)b * a.T + (qvalid ? qi : 0);
   if (a.nsplit == 1) {
+    if (!qvalid) return;
     const float inv = 1.f / lsum;
     TA* out = (TA*)a.out + row * (a.Hq * HD) + head * HD;
 #pragma unroll
     for (int ht = 0; ht < HD / 16; ht++)
 #pragma unroll
       for (int i = 0; i < 4; i++) stx(out, 16 * ht + 4 * g4 + i, o[ht][i] * inv);
-  } else {
-    const size_t e = ((size_t)split * a.rows + row) * a.Hq + head;
-    float* po = a.po + e * HD;
+    return;
+  }
+
+  // ---- key splits: unnormalised partials (O, m, l), merged by attn_merge_k ----
+  if (!qvalid) return;
+  const size_t e = split * (size_t)a.rows * a.Hq + row * a.Hq + head;
+  float* po = a.po + e * HD;
 #pragma unroll
-    for (int ht = 0; ht < HD / 16; ht++)
+  for (int ht = 0; ht < HD / 16; ht++)
 #pragma unroll
-      for (int i = 0; i < 4; i++) po[16 * ht + 4 * g4 + i] = o[ht][i];
-    if (g4 == 0) {
-      a.pml[2 * e] = mrow;
-      a.pml[2 * e + 1] = lsum;
-    }
+    for (int i = 0; i < 4; i++) po[16 * ht + 4 * g4 + i] = o[ht][i];
+  if (g4 == 0) {
+    a.pml[2 * e] = mrow;
+    a.pml[2 * e + 1] = lsum;
   }
 }
 
-// combine key splits in split order: o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
-template <typename TA>
+// combine key splits in split order: o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// A thread owns 8 consecutive head-dimension elements of one (row, head)
+// entry; the partial loads of several splits are in flight together.
+template <typename TA, int HD>
 __global__ __launch_bounds__(256) void attn_merge_k(const float* __restrict__ po,
                                                     const float* __restrict__ pml, int nsplit,
-                                                    int entries, int hd, TA* __restrict__ out) {
-  const int e = blockIdx.x * (256 / 64) + (threadIdx.x >> 6);   // (row, head) entry
+                                                    int entries, TA* __restrict__ out) {
+  constexpr int TPE = HD / 8;   // threads per entry
+  const int gt = blockIdx.x * 256 + threadIdx.x;
+  const int e = gt / TPE, d0 = (gt % TPE) * 8;
   if (e >= entries) return;
-  const int lane = threadIdx.x & 63;
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; s++) M = fmaxf(M, pml[2 * ((size_t)s * entries + e)]);
-  float den = 0.f;
-  for (int s = 0; s < nsplit; s++) {
-    const float m = pml[2 * ((size_t)s * entries + e)];
-    if (m != -INFINITY) den += exp2f(m - M) * pml[2 * ((size_t)s * entries + e) + 1];
+  for (int s0 = 0; s0 < nsplit; s0 += 8) {
+    float m[8];
+#pragma unroll
+    for (int j = 0; j < 8; j++) m[j] = s0 + j < nsplit ? pml[2 * ((size_t)(s0 + j) * entries + e)] : -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; j++) M = fmaxf(M, m[j]);
   }
-  for (int d = lane; d < hd; d += 64) {
-    float num = 0.f;
-    for (int s = 0; s < nsplit; s++) {
-      const float m = pml[2 * ((size_t)s * entries + e)];
-      if (m != -INFINITY) num += exp2f(m - M) * po[((size_t)s * entries + e) * hd + d];
+  float den = 0.f, num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nsplit; s0 += 4) {
+    float f[4], l[4];
+    float4 v0[4], v1[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const int sp = s0 + j < nsplit ? s0 + j : s0;
+      const size_t ee = (size_t)sp * entries + e;
+      const float mj = pml[2 * ee];
+      f[j] = (s0 + j < nsplit && mj != -INFINITY) ? __builtin_amdgcn_exp2f(mj - M) : 0.f;
+      l[j] = pml[2 * ee + 1];
+      v0[j] = *reinterpret_cast<const float4*>(po + ee * HD + d0);
+      v1[j] = *reinterpret_cast<const float4*>(po + ee * HD + d0 + 4);
     }
-    stx(out, (size_t)e * hd + d, num / den);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      den += f[j] * l[j];
+      num[0] += f[j] * v0[j].x;
+      num[1] += f[j] * v0[j].y;
+      num[2] += f[j] * v0[j].z;
+      num[3] += f[j] * v0[j].w;
+      num[4] += f[j] * v1[j].x;
+      num[5] += f[j] * v1[j].y;
+      num[6] += f[j] * v1[j].z;
+      num[7] += f[j] * v1[j].w;
+    }
   }
+  const float inv = 1.f / den;
+  float r[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) r[i] = num[i] * inv;
+  st8(out + (size_t)e * HD + d0, r);
 }
 
 // ---------------------------------------------------------------------------
@@ -320,12 +387,14 @@ void launch_attention(const AttnArgsHost& h, hipStream_t s) {
   }
   if (nsplit > 1) {
     const int entries = a.rows * h.Hq;
-    if (h.act == ACT_BF16)
-      attn_merge_k<uint16_t><<<(entries + 3) / 4, 256, 0, s>>>(h.po, h.pml, nsplit, entries, h.hd,
-                                                               (uint16_t*)h.out);
-    else
-      attn_merge_k<float><<<(entries + 3) / 4, 256, 0, s>>>(h.po, h.pml, nsplit, entries, h.hd,
-                                                            (float*)h.out);
+    const int blocks = (int)(((long)entries * (h.hd / 8) + 255) / 256);
+    if (h.act == ACT_BF16) {
+      if (h.hd == 128) attn_merge_k<uint16_t, 128><<<blocks, 256, 0, s>>>(h.po, h.pml, nsplit, entries, (uint16_t*)h.out);
+      else attn_merge_k<uint16_t, 64><<<blocks, 256, 0, s>>>(h.po, h.pml, nsplit, entries, (uint16_t*)h.out);
+    } else {
+      if (h.hd == 128) attn_merge_k<float, 128><<<blocks, 256, 0, s>>>(h.po, h.pml, nsplit, entries, (float*)h.out);
+      else attn_merge_k<float, 64><<<blocks, 256, 0, s>>>(h.po, h.pml, nsplit, entries, (float*)h.out);
+    }
   }
 }
 
