@@ -8,6 +8,9 @@ namespace dg {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// 16 raw bytes in registers (a native vector: plain loads and stores, never
+// a struct copy through private memory)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // scalar conversions

@@ -27,6 +27,24 @@ struct Layout {
   int max_tiles;
 };
 
+// router logits: R x E floats, times the contraction splits of the router
+// GEMM when few rows leave the GPU idle (partials summed by the top-k kernel)
+constexpr size_t ROUTER_SPLIT_CAP = (size_t)1 << 21;   // floats of partials at most
+int router_split(const dg_config& c, int rows) {
+  const int nch = c.D * esize(c.act_dtype) / 128;   // packed pieces per router row
+  const size_t re = (size_t)rows * c.E;
+  int S = 1;
+  // aim at >= 256 blocks: (E/64 column chunks) x (rows/32 row tiles) x S
+  const long base = (long)((c.E + 63) / 64) * ((rows + 31) / 32);
+  while (S < ROUTER_MAX_SPLIT && base * S < 256 && nch % (2 * S) == 0 && nch / (2 * S) >= 4 &&
+         re * 2 * S <= ROUTER_SPLIT_CAP)
+    S *= 2;
+  return S;
+}
+size_t router_floats(const dg_config& c, int rows) {
+  return (size_t)rows * c.E * router_split(c, rows);
+}
+
 Layout layout(const dg_config& c, int rows) {
   Layout L{};
   const size_t a = esize(c.act_dtype);
@@ -46,7 +64,7 @@ Layout layout(const dg_config& c, int rows) {
   L.o = take(R * QD * a);
   L.x1 = take(R * c.D * a);
   L.u2 = take(R * c.D * a);
-  L.rl = take(R * c.E * 4);
+  L.rl = take(router_floats(c, (int)R) * 4);
   L.ids = take(slots * 4);
   L.gates = take(slots * 4);
   L.counts = take((size_t)c.E * 4);
@@ -181,10 +199,30 @@ void moe_block(const Ctx& c, int l, const float* gnext) {
   // the fused kernel works on 16-token tiles: worth it only with many tiles
   if (c.R < 2048 || !launch_route(act, ra, s)) {
     launch_rmsnorm(act, at<void>(c, c.L.x1), w.g2, c.R, cf.D, cf.eps, at<void>(c, c.L.u2), s);
-    if (!(t && t->inject_router))
-      dense_gemm(c, GEMM_F32, at<void>(c, c.L.u2), c.R, cf.D, w.wr, cf.E, nullptr, 0, nullptr, cf.E,
-                 at<void>(c, c.L.rl), cf.E, nullptr, nullptr);
-    launch_topk(rl, c.R, cf.E, cf.k, at<int32_t>(c, c.L.ids), at<float>(c, c.L.gates), s);
+    int S = 1;
+    if (!(t && t->inject_router)) {
+      if (c.R <= STREAM_MAX_ROWS) {
+        // weight streaming with contraction splits; top-k sums the partials
+        S = router_split(cf, c.R);
+        StreamGemm g{};
+        g.A = at<void>(c, c.L.u2);
+        g.M = c.R;
+        g.K = cf.D;
+        g.W0 = w.wr;
+        g.n1 = cf.E;
+        g.N = cf.E;
+        g.nchunks = (cf.E + 63) / 64;
+        g.ksplit = S;
+        g.out = at<void>(c, c.L.rl);
+        g.ldo = cf.E;
+        launch_stream_gemm(act, cf.act_dtype, SG_F32, 4, g, (c.R + STREAM_TILE - 1) / STREAM_TILE, s);
+      } else {
+        dense_gemm(c, GEMM_F32, at<void>(c, c.L.u2), c.R, cf.D, w.wr, cf.E, nullptr, 0, nullptr, cf.E,
+                   at<void>(c, c.L.rl), cf.E, nullptr, nullptr);
+      }
+    }
+    launch_topk(const_cast<float*>(rl), S, c.R, cf.E, cf.k, at<int32_t>(c, c.L.ids),
+                at<float>(c, c.L.gates), s);
   }
   if (t) {
     tap_copy(t->u2 ? (char*)t->u2 + l * R * D * a : nullptr, at<void>(c, c.L.u2), R * D * a, s);

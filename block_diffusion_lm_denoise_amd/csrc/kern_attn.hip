@@ -104,9 +104,7 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
     const int k = kk < kend ? kk : kbeg;
     return k >= fresh0 ? fresh + (size_t)(k - fresh0) * a.ldq : cache + (size_t)k * HD;
   };
-  // register copy of the next tile: K chunks and V 4-key groups (a native
-  // vector type: plain loads and stores, no struct copies through memory)
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  // register copy of the next tile: K chunks and V 4-key groups
   u32x4 rk[KCH], rv[VCH][4];
   auto gload = [&](int k0) {
 #pragma unroll

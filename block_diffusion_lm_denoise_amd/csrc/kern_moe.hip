@@ -15,59 +15,78 @@ namespace dg {
 
 // ---------------------------------------------------------------------------
 // top-k: one wave per token.  Experts are ranked by (logit descending, index
-// ascending); gates are the softmax of the k selected logits.
+// ascending).  That order is the order of one 64-bit key per expert (the
+// logit's bits mapped to an order-preserving unsigned integer, then the
+// complemented index), a strict total order, so the ranks are a permutation:
+// each lane counts, for its experts, the keys above theirs (all keys are read
+// back from LDS as broadcasts); the experts of rank < k are the selection, in
+// rank order.  Gates are the softmax of the k selected logits.  The logits
+// arrive as nsplit partial sums (contraction splits), added in split order.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bool better(float v, int i, float w, int j) {
-  return v > w || (v == w && i < j);
+  return (v > w) | ((v == w) & (i < j));   // bitwise: no short-circuit branches
 }
 
-__global__ __launch_bounds__(256) void topk_k(const float* __restrict__ logits, int rows, int E, int k,
-                                              int32_t* __restrict__ ids, float* __restrict__ gates) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+__device__ __forceinline__ uint64_t rank_key(float v, int e) {
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);   // order-preserving
+  return ((uint64_t)ord << 32) | (uint32_t)~e;
+}
+
+__global__ __launch_bounds__(64) void topk_k(float* __restrict__ logits, int nsplit, int rows, int E,
+                                             int k, int32_t* __restrict__ ids, float* __restrict__ gates) {
+  __shared__ __attribute__((aligned(16))) uint64_t sk[256];
+  __shared__ float selv[8];
+  __shared__ int seli[8];
+  const int lane = threadIdx.x;
+  const int row = blockIdx.x;
+  const size_t stride = (size_t)rows * E;
   float v[4];
-  bool taken[4];
+  uint64_t key[4];
 #pragma unroll
   for (int c = 0; c < 4; c++) {
     const int e = lane + 64 * c;
-    const float x = e < E ? logits[(size_t)row * E + e] : -INFINITY;
-    v[c] = x != x ? -INFINITY : x;  // a NaN logit ranks last (ids stay in range)
-    taken[c] = e >= E;
+    const size_t o = (size_t)row * E + (e < E ? e : 0);
+    // all partials in flight at once, then added in split order
+    float p[ROUTER_MAX_SPLIT];
+#pragma unroll
+    for (int sp = 0; sp < ROUTER_MAX_SPLIT; sp++) p[sp] = sp < nsplit ? logits[sp * stride + o] : 0.f;
+    float x = p[0];
+#pragma unroll
+    for (int sp = 1; sp < ROUTER_MAX_SPLIT; sp++) x = sp < nsplit ? x + p[sp] : x;
+    if (e < E && nsplit > 1) logits[o] = x;   // the logits routing used
+    x = e < E ? x : -INFINITY;
+    v[c] = x != x ? -INFINITY : x;  // a NaN logit ranks with -inf (ids stay in range)
+    key[c] = rank_key(v[c], e);
+    sk[e] = key[c];
   }
-  float sel_v[8];
-  int sel_i[8];
-  for (int j = 0; j < k; j++) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+  __syncthreads();
+  int rank[4] = {0, 0, 0, 0};
+  const int nc = (E + 63) / 64;   // lanes' experts actually present
+  // keys past E (set above) rank below every real key: counting them is harmless
+  for (int e0 = 0; e0 < E; e0 += 8) {
+    uint64_t kk[8];
 #pragma unroll
-    for (int c = 0; c < 4; c++)
-      if (!taken[c] && better(v[c], lane + 64 * c, bv, bi)) {
-        bv = v[c];
-        bi = lane + 64 * c;
-      }
+    for (int j = 0; j < 8; j++) kk[j] = sk[e0 + j];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
+    for (int j = 0; j < 8; j++)
+#pragma unroll
+      for (int c = 0; c < 4; c++) rank[c] += c < nc ? (int)(kk[j] > key[c]) : 0;
+  }
+#pragma unroll
+  for (int c = 0; c < 4; c++) {
+    const int e = lane + 64 * c;
+    if (e < E && rank[c] < k) {
+      selv[rank[c]] = v[c];
+      seli[rank[c]] = e;
     }
-    sel_v[j] = bv;
-    sel_i[j] = bi;
-#pragma unroll
-    for (int c = 0; c < 4; c++)
-      if (lane + 64 * c == bi) taken[c] = true;
   }
-  if (lane == 0) {
+  __syncthreads();
+  if (lane < k) {
     float den = 0.f;
-    for (int j = 0; j < k; j++) den += expf(sel_v[j] - sel_v[0]);
-    for (int j = 0; j < k; j++) {
-      ids[(size_t)row * k + j] = sel_i[j];
-      gates[(size_t)row * k + j] = expf(sel_v[j] - sel_v[0]) / den;
-    }
+    for (int j = 0; j < k; j++) den += expf(selv[j] - selv[0]);
+    ids[(size_t)row * k + lane] = seli[lane];
+    gates[(size_t)row * k + lane] = expf(selv[lane] - selv[0]) / den;
   }
 }
 
@@ -315,9 +334,9 @@ bool launch_route(int act, const RouteArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-void launch_topk(const float* logits, int rows, int E, int k, int32_t* ids, float* gates,
+void launch_topk(float* logits, int nsplit, int rows, int E, int k, int32_t* ids, float* gates,
                  hipStream_t s) {
-  topk_k<<<(rows + 3) / 4, 256, 0, s>>>(logits, rows, E, k, ids, gates);
+  topk_k<<<rows, 64, 0, s>>>(logits, nsplit, rows, E, k, ids, gates);
 }
 
 void launch_plan(const int32_t* ids, int rows, int k, int E, int tile_rows, int32_t* counts,

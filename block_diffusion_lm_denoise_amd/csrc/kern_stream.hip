@@ -42,7 +42,7 @@ template <> struct Piece<float, float> {
   static __device__ __forceinline__ int a_off(int j, int g) { return 16 * j + 4 * g; }
 };
 
-__device__ __forceinline__ void zero_unless(uint4& u, bool ok) {
+__device__ __forceinline__ void zero_unless(u32x4& u, bool ok) {
   u.x = ok ? u.x : 0u;
   u.y = ok ? u.y : 0u;
   u.z = ok ? u.z : 0u;
@@ -50,8 +50,8 @@ __device__ __forceinline__ void zero_unless(uint4& u, bool ok) {
 }
 
 // acc[rt][ct] += A[rt] . W[ct] over one piece, from raw 16-byte registers
-__device__ __forceinline__ void piece_mma(f32x4_t (&acc)[2][4], const uint4 (&wr)[4][2],
-                                          const uint4 (&ar)[2][2], uint16_t*, uint16_t*) {
+__device__ __forceinline__ void piece_mma(f32x4_t (&acc)[2][4], const u32x4 (&wr)[4][2],
+                                          const u32x4 (&ar)[2][2], uint16_t*, uint16_t*) {
 #pragma unroll
   for (int j = 0; j < 2; j++)
 #pragma unroll
@@ -64,13 +64,13 @@ __device__ __forceinline__ void piece_mma(f32x4_t (&acc)[2][4], const uint4 (&wr
         mma(acc[rt][ct], x, y);
       }
 }
-__device__ __forceinline__ void piece_mma(f32x4_t (&acc)[2][4], const uint4 (&wr)[4][2],
-                                          const uint4 (&ar)[2][4], uint16_t*, uint8_t*) {
+__device__ __forceinline__ void piece_mma(f32x4_t (&acc)[2][4], const u32x4 (&wr)[4][2],
+                                          const u32x4 (&ar)[2][4], uint16_t*, uint8_t*) {
 #pragma unroll
   for (int j = 0; j < 4; j++)
 #pragma unroll
     for (int ct = 0; ct < 4; ct++) {
-      const uint4 u = wr[ct][j >> 1];
+      const u32x4 u = wr[ct][j >> 1];
       FragBF y;
       y.v = __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8((j & 1) ? make_uint2(u.z, u.w) : make_uint2(u.x, u.y)));
 #pragma unroll
@@ -81,8 +81,8 @@ __device__ __forceinline__ void piece_mma(f32x4_t (&acc)[2][4], const uint4 (&wr
       }
     }
 }
-__device__ __forceinline__ void piece_mma(f32x4_t (&acc)[2][4], const uint4 (&wr)[4][2],
-                                          const uint4 (&ar)[2][2], float*, float*) {
+__device__ __forceinline__ void piece_mma(f32x4_t (&acc)[2][4], const u32x4 (&wr)[4][2],
+                                          const u32x4 (&ar)[2][2], float*, float*) {
 #pragma unroll
   for (int rt = 0; rt < 2; rt++)
 #pragma unroll
@@ -90,7 +90,7 @@ __device__ __forceinline__ void piece_mma(f32x4_t (&acc)[2][4], const uint4 (&wr
       FragF32 x, y;
 #pragma unroll
       for (int j = 0; j < 2; j++) {
-        const uint4 ua = ar[rt][j], uw = wr[ct][j];
+        const u32x4 ua = ar[rt][j], uw = wr[ct][j];
         x.v[4 * j + 0] = __uint_as_float(ua.x);
         x.v[4 * j + 1] = __uint_as_float(ua.y);
         x.v[4 * j + 2] = __uint_as_float(ua.z);
@@ -106,15 +106,21 @@ __device__ __forceinline__ void piece_mma(f32x4_t (&acc)[2][4], const uint4 (&wr
 
 // KW waves split the contraction; the 4/KW wave groups take different 64-row
 // weight column groups (a block covers 64 * 4/KW weight rows).
-template <typename TA, typename TW, int MODE, int KW>
-__global__ __launch_bounds__(256) void wstream_k(StreamGemm a) {
+template <typename TA, typename TW, int MODE, int KW, int NB>
+__global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
   typedef Piece<TA, TW> PC;
   constexpr int NA = PC::NA;
   constexpr int CWG = 4 / KW;          // column groups per block
   __shared__ float red[4][4][64][4];   // [wave][col tile][lane][i], one 16-row tile at a time
   constexpr bool GROUPED = MODE == SG_GATEUP || MODE == SG_DOWN;
   const int C = a.nchunks;
-  const int chunk = blockIdx.x % C, tile = blockIdx.x / C;
+  const int chunk = blockIdx.x % C;
+  int tile = blockIdx.x / C, split = 0;
+  if (MODE == SG_F32 && a.ksplit > 1) {   // block id = chunk + C * (tile + T * split)
+    const int T = (a.M + 31) / 32;
+    split = tile / T;
+    tile -= split * T;
+  }
   int e = 0, row0, nrows;
   if (GROUPED) {
     if (tile >= *a.ntiles) return;
@@ -131,7 +137,10 @@ __global__ __launch_bounds__(256) void wstream_k(StreamGemm a) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
   const int kw = w % KW, cg = w / KW;  // contraction share, column group of this wave
   const int K = a.K;
-  const int nch = K / PC::EP;          // pieces (packed column blocks) per weight row
+  const int nch_all = K / PC::EP;      // pieces (packed column blocks) per weight row
+  // contraction split: this block takes pieces [pbeg, pbeg + nch)
+  const int nsp = MODE == SG_F32 && a.ksplit > 1 ? a.ksplit : 1;
+  const int nch = nch_all / nsp, pbeg = split * nch;
 
   // A row pointers of this lane (row l16 of each 16-row tile).  Rows past the
   // tile read a valid row and are zeroed by a select, so the load path has no
@@ -147,7 +156,7 @@ __global__ __launch_bounds__(256) void wstream_k(StreamGemm a) {
     arow[rt] = (const TA*)a.A + src * K;
   }
   // packed weight tiles of this wave's 4 column tiles: byte address of row
-  // group rg, piece c, load h, this lane = base + (rg * nch + c) * 2048 + h * 1024 + 16 * lane
+  // group rg, piece c, load h, this lane = base + (rg * nch_all + c) * 2048 + h * 1024 + 16 * lane
   const char* wtile[4];
   bool wok[4];
   const int n0 = (chunk * CWG + cg) * 64;   // first weight row (dense/down) of this wave
@@ -171,7 +180,7 @@ __global__ __launch_bounds__(256) void wstream_k(StreamGemm a) {
       else if (nn < a.n1 + a.n2) { base = (const char*)a.W1; row = nn - a.n1; }
       else { base = (const char*)a.W2; row = nn - a.n1 - a.n2; }
     }
-    wtile[ct] = base + (row / 16) * nch * 2048 + 16 * lane;
+    wtile[ct] = base + (row / 16) * nch_all * 2048 + 16 * lane;
     wok[ct] = ok;   // per 16-row group: rows past N within a valid group are masked at the store
   }
 
@@ -181,21 +190,23 @@ __global__ __launch_bounds__(256) void wstream_k(StreamGemm a) {
 #pragma unroll
     for (int ct = 0; ct < 4; ct++) acc[rt][ct] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-  uint4 wa[4][2], aa[2][NA], wb[4][2], ab[2][NA];
-  auto load = [&](uint4(&wr)[4][2], uint4(&ar)[2][NA], int c) {
+  // NB register buffers of one piece each: the loads of NB-1 later pieces are
+  // in flight while a piece is multiplied
+  u32x4 wbuf[NB][4][2], abuf[NB][2][NA];
+  auto load = [&](u32x4(&wr)[4][2], u32x4(&ar)[2][NA], int c) {
 #pragma unroll
     for (int h = 0; h < 2; h++)
 #pragma unroll
       for (int ct = 0; ct < 4; ct++)
-        wr[ct][h] = *reinterpret_cast<const uint4*>(wtile[ct] + (size_t)c * 2048 + h * 1024);
+        wr[ct][h] = *reinterpret_cast<const u32x4*>(wtile[ct] + (size_t)c * 2048 + h * 1024);
 #pragma unroll
     for (int j = 0; j < NA; j++)
 #pragma unroll
       for (int rt = 0; rt < 2; rt++)
-        ar[rt][j] = *reinterpret_cast<const uint4*>(arow[rt] + c * PC::EP + PC::a_off(j, g));
+        ar[rt][j] = *reinterpret_cast<const u32x4*>(arow[rt] + c * PC::EP + PC::a_off(j, g));
   };
   // ok = false: the piece is past the contraction (clamped load), zero its A
-  auto comp = [&](uint4(&wr)[4][2], uint4(&ar)[2][NA], bool ok) {
+  auto comp = [&](u32x4(&wr)[4][2], u32x4(&ar)[2][NA], bool ok) {
 #pragma unroll
     for (int ct = 0; ct < 4; ct++)
 #pragma unroll
@@ -207,32 +218,31 @@ __global__ __launch_bounds__(256) void wstream_k(StreamGemm a) {
     piece_mma(acc, wr, ar, (TA*)nullptr, (TW*)nullptr);
   };
 
-  // wave takes pieces kw, kw+KW, ...; two register buffers, straight-line
-  // code (indices past the end are clamped and masked) so that the waits
-  // before each MFMA group cover only the older buffer's loads
+  // wave takes pieces kw, kw+KW, ...; indices past the end are clamped and
+  // masked so the code is straight-line and the waits before each MFMA group
+  // cover only that buffer's loads.  sched_barrier keeps each refill ahead of
+  // the next buffers' MFMAs (otherwise the scheduler sinks the loads).
   const int per = (nch + KW - 1) / KW;
-  const int npairs = (per + 1) / 2;
-  auto cidx = [&](int i) { const int c = kw + KW * i; return c < nch ? c : nch - 1; };
+  const int nper = (per + NB - 1) / NB * NB;
+  auto cidx = [&](int i) { const int c = kw + KW * i; return pbeg + (c < nch ? c : nch - 1); };
   auto cok = [&](int i) { return kw + KW * i < nch; };
-  // sched_barrier pins each buffer's loads ahead of the other buffer's MFMAs
-  // (otherwise the scheduler sinks them to save registers)
-  load(wa, aa, cidx(0));
-  int pi = 0;
-  for (; pi + 1 < npairs; pi++) {
-    load(wb, ab, cidx(2 * pi + 1));
-    __builtin_amdgcn_sched_barrier(0);
-    comp(wa, aa, cok(2 * pi));
-    __builtin_amdgcn_sched_barrier(0);
-    load(wa, aa, cidx(2 * pi + 2));
-    __builtin_amdgcn_sched_barrier(0);
-    comp(wb, ab, cok(2 * pi + 1));
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int b = 0; b < NB; b++) load(wbuf[b], abuf[b], cidx(b));
+  int ib = 0;
+  for (; ib + NB < nper; ib += NB) {
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+      __builtin_amdgcn_sched_barrier(0);
+      comp(wbuf[b], abuf[b], cok(ib + b));
+      __builtin_amdgcn_sched_barrier(0);
+      load(wbuf[b], abuf[b], cidx(ib + NB + b));
+    }
   }
-  load(wb, ab, cidx(2 * pi + 1));
-  __builtin_amdgcn_sched_barrier(0);
-  comp(wa, aa, cok(2 * pi));
-  __builtin_amdgcn_sched_barrier(0);
-  comp(wb, ab, cok(2 * pi + 1));
+#pragma unroll
+  for (int b = 0; b < NB; b++) {   // last group: nothing left to load
+    __builtin_amdgcn_sched_barrier(0);
+    comp(wbuf[b], abuf[b], cok(ib + b));
+  }
 
   // ---- reduce the four waves' partial tiles, one 16-row tile at a time ----
   float sg = 1.f, su = 1.f, sd = 1.f;
@@ -287,7 +297,7 @@ __global__ __launch_bounds__(256) void wstream_k(StreamGemm a) {
           if (MODE == SG_DOWN) {
             stx((TA*)a.out, o, val * sd);
           } else if (MODE == SG_F32) {
-            ((float*)a.out)[o] = val;
+            ((float*)a.out)[o + (size_t)split * a.M * a.ldo] = val;
           } else {
             if (MODE == SG_RESID) val += ldx((const TA*)a.R, o);
             stx((TA*)a.out, o, val);
@@ -309,22 +319,35 @@ __global__ __launch_bounds__(256) void wstream_k(StreamGemm a) {
   }
 }
 
+// register buffers (pieces in flight) per wave, chosen by measurement: bf16
+// gate/up, bf16 down and dense projections, fp8 experts
+#ifndef STREAM_NB_GATEUP
+#define STREAM_NB_GATEUP 4
+#endif
+#ifndef STREAM_NB
+#define STREAM_NB 2
+#endif
+#ifndef STREAM_NB_FP8
+#define STREAM_NB_FP8 2
+#endif
+
 template <int MODE, int KW>
 static void dispatch(int act, int wdt, const StreamGemm& a, int nblocks, hipStream_t s) {
   if (nblocks <= 0) return;
   if (act == ACT_F32)
-    wstream_k<float, float, MODE, KW><<<nblocks, 256, 0, s>>>(a);
+    wstream_k<float, float, MODE, KW, 2><<<nblocks, 256, 0, s>>>(a);
   else if (wdt == DG_FP8E4M3)
-    wstream_k<uint16_t, uint8_t, MODE, KW><<<nblocks, 256, 0, s>>>(a);
+    wstream_k<uint16_t, uint8_t, MODE, KW, STREAM_NB_FP8><<<nblocks, 256, 0, s>>>(a);
   else
-    wstream_k<uint16_t, uint16_t, MODE, KW><<<nblocks, 256, 0, s>>>(a);
+    wstream_k<uint16_t, uint16_t, MODE, KW, MODE == SG_GATEUP ? STREAM_NB_GATEUP : STREAM_NB>
+        <<<nblocks, 256, 0, s>>>(a);
 }
 
 // kw: waves splitting the contraction (4, or 2 when the block should cover 128
 // weight rows, e.g. a short contraction); a.nchunks counts blocks per row tile
 void launch_stream_gemm(int act, int wdt, int mode, int kw, const StreamGemm& a, int ntiles_max,
                         hipStream_t s) {
-  const int nb = a.nchunks * ntiles_max;
+  const int nb = a.nchunks * ntiles_max * (mode == SG_F32 && a.ksplit > 1 ? a.ksplit : 1);
   if (kw == 2) {
     switch (mode) {
       case SG_STORE: dispatch<SG_STORE, 2>(act, wdt, a, nb, s); break;

@@ -37,7 +37,10 @@ void launch_lm_merge(const float* pmax, const int32_t* pidx, const float* psum, 
                      int ntiles, int32_t* argmax, float* conf, hipStream_t s);
 
 // ---- MoE routing (kern_moe.hip) ----
-void launch_topk(const float* logits, int rows, int E, int k, int32_t* ids, float* gates,
+// logits: nsplit (<= ROUTER_MAX_SPLIT) partial [rows][E] arrays (consecutive);
+// with nsplit > 1 the summed logits are written back over the first one
+constexpr int ROUTER_MAX_SPLIT = 16;
+void launch_topk(float* logits, int nsplit, int rows, int E, int k, int32_t* ids, float* gates,
                  hipStream_t s);
 // fused RMSNorm + router logits + top-k (false if D does not fit the LDS tile)
 struct RouteArgs {
@@ -110,6 +113,8 @@ struct StreamGemm {
   const int4* tiles;      // grouped: (expert, first row, rows)
   const int32_t* ntiles;
   int nchunks;            // 64-weight-row chunks per row tile (gate/up: F/32)
+  int ksplit;             // SG_F32: contraction splits (0 or 1 = none); split s writes
+                          // its partial sums to out + s * M * ldo
   void* out;
   int ldo;
   const void* R;          // residual (SG_RESID)
