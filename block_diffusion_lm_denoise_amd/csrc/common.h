@@ -192,6 +192,27 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v + dpp_f<DPP_ROW_MIRROR>(v);
 }
 
+// max of a 64-bit value over the wave (every lane gets it): DPP within the
+// 16-lane rows, then the four row results read as scalars
+template <int CTRL> __device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const int lo = dpp_i<CTRL>((int)(uint32_t)v), hi = dpp_i<CTRL>((int)(uint32_t)(v >> 32));
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = umax64(v, dpp_u64<DPP_QUAD_1032>(v));
+  v = umax64(v, dpp_u64<DPP_QUAD_2301>(v));
+  v = umax64(v, dpp_u64<DPP_ROW_HALF_MIRROR>(v));
+  v = umax64(v, dpp_u64<DPP_ROW_MIRROR>(v));
+  return umax64(umax64(readlane_u64(v, 0), readlane_u64(v, 16)),
+                umax64(readlane_u64(v, 32), readlane_u64(v, 48)));
+}
+
 // deterministic block sum for blockDim.x == 256 (4 waves); red: >= 4 floats of LDS
 __device__ __forceinline__ float block_sum256(float v, float* red) {
   v = wave_sum(v);

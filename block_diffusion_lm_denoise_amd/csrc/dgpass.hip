@@ -18,6 +18,7 @@ constexpr int MIN_TILE = 32;      // smallest expert row tile (sizes the tile li
 constexpr int STREAM_TILE = 32;   // row tile of the weight-streaming kernels
 constexpr int FAT_TILE = 128;     // row tile of the LDS-tiled expert kernels
 constexpr int STREAM_MAX_ROWS = 1024;  // dense projections: weight streaming up to this many rows
+constexpr int ROUTE_MIN_ROWS = 2048;   // fused routing kernel from this many token rows
 
 struct Layout {
   size_t cov;       // [L][E] int32 expert counts of the last pass (offset 0)
@@ -196,8 +197,10 @@ void moe_block(const Ctx& c, int l, const float* gnext) {
                (t && t->inject_router) ? rl : nullptr, at<void>(c, c.L.u2),
                (t && t->router && !t->inject_router) ? at<float>(c, c.L.rl) : nullptr,
                at<int32_t>(c, c.L.ids), at<float>(c, c.L.gates)};
-  // the fused kernel works on 16-token tiles: worth it only with many tiles
-  if (c.R < 2048 || !launch_route(act, ra, s)) {
+  // fused RMSNorm + router + top-k on 16-token tiles (bf16): only with many
+  // tiles, since each tile is a serial chain (with few, the unfused kernels
+  // spread the work over more of the chip)
+  if (c.R < ROUTE_MIN_ROWS || !launch_route(act, ra, s)) {
     launch_rmsnorm(act, at<void>(c, c.L.x1), w.g2, c.R, cf.D, cf.eps, at<void>(c, c.L.u2), s);
     int S = 1;
     if (!(t && t->inject_router)) {

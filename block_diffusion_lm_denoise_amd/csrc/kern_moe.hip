@@ -17,32 +17,56 @@ namespace dg {
 // top-k: one wave per token.  Experts are ranked by (logit descending, index
 // ascending).  That order is the order of one 64-bit key per expert (the
 // logit's bits mapped to an order-preserving unsigned integer, then the
-// complemented index), a strict total order, so the ranks are a permutation:
-// each lane counts, for its experts, the keys above theirs (all keys are read
-// back from LDS as broadcasts); the experts of rank < k are the selection, in
-// rank order.  Gates are the softmax of the k selected logits.  The logits
-// arrive as nsplit partial sums (contraction splits), added in split order.
+// complemented index), so each of the k rounds takes the wave maximum of the
+// keys not yet selected (DPP reductions, no LDS round trips).  Gates are the
+// softmax of the k selected logits.  The logits may arrive as nsplit partial
+// sums (contraction splits), added in split order.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bool better(float v, int i, float w, int j) {
-  return (v > w) | ((v == w) & (i < j));   // bitwise: no short-circuit branches
-}
-
 __device__ __forceinline__ uint64_t rank_key(float v, int e) {
   const uint32_t b = __float_as_uint(v);
   const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);   // order-preserving
   return ((uint64_t)ord << 32) | (uint32_t)~e;
 }
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t ord = (uint32_t)(key >> 32);
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord);
+}
+
+// the k best of one token's logits v[c] (expert lane + 64 c, c < 4; experts past
+// E hold key 0, below every real key); writes ids/gates from lanes < k
+__device__ __forceinline__ void select_topk(const float (&v)[4], int E, int k, int32_t* ids, float* gates) {
+  const int lane = threadIdx.x & 63;
+  uint64_t key[4];
+#pragma unroll
+  for (int c = 0; c < 4; c++) key[c] = lane + 64 * c < E ? rank_key(v[c], lane + 64 * c) : 0;
+  float myv = 0.f;
+  int myi = 0;
+  for (int j = 0; j < k; j++) {
+    uint64_t best = umax64(umax64(key[0], key[1]), umax64(key[2], key[3]));
+    best = wave_max_u64(best);
+    const int e = (int)~(uint32_t)best;
+    if (lane == j) {
+      myv = key_value(best);
+      myi = e;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; c++) key[c] = lane + 64 * c == e ? 0 : key[c];
+  }
+  const float m0 = __shfl(myv, 0, 64);
+  float den = 0.f;
+  for (int j = 0; j < k; j++) den += expf(__shfl(myv, j, 64) - m0);
+  if (lane < k) {
+    ids[lane] = myi;
+    gates[lane] = expf(myv - m0) / den;
+  }
+}
 
 __global__ __launch_bounds__(64) void topk_k(float* __restrict__ logits, int nsplit, int rows, int E,
                                              int k, int32_t* __restrict__ ids, float* __restrict__ gates) {
-  __shared__ __attribute__((aligned(16))) uint64_t sk[256];
-  __shared__ float selv[8];
-  __shared__ int seli[8];
   const int lane = threadIdx.x;
   const int row = blockIdx.x;
   const size_t stride = (size_t)rows * E;
   float v[4];
-  uint64_t key[4];
 #pragma unroll
   for (int c = 0; c < 4; c++) {
     const int e = lane + 64 * c;
@@ -55,39 +79,9 @@ __global__ __launch_bounds__(64) void topk_k(float* __restrict__ logits, int nsp
 #pragma unroll
     for (int sp = 1; sp < ROUTER_MAX_SPLIT; sp++) x = sp < nsplit ? x + p[sp] : x;
     if (e < E && nsplit > 1) logits[o] = x;   // the logits routing used
-    x = e < E ? x : -INFINITY;
     v[c] = x != x ? -INFINITY : x;  // a NaN logit ranks with -inf (ids stay in range)
-    key[c] = rank_key(v[c], e);
-    sk[e] = key[c];
   }
-  __syncthreads();
-  int rank[4] = {0, 0, 0, 0};
-  const int nc = (E + 63) / 64;   // lanes' experts actually present
-  // keys past E (set above) rank below every real key: counting them is harmless
-  for (int e0 = 0; e0 < E; e0 += 8) {
-    uint64_t kk[8];
-#pragma unroll
-    for (int j = 0; j < 8; j++) kk[j] = sk[e0 + j];
-#pragma unroll
-    for (int j = 0; j < 8; j++)
-#pragma unroll
-      for (int c = 0; c < 4; c++) rank[c] += c < nc ? (int)(kk[j] > key[c]) : 0;
-  }
-#pragma unroll
-  for (int c = 0; c < 4; c++) {
-    const int e = lane + 64 * c;
-    if (e < E && rank[c] < k) {
-      selv[rank[c]] = v[c];
-      seli[rank[c]] = e;
-    }
-  }
-  __syncthreads();
-  if (lane < k) {
-    float den = 0.f;
-    for (int j = 0; j < k; j++) den += expf(selv[j] - selv[0]);
-    ids[(size_t)row * k + lane] = seli[lane];
-    gates[(size_t)row * k + lane] = expf(selv[lane] - selv[0]) / den;
-  }
+  select_topk(v, E, k, ids + (size_t)row * k, gates + (size_t)row * k);
 }
 
 // ---------------------------------------------------------------------------
@@ -165,47 +159,53 @@ __global__ __launch_bounds__(256) void plan_k(const int32_t* __restrict__ ids, i
 
 
 // ---------------------------------------------------------------------------
-// route_k: RMSNorm of x1, router logits and top-k in one kernel for a tile of
-// 16 tokens.  The normalised rows stay in LDS as the A operand of the router
-// MFMAs (waves split the experts in 16-column tiles, packed W_r fragments
-// come from L2); the logits go to LDS and each wave then ranks 4 of the tokens.
+// route_k (bf16): RMSNorm of x1, router logits and top-k in one kernel for a
+// tile of 16 tokens.  The normalised rows (rounded to bf16, also written out
+// as u2) stay in LDS as the A operand of the router MFMAs; the waves split the
+// experts in 16-column tiles (NT tiles each) and stream the packed W_r pieces
+// through an NB-deep register ring; the logits go to LDS and each wave ranks 4
+// of the tokens with the selection of topk_k.
 // ---------------------------------------------------------------------------
-template <typename TA>
+template <int NT, int NB>
 __global__ __launch_bounds__(256) void route_k(RouteArgs a) {
-  typedef typename FragOf<TA>::type Frag;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   const int D = a.D, E = a.E;
-  const int LDA = D + 16 / (int)sizeof(TA);            // padded A row (elements)
-  TA* sa = reinterpret_cast<TA*>(smem_raw);             // [16][LDA]
-  float* sl = reinterpret_cast<float*>(smem_raw + (size_t)16 * LDA * sizeof(TA));  // [16][E]
+  const int LDA = D + 8;                                          // padded A row (elements)
+  uint16_t* sa = reinterpret_cast<uint16_t*>(smem_raw);          // [16][LDA]
+  float* sl = reinterpret_cast<float*>(smem_raw + (size_t)16 * LDA * 2);   // [16][E]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
   const int row0 = blockIdx.x * 16;
   const int nrows = min(16, a.rows - row0);
 
-  // ---- RMSNorm: wave w normalises rows w, w+4, w+8, w+12 ----
+  // ---- RMSNorm (same arithmetic as rmsnorm_k): wave w takes rows w, w+4, .. ----
   for (int rr = w; rr < 16; rr += 4) {
-    TA* dst = sa + rr * LDA;
+    uint16_t* dst = sa + rr * LDA;
     if (rr >= nrows) {
-      for (int d = lane; d < D; d += 64) dst[d] = 0;
+      for (int d = lane * 8; d < D; d += 512) *reinterpret_cast<uint4*>(dst + d) = make_uint4(0, 0, 0, 0);
       continue;
     }
-    const TA* src = (const TA*)a.x1 + (size_t)(row0 + rr) * D;
+    const uint16_t* src = (const uint16_t*)a.x1 + (size_t)(row0 + rr) * D;
     float ss = 0.f;
-    for (int d = lane; d < D; d += 64) {
-      const float v = ldx(src, d);
-      ss += v * v;
+    for (int d = lane * 8; d < D; d += 512) {
+      float v[8];
+      ld8(src + d, v);
+#pragma unroll
+      for (int i = 0; i < 8; i++) ss += v[i] * v[i];
     }
     ss = wave_sum(ss);
     const float r = rsqrtf(ss / (float)D + a.eps);
-    for (int d = lane; d < D; d += 64) {
-      const float v = ldx(src, d) * r * a.g2[d];
-      stx(dst, d, v);
-      stx((TA*)a.u2, (size_t)(row0 + rr) * D + d, v);
+    for (int d = lane * 8; d < D; d += 512) {
+      float v[8];
+      ld8(src + d, v);
+#pragma unroll
+      for (int i = 0; i < 8; i++) v[i] = v[i] * r * a.g2[d + i];
+      st8(dst + d, v);
+      st8((uint16_t*)a.u2 + (size_t)(row0 + rr) * D + d, v);
     }
   }
   __syncthreads();
 
-  // ---- router logits: column tiles of 16 experts split over the waves ----
+  // ---- router logits ----
   if (a.inject) {
     for (int i = threadIdx.x; i < 16 * E; i += 256) {
       const int rr = i / E, e = i % E;
@@ -213,123 +213,113 @@ __global__ __launch_bounds__(256) void route_k(RouteArgs a) {
     }
   } else {
     const int nct = (E + 15) / 16;
-    const int nkb = D * (int)sizeof(TA) / 128;   // packed pieces per router row
-    for (int ct = w; ct < nct; ct += 4) {
-      const int e = ct * 16 + l16;
-      // packed W_r: row group ct (rows past E are zero), this lane's 16 bytes
-      const char* wg = (const char*)a.wr + (size_t)ct * nkb * 2048 + 16 * lane;
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < D; k0 += 128) {   // D is a multiple of 128
-        Frag af[4], bf[4];
+    const int nkb = D / 64;   // packed pieces (128 bytes of bf16) per router row
+    const char* wg[NT];
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-          if constexpr (sizeof(TA) == 2) {
-            // piece of 64 elements; half u&1 holds elements 32(u&1) + 8g of it
-            const int piece = k0 / 64 + (u >> 1);
-            load_frag(af[u], sa + l16 * LDA + k0 + 32 * u + 8 * g);
-            bf[u].v = __builtin_bit_cast(bf16x8_t,
-                                         *reinterpret_cast<const uint4*>(wg + (size_t)piece * 2048 + (u & 1) * 1024));
-          } else {
-            // piece of 32 floats; lane g holds floats 4g.. and 16+4g.. of it
-            const int piece = k0 / 32 + u;
-            const float* ar = reinterpret_cast<const float*>(sa) + l16 * LDA + k0 + 32 * u + 4 * g;
-            const float4 a0 = *reinterpret_cast<const float4*>(ar);
-            const float4 a1 = *reinterpret_cast<const float4*>(ar + 16);
-            const float4 w0 = *reinterpret_cast<const float4*>(wg + (size_t)piece * 2048);
-            const float4 w1 = *reinterpret_cast<const float4*>(wg + (size_t)piece * 2048 + 1024);
-            float* fa = reinterpret_cast<float*>(&af[u]);
-            float* fb = reinterpret_cast<float*>(&bf[u]);
-            fa[0] = a0.x; fa[1] = a0.y; fa[2] = a0.z; fa[3] = a0.w;
-            fa[4] = a1.x; fa[5] = a1.y; fa[6] = a1.z; fa[7] = a1.w;
-            fb[0] = w0.x; fb[1] = w0.y; fb[2] = w0.z; fb[3] = w0.w;
-            fb[4] = w1.x; fb[5] = w1.y; fb[6] = w1.z; fb[7] = w1.w;
-          }
+    for (int t = 0; t < NT; t++) {
+      const int ct = w + 4 * t;
+      wg[t] = (const char*)a.wr + (size_t)(ct < nct ? ct : 0) * nkb * 2048 + 16 * lane;
+    }
+    f32x4_t acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++) acc[t] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    u32x4 wv[NB][NT][2];
+    auto load = [&](int b, int c) {
+#pragma unroll
+      for (int t = 0; t < NT; t++)
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+          wv[b][t][h] = *reinterpret_cast<const u32x4*>(wg[t] + (size_t)c * 2048 + h * 1024);
+    };
+    auto comp = [&](int b, int c) {
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        FragBF af;
+        load_frag(af, sa + l16 * LDA + c * 64 + 32 * h + 8 * g);
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+          FragBF bf;
+          bf.v = __builtin_bit_cast(bf16x8_t, wv[b][t][h]);
+          mma(acc[t], af, bf);
         }
-#pragma unroll
-        for (int u = 0; u < 4; u++) mma(acc, af[u], bf[u]);
       }
+    };
+#pragma unroll
+    for (int b = 0; b < NB; b++) load(b, b);
+    int c0 = 0;
+    for (; c0 + NB < nkb; c0 += NB) {   // nkb is a multiple of NB
+#pragma unroll
+      for (int b = 0; b < NB; b++) {
+        __builtin_amdgcn_sched_barrier(0);
+        comp(b, c0 + b);
+        __builtin_amdgcn_sched_barrier(0);
+        load(b, c0 + NB + b);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+      __builtin_amdgcn_sched_barrier(0);
+      comp(b, c0 + b);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+      const int e = (w + 4 * t) * 16 + l16;
 #pragma unroll
       for (int i = 0; i < 4; i++)
-        if (e < E) sl[(4 * g + i) * E + e] = acc[i];
+        if (w + 4 * t < nct && e < E) sl[(4 * g + i) * E + e] = acc[t][i];
     }
   }
   __syncthreads();
   if (a.logits)
-    for (int i = threadIdx.x; i < nrows * E; i += 256)
-      a.logits[(size_t)row0 * E + i] = sl[i];
+    for (int i = threadIdx.x; i < nrows * E; i += 256) a.logits[(size_t)row0 * E + i] = sl[i];
 
-  // ---- top-k: wave w ranks rows w, w+4, w+8, w+12 ----
+  // ---- top-k: wave w ranks rows w, w+4, w+8, w+12 (same selection as topk_k) ----
   for (int rr = w; rr < nrows; rr += 4) {
     float v[4];
-    bool taken[4];
 #pragma unroll
     for (int c = 0; c < 4; c++) {
       const int e = lane + 64 * c;
       const float x = e < E ? sl[rr * E + e] : -INFINITY;
       v[c] = x != x ? -INFINITY : x;
-      taken[c] = e >= E;
     }
-    float sel_v[8];
-    int sel_i[8];
-    for (int j = 0; j < a.k; j++) {
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-#pragma unroll
-      for (int c = 0; c < 4; c++)
-        if (!taken[c] && better(v[c], lane + 64 * c, bv, bi)) {
-          bv = v[c];
-          bi = lane + 64 * c;
-        }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
-        const int oi = __shfl_xor(bi, o, 64);
-        if (better(ov, oi, bv, bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      sel_v[j] = bv;
-      sel_i[j] = bi;
-#pragma unroll
-      for (int c = 0; c < 4; c++)
-        if (lane + 64 * c == bi) taken[c] = true;
-    }
-    if (lane == 0) {
-      float den = 0.f;
-      for (int j = 0; j < a.k; j++) den += expf(sel_v[j] - sel_v[0]);
-      const size_t row = (size_t)(row0 + rr);
-      for (int j = 0; j < a.k; j++) {
-        a.ids[row * a.k + j] = sel_i[j];
-        a.gates[row * a.k + j] = expf(sel_v[j] - sel_v[0]) / den;
-      }
-    }
+    select_topk(v, E, a.k, a.ids + (size_t)(row0 + rr) * a.k, a.gates + (size_t)(row0 + rr) * a.k);
   }
 }
 
-size_t route_smem_bytes(int act, int D, int E) {
-  const size_t esz = act == ACT_BF16 ? 2 : 4;
-  return (size_t)16 * (D + 16 / esz) * esz + (size_t)16 * E * 4;
+size_t route_smem_bytes(int D, int E) {
+  return (size_t)16 * (D + 8) * 2 + (size_t)16 * E * 4;
 }
 
+template <int NT>
+static void launch_route_nt(const RouteArgs& a, size_t smem, hipStream_t s) {
+  const int blocks = (a.rows + 15) / 16;
+  const int nkb = a.D / 64;
+  if (nkb % 8 == 0) route_k<NT, 8><<<blocks, 256, smem, s>>>(a);
+  else if (nkb % 4 == 0) route_k<NT, 4><<<blocks, 256, smem, s>>>(a);
+  else route_k<NT, 2><<<blocks, 256, smem, s>>>(a);
+}
+
+// bf16 activations only; false when the tile does not fit in LDS
 bool launch_route(int act, const RouteArgs& a, hipStream_t s) {
-  constexpr size_t kMaxSmem = 96 * 1024;
-  const size_t smem = route_smem_bytes(act, a.D, a.E);
+  if (act != ACT_BF16) return false;
+  constexpr size_t kMaxSmem = 160 * 1024;
+  const size_t smem = route_smem_bytes(a.D, a.E);
   if (smem > kMaxSmem) return false;
   // allow more than the default 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU)
   static const bool attr_set = [] {
-    hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_k<uint16_t>),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxSmem);
-    hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(&route_k<float>),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxSmem);
-    return e1 == hipSuccess && e2 == hipSuccess;
+    bool ok = true;
+    const void* fns[] = {(const void*)&route_k<1, 2>, (const void*)&route_k<1, 4>, (const void*)&route_k<1, 8>,
+                         (const void*)&route_k<2, 2>, (const void*)&route_k<2, 4>, (const void*)&route_k<2, 8>,
+                         (const void*)&route_k<4, 2>, (const void*)&route_k<4, 4>, (const void*)&route_k<4, 8>};
+    for (const void* f : fns)
+      ok = ok && hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxSmem) == hipSuccess;
+    return ok;
   }();
   if (!attr_set && smem > 64 * 1024) return false;
-  const int blocks = (a.rows + 15) / 16;
-  if (act == ACT_BF16)
-    route_k<uint16_t><<<blocks, 256, smem, s>>>(a);
-  else
-    route_k<float><<<blocks, 256, smem, s>>>(a);
+  const int nct = (a.E + 15) / 16;
+  if (nct <= 4) launch_route_nt<1>(a, smem, s);
+  else if (nct <= 8) launch_route_nt<2>(a, smem, s);
+  else launch_route_nt<4>(a, smem, s);
   return true;
 }
 
