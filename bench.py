@@ -23,9 +23,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 
+GATEUP_KERNEL = "dg::wstream_k<bf16, bf16, 4, 4, 4>"   # SG_GATEUP, 4 waves split K, 4 buffers
+
+
 def _gateup_source_hash():
+    """Hash of the sources the gate/up kernel is built from (the counter
+    summary is only used if it was taken on this code)."""
     h = hashlib.sha256()
-    for f in ("kern_moe.hip", "common.h"):
+    for f in ("kern_stream.hip", "common.h", "launch.h"):
         with open(os.path.join(ROOT, "block_diffusion_lm_denoise_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -163,7 +168,7 @@ def main():
                    "layers": cfg.L, "d_model": cfg.D, "experts": cfg.E, "top_k": cfg.k,
                    "expert_ffn": cfg.F, "vocab": cfg.V, "expert_dtype": cfg.expert,
                    "step": "init noise + 8 x (pass, coverage, re-noise) + append prefill"},
-        "roofline": {"kernel": "moe gate/up grouped GEMM (moe_stream_k)", "bound": "hbm",
+        "roofline": {"kernel": "moe gate/up grouped GEMM (" + GATEUP_KERNEL + ")", "bound": "hbm",
                      "achieved": achieved / 1e9, "peak": roofline.HBM_BYTES_PER_S / 1e9,
                      "unit": "GB/s", "frac": achieved / roofline.HBM_BYTES_PER_S,
                      "traffic": traffic, "alg_bytes_per_launch": gu_bytes,
@@ -175,12 +180,18 @@ def main():
     }
 
     if args.copy_probe:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        # counter calibration: a device copy of 4 GiB (16x the last-level
+        # cache, so its reads come from HBM) with known read and write bytes
+        n = 4 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
+        src.fill_(1)
+        dst.fill_(2)
         torch.cuda.synchronize()
-        out["copy_probe_bytes"] = 1 << 30
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_probe_bytes"] = n
+        del src, dst
 
     if not args.no_cpu_baseline:
         import oracle
