@@ -173,11 +173,12 @@ template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
 }
 constexpr int DPP_QUAD_1032 = 0xB1, DPP_QUAD_2301 = 0x4E, DPP_ROW_HALF_MIRROR = 0x141,
               DPP_ROW_MIRROR = 0x140;
+__device__ __forceinline__ float fmax_sel(float a, float b) { return b > a ? b : a; }   // no NaN canonicalising
 __device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp_f<DPP_QUAD_1032>(v));
-  v = fmaxf(v, dpp_f<DPP_QUAD_2301>(v));
-  v = fmaxf(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
-  return fmaxf(v, dpp_f<DPP_ROW_MIRROR>(v));
+  v = fmax_sel(v, dpp_f<DPP_QUAD_1032>(v));
+  v = fmax_sel(v, dpp_f<DPP_QUAD_2301>(v));
+  v = fmax_sel(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
+  return fmax_sel(v, dpp_f<DPP_ROW_MIRROR>(v));
 }
 __device__ __forceinline__ int row16_min(int v) {
   v = min(v, dpp_i<DPP_QUAD_1032>(v));

@@ -44,6 +44,7 @@ struct AttnArgs {
   float* po;      // [nsplit][rows*Hq][hd]
   float* pml;     // [nsplit][rows*Hq][2]
   int rows;       // B*T
+  int nqt, groups;   // query tiles; (request, kv head, split) groups
 };
 
 template <typename TA, int HD>
@@ -61,7 +62,14 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) TA ks[KT * KLD];
   __shared__ __attribute__((aligned(16))) TA vt[HD * VLD];
 
-  const int qt = blockIdx.x, b = blockIdx.y / a.Hkv, gh = blockIdx.y % a.Hkv, split = blockIdx.z;
+  // 1-D grid: the query tiles that share one (request, kv head, key split)
+  // -- and so read the same K/V -- have ids 8 apart and run on one XCD,
+  // whose L2 then serves the K/V tiles after the first read
+  const int id = blockIdx.x, nqt = a.nqt;
+  const int g = (id / (8 * nqt)) * 8 + id % 8, qt = (id % (8 * nqt)) / 8;
+  if (g >= a.groups) return;
+  const int bh = g / a.nsplit, split = g % a.nsplit;
+  const int b = bh / a.Hkv, gh = bh % a.Hkv;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, l16 = lane & 15, g4 = lane >> 4;
   const int P = a.len.v[b];
 
@@ -327,6 +335,15 @@ __global__ __launch_bounds__(256) void attn_merge_k(const float* __restrict__ po
 }
 
 // ---------------------------------------------------------------------------
+// key splits: enough blocks to fill the chip several times over (each block
+// is a short latency chain), at least ATTN_MIN_SPLIT_KEYS keys per split
+#ifndef ATTN_TARGET_BLOCKS
+#define ATTN_TARGET_BLOCKS 512
+#endif
+#ifndef ATTN_MIN_SPLIT_KEYS
+#define ATTN_MIN_SPLIT_KEYS 128
+#endif
+
 long attn_partial_entries(int rows, int Hq) {
   // bounded split buffer: at most 2^18 (row, head) entries across all splits
   long full = (long)rows * Hq * 16;
@@ -360,9 +377,9 @@ void launch_attention(const AttnArgsHost& h, hipStream_t s) {
   const int nqt = (h.T + a.QT - 1) / a.QT;
   const long base = (long)nqt * h.B * h.Hkv;
   int nsplit = 1;
-  if (base < 512) {
-    nsplit = (int)((512 + base - 1) / base);
-    const int by_keys = (maxkeys + 127) / 128;
+  if (base < ATTN_TARGET_BLOCKS) {
+    nsplit = (int)((ATTN_TARGET_BLOCKS + base - 1) / base);
+    const int by_keys = (maxkeys + ATTN_MIN_SPLIT_KEYS - 1) / ATTN_MIN_SPLIT_KEYS;
     if (nsplit > by_keys) nsplit = by_keys;
     const long entries = (long)a.rows * h.Hq;
     while (nsplit > 1 && entries * nsplit > h.part_cap) nsplit--;
@@ -375,7 +392,9 @@ void launch_attention(const AttnArgsHost& h, hipStream_t s) {
   a.split_len = split_len;
   a.nsplit = nsplit;
 
-  dim3 grid(nqt, h.B * h.Hkv, nsplit);
+  a.nqt = nqt;
+  a.groups = h.B * h.Hkv * nsplit;
+  const dim3 grid((unsigned)(((a.groups + 7) / 8) * 8 * nqt));
   if (h.act == ACT_BF16) {
     if (h.hd == 128) attn_k<uint16_t, 128><<<grid, 256, 0, s>>>(a);
     else attn_k<uint16_t, 64><<<grid, 256, 0, s>>>(a);

@@ -477,14 +477,18 @@ __device__ __forceinline__ void mrg_bf(float& m, int& i, float& s, float m2, int
   i = id;
 }
 
-template <int P>
-__global__ __launch_bounds__(256, 1) void lmhead_direct_k(HeadArgs a) {
-  constexpr int BM = 128, BN = 256, BK = 64, LDK = 72, RT = 8, CT = 4;
+template <int P, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void lmhead_direct_k(HeadArgs a) {
+  constexpr int NT = NW * 64;                 // threads
+  constexpr int BM = 128, BN = 256, BK = 64, LDK = 72, RT = 8;
+  constexpr int WC = BN / NW, CT = WC / 16;   // vocabulary columns per wave
+  constexpr int A_LD = BM * BK * 2 / 16 / NT;   // 16-byte A chunks staged per thread
+  constexpr int A_RSTEP = NT / 8;             // rows between a thread's chunks
   // three LDS buffers: while tile kt is consumed, tile kt+1 is readable (its
   // first fragments are prefetched) and tile kt+2 is being written
   __shared__ __attribute__((aligned(16))) uint16_t sA[3][BM * LDK];
-  __shared__ float xm[4][BM], xs[4][BM];
-  __shared__ int xi[4][BM];
+  __shared__ float xm[NW][BM], xs[NW][BM];
+  __shared__ int xi[NW][BM];
   const int b8 = blockIdx.x >> 3, mtiles = a.mtiles;
   const int nt = (b8 / mtiles) * 8 + (blockIdx.x & 7), mt = b8 % mtiles;
   if (nt >= a.ntiles) return;
@@ -494,11 +498,11 @@ __global__ __launch_bounds__(256, 1) void lmhead_direct_k(HeadArgs a) {
   const uint16_t* W = (const uint16_t*)a.B;
   const int K = a.K, nk = K / BK, nkp = (nk + P - 1) / P * P;
 
-  const uint16_t* ap[4];
-  bool aok[4];
+  const uint16_t* ap[A_LD];
+  bool aok[A_LD];
 #pragma unroll
-  for (int p = 0; p < 4; p++) {
-    const int r = m0 + (t >> 3) + 32 * p;
+  for (int p = 0; p < A_LD; p++) {
+    const int r = m0 + (t >> 3) + A_RSTEP * p;
     aok[p] = r < a.M;
     ap[p] = A + (size_t)(aok[p] ? r : 0) * K + (t & 7) * 8;
   }
@@ -506,7 +510,7 @@ __global__ __launch_bounds__(256, 1) void lmhead_direct_k(HeadArgs a) {
   const char* bp[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ct++) {
-    const int n = n0 + 64 * w + 16 * ct;
+    const int n = n0 + WC * w + 16 * ct;
     bp[ct] = packed_group(W, n < a.V ? n : 0, nk) + 16 * lane;   // groups past V: masked in the epilogue
   }
 
@@ -516,12 +520,12 @@ __global__ __launch_bounds__(256, 1) void lmhead_direct_k(HeadArgs a) {
 #pragma unroll
     for (int ct = 0; ct < CT; ct++) acc[rt][ct] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
-  uint4 ra[P][4];
+  uint4 ra[P][A_LD];
   FragBF rb[P][2][CT];
   auto gload = [&](int st, int kt) {
     const int k0 = (kt < nk ? kt : nk - 1) * BK;   // clamped: always issued
 #pragma unroll
-    for (int p = 0; p < 4; p++) ra[st][p] = *reinterpret_cast<const uint4*>(ap[p] + k0);
+    for (int p = 0; p < A_LD; p++) ra[st][p] = *reinterpret_cast<const uint4*>(ap[p] + k0);
 #pragma unroll
     for (int ks = 0; ks < 2; ks++)
 #pragma unroll
@@ -531,14 +535,14 @@ __global__ __launch_bounds__(256, 1) void lmhead_direct_k(HeadArgs a) {
   // tiles past the end are stored as zeros, so their MFMAs add nothing
   auto astore = [&](int st, int buf, bool ok) {
 #pragma unroll
-    for (int p = 0; p < 4; p++) {
+    for (int p = 0; p < A_LD; p++) {
       uint4 u = ra[st][p];
       const bool z = aok[p] && ok;
       u.x = z ? u.x : 0u;
       u.y = z ? u.y : 0u;
       u.z = z ? u.z : 0u;
       u.w = z ? u.w : 0u;
-      *reinterpret_cast<uint4*>(&sA[buf][((t >> 3) + 32 * p) * LDK + (t & 7) * 8]) = u;
+      *reinterpret_cast<uint4*>(&sA[buf][((t >> 3) + A_RSTEP * p) * LDK + (t & 7) * 8]) = u;
     }
   };
   FragBF af[2][RT];
@@ -550,7 +554,7 @@ __global__ __launch_bounds__(256, 1) void lmhead_direct_k(HeadArgs a) {
 #pragma unroll
     for (int rt = 0; rt < RT; rt++)
 #pragma unroll
-      for (int ct = 0; ct < CT; ct++) mma(acc[rt][ct], af[ks][rt], rb[st][ks][ct]);
+      for (int ct = 0; ct < CT; ct++) mma(acc[rt][ct], rb[st][ks][ct], af[ks][rt]);   // logits^T
   };
 
 #pragma unroll
@@ -581,53 +585,67 @@ __global__ __launch_bounds__(256, 1) void lmhead_direct_k(HeadArgs a) {
     }
   }
 
-  if (a.logits) {   // debug tap: raw logits
+  // acc[rt][ct] is the transposed tile: lane (l16, g) holds vocabulary rows
+  // n0 + WC w + 16ct + 4g + i (i = 0..3) of token m0 + 16rt + l16, so a
+  // token's WC columns of this wave sit in 4 CT registers of 4 lanes (g = 0..3)
+  if (a.logits) {   // debug tap: raw logits, 4 consecutive columns per store
 #pragma unroll
     for (int rt = 0; rt < RT; rt++)
 #pragma unroll
-      for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int ct = 0; ct < CT; ct++) {
-          const int r = m0 + 16 * rt + 4 * g + i, n = n0 + 64 * w + 16 * ct + l16;
-          if (r < a.M && n < a.V) a.logits[(size_t)r * a.V + n] = acc[rt][ct][i];
-        }
-  }
-  // epilogue: per row, (max, lowest argmax, sum exp) over this wave's 64
-  // columns: a lane folds its 4 columns, then DPP reductions over the 16
-  // lanes that share the row
-#pragma unroll
-  for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int rl = 16 * rt + 4 * g + i;
-      float v[CT];
-      float lm = -INFINITY;
-      int li = 0x7fffffff;
-#pragma unroll
       for (int ct = 0; ct < CT; ct++) {
-        const int n = n0 + 64 * w + 16 * ct + l16;
-        v[ct] = n < a.V ? acc[rt][ct][i] : -INFINITY;
-        li = v[ct] > lm ? n : li;   // columns ascend with ct: the lowest index wins ties
-        lm = fmaxf(lm, v[ct]);
-      }
-      const float m = row16_max(lm);
-      const int idx = row16_min(lm == m ? li : 0x7fffffff);
-      float s = 0.f;
+        const int r = m0 + 16 * rt + l16, n = n0 + WC * w + 16 * ct + 4 * g;
+        if (r < a.M)
 #pragma unroll
-      for (int ct = 0; ct < CT; ct++) s += m == -INFINITY ? 0.f : __expf(v[ct] - m);
-      s = row16_sum(s);
-      if (l16 == 0) {
-        xm[w][rl] = m;
-        xs[w][rl] = s;
-        xi[w][rl] = idx;
+          for (int i = 0; i < 4; i++)
+            if (n + i < a.V) a.logits[(size_t)r * a.V + n + i] = acc[rt][ct][i];
       }
+  }
+  // epilogue: per token, (max, lowest argmax, sum exp) over this wave's WC
+  // columns: 4 CT in-lane values, then two exchanges between the 4 lanes
+#pragma unroll
+  for (int rt = 0; rt < RT; rt++) {
+    float lm = -INFINITY;
+    int li = 0x7fffffff;
+#pragma unroll
+    for (int ct = 0; ct < CT; ct++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {   // columns ascend: the first maximum is the lowest index
+        const int n = n0 + WC * w + 16 * ct + 4 * g + i;
+        const float v = n < a.V ? acc[rt][ct][i] : -INFINITY;
+        li = v > lm ? n : li;
+        lm = v > lm ? v : lm;
+      }
+    float m = lm;
+    m = fmax_sel(m, __shfl_xor(m, 16, 64));
+    m = fmax_sel(m, __shfl_xor(m, 32, 64));
+    int idx = lm == m ? li : 0x7fffffff;
+    idx = min(idx, __shfl_xor(idx, 16, 64));
+    idx = min(idx, __shfl_xor(idx, 32, 64));
+    float s = 0.f;
+#pragma unroll
+    for (int ct = 0; ct < CT; ct++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int n = n0 + WC * w + 16 * ct + 4 * g + i;
+        const float e = __builtin_amdgcn_exp2f((acc[rt][ct][i] - m) * 1.4426950408889634f);
+        s += n < a.V ? e : 0.f;
+      }
+    s = m == -INFINITY ? 0.f : s;
+    s += __shfl_xor(s, 16, 64);
+    s += __shfl_xor(s, 32, 64);
+    if (g == 0) {
+      const int rl = 16 * rt + l16;
+      xm[w][rl] = m;
+      xs[w][rl] = s;
+      xi[w][rl] = idx;
     }
+  }
   __syncthreads();
   if (t < BM && m0 + t < a.M) {
     float m = xm[0][t], s = xs[0][t];
     int idx = xi[0][t];
 #pragma unroll
-    for (int q = 1; q < 4; q++) mrg_bf(m, idx, s, xm[q][t], xi[q][t], xs[q][t]);
+    for (int q = 1; q < NW; q++) mrg_bf(m, idx, s, xm[q][t], xi[q][t], xs[q][t]);
     const size_t o = (size_t)(m0 + t) * a.ntiles + nt;
     a.pmax[o] = m;
     a.pidx[o] = idx;
@@ -671,9 +689,12 @@ void launch_down_lds(int act, const void* H, const MoeW& w, const int4* tiles,
   else down_lds_k<uint16_t, uint16_t, 128, 128><<<grid, 256, 0, s>>>(a);
 }
 
-// contraction tiles in flight in the bf16 LM head
+// contraction tiles in flight in the bf16 LM head, and its waves per block
 #ifndef LMHEAD_P
-#define LMHEAD_P 3
+#define LMHEAD_P 4
+#endif
+#ifndef LMHEAD_NW
+#define LMHEAD_NW 8
 #endif
 
 int launch_lmhead(int act, const void* uf, int M, int D, const void* lm, int V, float* pmax,
@@ -681,7 +702,7 @@ int launch_lmhead(int act, const void* uf, int M, int D, const void* lm, int V, 
   if (act == ACT_BF16 && M > 64) {
     const int nt = (V + 255) / 256;
     HeadArgs a{uf, M, D, lm, V, pmax, pidx, psum, logits, nt, (M + 127) / 128};
-    lmhead_direct_k<LMHEAD_P><<<((nt + 7) / 8) * 8 * a.mtiles, 256, 0, s>>>(a);
+    lmhead_direct_k<LMHEAD_P, LMHEAD_NW><<<((nt + 7) / 8) * 8 * a.mtiles, LMHEAD_NW * 64, 0, s>>>(a);
     return nt;
   }
   const int nt = (V + 127) / 128, bm = M > 64 ? 128 : 64;
