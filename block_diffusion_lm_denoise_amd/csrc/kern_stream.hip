@@ -104,6 +104,11 @@ __device__ __forceinline__ void piece_mma(f32x4_t (&acc)[2][4], const u32x4 (&wr
     }
 }
 
+// weights are read once per row tile: nontemporal loads (streamed, not kept)
+#ifndef STREAM_NT
+#define STREAM_NT 1
+#endif
+
 // KW waves split the contraction; the 4/KW wave groups take different 64-row
 // weight column groups (a block covers 64 * 4/KW weight rows).
 template <typename TA, typename TW, int MODE, int KW, int NB>
@@ -198,7 +203,8 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
     for (int h = 0; h < 2; h++)
 #pragma unroll
       for (int ct = 0; ct < 4; ct++)
-        wr[ct][h] = *reinterpret_cast<const u32x4*>(wtile[ct] + (size_t)c * 2048 + h * 1024);
+        wr[ct][h] = STREAM_NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wtile[ct] + (size_t)c * 2048 + h * 1024))
+                              : *reinterpret_cast<const u32x4*>(wtile[ct] + (size_t)c * 2048 + h * 1024);
 #pragma unroll
     for (int j = 0; j < NA; j++)
 #pragma unroll
