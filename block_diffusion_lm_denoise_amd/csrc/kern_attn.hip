@@ -56,7 +56,11 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
   constexpr int KLD = HD + EPC;                 // padded row of the K tile
   constexpr int VLD = KT + EPC;                 // padded row of the transposed V tile
   constexpr int KCH = KT * CPR / 256;           // K chunks staged per thread
-  constexpr int NVG = (KT / 4) * CPR;           // V groups (4 keys x 1 chunk)
+  constexpr int NKG = KT / 4;                   // 4-key groups per tile
+  constexpr int NVG = NKG * CPR;                // V groups (4 keys x 1 chunk); the
+                                                // key group runs fastest over the
+                                                // lanes, so the transposed stores
+                                                // of a wave are contiguous in LDS
   constexpr int VCH = (NVG + 255) / 256;        // V groups per thread
   static_assert(KT * CPR % 256 == 0, "K staging");
   __shared__ __attribute__((aligned(16))) TA ks[KT * KLD];
@@ -123,7 +127,7 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
 #pragma unroll
     for (int u = 0; u < VCH; u++) {
       const int id = t + 256 * u;
-      const int jg = (id < NVG ? id : 0) / CPR, dq = (id < NVG ? id : 0) % CPR;
+      const int jg = (id < NVG ? id : 0) % NKG, dq = (id < NVG ? id : 0) / NKG;
 #pragma unroll
       for (int jj = 0; jj < 4; jj++)
         rv[u][jj] = *reinterpret_cast<const u32x4*>(kptr(k0 + 4 * jg + jj, vc, vn) + dq * EPC);
@@ -141,7 +145,7 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
     for (int u = 0; u < VCH; u++) {
       const int id = t + 256 * u;
       if (NVG % 256 != 0 && id >= NVG) continue;
-      const int jg = id / CPR, dq = id % CPR;
+      const int jg = id % NKG, dq = id / NKG;
 #pragma unroll
       for (int k = 0; k < 4; k++) {
         const uint32_t a0 = word(rv[u][0], k), a1 = word(rv[u][1], k);

@@ -148,28 +148,25 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
   const int nch = nch_all / nsp, pbeg = split * nch;
 
   // A row pointers of this lane (row l16 of each 16-row tile).  Rows past the
-  // tile read a valid row and are zeroed by a select, so the load path has no
-  // branches and the next piece's loads stay in flight during the MFMAs.
+  // tile read a valid row: an MFMA output row depends on its own A row only,
+  // and those rows are never stored, so the load path needs no branches or
+  // masks and the next piece's loads stay in flight during the MFMAs.
   const TA* arow[2];
-  bool aok[2];
 #pragma unroll
   for (int rt = 0; rt < 2; rt++) {
     const int r = rt * 16 + l16;
-    aok[rt] = r < nrows;
-    const int slot = row0 + (aok[rt] ? r : 0);
+    const int slot = row0 + (r < nrows ? r : 0);
     const size_t src = MODE == SG_GATEUP ? (size_t)(a.perm[slot] / a.k) : (size_t)slot;
     arow[rt] = (const TA*)a.A + src * K;
   }
   // packed weight tiles of this wave's 4 column tiles: byte address of row
   // group rg, piece c, load h, this lane = base + (rg * nch_all + c) * 2048 + h * 1024 + 16 * lane
   const char* wtile[4];
-  bool wok[4];
   const int n0 = (chunk * CWG + cg) * 64;   // first weight row (dense/down) of this wave
 #pragma unroll
   for (int ct = 0; ct < 4; ct++) {
     const char* base;
     size_t row;   // first row of the 16-row group in its matrix
-    bool ok = true;
     if (MODE == SG_GATEUP) {
       // 32 SwiGLU outputs per column group: tiles [gate f, up f, gate f+16, up f+16]
       row = (size_t)e * a.NW + (chunk * CWG + cg) * 32 + 16 * (ct >> 1);
@@ -178,15 +175,14 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
       row = (size_t)e * a.NW + n0 + 16 * ct;
       base = (const char*)a.W0;
     } else {
+      // groups past N read group 0: their output columns are never stored
       const int n = n0 + 16 * ct;
-      ok = n < a.N;
-      const int nn = ok ? n : 0;
+      const int nn = n < a.N ? n : 0;
       if (nn < a.n1) { base = (const char*)a.W0; row = nn; }
       else if (nn < a.n1 + a.n2) { base = (const char*)a.W1; row = nn - a.n1; }
       else { base = (const char*)a.W2; row = nn - a.n1 - a.n2; }
     }
     wtile[ct] = base + (row / 16) * nch_all * 2048 + 16 * lane;
-    wok[ct] = ok;   // per 16-row group: rows past N within a valid group are masked at the store
   }
 
   f32x4_t acc[2][4];
@@ -211,23 +207,23 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
       for (int rt = 0; rt < 2; rt++)
         ar[rt][j] = *reinterpret_cast<const u32x4*>(arow[rt] + c * PC::EP + PC::a_off(j, g));
   };
-  // ok = false: the piece is past the contraction (clamped load), zero its A
-  auto comp = [&](u32x4(&wr)[4][2], u32x4(&ar)[2][NA], bool ok) {
-#pragma unroll
-    for (int ct = 0; ct < 4; ct++)
-#pragma unroll
-      for (int h = 0; h < 2; h++) zero_unless(wr[ct][h], wok[ct]);
+  auto comp = [&](u32x4(&wr)[4][2], u32x4(&ar)[2][NA]) { piece_mma(acc, wr, ar, (TA*)nullptr, (TW*)nullptr); };
+  // ok = false: the piece is past the contraction (a clamped load of the last
+  // piece), so its A is zeroed
+  auto comp_masked = [&](u32x4(&wr)[4][2], u32x4(&ar)[2][NA], bool ok) {
 #pragma unroll
     for (int rt = 0; rt < 2; rt++)
 #pragma unroll
-      for (int j = 0; j < NA; j++) zero_unless(ar[rt][j], aok[rt] && ok);
+      for (int j = 0; j < NA; j++) zero_unless(ar[rt][j], ok);
     piece_mma(acc, wr, ar, (TA*)nullptr, (TW*)nullptr);
   };
 
   // wave takes pieces kw, kw+KW, ...; indices past the end are clamped and
   // masked so the code is straight-line and the waits before each MFMA group
-  // cover only that buffer's loads.  sched_barrier keeps each refill ahead of
-  // the next buffers' MFMAs (otherwise the scheduler sinks the loads).
+  // cover only that buffer's loads.  Every index past the end falls in the
+  // last group (the count is rounded up to a multiple of NB), so only that
+  // group is masked.  sched_barrier keeps each refill ahead of the next
+  // buffers' MFMAs (otherwise the scheduler sinks the loads).
   const int per = (nch + KW - 1) / KW;
   const int nper = (per + NB - 1) / NB * NB;
   auto cidx = [&](int i) { const int c = kw + KW * i; return pbeg + (c < nch ? c : nch - 1); };
@@ -239,7 +235,7 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
 #pragma unroll
     for (int b = 0; b < NB; b++) {
       __builtin_amdgcn_sched_barrier(0);
-      comp(wbuf[b], abuf[b], cok(ib + b));
+      comp(wbuf[b], abuf[b]);
       __builtin_amdgcn_sched_barrier(0);
       load(wbuf[b], abuf[b], cidx(ib + NB + b));
     }
@@ -247,7 +243,7 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
 #pragma unroll
   for (int b = 0; b < NB; b++) {   // last group: nothing left to load
     __builtin_amdgcn_sched_barrier(0);
-    comp(wbuf[b], abuf[b], cok(ib + b));
+    comp_masked(wbuf[b], abuf[b], cok(ib + b));
   }
 
   // ---- reduce the four waves' partial tiles, one 16-row tile at a time ----
