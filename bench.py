@@ -23,7 +23,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 
-GATEUP_KERNEL = "dg::wstream_k<bf16, bf16, 4, 4, 4>"   # SG_GATEUP, 4 waves split K, 4 buffers
+GATEUP_KERNEL = "dg::wstream_k<bf16, bf16, 4, 4, 2, 4>"   # SG_GATEUP, 4 waves split K, 2 buffers, 64-row tiles
 
 
 def _gateup_source_hash():

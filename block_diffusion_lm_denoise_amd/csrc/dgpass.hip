@@ -237,7 +237,7 @@ void moe_block(const Ctx& c, int l, const float* gnext) {
   // permutation and row tiles
   const int avg = (int)(R * k / E);
   const bool stream = avg <= 64;
-  const int tile_rows = stream ? STREAM_TILE : FAT_TILE;
+  const int tile_rows = stream ? stream_tile_rows(act, cf.expert_dtype) : FAT_TILE;
   const int max_tiles = (int)((R * k + tile_rows - 1) / tile_rows) + (int)E;
   int32_t* counts = c.pass ? at<int32_t>(c, c.L.cov) + l * E : at<int32_t>(c, c.L.counts);
   launch_plan(at<int32_t>(c, c.L.ids), c.R, cf.k, cf.E, tile_rows, counts, at<int32_t>(c, c.L.offsets),

@@ -112,17 +112,20 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
   const TA* const kn = a.mode == 0 ? (const TA*)a.kn + (size_t)b * a.T * a.ldq + gh * HD : kc;
   const TA* const vn = a.mode == 0 ? (const TA*)a.vn + (size_t)b * a.T * a.ldq + gh * HD : vc;
   const int fresh0 = a.mode == 0 ? P : 0x7fffffff;   // first key read from the qkv rows
+  const size_t ldq = (size_t)a.ldq;
   auto kptr = [&](int kk, const TA* cache, const TA* fresh) -> const TA* {
     const int k = kk < kend ? kk : kbeg;
-    return k >= fresh0 ? fresh + (size_t)(k - fresh0) * a.ldq : cache + (size_t)k * HD;
+    const bool f = k >= fresh0;
+    return (f ? fresh : cache) + (size_t)(f ? k - fresh0 : k) * (f ? ldq : (size_t)HD);
   };
-  // register copy of the next tile: K chunks and V 4-key groups
-  u32x4 rk[KCH], rv[VCH][4];
-  auto gload = [&](int k0) {
+  // register ring of two tiles (K chunks and V 4-key groups): the loads of
+  // the next two tiles are in flight while a tile is used
+  u32x4 rk[2][KCH], rv[2][VCH][4];
+  auto gload = [&](int buf, int k0) {
 #pragma unroll
     for (int u = 0; u < KCH; u++) {
       const int id = t + 256 * u, j = id / CPR, q = id % CPR;
-      rk[u] = *reinterpret_cast<const u32x4*>(kptr(k0 + j, kc, kn) + q * EPC);
+      rk[buf][u] = *reinterpret_cast<const u32x4*>(kptr(k0 + j, kc, kn) + q * EPC);
     }
 #pragma unroll
     for (int u = 0; u < VCH; u++) {
@@ -130,16 +133,16 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
       const int jg = (id < NVG ? id : 0) % NKG, dq = (id < NVG ? id : 0) / NKG;
 #pragma unroll
       for (int jj = 0; jj < 4; jj++)
-        rv[u][jj] = *reinterpret_cast<const u32x4*>(kptr(k0 + 4 * jg + jj, vc, vn) + dq * EPC);
+        rv[buf][u][jj] = *reinterpret_cast<const u32x4*>(kptr(k0 + 4 * jg + jj, vc, vn) + dq * EPC);
     }
   };
   auto word = [](u32x4 v, int k) -> uint32_t { return v[k]; };
   // LDS: K row-major; V transposed (vt[d][key]), 4 keys of one d per store
-  auto sstore = [&]() {
+  auto sstore = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < KCH; u++) {
       const int id = t + 256 * u, j = id / CPR, q = id % CPR;
-      *reinterpret_cast<u32x4*>(ks + j * KLD + q * EPC) = rk[u];
+      *reinterpret_cast<u32x4*>(ks + j * KLD + q * EPC) = rk[buf][u];
     }
 #pragma unroll
     for (int u = 0; u < VCH; u++) {
@@ -148,8 +151,8 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
       const int jg = id % NKG, dq = id / NKG;
 #pragma unroll
       for (int k = 0; k < 4; k++) {
-        const uint32_t a0 = word(rv[u][0], k), a1 = word(rv[u][1], k);
-        const uint32_t a2 = word(rv[u][2], k), a3 = word(rv[u][3], k);
+        const uint32_t a0 = word(rv[buf][u][0], k), a1 = word(rv[buf][u][1], k);
+        const uint32_t a2 = word(rv[buf][u][2], k), a3 = word(rv[buf][u][3], k);
         if constexpr (ES == 2) {
           // elements 2k (low halves) and 2k+1 (high halves) of the chunk
           const uint2 lo = make_uint2((a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16));
@@ -163,13 +166,8 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
     }
   };
 
-  if (kbeg < kend) gload(kbeg);
-  for (int k0 = kbeg; k0 < kend; k0 += KT) {
-    __syncthreads();   // the previous tile's readers are done with LDS
-    sstore();
-    if (k0 + KT < kend) gload(k0 + KT);   // next tile in flight during this one
-    __syncthreads();
-
+  // one key tile: S, online softmax, O update (K and V tiles in LDS)
+  auto compute = [&](int k0) {
     // ---- S^T = K Q^T: lane holds keys 16*mt + 4*g4 + i for query row l16 ----
     f32x4_t s[KT / 16];
 #pragma unroll
@@ -255,6 +253,30 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
         }
       }
     }
+  };
+
+  // tiles past the split load key kbeg (clamped) and are never computed, so
+  // every load is issued unconditionally and the ring indices are constants
+  const int ntile = kend > kbeg ? (kend - kbeg + KT - 1) / KT : 0;
+  gload(0, kbeg);
+  gload(1, kbeg + KT);
+  int it = 0;
+  for (; it + 2 <= ntile; it += 2) {
+#pragma unroll
+    for (int buf = 0; buf < 2; buf++) {
+      const int k0 = kbeg + (it + buf) * KT;
+      __syncthreads();   // the previous tile's readers are done with LDS
+      sstore(buf);
+      __syncthreads();
+      gload(buf, k0 + 2 * KT);
+      compute(k0);
+    }
+  }
+  if (it < ntile) {
+    __syncthreads();
+    sstore(0);
+    __syncthreads();
+    compute(kbeg + it * KT);
   }
 
   lsum += __shfl_xor(lsum, 16, 64);

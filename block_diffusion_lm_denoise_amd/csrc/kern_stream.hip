@@ -49,23 +49,28 @@ __device__ __forceinline__ void zero_unless(u32x4& u, bool ok) {
   u.w = ok ? u.w : 0u;
 }
 
-// acc[rt][ct] += A[rt] . W[ct] over one piece, from raw 16-byte registers
-__device__ __forceinline__ void piece_mma(f32x4_t (&acc)[2][4], const u32x4 (&wr)[4][2],
-                                          const u32x4 (&ar)[2][2], uint16_t*, uint16_t*) {
+// acc[rt][ct] += A[rt] . W[ct] over one piece, from raw 16-byte registers.
+// Row tiles rt >= 2 are multiplied only when the tile has rows there (nrt is
+// uniform over the wave, so the test is a scalar branch).
+template <int RT>
+__device__ __forceinline__ void piece_mma(f32x4_t (&acc)[RT][4], const u32x4 (&wr)[4][2],
+                                          const u32x4 (&ar)[RT][2], int nrt, uint16_t*, uint16_t*) {
 #pragma unroll
   for (int j = 0; j < 2; j++)
 #pragma unroll
-    for (int rt = 0; rt < 2; rt++)
+    for (int rt = 0; rt < RT; rt++)
+      if (rt < 2 || rt < nrt)
 #pragma unroll
-      for (int ct = 0; ct < 4; ct++) {
-        FragBF x, y;
-        x.v = __builtin_bit_cast(bf16x8_t, ar[rt][j]);
-        y.v = __builtin_bit_cast(bf16x8_t, wr[ct][j]);
-        mma(acc[rt][ct], x, y);
-      }
+        for (int ct = 0; ct < 4; ct++) {
+          FragBF x, y;
+          x.v = __builtin_bit_cast(bf16x8_t, ar[rt][j]);
+          y.v = __builtin_bit_cast(bf16x8_t, wr[ct][j]);
+          mma(acc[rt][ct], x, y);
+        }
 }
-__device__ __forceinline__ void piece_mma(f32x4_t (&acc)[2][4], const u32x4 (&wr)[4][2],
-                                          const u32x4 (&ar)[2][4], uint16_t*, uint8_t*) {
+template <int RT>
+__device__ __forceinline__ void piece_mma(f32x4_t (&acc)[RT][4], const u32x4 (&wr)[4][2],
+                                          const u32x4 (&ar)[RT][4], int nrt, uint16_t*, uint8_t*) {
 #pragma unroll
   for (int j = 0; j < 4; j++)
 #pragma unroll
@@ -74,17 +79,20 @@ __device__ __forceinline__ void piece_mma(f32x4_t (&acc)[2][4], const u32x4 (&wr
       FragBF y;
       y.v = __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8((j & 1) ? make_uint2(u.z, u.w) : make_uint2(u.x, u.y)));
 #pragma unroll
-      for (int rt = 0; rt < 2; rt++) {
-        FragBF x;
-        x.v = __builtin_bit_cast(bf16x8_t, ar[rt][j]);
-        mma(acc[rt][ct], x, y);
-      }
+      for (int rt = 0; rt < RT; rt++)
+        if (rt < 2 || rt < nrt) {
+          FragBF x;
+          x.v = __builtin_bit_cast(bf16x8_t, ar[rt][j]);
+          mma(acc[rt][ct], x, y);
+        }
     }
 }
-__device__ __forceinline__ void piece_mma(f32x4_t (&acc)[2][4], const u32x4 (&wr)[4][2],
-                                          const u32x4 (&ar)[2][2], float*, float*) {
+template <int RT>
+__device__ __forceinline__ void piece_mma(f32x4_t (&acc)[RT][4], const u32x4 (&wr)[4][2],
+                                          const u32x4 (&ar)[RT][2], int nrt, float*, float*) {
 #pragma unroll
-  for (int rt = 0; rt < 2; rt++)
+  for (int rt = 0; rt < RT; rt++)
+    if (rt < 2 || rt < nrt)
 #pragma unroll
     for (int ct = 0; ct < 4; ct++) {
       FragF32 x, y;
@@ -110,8 +118,10 @@ __device__ __forceinline__ void piece_mma(f32x4_t (&acc)[2][4], const u32x4 (&wr
 #endif
 
 // KW waves split the contraction; the 4/KW wave groups take different 64-row
-// weight column groups (a block covers 64 * 4/KW weight rows).
-template <typename TA, typename TW, int MODE, int KW, int NB>
+// weight column groups (a block covers 64 * 4/KW weight rows).  A row tile
+// holds up to 16 RT rows: RT = 4 for the grouped bf16 expert GEMMs, so an
+// expert with up to 64 routed rows reads its weights once.
+template <typename TA, typename TW, int MODE, int KW, int NB, int RT>
 __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
   typedef Piece<TA, TW> PC;
   constexpr int NA = PC::NA;
@@ -122,7 +132,7 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
   const int chunk = blockIdx.x % C;
   int tile = blockIdx.x / C, split = 0;
   if (MODE == SG_F32 && a.ksplit > 1) {   // block id = chunk + C * (tile + T * split)
-    const int T = (a.M + 31) / 32;
+    const int T = (a.M + 16 * RT - 1) / (16 * RT);
     split = tile / T;
     tile -= split * T;
   }
@@ -134,9 +144,9 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
     row0 = t.y;
     nrows = t.z;
   } else {
-    row0 = tile * 32;
+    row0 = tile * 16 * RT;
     if (row0 >= a.M) return;
-    nrows = min(32, a.M - row0);
+    nrows = min(16 * RT, a.M - row0);
   }
   const int nrt = (nrows + 15) >> 4;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
@@ -151,9 +161,9 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
   // tile read a valid row: an MFMA output row depends on its own A row only,
   // and those rows are never stored, so the load path needs no branches or
   // masks and the next piece's loads stay in flight during the MFMAs.
-  const TA* arow[2];
+  const TA* arow[RT];
 #pragma unroll
-  for (int rt = 0; rt < 2; rt++) {
+  for (int rt = 0; rt < RT; rt++) {
     const int r = rt * 16 + l16;
     const int slot = row0 + (r < nrows ? r : 0);
     const size_t src = MODE == SG_GATEUP ? (size_t)(a.perm[slot] / a.k) : (size_t)slot;
@@ -185,16 +195,16 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
     wtile[ct] = base + (row / 16) * nch_all * 2048 + 16 * lane;
   }
 
-  f32x4_t acc[2][4];
+  f32x4_t acc[RT][4];
 #pragma unroll
-  for (int rt = 0; rt < 2; rt++)
+  for (int rt = 0; rt < RT; rt++)
 #pragma unroll
     for (int ct = 0; ct < 4; ct++) acc[rt][ct] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
   // NB register buffers of one piece each: the loads of NB-1 later pieces are
   // in flight while a piece is multiplied
-  u32x4 wbuf[NB][4][2], abuf[NB][2][NA];
-  auto load = [&](u32x4(&wr)[4][2], u32x4(&ar)[2][NA], int c) {
+  u32x4 wbuf[NB][4][2], abuf[NB][RT][NA];
+  auto load = [&](u32x4(&wr)[4][2], u32x4(&ar)[RT][NA], int c) {
 #pragma unroll
     for (int h = 0; h < 2; h++)
 #pragma unroll
@@ -204,18 +214,20 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
 #pragma unroll
     for (int j = 0; j < NA; j++)
 #pragma unroll
-      for (int rt = 0; rt < 2; rt++)
+      for (int rt = 0; rt < RT; rt++)
         ar[rt][j] = *reinterpret_cast<const u32x4*>(arow[rt] + c * PC::EP + PC::a_off(j, g));
   };
-  auto comp = [&](u32x4(&wr)[4][2], u32x4(&ar)[2][NA]) { piece_mma(acc, wr, ar, (TA*)nullptr, (TW*)nullptr); };
+  auto comp = [&](u32x4(&wr)[4][2], u32x4(&ar)[RT][NA]) {
+    piece_mma<RT>(acc, wr, ar, nrt, (TA*)nullptr, (TW*)nullptr);
+  };
   // ok = false: the piece is past the contraction (a clamped load of the last
   // piece), so its A is zeroed
-  auto comp_masked = [&](u32x4(&wr)[4][2], u32x4(&ar)[2][NA], bool ok) {
+  auto comp_masked = [&](u32x4(&wr)[4][2], u32x4(&ar)[RT][NA], bool ok) {
 #pragma unroll
-    for (int rt = 0; rt < 2; rt++)
+    for (int rt = 0; rt < RT; rt++)
 #pragma unroll
       for (int j = 0; j < NA; j++) zero_unless(ar[rt][j], ok);
-    piece_mma(acc, wr, ar, (TA*)nullptr, (TW*)nullptr);
+    piece_mma<RT>(acc, wr, ar, nrt, (TA*)nullptr, (TW*)nullptr);
   };
 
   // wave takes pieces kw, kw+KW, ...; indices past the end are clamped and
@@ -253,7 +265,9 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
     su = a.escale[e * 3 + 1];
     sd = a.escale[e * 3 + 2];
   }
-  for (int rt = 0; rt < nrt; rt++) {
+#pragma unroll
+  for (int rt = 0; rt < RT; rt++) {   // constant register indices; tiles past nrt stop
+    if (rt >= nrt) break;
 #pragma unroll
     for (int ct = 0; ct < 4; ct++)
 #pragma unroll
@@ -324,7 +338,7 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
 // register buffers (pieces in flight) per wave, chosen by measurement: bf16
 // gate/up, bf16 down and dense projections, fp8 experts
 #ifndef STREAM_NB_GATEUP
-#define STREAM_NB_GATEUP 4
+#define STREAM_NB_GATEUP 2
 #endif
 #ifndef STREAM_NB
 #define STREAM_NB 2
@@ -332,17 +346,29 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
 #ifndef STREAM_NB_FP8
 #define STREAM_NB_FP8 2
 #endif
+// 16-row tiles per expert tile of the bf16 grouped GEMMs
+#ifndef STREAM_RT_BF16
+#define STREAM_RT_BF16 4
+#endif
+
+// rows per expert tile of the grouped modes (the plan cuts tiles this size)
+int stream_tile_rows(int act, int wdt) {
+  return act == ACT_BF16 && wdt == DG_BF16 ? 16 * STREAM_RT_BF16 : 32;
+}
 
 template <int MODE, int KW>
 static void dispatch(int act, int wdt, const StreamGemm& a, int nblocks, hipStream_t s) {
+  constexpr bool GROUPED = MODE == SG_GATEUP || MODE == SG_DOWN;
   if (nblocks <= 0) return;
   if (act == ACT_F32)
-    wstream_k<float, float, MODE, KW, 2><<<nblocks, 256, 0, s>>>(a);
+    wstream_k<float, float, MODE, KW, 2, 2><<<nblocks, 256, 0, s>>>(a);
   else if (wdt == DG_FP8E4M3)
-    wstream_k<uint16_t, uint8_t, MODE, KW, STREAM_NB_FP8><<<nblocks, 256, 0, s>>>(a);
+    wstream_k<uint16_t, uint8_t, MODE, KW, STREAM_NB_FP8, 2><<<nblocks, 256, 0, s>>>(a);
+  else if constexpr (GROUPED)
+    wstream_k<uint16_t, uint16_t, MODE, KW, MODE == SG_GATEUP ? STREAM_NB_GATEUP : STREAM_NB,
+              STREAM_RT_BF16><<<nblocks, 256, 0, s>>>(a);
   else
-    wstream_k<uint16_t, uint16_t, MODE, KW, MODE == SG_GATEUP ? STREAM_NB_GATEUP : STREAM_NB>
-        <<<nblocks, 256, 0, s>>>(a);
+    wstream_k<uint16_t, uint16_t, MODE, KW, STREAM_NB, 2><<<nblocks, 256, 0, s>>>(a);
 }
 
 // kw: waves splitting the contraction (4, or 2 when the block should cover 128

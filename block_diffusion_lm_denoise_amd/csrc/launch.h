@@ -120,6 +120,7 @@ struct StreamGemm {
   const void* R;          // residual (SG_RESID)
   CacheDst cache;         // SG_QKV_CACHE
 };
+int stream_tile_rows(int act, int wdt);
 void launch_stream_gemm(int act, int wdt, int mode, int kw, const StreamGemm& a, int ntiles_max,
                         hipStream_t s);
 
