@@ -15,7 +15,6 @@ size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 int esize(int dt) { return dt == DG_F32 ? 4 : dt == DG_BF16 ? 2 : 1; }
 
 constexpr int MIN_TILE = 32;      // smallest expert row tile (sizes the tile list)
-constexpr int STREAM_TILE = 32;   // row tile of the weight-streaming kernels
 constexpr int FAT_TILE = 128;     // row tile of the LDS-tiled expert kernels
 constexpr int STREAM_MAX_ROWS = 1024;  // dense projections: weight streaming up to this many rows
 constexpr int ROUTE_MIN_ROWS = 2048;   // fused routing kernel from this many token rows
@@ -171,7 +170,7 @@ void dense_gemm(const Ctx& c, int mode, const void* A, int M, int K, const void*
     if (cache) g.cache = *cache;
     const int sm = mode == GEMM_STORE ? SG_STORE : mode == GEMM_RESID ? SG_RESID
                  : mode == GEMM_F32 ? SG_F32 : SG_QKV_CACHE;
-    launch_stream_gemm(act, cf.act_dtype, sm, kw, g, (M + STREAM_TILE - 1) / STREAM_TILE, c.s);
+    launch_stream_gemm(act, cf.act_dtype, sm, kw, g, 0, c.s);
   } else {
     launch_gemm(act, mode, A, M, K, B0, n1, B1, n2, B2, N, C, ldc, R, cache, c.s);
   }
@@ -218,7 +217,7 @@ void moe_block(const Ctx& c, int l, const float* gnext) {
         g.ksplit = S;
         g.out = at<void>(c, c.L.rl);
         g.ldo = cf.E;
-        launch_stream_gemm(act, cf.act_dtype, SG_F32, 4, g, (c.R + STREAM_TILE - 1) / STREAM_TILE, s);
+        launch_stream_gemm(act, cf.act_dtype, SG_F32, 4, g, 0, s);
       } else {
         dense_gemm(c, GEMM_F32, at<void>(c, c.L.u2), c.R, cf.D, w.wr, cf.E, nullptr, 0, nullptr, cf.E,
                    at<void>(c, c.L.rl), cf.E, nullptr, nullptr);

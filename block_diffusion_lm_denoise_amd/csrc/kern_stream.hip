@@ -346,6 +346,10 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
 #ifndef STREAM_NB_FP8
 #define STREAM_NB_FP8 2
 #endif
+// blocks a dense bf16 launch needs to take 64-row tiles
+#ifndef STREAM_DENSE_RT4_BLOCKS
+#define STREAM_DENSE_RT4_BLOCKS 256
+#endif
 // 16-row tiles per expert tile of the bf16 grouped GEMMs
 #ifndef STREAM_RT_BF16
 #define STREAM_RT_BF16 4
@@ -356,26 +360,40 @@ int stream_tile_rows(int act, int wdt) {
   return act == ACT_BF16 && wdt == DG_BF16 ? 16 * STREAM_RT_BF16 : 32;
 }
 
+
+// dense bf16 projections take 64-row tiles when that still gives at least
+// one block per CU (fewer re-reads of each weight chunk), else 32-row tiles
 template <int MODE, int KW>
-static void dispatch(int act, int wdt, const StreamGemm& a, int nblocks, hipStream_t s) {
+static void dispatch(int act, int wdt, const StreamGemm& a, int ntiles_max, hipStream_t s) {
   constexpr bool GROUPED = MODE == SG_GATEUP || MODE == SG_DOWN;
-  if (nblocks <= 0) return;
-  if (act == ACT_F32)
-    wstream_k<float, float, MODE, KW, 2, 2><<<nblocks, 256, 0, s>>>(a);
-  else if (wdt == DG_FP8E4M3)
-    wstream_k<uint16_t, uint8_t, MODE, KW, STREAM_NB_FP8, 2><<<nblocks, 256, 0, s>>>(a);
-  else if constexpr (GROUPED)
-    wstream_k<uint16_t, uint16_t, MODE, KW, MODE == SG_GATEUP ? STREAM_NB_GATEUP : STREAM_NB,
-              STREAM_RT_BF16><<<nblocks, 256, 0, s>>>(a);
-  else
-    wstream_k<uint16_t, uint16_t, MODE, KW, STREAM_NB, 2><<<nblocks, 256, 0, s>>>(a);
+  const int nsp = MODE == SG_F32 && a.ksplit > 1 ? a.ksplit : 1;
+  if (act == ACT_F32) {
+    const int nb = a.nchunks * (GROUPED ? ntiles_max : (a.M + 31) / 32) * nsp;
+    if (nb > 0) wstream_k<float, float, MODE, KW, 2, 2><<<nb, 256, 0, s>>>(a);
+  } else if (wdt == DG_FP8E4M3) {
+    const int nb = a.nchunks * (GROUPED ? ntiles_max : (a.M + 31) / 32) * nsp;
+    if (nb > 0) wstream_k<uint16_t, uint8_t, MODE, KW, STREAM_NB_FP8, 2><<<nb, 256, 0, s>>>(a);
+  } else if constexpr (GROUPED) {
+    const int nb = a.nchunks * ntiles_max;
+    if (nb > 0)
+      wstream_k<uint16_t, uint16_t, MODE, KW, MODE == SG_GATEUP ? STREAM_NB_GATEUP : STREAM_NB,
+                STREAM_RT_BF16><<<nb, 256, 0, s>>>(a);
+  } else {
+    const int nb4 = a.nchunks * ((a.M + 63) / 64) * nsp, nb2 = a.nchunks * ((a.M + 31) / 32) * nsp;
+    if (nb4 >= STREAM_DENSE_RT4_BLOCKS)
+      wstream_k<uint16_t, uint16_t, MODE, KW, STREAM_NB, 4><<<nb4, 256, 0, s>>>(a);
+    else if (nb2 > 0)
+      wstream_k<uint16_t, uint16_t, MODE, KW, STREAM_NB, 2><<<nb2, 256, 0, s>>>(a);
+  }
 }
 
 // kw: waves splitting the contraction (4, or 2 when the block should cover 128
-// weight rows, e.g. a short contraction); a.nchunks counts blocks per row tile
+// weight rows, e.g. a short contraction); a.nchunks counts blocks per row
+// tile; ntiles_max bounds the expert row tiles of the grouped modes (the
+// dense modes tile a.M rows themselves)
 void launch_stream_gemm(int act, int wdt, int mode, int kw, const StreamGemm& a, int ntiles_max,
                         hipStream_t s) {
-  const int nb = a.nchunks * ntiles_max * (mode == SG_F32 && a.ksplit > 1 ? a.ksplit : 1);
+  const int nb = ntiles_max;
   if (kw == 2) {
     switch (mode) {
       case SG_STORE: dispatch<SG_STORE, 2>(act, wdt, a, nb, s); break;
