@@ -195,6 +195,24 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
     wtile[ct] = base + (row / 16) * nch_all * 2048 + 16 * lane;
   }
 
+  // residual values of this thread's outputs (stored by thread (w, lane) in
+  // the epilogue: rows 16rt + 4g + i, column tile w of each column group),
+  // loaded now so that their latency hides behind the main loop
+  float res[MODE == SG_RESID ? RT : 1][MODE == SG_RESID ? CWG : 1][4];
+  if (MODE == SG_RESID) {
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+      for (int grp = 0; grp < CWG; grp++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int r = rt * 16 + 4 * g + i;
+          const int n = (chunk * CWG + grp) * 64 + 16 * w + l16;
+          const bool ok = r < nrows && n < a.N;
+          res[rt][grp][i] = ldx((const TA*)a.R, ok ? (size_t)(row0 + r) * a.ldo + n : 0);
+        }
+  }
+
   f32x4_t acc[RT][4];
 #pragma unroll
   for (int rt = 0; rt < RT; rt++)
@@ -315,7 +333,7 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
           } else if (MODE == SG_F32) {
             ((float*)a.out)[o + (size_t)split * a.M * a.ldo] = val;
           } else {
-            if (MODE == SG_RESID) val += ldx((const TA*)a.R, o);
+            if (MODE == SG_RESID) val += res[MODE == SG_RESID ? rt : 0][MODE == SG_RESID ? grp : 0][i];
             stx((TA*)a.out, o, val);
             if (MODE == SG_QKV_CACHE && n >= a.cache.QD) {
               const int c = n - a.cache.QD;
@@ -345,6 +363,13 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
 #endif
 #ifndef STREAM_NB_FP8
 #define STREAM_NB_FP8 2
+#endif
+// register buffers of the dense bf16 projections (64- and 32-row tiles)
+#ifndef STREAM_NB_DENSE4
+#define STREAM_NB_DENSE4 2
+#endif
+#ifndef STREAM_NB_DENSE2
+#define STREAM_NB_DENSE2 2
 #endif
 // blocks a dense bf16 launch needs to take 64-row tiles
 #ifndef STREAM_DENSE_RT4_BLOCKS
@@ -381,9 +406,9 @@ static void dispatch(int act, int wdt, const StreamGemm& a, int ntiles_max, hipS
   } else {
     const int nb4 = a.nchunks * ((a.M + 63) / 64) * nsp, nb2 = a.nchunks * ((a.M + 31) / 32) * nsp;
     if (nb4 >= STREAM_DENSE_RT4_BLOCKS)
-      wstream_k<uint16_t, uint16_t, MODE, KW, STREAM_NB, 4><<<nb4, 256, 0, s>>>(a);
+      wstream_k<uint16_t, uint16_t, MODE, KW, STREAM_NB_DENSE4, 4><<<nb4, 256, 0, s>>>(a);
     else if (nb2 > 0)
-      wstream_k<uint16_t, uint16_t, MODE, KW, STREAM_NB, 2><<<nb2, 256, 0, s>>>(a);
+      wstream_k<uint16_t, uint16_t, MODE, KW, STREAM_NB_DENSE2, 2><<<nb2, 256, 0, s>>>(a);
   }
 }
 
