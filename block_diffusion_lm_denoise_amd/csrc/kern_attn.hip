@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
   constexpr int ES = (int)sizeof(TA);
   constexpr int EPC = 16 / ES;                  // elements per 16-byte chunk
   constexpr int CPR = HD / EPC;                 // chunks per key row
-  constexpr int KLD = HD + EPC;                 // padded row of the K tile
+  constexpr int KLD = HD + 16 * EPC / 8;        // padded row of the K tile (bf16: 288 B, conflict-free fragment reads)
   constexpr int VLD = KT + EPC;                 // padded row of the transposed V tile
   constexpr int KCH = KT * CPR / 256;           // K chunks staged per thread
   constexpr int NKG = KT / 4;                   // 4-key groups per tile

@@ -24,7 +24,7 @@ __device__ __forceinline__ const char* packed_group(const void* base, size_t row
 template <typename TA, typename TW, int BM, int BN, int P = 1>
 struct Mainloop {
   static constexpr int BK = 128 / (int)sizeof(TA);            // elements per staged row
-  static constexpr int LDK = 144 / (int)sizeof(TA);           // padded LDS row (elements)
+  static constexpr int LDK = 160 / (int)sizeof(TA);           // padded LDS row: 160 B keeps fragment reads conflict-free
   static constexpr bool FP8 = sizeof(TW) == 1;
   static constexpr int A_LD = BM / 32;                         // 16-byte A chunks per thread
   static constexpr int B_ROWS_PER_PASS = FP8 ? 64 : 32;        // rows covered by 256 threads
@@ -480,7 +480,7 @@ __device__ __forceinline__ void mrg_bf(float& m, int& i, float& s, float m2, int
 template <int P, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void lmhead_direct_k(HeadArgs a) {
   constexpr int NT = NW * 64;                 // threads
-  constexpr int BM = 128, BN = 256, BK = 64, LDK = 72, RT = 8;
+  constexpr int BM = 128, BN = 256, BK = 64, LDK = 80, RT = 8;   // 160-byte LDS rows: conflict-free fragment reads
   constexpr int WC = BN / NW, CT = WC / 16;   // vocabulary columns per wave
   constexpr int A_LD = BM * BK * 2 / 16 / NT;   // 16-byte A chunks staged per thread
   constexpr int A_RSTEP = NT / 8;             // rows between a thread's chunks
