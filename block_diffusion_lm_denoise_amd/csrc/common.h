@@ -148,6 +148,26 @@ __device__ __forceinline__ void st8(float* p, const float (&v)[8]) {
 }
 
 // ---------------------------------------------------------------------------
+// the value of lane l ^ 16 / l ^ 32 of a wave.  The gfx950 permlane swaps
+// exchange 16-lane rows between two registers in the VALU (no LDS round trip
+// as with ds_bpermute): with both operands x, lanes of an even row receive
+// the next row's x in the second result and lanes of an odd row the previous
+// row's x in the first (permlane32: the same for the two halves of the wave).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t lane_xor16(uint32_t x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return (threadIdx.x & 16) ? p[0] : p[1];
+}
+__device__ __forceinline__ uint32_t lane_xor32(uint32_t x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return (threadIdx.x & 32) ? p[0] : p[1];
+}
+__device__ __forceinline__ float lane_xor16(float x) { return __uint_as_float(lane_xor16(__float_as_uint(x))); }
+__device__ __forceinline__ float lane_xor32(float x) { return __uint_as_float(lane_xor32(__float_as_uint(x))); }
+__device__ __forceinline__ int lane_xor16(int x) { return (int)lane_xor16((uint32_t)x); }
+__device__ __forceinline__ int lane_xor32(int x) { return (int)lane_xor32((uint32_t)x); }
+
+// ---------------------------------------------------------------------------
 // wave / block reductions (wave64)
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float wave_sum(float v) {

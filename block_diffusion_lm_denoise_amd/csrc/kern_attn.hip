@@ -191,8 +191,8 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
         s[mt][i] = v;
         tmax = fmaxf(tmax, v);
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    tmax = fmaxf(tmax, lane_xor16(tmax));
+    tmax = fmaxf(tmax, lane_xor32(tmax));
     const float mnew = fmaxf(mrow, tmax);
     const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mrow - mnew);
     float psum = 0.f;
@@ -279,8 +279,8 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
     compute(kbeg + it * KT);
   }
 
-  lsum += __shfl_xor(lsum, 16, 64);
-  lsum += __shfl_xor(lsum, 32, 64);
+  lsum += lane_xor16(lsum);
+  lsum += lane_xor32(lsum);
   const size_t row = (size_t)b * a.T + (qvalid ? qi : 0);
   if (a.nsplit == 1) {
     if (!qvalid) return;

@@ -616,11 +616,11 @@ __global__ __launch_bounds__(NW * 64, 1) void lmhead_direct_k(HeadArgs a) {
         lm = v > lm ? v : lm;
       }
     float m = lm;
-    m = fmax_sel(m, __shfl_xor(m, 16, 64));
-    m = fmax_sel(m, __shfl_xor(m, 32, 64));
+    m = fmax_sel(m, lane_xor16(m));
+    m = fmax_sel(m, lane_xor32(m));
     int idx = lm == m ? li : 0x7fffffff;
-    idx = min(idx, __shfl_xor(idx, 16, 64));
-    idx = min(idx, __shfl_xor(idx, 32, 64));
+    idx = min(idx, lane_xor16(idx));
+    idx = min(idx, lane_xor32(idx));
     float s = 0.f;
 #pragma unroll
     for (int ct = 0; ct < CT; ct++)
@@ -631,8 +631,8 @@ __global__ __launch_bounds__(NW * 64, 1) void lmhead_direct_k(HeadArgs a) {
         s += n < a.V ? e : 0.f;
       }
     s = m == -INFINITY ? 0.f : s;
-    s += __shfl_xor(s, 16, 64);
-    s += __shfl_xor(s, 32, 64);
+    s += lane_xor16(s);
+    s += lane_xor32(s);
     if (g == 0) {
       const int rl = 16 * rt + l16;
       xm[w][rl] = m;
