@@ -152,13 +152,15 @@ __global__ __launch_bounds__(256) void renoise_k(RenoiseArgs a) {
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= a.B * a.N) return;
   const int b = idx / a.N, i = idx % a.N;
-  if (a.conf && a.conf[idx] >= a.tau) {  // NaN compares false: noised
-    a.canvas[idx] = a.argmax[idx];
-    return;
-  }
+  // confidence and argmax are loaded together (one memory round trip) and the
+  // noise token is always drawn; the select keeps argmax where conf >= tau
+  // (NaN compares false: noised)
+  const bool keep = a.conf ? a.conf[idx] >= a.tau : false;
+  const int32_t am = a.conf ? a.argmax[idx] : 0;
   uint64_t c[4] = {(uint64_t)(int64_t)(a.pos0.v[b] + i), (uint64_t)a.tag, (uint64_t)a.req.v[b], 0};
   philox4x64_10(c, a.seed, 0);
-  a.canvas[idx] = (int32_t)__umul64hi(c[0], (uint64_t)a.V);  // floor(r * V / 2^64)
+  const int32_t noise = (int32_t)__umul64hi(c[0], (uint64_t)a.V);  // floor(r * V / 2^64)
+  a.canvas[idx] = keep ? am : noise;
 }
 
 __global__ __launch_bounds__(256) void coverage_k(const int32_t* __restrict__ counts, int E,
@@ -172,7 +174,9 @@ __global__ __launch_bounds__(256) void coverage_k(const int32_t* __restrict__ co
     t += c > 0;
     if (counts_out) counts_out[l * E + e] = c;
   }
-  for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+  t += lane_xor32(t);
+  t += lane_xor16(t);
+  t = (int)row16_sum((float)t);   // counts of at most 256 experts: exact in fp32
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = t;
   __syncthreads();
   if (threadIdx.x == 0) touched[l] = red[0] + red[1] + red[2] + red[3];

@@ -101,10 +101,21 @@ __global__ __launch_bounds__(256) void plan_k(const int32_t* __restrict__ ids, i
   __shared__ int tst[257];
   __shared__ int wsum[4];
   const int tid = threadIdx.x, e = blockIdx.x;
+  // thread tid reads the k ids of rows tid, tid + 256, ...: all k loads of a
+  // row are issued together (k <= 8), and the listing below reads the same rows
+  auto load_row = [&](int r, int (&v)[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) v[j] = r < rows && j < k ? ids[(size_t)r * k + j] : -1;
+  };
   hist[tid] = 0;
   __syncthreads();
-  const int n = rows * k;
-  for (int i = tid; i < n; i += 256) atomicAdd(&hist[ids[i]], 1);
+  for (int r0 = 0; r0 < rows; r0 += 256) {
+    int v[8];
+    load_row(r0 + tid, v);
+#pragma unroll
+    for (int j = 0; j < 8; j++)
+      if (v[j] >= 0) atomicAdd(&hist[v[j]], 1);
+  }
   __syncthreads();
   // inclusive scans of counts and of tile counts (Hillis-Steele over 256 slots)
   int c = tid < E ? hist[tid] : 0;
@@ -134,10 +145,11 @@ __global__ __launch_bounds__(256) void plan_k(const int32_t* __restrict__ ids, i
   int base = off[e];
   for (int r0 = 0; r0 < rows; r0 += 256) {
     const int r = r0 + tid;
+    int v[8];
+    load_row(r, v);
     int js = -1;
-    if (r < rows)
-      for (int j = 0; j < k; j++)
-        if (ids[(size_t)r * k + j] == e) js = j;
+#pragma unroll
+    for (int j = 0; j < 8; j++) js = v[j] == e ? j : js;
     const uint64_t m = __ballot(js >= 0);
     const int pre = __popcll(m & ((1ull << lane) - 1ull));
     __syncthreads();
