@@ -32,32 +32,51 @@ __device__ __forceinline__ float key_value(uint64_t key) {
   return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord);
 }
 
-// the k best of one token's logits v[c] (expert lane + 64 c, c < 4; experts past
-// E hold key 0, below every real key); writes ids/gates from lanes < k
-__device__ __forceinline__ void select_topk(const float (&v)[4], int E, int k, int32_t* ids, float* gates) {
+// the k best of the logits of R tokens at once (R independent selections, so
+// their wave reductions overlap): v[r][c] is the logit of expert lane + 64 c
+// (c < 4; experts past E hold key 0, below every real key).  Writes ids/gates
+// of token r from lanes < k when valid[r].
+template <int R>
+__device__ __forceinline__ void select_topk(const float (&v)[R][4], const bool (&valid)[R], int E, int k,
+                                            int32_t* const (&ids)[R], float* const (&gates)[R]) {
   const int lane = threadIdx.x & 63;
-  uint64_t key[4];
+  uint64_t key[R][4];
 #pragma unroll
-  for (int c = 0; c < 4; c++) key[c] = lane + 64 * c < E ? rank_key(v[c], lane + 64 * c) : 0;
-  float myv = 0.f;
-  int myi = 0;
-  for (int j = 0; j < k; j++) {
-    uint64_t best = umax64(umax64(key[0], key[1]), umax64(key[2], key[3]));
-    best = wave_max_u64(best);
-    const int e = (int)~(uint32_t)best;
-    if (lane == j) {
-      myv = key_value(best);
-      myi = e;
-    }
+  for (int r = 0; r < R; r++)
 #pragma unroll
-    for (int c = 0; c < 4; c++) key[c] = lane + 64 * c == e ? 0 : key[c];
+    for (int c = 0; c < 4; c++) key[r][c] = lane + 64 * c < E ? rank_key(v[r][c], lane + 64 * c) : 0;
+  float myv[R];
+  int myi[R];
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+    myv[r] = 0.f;
+    myi[r] = 0;
   }
-  const float m0 = __shfl(myv, 0, 64);
-  float den = 0.f;
-  for (int j = 0; j < k; j++) den += expf(__shfl(myv, j, 64) - m0);
-  if (lane < k) {
-    ids[lane] = myi;
-    gates[lane] = expf(myv - m0) / den;
+  for (int j = 0; j < k; j++) {
+    uint64_t best[R];
+#pragma unroll
+    for (int r = 0; r < R; r++) best[r] = wave_max_u64(umax64(umax64(key[r][0], key[r][1]), umax64(key[r][2], key[r][3])));
+#pragma unroll
+    for (int r = 0; r < R; r++) {
+      const int e = (int)~(uint32_t)best[r];
+      if (lane == j) {
+        myv[r] = key_value(best[r]);
+        myi[r] = e;
+      }
+#pragma unroll
+      for (int c = 0; c < 4; c++) key[r][c] = lane + 64 * c == e ? 0 : key[r][c];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+    // lane j < k holds the j-th selected logit: read them as scalars
+    const float m0 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(myv[r]), 0));
+    float den = 0.f;
+    for (int j = 0; j < k; j++) den += expf(__uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(myv[r]), j)) - m0);
+    if (valid[r] && lane < k) {
+      ids[r][lane] = myi[r];
+      gates[r][lane] = expf(myv[r] - m0) / den;
+    }
   }
 }
 
@@ -66,7 +85,7 @@ __global__ __launch_bounds__(64) void topk_k(float* __restrict__ logits, int nsp
   const int lane = threadIdx.x;
   const int row = blockIdx.x;
   const size_t stride = (size_t)rows * E;
-  float v[4];
+  float v[1][4];
 #pragma unroll
   for (int c = 0; c < 4; c++) {
     const int e = lane + 64 * c;
@@ -74,14 +93,18 @@ __global__ __launch_bounds__(64) void topk_k(float* __restrict__ logits, int nsp
     // all partials in flight at once, then added in split order
     float p[ROUTER_MAX_SPLIT];
 #pragma unroll
-    for (int sp = 0; sp < ROUTER_MAX_SPLIT; sp++) p[sp] = sp < nsplit ? logits[sp * stride + o] : 0.f;
+    for (int sp = 0; sp < ROUTER_MAX_SPLIT; sp++)   // splits past nsplit re-read split 0 (not added): no branches
+      p[sp] = logits[(sp < nsplit ? sp : 0) * stride + o];
     float x = p[0];
 #pragma unroll
     for (int sp = 1; sp < ROUTER_MAX_SPLIT; sp++) x = sp < nsplit ? x + p[sp] : x;
     if (e < E && nsplit > 1) logits[o] = x;   // the logits routing used
-    v[c] = x != x ? -INFINITY : x;  // a NaN logit ranks with -inf (ids stay in range)
+    v[0][c] = x != x ? -INFINITY : x;  // a NaN logit ranks with -inf (ids stay in range)
   }
-  select_topk(v, E, k, ids + (size_t)row * k, gates + (size_t)row * k);
+  const bool valid[1] = {true};
+  int32_t* const idp[1] = {ids + (size_t)row * k};
+  float* const gp[1] = {gates + (size_t)row * k};
+  select_topk<1>(v, valid, E, k, idp, gp);
 }
 
 // ---------------------------------------------------------------------------
@@ -103,9 +126,13 @@ __global__ __launch_bounds__(256) void plan_k(const int32_t* __restrict__ ids, i
   const int tid = threadIdx.x, e = blockIdx.x;
   // thread tid reads the k ids of rows tid, tid + 256, ...: all k loads of a
   // row are issued together (k <= 8), and the listing below reads the same rows
-  auto load_row = [&](int r, int (&v)[8]) {
+  auto load_row = [&](int r, int (&v)[8]) {   // clamped loads, then a select: no branches
+    const bool rok = r < rows;
+    const size_t base = (size_t)(rok ? r : 0) * k;
 #pragma unroll
-    for (int j = 0; j < 8; j++) v[j] = r < rows && j < k ? ids[(size_t)r * k + j] : -1;
+    for (int j = 0; j < 8; j++) v[j] = ids[base + (j < k ? j : 0)];
+#pragma unroll
+    for (int j = 0; j < 8; j++) v[j] = rok && j < k ? v[j] : -1;
   };
   hist[tid] = 0;
   __syncthreads();
@@ -172,64 +199,130 @@ __global__ __launch_bounds__(256) void plan_k(const int32_t* __restrict__ ids, i
 
 // ---------------------------------------------------------------------------
 // route_k (bf16): RMSNorm of x1, router logits and top-k in one kernel for a
-// tile of 16 tokens.  The normalised rows (rounded to bf16, also written out
-// as u2) stay in LDS as the A operand of the router MFMAs; the waves split the
-// experts in 16-column tiles (NT tiles each) and stream the packed W_r pieces
-// through an NB-deep register ring; the logits go to LDS and each wave ranks 4
-// of the tokens with the selection of topk_k.
+// tile of 16 tokens, 8 waves.  The normalised rows (rounded to bf16, also
+// written out as u2) stay in LDS (rows padded to a 32 mod 64 byte stride) as
+// the A operand of the router MFMAs.  Wave w takes the expert column tiles of
+// group w % 4 (NT 16-column tiles) over half w / 4 of the contraction and
+// streams the packed W_r pieces through an NB-deep register ring; the two
+// halves are added in LDS in a fixed order; each wave then ranks 2 tokens
+// with the selection of topk_k.
 // ---------------------------------------------------------------------------
+constexpr int ROUTE_THREADS = 512;
+
 template <int NT, int NB>
-__global__ __launch_bounds__(256) void route_k(RouteArgs a) {
+__global__ __launch_bounds__(ROUTE_THREADS) void route_k(RouteArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   const int D = a.D, E = a.E;
-  const int LDA = D + 8;                                          // padded A row (elements)
+  const int LDA = D + 16;                                         // padded A row (elements)
+  const int nct = (E + 15) / 16;
   uint16_t* sa = reinterpret_cast<uint16_t*>(smem_raw);          // [16][LDA]
   float* sl = reinterpret_cast<float*>(smem_raw + (size_t)16 * LDA * 2);   // [16][E]
+  float* red = sl + 16 * E;                                       // [2][nct][16][16]
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
   const int row0 = blockIdx.x * 16;
   const int nrows = min(16, a.rows - row0);
 
-  // ---- RMSNorm (same arithmetic as rmsnorm_k): wave w takes rows w, w+4, .. ----
-  for (int rr = w; rr < 16; rr += 4) {
-    uint16_t* dst = sa + rr * LDA;
-    if (rr >= nrows) {
-      for (int d = lane * 8; d < D; d += 512) *reinterpret_cast<uint4*>(dst + d) = make_uint4(0, 0, 0, 0);
-      continue;
-    }
-    const uint16_t* src = (const uint16_t*)a.x1 + (size_t)(row0 + rr) * D;
-    float ss = 0.f;
-    for (int d = lane * 8; d < D; d += 512) {
-      float v[8];
-      ld8(src + d, v);
+  // ---- RMSNorm (same arithmetic as rmsnorm_k): wave w takes rows w, w + 8 ----
+  if (D % 512 == 0 && D <= 2048) {
+    // all loads of the wave's rows in flight at once; the values stay in
+    // registers for the scaling pass
+    const int nc = D / 512;
+    u32x4 raw[2][4];
 #pragma unroll
-      for (int i = 0; i < 8; i++) ss += v[i] * v[i];
-    }
-    ss = wave_sum(ss);
-    const float r = rsqrtf(ss / (float)D + a.eps);
-    for (int d = lane * 8; d < D; d += 512) {
-      float v[8];
-      ld8(src + d, v);
+    for (int j = 0; j < 2; j++) {
+      const int rr = w + 8 * j;
+      const uint16_t* src = (const uint16_t*)a.x1 + (size_t)(row0 + (rr < nrows ? rr : 0)) * D;
 #pragma unroll
-      for (int i = 0; i < 8; i++) v[i] = v[i] * r * a.g2[d + i];
-      st8(dst + d, v);
-      st8((uint16_t*)a.u2 + (size_t)(row0 + rr) * D + d, v);
+      for (int i = 0; i < 4; i++)   // chunks past the row re-read chunk 0 (never used): no branches
+        raw[j][i] = *reinterpret_cast<const u32x4*>(src + lane * 8 + 512 * (i < nc ? i : 0));
+    }
+    float gv[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const float4* gp4 = reinterpret_cast<const float4*>(a.g2 + lane * 8 + 512 * (i < nc ? i : 0));
+      const float4 g0 = gp4[0], g1 = gp4[1];
+      gv[i][0] = g0.x; gv[i][1] = g0.y; gv[i][2] = g0.z; gv[i][3] = g0.w;
+      gv[i][4] = g1.x; gv[i][5] = g1.y; gv[i][6] = g1.z; gv[i][7] = g1.w;
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every load above is issued before the first use
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      const int rr = w + 8 * j;
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const float lo = __uint_as_float(raw[j][i][q] << 16), hi = __uint_as_float(raw[j][i][q] & 0xffff0000u);
+          ss += i < nc ? lo * lo : 0.f;
+          ss += i < nc ? hi * hi : 0.f;
+        }
+      ss = row16_sum(ss);
+      ss += lane_xor16(ss);
+      ss += lane_xor32(ss);
+      const float r = rsqrtf(ss / (float)D + a.eps);
+      uint16_t* dst = sa + rr * LDA;
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        if (i >= nc) continue;
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          v[2 * q] = __uint_as_float(raw[j][i][q] << 16) * r * gv[i][2 * q];
+          v[2 * q + 1] = __uint_as_float(raw[j][i][q] & 0xffff0000u) * r * gv[i][2 * q + 1];
+        }
+        if (rr >= nrows) {
+#pragma unroll
+          for (int q = 0; q < 8; q++) v[q] = 0.f;
+        }
+        st8(dst + lane * 8 + 512 * i, v);
+        if (rr < nrows) st8((uint16_t*)a.u2 + (size_t)(row0 + rr) * D + lane * 8 + 512 * i, v);
+      }
+    }
+  } else {
+    for (int rr = w; rr < 16; rr += 8) {
+      uint16_t* dst = sa + rr * LDA;
+      if (rr >= nrows) {
+        for (int d = lane * 8; d < D; d += 512) *reinterpret_cast<uint4*>(dst + d) = make_uint4(0, 0, 0, 0);
+        continue;
+      }
+      const uint16_t* src = (const uint16_t*)a.x1 + (size_t)(row0 + rr) * D;
+      float ss = 0.f;
+      for (int d = lane * 8; d < D; d += 512) {
+        float v[8];
+        ld8(src + d, v);
+#pragma unroll
+        for (int i = 0; i < 8; i++) ss += v[i] * v[i];
+      }
+      ss = wave_sum(ss);
+      const float r = rsqrtf(ss / (float)D + a.eps);
+      for (int d = lane * 8; d < D; d += 512) {
+        float v[8];
+        ld8(src + d, v);
+#pragma unroll
+        for (int i = 0; i < 8; i++) v[i] = v[i] * r * a.g2[d + i];
+        st8(dst + d, v);
+        st8((uint16_t*)a.u2 + (size_t)(row0 + rr) * D + d, v);
+      }
     }
   }
   __syncthreads();
 
   // ---- router logits ----
   if (a.inject) {
-    for (int i = threadIdx.x; i < 16 * E; i += 256) {
+    for (int i = threadIdx.x; i < 16 * E; i += ROUTE_THREADS) {
       const int rr = i / E, e = i % E;
       sl[i] = rr < nrows ? a.inject[(size_t)(row0 + rr) * E + e] : 0.f;
     }
   } else {
-    const int nct = (E + 15) / 16;
-    const int nkb = D / 64;   // packed pieces (128 bytes of bf16) per router row
+    const int cgp = w & 3, kh = w >> 2;
+    const int nkb = D / 64;           // packed pieces (128 bytes of bf16) per router row
+    const int per = nkb / 2;          // pieces of this wave's contraction half (a multiple of NB)
+    const int c0 = kh * per;
     const char* wg[NT];
 #pragma unroll
     for (int t = 0; t < NT; t++) {
-      const int ct = w + 4 * t;
+      const int ct = cgp + 4 * t;
       wg[t] = (const char*)a.wr + (size_t)(ct < nct ? ct : 0) * nkb * 2048 + 16 * lane;
     }
     f32x4_t acc[NT];
@@ -257,58 +350,74 @@ __global__ __launch_bounds__(256) void route_k(RouteArgs a) {
       }
     };
 #pragma unroll
-    for (int b = 0; b < NB; b++) load(b, b);
-    int c0 = 0;
-    for (; c0 + NB < nkb; c0 += NB) {   // nkb is a multiple of NB
+    for (int b = 0; b < NB; b++) load(b, c0 + b);
+    int i0 = 0;
+    for (; i0 + NB < per; i0 += NB) {
 #pragma unroll
       for (int b = 0; b < NB; b++) {
         __builtin_amdgcn_sched_barrier(0);
-        comp(b, c0 + b);
+        comp(b, c0 + i0 + b);
         __builtin_amdgcn_sched_barrier(0);
-        load(b, c0 + NB + b);
+        load(b, c0 + i0 + NB + b);
       }
     }
 #pragma unroll
     for (int b = 0; b < NB; b++) {
       __builtin_amdgcn_sched_barrier(0);
-      comp(b, c0 + b);
+      comp(b, c0 + i0 + b);
     }
 #pragma unroll
     for (int t = 0; t < NT; t++) {
-      const int e = (w + 4 * t) * 16 + l16;
+      const int ct = cgp + 4 * t;
+      if (ct < nct)
 #pragma unroll
-      for (int i = 0; i < 4; i++)
-        if (w + 4 * t < nct && e < E) sl[(4 * g + i) * E + e] = acc[t][i];
+        for (int i = 0; i < 4; i++) red[((kh * nct + ct) * 16 + 4 * g + i) * 16 + l16] = acc[t][i];
+    }
+    __syncthreads();
+    // the two contraction halves, added in a fixed order
+    for (int i = threadIdx.x; i < 16 * E; i += ROUTE_THREADS) {
+      const int rr = i / E, e = i % E, ct = e >> 4, col = e & 15;
+      sl[i] = red[(ct * 16 + rr) * 16 + col] + red[((nct + ct) * 16 + rr) * 16 + col];
     }
   }
   __syncthreads();
   if (a.logits)
-    for (int i = threadIdx.x; i < nrows * E; i += 256) a.logits[(size_t)row0 * E + i] = sl[i];
+    for (int i = threadIdx.x; i < nrows * E; i += ROUTE_THREADS) a.logits[(size_t)row0 * E + i] = sl[i];
 
-  // ---- top-k: wave w ranks rows w, w+4, w+8, w+12 (same selection as topk_k) ----
-  for (int rr = w; rr < nrows; rr += 4) {
-    float v[4];
+  // ---- top-k: wave w ranks rows w and w + 8 together (the selection of topk_k) ----
+  float v[2][4];
+  bool valid[2];
+  int32_t* idp[2];
+  float* gp[2];
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    const int rr = w + 8 * j;
+    valid[j] = rr < nrows;
+    idp[j] = a.ids + (size_t)(row0 + (valid[j] ? rr : 0)) * a.k;
+    gp[j] = a.gates + (size_t)(row0 + (valid[j] ? rr : 0)) * a.k;
 #pragma unroll
     for (int c = 0; c < 4; c++) {
       const int e = lane + 64 * c;
       const float x = e < E ? sl[rr * E + e] : -INFINITY;
-      v[c] = x != x ? -INFINITY : x;
+      v[j][c] = x != x ? -INFINITY : x;
     }
-    select_topk(v, E, a.k, a.ids + (size_t)(row0 + rr) * a.k, a.gates + (size_t)(row0 + rr) * a.k);
   }
+  select_topk<2>(v, valid, E, a.k, idp, gp);
 }
 
 size_t route_smem_bytes(int D, int E) {
-  return (size_t)16 * (D + 8) * 2 + (size_t)16 * E * 4;
+  const size_t nct = (size_t)(E + 15) / 16;
+  return (size_t)16 * (D + 16) * 2 + (size_t)16 * E * 4 + 2 * nct * 256 * 4;
 }
 
 template <int NT>
 static void launch_route_nt(const RouteArgs& a, size_t smem, hipStream_t s) {
   const int blocks = (a.rows + 15) / 16;
-  const int nkb = a.D / 64;
-  if (nkb % 8 == 0) route_k<NT, 8><<<blocks, 256, smem, s>>>(a);
-  else if (nkb % 4 == 0) route_k<NT, 4><<<blocks, 256, smem, s>>>(a);
-  else route_k<NT, 2><<<blocks, 256, smem, s>>>(a);
+  const int per = a.D / 128;   // pieces per contraction half
+  if (NT < 4 && per % 8 == 0) route_k<NT, 8><<<blocks, ROUTE_THREADS, smem, s>>>(a);   // 4 tiles x 8 spills
+  else if (per % 4 == 0) route_k<NT, 4><<<blocks, ROUTE_THREADS, smem, s>>>(a);
+  else if (per % 2 == 0) route_k<NT, 2><<<blocks, ROUTE_THREADS, smem, s>>>(a);
+  else route_k<NT, 1><<<blocks, ROUTE_THREADS, smem, s>>>(a);
 }
 
 // bf16 activations only; false when the tile does not fit in LDS
@@ -320,9 +429,10 @@ bool launch_route(int act, const RouteArgs& a, hipStream_t s) {
   // allow more than the default 64 KiB of dynamic LDS (gfx950 has 160 KiB per CU)
   static const bool attr_set = [] {
     bool ok = true;
-    const void* fns[] = {(const void*)&route_k<1, 2>, (const void*)&route_k<1, 4>, (const void*)&route_k<1, 8>,
-                         (const void*)&route_k<2, 2>, (const void*)&route_k<2, 4>, (const void*)&route_k<2, 8>,
-                         (const void*)&route_k<4, 2>, (const void*)&route_k<4, 4>, (const void*)&route_k<4, 8>};
+    const void* fns[] = {(const void*)&route_k<1, 1>, (const void*)&route_k<1, 2>, (const void*)&route_k<1, 4>,
+                         (const void*)&route_k<1, 8>, (const void*)&route_k<2, 1>, (const void*)&route_k<2, 2>,
+                         (const void*)&route_k<2, 4>, (const void*)&route_k<2, 8>, (const void*)&route_k<4, 1>,
+                         (const void*)&route_k<4, 2>, (const void*)&route_k<4, 4>};
     for (const void* f : fns)
       ok = ok && hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMaxSmem) == hipSuccess;
     return ok;
