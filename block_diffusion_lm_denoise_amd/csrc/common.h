@@ -170,16 +170,6 @@ __device__ __forceinline__ int lane_xor32(int x) { return (int)lane_xor32((uint3
 // ---------------------------------------------------------------------------
 // wave / block reductions (wave64)
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
 
 // reductions over the 16 lanes of a DPP row (lanes 16j .. 16j+15) with DPP
 // moves: two quad permutations, then the half-row and row mirrors.  Max and
@@ -211,6 +201,19 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += dpp_f<DPP_QUAD_2301>(v);
   v += dpp_f<DPP_ROW_HALF_MIRROR>(v);
   return v + dpp_f<DPP_ROW_MIRROR>(v);
+}
+
+// sums / maxima over the wave (every lane gets the result): DPP within the
+// 16-lane rows, then the permlane swaps across rows and wave halves
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  v += lane_xor16(v);
+  return v + lane_xor32(v);
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  v = fmax_sel(v, lane_xor16(v));
+  return fmax_sel(v, lane_xor32(v));
 }
 
 // max of a 64-bit value over the wave (every lane gets it): DPP within the

@@ -8,7 +8,10 @@
 namespace dg {
 
 // Row kernels: one block of 256 threads per token row, 8 consecutive elements
-// per thread and step (D is a multiple of 128).
+// per thread and step (D is a multiple of 128).  A thread's chunks stay in
+// registers between the sum of squares and the scaling (rows of up to
+// 256 * 8 * ROWC elements); all loads of a phase are issued together.
+constexpr int ROWC = 2;
 
 // x[row] = emb[tok[row]] (copied), u[row] = round(x * rsqrt(mean(x^2)+eps) * g)
 // (token ids outside [0, V) are clamped into range rather than read out of bounds)
@@ -22,22 +25,48 @@ __global__ __launch_bounds__(256) void embed_norm_k(const int32_t* __restrict__ 
   const size_t row = blockIdx.x;
   const int tk = min(max(tok[row], 0), V - 1);
   const TA* src = emb + (size_t)tk * D;
+  float v[ROWC][8], gv[ROWC][8];
   float ss = 0.f;
-  for (int c = threadIdx.x * 8; c < D; c += 2048) {
-    float v[8];
-    ld8(src + c, v);
-    st8(x + row * D + c, v);
 #pragma unroll
-    for (int i = 0; i < 8; i++) ss += v[i] * v[i];
+  for (int q = 0; q < ROWC; q++) {
+    const int c = threadIdx.x * 8 + 2048 * q, cc = c < D ? c : 0;   // clamped: no branch per load
+    ld8(src + cc, v[q]);
+    ld8(g + cc, gv[q]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < ROWC; q++) {
+    const int c = threadIdx.x * 8 + 2048 * q;
+    if (c < D) {
+      st8(x + row * D + c, v[q]);
+#pragma unroll
+      for (int i = 0; i < 8; i++) ss += v[q][i] * v[q][i];
+    }
+  }
+  for (int c = threadIdx.x * 8 + 2048 * ROWC; c < D; c += 2048) {   // longer rows
+    float w[8];
+    ld8(src + c, w);
+    st8(x + row * D + c, w);
+#pragma unroll
+    for (int i = 0; i < 8; i++) ss += w[i] * w[i];
   }
   ss = block_sum256(ss, red);
   const float r = rsqrtf(ss / (float)D + eps);
-  for (int c = threadIdx.x * 8; c < D; c += 2048) {
-    float v[8];
-    ld8(src + c, v);
 #pragma unroll
-    for (int i = 0; i < 8; i++) v[i] = v[i] * r * g[c + i];
-    st8(u + row * D + c, v);
+  for (int q = 0; q < ROWC; q++) {
+    const int c = threadIdx.x * 8 + 2048 * q;
+    if (c < D) {
+#pragma unroll
+      for (int i = 0; i < 8; i++) v[q][i] = v[q][i] * r * gv[q][i];
+      st8(u + row * D + c, v[q]);
+    }
+  }
+  for (int c = threadIdx.x * 8 + 2048 * ROWC; c < D; c += 2048) {
+    float w[8];
+    ld8(src + c, w);
+#pragma unroll
+    for (int i = 0; i < 8; i++) w[i] = w[i] * r * g[c + i];
+    st8(u + row * D + c, w);
   }
 }
 
@@ -46,25 +75,49 @@ __global__ __launch_bounds__(256) void rmsnorm_k(const TA* __restrict__ x, const
                                                  int D, float eps, TA* __restrict__ u) {
   __shared__ float red[4];
   const size_t row = blockIdx.x;
+  float v[ROWC][8], gv[ROWC][8];
   float ss = 0.f;
-  for (int c = threadIdx.x * 8; c < D; c += 2048) {
-    float v[8];
-    ld8(x + row * D + c, v);
 #pragma unroll
-    for (int i = 0; i < 8; i++) ss += v[i] * v[i];
+  for (int q = 0; q < ROWC; q++) {
+    const int c = threadIdx.x * 8 + 2048 * q, cc = c < D ? c : 0;
+    ld8(x + row * D + cc, v[q]);
+    ld8(g + cc, gv[q]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < ROWC; q++)
+    if (threadIdx.x * 8 + 2048 * q < D)
+#pragma unroll
+      for (int i = 0; i < 8; i++) ss += v[q][i] * v[q][i];
+  for (int c = threadIdx.x * 8 + 2048 * ROWC; c < D; c += 2048) {
+    float w[8];
+    ld8(x + row * D + c, w);
+#pragma unroll
+    for (int i = 0; i < 8; i++) ss += w[i] * w[i];
   }
   ss = block_sum256(ss, red);
   const float r = rsqrtf(ss / (float)D + eps);
-  for (int c = threadIdx.x * 8; c < D; c += 2048) {
-    float v[8];
-    ld8(x + row * D + c, v);
 #pragma unroll
-    for (int i = 0; i < 8; i++) v[i] = v[i] * r * g[c + i];
-    st8(u + row * D + c, v);
+  for (int q = 0; q < ROWC; q++) {
+    const int c = threadIdx.x * 8 + 2048 * q;
+    if (c < D) {
+#pragma unroll
+      for (int i = 0; i < 8; i++) v[q][i] = v[q][i] * r * gv[q][i];
+      st8(u + row * D + c, v[q]);
+    }
+  }
+  for (int c = threadIdx.x * 8 + 2048 * ROWC; c < D; c += 2048) {
+    float w[8];
+    ld8(x + row * D + c, w);
+#pragma unroll
+    for (int i = 0; i < 8; i++) w[i] = w[i] * r * g[c + i];
+    st8(u + row * D + c, w);
   }
 }
 
-// x = round(x1 + sum_j g_j y_j) in slot order j; u = round(rmsnorm(x) * gnext)
+// x = round(x1 + sum_j g_j y_j) in slot order j; u = round(rmsnorm(x) * gnext).
+// The k gates and slot indices of the row are uniform loads; all k expert rows
+// of a chunk are loaded before they are added (k <= 8).
 template <typename TA>
 __global__ __launch_bounds__(256) void combine_norm_k(const TA* __restrict__ x1,
                                                       const TA* __restrict__ Y,
@@ -73,36 +126,70 @@ __global__ __launch_bounds__(256) void combine_norm_k(const TA* __restrict__ x1,
                                                       const float* __restrict__ gnext, float eps,
                                                       TA* __restrict__ x, TA* __restrict__ u) {
   __shared__ float red[4];
-  __shared__ float gs[8];
-  __shared__ int32_t rs[8];
   const size_t row = blockIdx.x;
-  if (threadIdx.x < k) {
-    gs[threadIdx.x] = gates[row * k + threadIdx.x];
-    rs[threadIdx.x] = inv[row * k + threadIdx.x];
+  float gs[8];
+  int32_t rs[8];
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const int jj = j < k ? j : 0;
+    gs[j] = gates[row * k + jj];
+    rs[j] = inv[row * k + jj];
   }
-  __syncthreads();
+  float acc[ROWC][8], gv[ROWC][8];
   float ss = 0.f;
-  for (int c = threadIdx.x * 8; c < D; c += 2048) {
-    float acc[8], mix[8], y[8];
-    ld8(x1 + row * D + c, acc);
+#pragma unroll
+  for (int q = 0; q < ROWC; q++) {
+    const int c = threadIdx.x * 8 + 2048 * q, cc = c < D ? c : 0;
+    float y[8][8];
+    ld8(x1 + row * D + cc, acc[q]);
+    ld8(gnext + cc, gv[q]);
+#pragma unroll
+    for (int j = 0; j < 8; j++) ld8(Y + (size_t)rs[j] * D + cc, y[j]);
+    __builtin_amdgcn_sched_barrier(0);   // every load above is issued before the first use
+    float mix[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) mix[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; j++)   // slots past k select the unchanged sum (no branch)
+#pragma unroll
+      for (int i = 0; i < 8; i++) mix[i] = j < k ? mix[i] + gs[j] * y[j][i] : mix[i];
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc[q][i] = rnd(acc[q][i] + mix[i], x);
+    if (c < D) {
+#pragma unroll
+      for (int i = 0; i < 8; i++) ss += acc[q][i] * acc[q][i];
+      st8(x + row * D + c, acc[q]);
+    }
+  }
+  for (int c = threadIdx.x * 8 + 2048 * ROWC; c < D; c += 2048) {   // longer rows
+    float a2[8], mix[8], y[8];
+    ld8(x1 + row * D + c, a2);
 #pragma unroll
     for (int i = 0; i < 8; i++) mix[i] = 0.f;
     for (int j = 0; j < k; j++) {
       ld8(Y + (size_t)rs[j] * D + c, y);
-      const float gj = gs[j];
 #pragma unroll
-      for (int i = 0; i < 8; i++) mix[i] += gj * y[i];
+      for (int i = 0; i < 8; i++) mix[i] += gs[j] * y[i];
     }
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-      acc[i] = rnd(acc[i] + mix[i], x);
-      ss += acc[i] * acc[i];
+      a2[i] = rnd(a2[i] + mix[i], x);
+      ss += a2[i] * a2[i];
     }
-    st8(x + row * D + c, acc);
+    st8(x + row * D + c, a2);
   }
   ss = block_sum256(ss, red);
   const float r = rsqrtf(ss / (float)D + eps);
-  for (int c = threadIdx.x * 8; c < D; c += 2048) {
+#pragma unroll
+  for (int q = 0; q < ROWC; q++) {
+    const int c = threadIdx.x * 8 + 2048 * q;
+    if (c < D) {
+#pragma unroll
+      for (int i = 0; i < 8; i++) acc[q][i] = acc[q][i] * r * gv[q][i];
+      st8(u + row * D + c, acc[q]);
+    }
+  }
+  for (int c = threadIdx.x * 8 + 2048 * ROWC; c < D; c += 2048) {
     float v[8];
     ld8(x + row * D + c, v);
 #pragma unroll
