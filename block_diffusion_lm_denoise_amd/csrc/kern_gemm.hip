@@ -477,10 +477,10 @@ __device__ __forceinline__ void mrg_bf(float& m, int& i, float& s, float m2, int
   i = id;
 }
 
-template <int P, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void lmhead_direct_k(HeadArgs a) {
+template <int P, int NW, int BN, int MINB>
+__global__ __launch_bounds__(NW * 64, MINB) void lmhead_direct_k(HeadArgs a) {
   constexpr int NT = NW * 64;                 // threads
-  constexpr int BM = 128, BN = 256, BK = 64, LDK = 80, RT = 8;   // 160-byte LDS rows: conflict-free fragment reads
+  constexpr int BM = 128, BK = 64, LDK = 80, RT = 8;   // 160-byte LDS rows: conflict-free fragment reads
   constexpr int WC = BN / NW, CT = WC / 16;   // vocabulary columns per wave
   constexpr int A_LD = BM * BK * 2 / 16 / NT;   // 16-byte A chunks staged per thread
   constexpr int A_RSTEP = NT / 8;             // rows between a thread's chunks
@@ -696,13 +696,20 @@ void launch_down_lds(int act, const void* H, const MoeW& w, const int4* tiles,
 #ifndef LMHEAD_NW
 #define LMHEAD_NW 8
 #endif
+#ifndef LMHEAD_BN
+#define LMHEAD_BN 256
+#endif
+#ifndef LMHEAD_MINB
+#define LMHEAD_MINB 1
+#endif
 
 int launch_lmhead(int act, const void* uf, int M, int D, const void* lm, int V, float* pmax,
                   int32_t* pidx, float* psum, float* logits, hipStream_t s) {
   if (act == ACT_BF16 && M > 64) {
-    const int nt = (V + 255) / 256;
+    const int nt = (V + LMHEAD_BN - 1) / LMHEAD_BN;
     HeadArgs a{uf, M, D, lm, V, pmax, pidx, psum, logits, nt, (M + 127) / 128};
-    lmhead_direct_k<LMHEAD_P, LMHEAD_NW><<<((nt + 7) / 8) * 8 * a.mtiles, LMHEAD_NW * 64, 0, s>>>(a);
+    lmhead_direct_k<LMHEAD_P, LMHEAD_NW, LMHEAD_BN, LMHEAD_MINB>
+        <<<((nt + 7) / 8) * 8 * a.mtiles, LMHEAD_NW * 64, 0, s>>>(a);
     return nt;
   }
   const int nt = (V + 127) / 128, bm = M > 64 ? 128 : 64;
