@@ -112,7 +112,12 @@ __device__ __forceinline__ void piece_mma(f32x4_t (&acc)[RT][4], const u32x4 (&w
     }
 }
 
-// weights are read once per row tile: nontemporal loads (streamed, not kept)
+// expert weights are read once per expert tile: nontemporal loads (streamed,
+// not kept); the dense projections' weights are shared by several row tiles
+// (and read again every pass), so they are loaded normally
+#ifndef STREAM_NT_DENSE
+#define STREAM_NT_DENSE 0
+#endif
 #ifndef STREAM_NT
 #define STREAM_NT 1
 #endif
@@ -227,7 +232,7 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
     for (int h = 0; h < 2; h++)
 #pragma unroll
       for (int ct = 0; ct < 4; ct++)
-        wr[ct][h] = STREAM_NT ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wtile[ct] + (size_t)c * 2048 + h * 1024))
+        wr[ct][h] = (GROUPED ? STREAM_NT : STREAM_NT_DENSE) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wtile[ct] + (size_t)c * 2048 + h * 1024))
                               : *reinterpret_cast<const u32x4*>(wtile[ct] + (size_t)c * 2048 + h * 1024);
 #pragma unroll
     for (int j = 0; j < NA; j++)
