@@ -601,43 +601,60 @@ __global__ __launch_bounds__(NW * 64, MINB) void lmhead_direct_k(HeadArgs a) {
       }
   }
   // epilogue: per token, (max, lowest argmax, sum exp) over this wave's WC
-  // columns: 4 CT in-lane values, then two exchanges between the 4 lanes
+  // columns: 4 CT in-lane values, then two exchanges between the 4 lanes.
+  // Each step runs over the RT row tiles together (independent chains, so the
+  // latency of one tile's dependent steps hides behind the others).
+  float lm[RT], m[RT], s[RT];
+  int li[RT], idx[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; rt++) {
-    float lm = -INFINITY;
-    int li = 0x7fffffff;
+    lm[rt] = -INFINITY;
+    li[rt] = 0x7fffffff;
 #pragma unroll
     for (int ct = 0; ct < CT; ct++)
 #pragma unroll
       for (int i = 0; i < 4; i++) {   // columns ascend: the first maximum is the lowest index
         const int n = n0 + WC * w + 16 * ct + 4 * g + i;
         const float v = n < a.V ? acc[rt][ct][i] : -INFINITY;
-        li = v > lm ? n : li;
-        lm = v > lm ? v : lm;
+        li[rt] = v > lm[rt] ? n : li[rt];
+        lm[rt] = v > lm[rt] ? v : lm[rt];
       }
-    float m = lm;
-    m = fmax_sel(m, lane_xor16(m));
-    m = fmax_sel(m, lane_xor32(m));
-    int idx = lm == m ? li : 0x7fffffff;
-    idx = min(idx, lane_xor16(idx));
-    idx = min(idx, lane_xor32(idx));
-    float s = 0.f;
+  }
+#pragma unroll
+  for (int rt = 0; rt < RT; rt++) m[rt] = fmax_sel(lm[rt], lane_xor16(lm[rt]));
+#pragma unroll
+  for (int rt = 0; rt < RT; rt++) m[rt] = fmax_sel(m[rt], lane_xor32(m[rt]));
+#pragma unroll
+  for (int rt = 0; rt < RT; rt++) {
+    idx[rt] = lm[rt] == m[rt] ? li[rt] : 0x7fffffff;
+    idx[rt] = min(idx[rt], lane_xor16(idx[rt]));
+  }
+#pragma unroll
+  for (int rt = 0; rt < RT; rt++) idx[rt] = min(idx[rt], lane_xor32(idx[rt]));
+#pragma unroll
+  for (int rt = 0; rt < RT; rt++) {
+    s[rt] = 0.f;
 #pragma unroll
     for (int ct = 0; ct < CT; ct++)
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int n = n0 + WC * w + 16 * ct + 4 * g + i;
-        const float e = __builtin_amdgcn_exp2f((acc[rt][ct][i] - m) * 1.4426950408889634f);
-        s += n < a.V ? e : 0.f;
+        const float e = __builtin_amdgcn_exp2f((acc[rt][ct][i] - m[rt]) * 1.4426950408889634f);
+        s[rt] += n < a.V ? e : 0.f;
       }
-    s = m == -INFINITY ? 0.f : s;
-    s += lane_xor16(s);
-    s += lane_xor32(s);
-    if (g == 0) {
+    s[rt] = m[rt] == -INFINITY ? 0.f : s[rt];
+  }
+#pragma unroll
+  for (int rt = 0; rt < RT; rt++) s[rt] += lane_xor16(s[rt]);
+#pragma unroll
+  for (int rt = 0; rt < RT; rt++) s[rt] += lane_xor32(s[rt]);
+  if (g == 0) {
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++) {
       const int rl = 16 * rt + l16;
-      xm[w][rl] = m;
-      xs[w][rl] = s;
-      xi[w][rl] = idx;
+      xm[w][rl] = m[rt];
+      xs[w][rl] = s[rt];
+      xi[w][rl] = idx[rt];
     }
   }
   __syncthreads();
