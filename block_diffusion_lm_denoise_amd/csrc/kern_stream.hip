@@ -162,18 +162,6 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
   const int nsp = MODE == SG_F32 && a.ksplit > 1 ? a.ksplit : 1;
   const int nch = nch_all / nsp, pbeg = split * nch;
 
-  // A row pointers of this lane (row l16 of each 16-row tile).  Rows past the
-  // tile read a valid row: an MFMA output row depends on its own A row only,
-  // and those rows are never stored, so the load path needs no branches or
-  // masks and the next piece's loads stay in flight during the MFMAs.
-  const TA* arow[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; rt++) {
-    const int r = rt * 16 + l16;
-    const int slot = row0 + (r < nrows ? r : 0);
-    const size_t src = MODE == SG_GATEUP ? (size_t)(a.perm[slot] / a.k) : (size_t)slot;
-    arow[rt] = (const TA*)a.A + src * K;
-  }
   // packed weight tiles of this wave's 4 column tiles: byte address of row
   // group rg, piece c, load h, this lane = base + (rg * nch_all + c) * 2048 + h * 1024 + 16 * lane
   const char* wtile[4];
@@ -227,18 +215,25 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
   // NB register buffers of one piece each: the loads of NB-1 later pieces are
   // in flight while a piece is multiplied
   u32x4 wbuf[NB][4][2], abuf[NB][RT][NA];
-  auto load = [&](u32x4(&wr)[4][2], u32x4(&ar)[RT][NA], int c) {
+  auto load_w = [&](u32x4(&wr)[4][2], int c) {
 #pragma unroll
     for (int h = 0; h < 2; h++)
 #pragma unroll
       for (int ct = 0; ct < 4; ct++)
         wr[ct][h] = (GROUPED ? STREAM_NT : STREAM_NT_DENSE) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wtile[ct] + (size_t)c * 2048 + h * 1024))
                               : *reinterpret_cast<const u32x4*>(wtile[ct] + (size_t)c * 2048 + h * 1024);
+  };
+  const TA* arow[RT];
+  auto load_a = [&](u32x4(&ar)[RT][NA], int c) {
 #pragma unroll
     for (int j = 0; j < NA; j++)
 #pragma unroll
       for (int rt = 0; rt < RT; rt++)
         ar[rt][j] = *reinterpret_cast<const u32x4*>(arow[rt] + c * PC::EP + PC::a_off(j, g));
+  };
+  auto load = [&](u32x4(&wr)[4][2], u32x4(&ar)[RT][NA], int c) {
+    load_w(wr, c);
+    load_a(ar, c);
   };
   auto comp = [&](u32x4(&wr)[4][2], u32x4(&ar)[RT][NA]) {
     piece_mma<RT>(acc, wr, ar, nrt, (TA*)nullptr, (TW*)nullptr);
@@ -263,8 +258,31 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
   const int nper = (per + NB - 1) / NB * NB;
   auto cidx = [&](int i) { const int c = kw + KW * i; return pbeg + (c < nch ? c : nch - 1); };
   auto cok = [&](int i) { return kw + KW * i < nch; };
+  // A rows of this lane (row l16 of each 16-row tile).  Rows past the tile
+  // read a valid row: an MFMA output row depends on its own A row only, and
+  // those rows are never stored, so the load path needs no branches or masks
+  // and the next piece's loads stay in flight during the MFMAs.  For the
+  // gate/up GEMM the rows come through the permutation: those loads are
+  // issued first and the first piece's weight loads right behind them, so
+  // the wait for the permutation (an in-order counter) does not hold back
+  // the weight stream.  Each buffer keeps its weight loads just ahead of its
+  // A loads: a piece's MFMAs then wait for that buffer only.
+  int src[RT];
 #pragma unroll
-  for (int b = 0; b < NB; b++) load(wbuf[b], abuf[b], cidx(b));
+  for (int rt = 0; rt < RT; rt++) {
+    const int r = rt * 16 + l16;
+    const int slot = row0 + (r < nrows ? r : 0);
+    src[rt] = MODE == SG_GATEUP ? a.perm[slot] : slot;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(wbuf[0], cidx(0));
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int rt = 0; rt < RT; rt++)
+    arow[rt] = (const TA*)a.A + (size_t)(MODE == SG_GATEUP ? src[rt] / a.k : src[rt]) * K;
+  load_a(abuf[0], cidx(0));
+#pragma unroll
+  for (int b = 1; b < NB; b++) load(wbuf[b], abuf[b], cidx(b));
   int ib = 0;
   for (; ib + NB < nper; ib += NB) {
 #pragma unroll
