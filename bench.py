@@ -4,7 +4,8 @@ Workload: one bf16 MoE layer (D 2048, 16 q / 8 kv heads x 128, 128 experts
 top-8, expert FFN 768, vocabulary 32768), a 1024-token cached prefix and a
 256-token canvas denoised in 8 passes.  One step is one whole canvas: noise
 initialisation, 8 x (denoising pass, expert coverage, re-noise between
-passes), then the causal append-prefill of the committed canvas; the cache
+passes; the last two run inside the pass's final kernel), then the causal
+append-prefill of the committed canvas; the cache
 length is reset afterwards so every step sees the same 1024-token prefix.
 
 Prints one JSON line:  value = canvas-token passes per second (B*N*S per
@@ -96,10 +97,10 @@ def main():
         dgpass.renoise(canvas, None, None, wl.tau, wl.seed, 0, pos0, cfg.V)
         for p in range(S):
             ev = None if events is None else events[p]
-            model.denoise_pass(kv, canvas, argmax, conf, ws, events=ev)
-            model.expert_coverage(ws, touched[p])
-            if p < S - 1:
-                dgpass.renoise(canvas, argmax, conf, wl.tau, wl.seed, p + 1, pos0, cfg.V)
+            # coverage and the re-noise for the next pass run in the pass's last kernel
+            nxt = dict(tau=wl.tau, seed=wl.seed, pass_tag=p + 1, pos0=pos0) if p < S - 1 else None
+            model.denoise_pass_next(kv, canvas, argmax, conf, ws, touched=touched[p], renoise=nxt,
+                                    events=ev)
         model.kv_prefill(kv, argmax, ws)   # append the committed canvas
 
     for _ in range(args.warmup):
@@ -167,7 +168,7 @@ def main():
         "config": {"workload": wl.name, "B": B, "canvas": N, "prefix": P, "passes": S,
                    "layers": cfg.L, "d_model": cfg.D, "experts": cfg.E, "top_k": cfg.k,
                    "expert_ffn": cfg.F, "vocab": cfg.V, "expert_dtype": cfg.expert,
-                   "step": "init noise + 8 x (pass, coverage, re-noise) + append prefill"},
+                   "step": "init noise + 8 x (pass + coverage + re-noise, fused tail) + append prefill"},
         "roofline": {"kernel": "moe gate/up grouped GEMM (" + GATEUP_KERNEL + ")", "bound": "hbm",
                      "achieved": achieved / 1e9, "peak": roofline.HBM_BYTES_PER_S / 1e9,
                      "unit": "GB/s", "frac": achieved / roofline.HBM_BYTES_PER_S,

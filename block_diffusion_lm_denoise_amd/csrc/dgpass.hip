@@ -396,9 +396,10 @@ dg_status dg_kv_prefill(const dg_model* m, dg_kv* kv, const int32_t* tokens, int
   return DG_OK;
 }
 
-dg_status dg_denoise_pass(const dg_model* m, const dg_kv* kv, const int32_t* canvas, int32_t B,
-                          int32_t N, int32_t* argmax, float* conf, const dg_taps* taps, void* ws,
-                          size_t ws_bytes, void* stream) {
+// one pass; nx carries the between-pass work its last kernel takes over
+static dg_status denoise(const dg_model* m, const dg_kv* kv, const int32_t* canvas, int32_t B,
+                         int32_t N, int32_t* argmax, float* conf, const dg_taps* taps, void* ws,
+                         size_t ws_bytes, void* stream, MergeNext nx) {
   if (!model_ok(m) || !kv || !kv->len || !canvas || !argmax || !conf || !ws) return DG_ERR_INVALID;
   if (B < 1 || B > DG_MAX_BATCH || N < 1) return DG_ERR_INVALID;
   const dg_config& cf = m->cfg;
@@ -444,9 +445,45 @@ dg_status dg_denoise_pass(const dg_model* m, const dg_kv* kv, const int32_t* can
                                    at<int32_t>(c, c.L.lpi), at<float>(c, c.L.lps),
                                    taps ? taps->logits : nullptr, s);
   if (taps) tap_copy(taps->uf, at<void>(c, c.L.u), (size_t)R * cf.D * a, s);
+  nx.counts = at<int32_t>(c, c.L.cov);
+  nx.L = cf.L;
+  nx.E = cf.E;
+  nx.rn.argmax = argmax;
+  nx.rn.conf = conf;
+  nx.rn.B = B;
+  nx.rn.N = N;
+  nx.rn.V = (uint32_t)cf.V;
   launch_lm_merge(at<float>(c, c.L.lpm), at<int32_t>(c, c.L.lpi), at<float>(c, c.L.lps), R, nparts,
-                  argmax, conf, s);
+                  argmax, conf, nx, s);
   return check_hip();
+}
+
+dg_status dg_denoise_pass(const dg_model* m, const dg_kv* kv, const int32_t* canvas, int32_t B,
+                          int32_t N, int32_t* argmax, float* conf, const dg_taps* taps, void* ws,
+                          size_t ws_bytes, void* stream) {
+  return denoise(m, kv, canvas, B, N, argmax, conf, taps, ws, ws_bytes, stream, MergeNext{});
+}
+
+dg_status dg_denoise_pass_next(const dg_model* m, const dg_kv* kv, int32_t* canvas, int32_t B,
+                               int32_t N, int32_t* argmax, float* conf, int32_t* touched,
+                               const dg_renoise_args* next, const dg_taps* taps, void* ws,
+                               size_t ws_bytes, void* stream) {
+  MergeNext nx{};
+  nx.touched = touched;
+  if (next) {
+    if (!next->pos0 || B < 1 || B > DG_MAX_BATCH) return DG_ERR_INVALID;
+    if (!canvas || canvas == argmax || (const void*)canvas == (const void*)conf) return DG_ERR_INVALID;
+    for (int b = 0; b < B; b++) {
+      if (next->pos0[b] < 0) return DG_ERR_INVALID;
+      nx.rn.pos0.v[b] = next->pos0[b];
+      nx.rn.req.v[b] = next->req_id ? next->req_id[b] : (uint32_t)b;
+    }
+    nx.rn.canvas = canvas;
+    nx.rn.tau = next->tau;
+    nx.rn.seed = next->seed;
+    nx.rn.tag = next->pass_tag;
+  }
+  return denoise(m, kv, canvas, B, N, argmax, conf, taps, ws, ws_bytes, stream, nx);
 }
 
 dg_status dg_renoise(int32_t* canvas, const int32_t* argmax, const float* conf, float tau,

@@ -222,39 +222,32 @@ __device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64
   }
 }
 
-struct RenoiseArgs {
-  int32_t* canvas;
-  const int32_t* argmax;
-  const float* conf;
-  float tau;
-  uint64_t seed;
-  uint32_t tag;
-  int B, N;
-  uint32_t V;
-  Lens pos0;
-  ReqIds req;
-};
+// the token of slot idx (request b, position i) after re-noise: argmax when
+// kept, else a uniform draw floor(r * V / 2^64) from word 0 of Philox4x64-10
+// with counter (pos0[b] + i, tag, req[b], 0) and key (seed, 0)
+__device__ __forceinline__ int32_t renoise_token(const RenoiseArgs& a, int b, int i, bool keep,
+                                                 int32_t am) {
+  uint64_t c[4] = {(uint64_t)(int64_t)(a.pos0.v[b] + i), (uint64_t)a.tag, (uint64_t)a.req.v[b], 0};
+  philox4x64_10(c, a.seed, 0);
+  const int32_t noise = (int32_t)__umul64hi(c[0], (uint64_t)a.V);
+  return keep ? am : noise;
+}
 
 __global__ __launch_bounds__(256) void renoise_k(RenoiseArgs a) {
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= a.B * a.N) return;
-  const int b = idx / a.N, i = idx % a.N;
   // confidence and argmax are loaded together (one memory round trip) and the
   // noise token is always drawn; the select keeps argmax where conf >= tau
   // (NaN compares false: noised)
   const bool keep = a.conf ? a.conf[idx] >= a.tau : false;
   const int32_t am = a.conf ? a.argmax[idx] : 0;
-  uint64_t c[4] = {(uint64_t)(int64_t)(a.pos0.v[b] + i), (uint64_t)a.tag, (uint64_t)a.req.v[b], 0};
-  philox4x64_10(c, a.seed, 0);
-  const int32_t noise = (int32_t)__umul64hi(c[0], (uint64_t)a.V);  // floor(r * V / 2^64)
-  a.canvas[idx] = keep ? am : noise;
+  a.canvas[idx] = renoise_token(a, idx / a.N, idx % a.N, keep, am);
 }
 
-__global__ __launch_bounds__(256) void coverage_k(const int32_t* __restrict__ counts, int E,
-                                                  int32_t* __restrict__ touched,
-                                                  int32_t* __restrict__ counts_out) {
-  __shared__ int red[4];
-  const int l = blockIdx.x;
+// one block per layer l: touched[l] = #{e : counts[l][e] > 0}
+__device__ __forceinline__ void coverage_block(const int32_t* __restrict__ counts, int E, int l,
+                                               int32_t* __restrict__ touched,
+                                               int32_t* __restrict__ counts_out, int* red) {
   int t = 0;
   for (int e = threadIdx.x; e < E; e += 256) {
     int c = counts[l * E + e];
@@ -267,6 +260,13 @@ __global__ __launch_bounds__(256) void coverage_k(const int32_t* __restrict__ co
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = t;
   __syncthreads();
   if (threadIdx.x == 0) touched[l] = red[0] + red[1] + red[2] + red[3];
+}
+
+__global__ __launch_bounds__(256) void coverage_k(const int32_t* __restrict__ counts, int E,
+                                                  int32_t* __restrict__ touched,
+                                                  int32_t* __restrict__ counts_out) {
+  __shared__ int red[4];
+  coverage_block(counts, E, blockIdx.x, touched, counts_out, red);
 }
 
 // dst[slot][c] = src[inv[slot]][c]
@@ -292,13 +292,21 @@ __device__ __forceinline__ void merge3(float& m, int& i, float& s, float m2, int
   }
 }
 
+// Blocks 0..rows-1 merge one row each; with nx.touched set, blocks rows..
+// rows+L-1 write the expert coverage of the pass, and with nx.rn.canvas set
+// each row's slot is re-noised for the next pass from the argmax and conf just
+// computed (the same values renoise_k would read back).
 __global__ __launch_bounds__(256) void lm_merge_k(const float* __restrict__ pmax,
                                                   const int32_t* __restrict__ pidx,
                                                   const float* __restrict__ psum, int ntiles,
-                                                  int32_t* __restrict__ argmax,
-                                                  float* __restrict__ conf) {
+                                                  int rows, int32_t* __restrict__ argmax,
+                                                  float* __restrict__ conf, MergeNext nx) {
   __shared__ float sm[4], ss[4];
   __shared__ int si[4];
+  if ((int)blockIdx.x >= rows) {
+    coverage_block(nx.counts, nx.E, blockIdx.x - rows, nx.touched, nullptr, si);
+    return;
+  }
   const size_t row = blockIdx.x;
   float m = -INFINITY, s = 0.f;
   int i = 0x7fffffff;
@@ -322,8 +330,13 @@ __global__ __launch_bounds__(256) void lm_merge_k(const float* __restrict__ pmax
     s = ss[0];
     i = si[0];
     for (int q = 1; q < 4; q++) merge3(m, i, s, sm[q], si[q], ss[q]);
+    const float cf = 1.f / s;
     argmax[row] = i;
-    conf[row] = 1.f / s;
+    conf[row] = cf;
+    if (nx.rn.canvas) {
+      const int b = (int)row / nx.rn.N, p = (int)row % nx.rn.N;
+      nx.rn.canvas[row] = renoise_token(nx.rn, b, p, cf >= nx.rn.tau, i);
+    }
   }
 }
 
@@ -401,8 +414,9 @@ void launch_unpermute(int act, const void* src, const int32_t* inv, int slots, i
 }
 
 void launch_lm_merge(const float* pmax, const int32_t* pidx, const float* psum, int rows,
-                     int ntiles, int32_t* argmax, float* conf, hipStream_t s) {
-  lm_merge_k<<<rows, 256, 0, s>>>(pmax, pidx, psum, ntiles, argmax, conf);
+                     int ntiles, int32_t* argmax, float* conf, const MergeNext& nx, hipStream_t s) {
+  lm_merge_k<<<rows + (nx.touched ? nx.L : 0), 256, 0, s>>>(pmax, pidx, psum, ntiles, rows, argmax,
+                                                            conf, nx);
 }
 
 void launch_pack(const void* src, void* dst, int rows, int rowbytes, hipStream_t s) {

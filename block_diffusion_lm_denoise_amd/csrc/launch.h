@@ -33,8 +33,30 @@ void launch_coverage(const int32_t* counts, int L, int E, int32_t* touched, int3
                      hipStream_t s);
 void launch_unpermute(int act, const void* src, const int32_t* inv, int slots, int C, void* dst,
                       hipStream_t s);
+// work a pass's last kernel can take over from the calls that follow it:
+// rn.canvas != nullptr re-noises the canvas for the next pass (argmax and
+// conf are this merge's outputs), touched != nullptr writes the expert
+// coverage from counts [L][E]
+struct RenoiseArgs {
+  int32_t* canvas;
+  const int32_t* argmax;
+  const float* conf;
+  float tau;
+  uint64_t seed;
+  uint32_t tag;
+  int B, N;
+  uint32_t V;
+  Lens pos0;
+  ReqIds req;
+};
+struct MergeNext {
+  RenoiseArgs rn;
+  const int32_t* counts;
+  int L, E;
+  int32_t* touched;
+};
 void launch_lm_merge(const float* pmax, const int32_t* pidx, const float* psum, int rows,
-                     int ntiles, int32_t* argmax, float* conf, hipStream_t s);
+                     int ntiles, int32_t* argmax, float* conf, const MergeNext& nx, hipStream_t s);
 
 // ---- MoE routing (kern_moe.hip) ----
 // logits: nsplit (<= ROUTER_MAX_SPLIT) partial [rows][E] arrays (consecutive);

@@ -62,8 +62,14 @@ class dg_taps(C.Structure):
                                                          ("ev_gateup", C.c_void_p)]
 
 
-EXPORTS = ("dg_model_init", "dg_workspace_bytes", "dg_kv_prefill", "dg_denoise_pass", "dg_renoise",
-           "dg_expert_coverage", "dg_packed_bytes", "dg_pack_weight", "dg_status_str")
+class dg_renoise_args(C.Structure):
+    _fields_ = [("tau", C.c_float), ("seed", C.c_uint64), ("pass_tag", C.c_uint32),
+                ("pos0", C.c_void_p), ("req_id", C.c_void_p)]
+
+
+EXPORTS = ("dg_model_init", "dg_workspace_bytes", "dg_kv_prefill", "dg_denoise_pass",
+           "dg_denoise_pass_next", "dg_renoise", "dg_expert_coverage", "dg_packed_bytes",
+           "dg_pack_weight", "dg_status_str")
 
 _lib = None
 
@@ -84,6 +90,8 @@ def lib():
         L.dg_kv_prefill.restype = i32
         L.dg_denoise_pass.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
         L.dg_denoise_pass.restype = i32
+        L.dg_denoise_pass_next.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.dg_denoise_pass_next.restype = i32
         L.dg_renoise.argtypes = [vp, vp, vp, C.c_float, C.c_uint64, C.c_uint32, vp, vp, i32, i32, i32,
                                  vp]
         L.dg_renoise.restype = i32
@@ -260,6 +268,32 @@ class Model:
                                    _stream(stream))
         del keep
         _check(st, "dg_denoise_pass")
+
+    def denoise_pass_next(self, kv: KVCache, canvas: torch.Tensor, argmax: torch.Tensor,
+                          conf: torch.Tensor, ws: torch.Tensor, touched=None, renoise=None, taps=None,
+                          inject_router=None, events=None, stream=None):
+        """A pass whose last kernel also writes the expert coverage (touched:
+        device [L] int32, or None) and, with renoise = dict(tau, seed,
+        pass_tag, pos0[, req_id]), re-noises canvas in place for the next pass."""
+        B, N = canvas.shape
+        s = kv.struct()
+        ts, keep = _taps_struct(taps, inject_router, events)
+        nx, arrs = None, None
+        if renoise is not None:
+            p0 = np.ascontiguousarray(renoise["pos0"], dtype=np.int32)
+            rq = renoise.get("req_id")
+            rq = None if rq is None else np.ascontiguousarray(rq, dtype=np.uint32)
+            arrs = (p0, rq)
+            nx = dg_renoise_args(float(renoise["tau"]), int(renoise["seed"]) & (2**64 - 1),
+                                 int(renoise["pass_tag"]) & 0xFFFFFFFF, p0.ctypes.data_as(C.c_void_p),
+                                 None if rq is None else rq.ctypes.data_as(C.c_void_p))
+        st = lib().dg_denoise_pass_next(C.byref(self._m), C.byref(s), canvas.data_ptr(), B, N,
+                                        argmax.data_ptr(), conf.data_ptr(), _ptr(touched),
+                                        None if nx is None else C.byref(nx),
+                                        None if ts is None else C.byref(ts), ws.data_ptr(), ws.numel(),
+                                        _stream(stream))
+        del keep, arrs
+        _check(st, "dg_denoise_pass_next")
 
     def expert_coverage(self, ws: torch.Tensor, touched: torch.Tensor, counts=None, stream=None):
         st = lib().dg_expert_coverage(C.byref(self._m), ws.data_ptr(), ws.numel(), touched.data_ptr(),

@@ -41,10 +41,11 @@ def generate(model: dgpass.Model, kv: dgpass.KVCache, prompt: torch.Tensor, n_ca
         pos0 = kv.lens.copy()
         dgpass.renoise(canvas, None, None, tau, seed, 0, pos0, cfg.V, stream=stream)
         for p in range(S):
-            model.denoise_pass(kv, canvas, argmax, conf, ws, stream=stream)
-            model.expert_coverage(ws, touched[c, p], stream=stream)
-            if p < S - 1:
-                dgpass.renoise(canvas, argmax, conf, tau, seed, p + 1, pos0, cfg.V, stream=stream)
+            # the pass's last kernel writes the coverage and, before every pass
+            # but the last, re-noises the canvas for the next one
+            nxt = dict(tau=tau, seed=seed, pass_tag=p + 1, pos0=pos0) if p < S - 1 else None
+            model.denoise_pass_next(kv, canvas, argmax, conf, ws, touched=touched[c, p], renoise=nxt,
+                                    stream=stream)
         committed = argmax.clone()
         model.kv_prefill(kv, committed, ws, stream=stream)
         out.append(committed)

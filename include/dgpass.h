@@ -195,6 +195,35 @@ dg_status dg_renoise(int32_t* canvas, const int32_t* argmax, const float* conf, 
                      uint64_t seed, uint32_t pass_tag, const int32_t* pos0,
                      const uint32_t* req_id, int32_t B, int32_t N, int32_t V, void* stream);
 
+/* Parameters of a re-noise, as the arguments of dg_renoise: pos0 host [B],
+ * req_id host [B] or NULL for b. */
+typedef struct dg_renoise_args {
+  float tau;
+  uint64_t seed;
+  uint32_t pass_tag;
+  const int32_t* pos0;
+  const uint32_t* req_id;
+} dg_renoise_args;
+
+/* A denoising pass (arguments and results as dg_denoise_pass) whose last
+ * kernel also does the work that follows a pass inside a canvas ("Uniform
+ * State Diffusion": every pass but the last re-noises the low-confidence
+ * slots; newsletter comment: the expert coverage per step), so a canvas of S
+ * passes launches no separate kernels for it:
+ *  - touched: device [L] int32, or NULL; receives what dg_expert_coverage
+ *    would write after this pass (the counts stay in the workspace as well);
+ *  - next: or NULL; the canvas (device [B][N], read by this pass) is then
+ *    re-noised in place from this pass's argmax and conf, with the same
+ *    tokens dg_renoise(canvas, argmax, conf, next->tau, next->seed,
+ *    next->pass_tag, next->pos0, next->req_id, B, N, V) gives after the pass.
+ * With both NULL this is dg_denoise_pass.  Errors: those of dg_denoise_pass;
+ * INVALID also for a null next->pos0, a negative next->pos0[b], or a canvas
+ * that aliases argmax or conf. */
+dg_status dg_denoise_pass_next(const dg_model* m, const dg_kv* kv, int32_t* canvas, int32_t B,
+                               int32_t N, int32_t* argmax, float* conf, int32_t* touched,
+                               const dg_renoise_args* next, const dg_taps* taps, void* ws,
+                               size_t ws_bytes, void* stream);
+
 /* Experts touched per layer by the last pass run with this workspace: device
  * touched [L] int32 = #{e : count[l][e] > 0} (the union over the batch), and
  * optionally device counts [L][E] int32. */

@@ -124,6 +124,22 @@ def test_calls_reject_bad_arguments_before_launching():
     assert L.dg_renoise(dev, None, None, 0.5, 1, 0, p0, None, 65, 4, 512, None) == -1
     assert L.dg_expert_coverage(C.byref(m), dev, 4, dev, None, None) == -4
     assert L.dg_expert_coverage(C.byref(m), dev, 1 << 20, None, None, None) == -1
+    # the pass with the between-pass work: same checks as the pass, plus its
+    # re-noise arguments
+    nxt = dgpass.dg_renoise_args(0.5, 1, 1, p0, None)
+    d2, d3 = C.c_void_p(0x6000), C.c_void_p(0x7000)
+    args = lambda cv, am, nx, wsb: (C.byref(m), C.byref(kv), cv, 2, 4, am, d3, dev, nx, None, dev, wsb,
+                                    None)
+    assert L.dg_denoise_pass_next(*args(dev, d2, C.byref(nxt), 16)) == -4
+    assert L.dg_denoise_pass_next(*args(dev, d2, None, 16)) == -4
+    assert L.dg_denoise_pass_next(*args(dev, dev, C.byref(nxt), need)) == -1   # canvas is argmax
+    assert L.dg_denoise_pass_next(*args(d3, d2, C.byref(nxt), need)) == -1     # canvas is conf
+    assert L.dg_denoise_pass_next(*args(None, d2, C.byref(nxt), need)) == -1
+    no_pos = dgpass.dg_renoise_args(0.5, 1, 1, None, None)
+    assert L.dg_denoise_pass_next(*args(dev, d2, C.byref(no_pos), need)) == -1
+    neg = np.array([0, -1], np.int32)
+    bad_pos = dgpass.dg_renoise_args(0.5, 1, 1, neg.ctypes.data_as(C.c_void_p), None)
+    assert L.dg_denoise_pass_next(*args(dev, d2, C.byref(bad_pos), need)) == -1
 
 
 def test_packed_bytes_pads_rows_and_requires_128_byte_rows():
