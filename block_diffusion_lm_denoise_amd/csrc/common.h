@@ -166,6 +166,39 @@ __device__ __forceinline__ float lane_xor16(float x) { return __uint_as_float(la
 __device__ __forceinline__ float lane_xor32(float x) { return __uint_as_float(lane_xor32(__float_as_uint(x))); }
 __device__ __forceinline__ int lane_xor16(int x) { return (int)lane_xor16((uint32_t)x); }
 __device__ __forceinline__ int lane_xor32(int x) { return (int)lane_xor32((uint32_t)x); }
+// Symmetric reductions over a lane and its partner 16 (32) lanes apart, the
+// result in both: the swap of two copies of x leaves rows (0, 0, 2, 2) in one
+// and rows (1, 1, 3, 3) in the other (for 32: (0, 1, 0, 1) and (2, 3, 2, 3)),
+// so an operation on the pair needs no lane select.
+__device__ __forceinline__ float max_nn(float a, float b) {   // non-NaN operands, no quieting
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float pair_max16(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max_nn(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float pair_max32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return max_nn(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float pair_sum16(float x) {   // row r + row r^1, the lower row first
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ int pair_min16(int x) {
+  const auto p = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+  return min((int)p[0], (int)p[1]);
+}
+__device__ __forceinline__ int pair_min32(int x) {
+  const auto p = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  return min((int)p[0], (int)p[1]);
+}
 
 // ---------------------------------------------------------------------------
 // wave / block reductions (wave64)
@@ -184,6 +217,13 @@ template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
 constexpr int DPP_QUAD_1032 = 0xB1, DPP_QUAD_2301 = 0x4E, DPP_ROW_HALF_MIRROR = 0x141,
               DPP_ROW_MIRROR = 0x140;
 __device__ __forceinline__ float fmax_sel(float a, float b) { return b > a ? b : a; }   // no NaN canonicalising
+// maximum of three non-NaN floats in one VALU instruction (the builtin max
+// quiets its inputs first; these operands are never NaN)
+__device__ __forceinline__ float max3_nn(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 __device__ __forceinline__ float row16_max(float v) {
   v = fmax_sel(v, dpp_f<DPP_QUAD_1032>(v));
   v = fmax_sel(v, dpp_f<DPP_QUAD_2301>(v));

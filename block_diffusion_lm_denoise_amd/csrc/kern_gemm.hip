@@ -10,6 +10,8 @@
 // banks.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -465,18 +467,6 @@ __global__ __launch_bounds__(256) void lmhead_k(HeadArgs a) {
 // registers, LDS double buffer).  Staging both operands through LDS would make
 // the LDS write port the bottleneck.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void mrg_bf(float& m, int& i, float& s, float m2, int i2, float s2) {
-  // branch-free merge of two (max, lowest argmax, sum exp(x - max)) triples;
-  // an empty triple has max -inf and sum 0
-  const float M = fmaxf(m, m2);
-  const float e1 = m == -INFINITY ? 0.f : __expf(m - M);
-  const float e2 = m2 == -INFINITY ? 0.f : __expf(m2 - M);
-  const int id = m > m2 ? i : (m2 > m ? i2 : min(i, i2));
-  s = s * e1 + s2 * e2;
-  m = M;
-  i = id;
-}
-
 template <int P, int NW, int BN, int MINB>
 __global__ __launch_bounds__(NW * 64, MINB) void lmhead_direct_k(HeadArgs a) {
   constexpr int NT = NW * 64;                 // threads
@@ -564,26 +554,33 @@ __global__ __launch_bounds__(NW * 64, MINB) void lmhead_direct_k(HeadArgs a) {
   __syncthreads();
   lload(0, 0);
   int cur = 0;   // LDS buffer of tile kt
-  for (int kb = 0; kb < nkp; kb += P) {
-#pragma unroll
-    for (int st = 0; st < P; st++) {
-      const int kt = kb + st;
-      const int nxt = cur == 2 ? 0 : cur + 1, nn = nxt == 2 ? 0 : nxt + 1;
-      lload(cur, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      mmas(st, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      lload(nxt, 0);   // tile kt+1: written one step ago, behind the last barrier
-      __builtin_amdgcn_sched_barrier(0);
-      mmas(st, 1);
-      __builtin_amdgcn_sched_barrier(0);
+  auto step = [&](int st, int kt, auto with_load) {
+    const int nxt = cur == 2 ? 0 : cur + 1, nn = nxt == 2 ? 0 : nxt + 1;
+    lload(cur, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mmas(st, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    lload(nxt, 0);   // tile kt+1: written one step ago, behind the last barrier
+    __builtin_amdgcn_sched_barrier(0);
+    mmas(st, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (decltype(with_load)::value) {
       gload(st, kt + P);   // stage st: its A tile is in LDS, its B fragments consumed
       __builtin_amdgcn_sched_barrier(0);
-      astore((st + 2) % P, nn, kt + 2 < nk);
-      __syncthreads();
-      cur = nxt;
     }
+    astore((st + 2) % P, nn, kt + 2 < nk);
+    __syncthreads();
+    cur = nxt;
+  };
+  int kb = 0;
+  for (; kb + P < nkp; kb += P) {
+#pragma unroll
+    for (int st = 0; st < P; st++) step(st, kb + st, std::integral_constant<bool, true>{});
   }
+  // last group: every tile it needs is already loaded, so it issues no loads
+  // (loads past the end would only hold the epilogue's registers)
+#pragma unroll
+  for (int st = 0; st < P; st++) step(st, kb + st, std::integral_constant<bool, false>{});
 
   // acc[rt][ct] is the transposed tile: lane (l16, g) holds vocabulary rows
   // n0 + WC w + 16ct + 4g + i (i = 0..3) of token m0 + 16rt + l16, so a
@@ -600,54 +597,79 @@ __global__ __launch_bounds__(NW * 64, MINB) void lmhead_direct_k(HeadArgs a) {
             if (n + i < a.V) a.logits[(size_t)r * a.V + n + i] = acc[rt][ct][i];
       }
   }
-  // epilogue: per token, (max, lowest argmax, sum exp) over this wave's WC
-  // columns: 4 CT in-lane values, then two exchanges between the 4 lanes.
-  // Each step runs over the RT row tiles together (independent chains, so the
-  // latency of one tile's dependent steps hides behind the others).
-  float lm[RT], m[RT], s[RT];
-  int li[RT], idx[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; rt++) {
-    lm[rt] = -INFINITY;
-    li[rt] = 0x7fffffff;
-#pragma unroll
-    for (int ct = 0; ct < CT; ct++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {   // columns ascend: the first maximum is the lowest index
-        const int n = n0 + WC * w + 16 * ct + 4 * g + i;
-        const float v = n < a.V ? acc[rt][ct][i] : -INFINITY;
-        li[rt] = v > lm[rt] ? n : li[rt];
-        lm[rt] = v > lm[rt] ? v : lm[rt];
-      }
-  }
-#pragma unroll
-  for (int rt = 0; rt < RT; rt++) m[rt] = fmax_sel(lm[rt], lane_xor16(lm[rt]));
-#pragma unroll
-  for (int rt = 0; rt < RT; rt++) m[rt] = fmax_sel(m[rt], lane_xor32(m[rt]));
-#pragma unroll
-  for (int rt = 0; rt < RT; rt++) {
-    idx[rt] = lm[rt] == m[rt] ? li[rt] : 0x7fffffff;
-    idx[rt] = min(idx[rt], lane_xor16(idx[rt]));
-  }
-#pragma unroll
-  for (int rt = 0; rt < RT; rt++) idx[rt] = min(idx[rt], lane_xor32(idx[rt]));
-#pragma unroll
-  for (int rt = 0; rt < RT; rt++) {
-    s[rt] = 0.f;
+  // epilogue: per token (a row of the transposed tile) the maximum over this
+  // wave's WC columns, the lowest column attaining it and sum exp(l - max).
+  // Lane maxima (max3 chains), two exchanges for the wave maximum, then per value one
+  // compare-select against it (columns visited in descending order, so the
+  // last hit is the lowest; the select keeps a small column code) and one
+  // fused exponent argument.  The RT row tiles step together (independent
+  // chains).  Column tiles inside the vocabulary take the path without masks.
+  float m[RT], s[RT];
+  int idx[RT];
+  auto epilogue = [&](auto full) {
+    constexpr bool FULL = decltype(full)::value;
+    const int nl = n0 + WC * w + 4 * g;   // column of value (ct, i) = nl + 16 ct + i
+    bool ok[CT][4];
 #pragma unroll
     for (int ct = 0; ct < CT; ct++)
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int n = n0 + WC * w + 16 * ct + 4 * g + i;
-        const float e = __builtin_amdgcn_exp2f((acc[rt][ct][i] - m[rt]) * 1.4426950408889634f);
-        s[rt] += n < a.V ? e : 0.f;
-      }
-    s[rt] = m[rt] == -INFINITY ? 0.f : s[rt];
-  }
+      for (int i = 0; i < 4; i++) ok[ct][i] = FULL || nl + 16 * ct + i < a.V;
 #pragma unroll
-  for (int rt = 0; rt < RT; rt++) s[rt] += lane_xor16(s[rt]);
+    for (int rt = 0; rt < RT; rt++) {   // 4 CT values: one max3 per two after the first
+      float x[4 * CT];
 #pragma unroll
-  for (int rt = 0; rt < RT; rt++) s[rt] += lane_xor32(s[rt]);
+      for (int ct = 0; ct < CT; ct++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) x[4 * ct + i] = ok[ct][i] ? acc[rt][ct][i] : -INFINITY;
+      float v = x[0];
+#pragma unroll
+      for (int j = 1; j + 1 < 4 * CT; j += 2) v = max3_nn(v, x[j], x[j + 1]);
+      m[rt] = max3_nn(v, x[4 * CT - 1], x[4 * CT - 1]);
+    }
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++) m[rt] = pair_max16(m[rt]);
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++) m[rt] = pair_max32(m[rt]);
+    int c[RT];   // code 4 ct + i of the lowest hit; 4 CT = none
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++) c[rt] = 4 * CT;
+#pragma unroll
+    for (int ct = CT - 1; ct >= 0; ct--)
+#pragma unroll
+      for (int i = 3; i >= 0; i--)
+#pragma unroll
+        for (int rt = 0; rt < RT; rt++) c[rt] = ok[ct][i] && acc[rt][ct][i] == m[rt] ? 4 * ct + i : c[rt];
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++) idx[rt] = c[rt] == 4 * CT ? 0x7fffffff : nl + 16 * (c[rt] >> 2) + (c[rt] & 3);
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++) idx[rt] = pair_min16(idx[rt]);
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++) idx[rt] = pair_min32(idx[rt]);
+    constexpr float L2E = 1.4426950408889634f;
+    float mb[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++) {
+      mb[rt] = m[rt] * L2E;
+      s[rt] = 0.f;
+    }
+#pragma unroll
+    for (int ct = 0; ct < CT; ct++)
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int rt = 0; rt < RT; rt++) {
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[rt][ct][i], L2E, -mb[rt]));
+          s[rt] += ok[ct][i] ? e : 0.f;
+        }
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++) s[rt] = m[rt] == -INFINITY ? 0.f : s[rt];
+  };
+  if (n0 + WC * NW <= a.V) epilogue(std::integral_constant<bool, true>{});
+  else epilogue(std::integral_constant<bool, false>{});
+#pragma unroll
+  for (int rt = 0; rt < RT; rt++) s[rt] = pair_sum16(s[rt]);
+#pragma unroll
+  for (int rt = 0; rt < RT; rt++) s[rt] = pair_sum32(s[rt]);
   if (g == 0) {
 #pragma unroll
     for (int rt = 0; rt < RT; rt++) {
@@ -659,14 +681,33 @@ __global__ __launch_bounds__(NW * 64, MINB) void lmhead_direct_k(HeadArgs a) {
   }
   __syncthreads();
   if (t < BM && m0 + t < a.M) {
-    float m = xm[0][t], s = xs[0][t];
-    int idx = xi[0][t];
+    // the NW wave partials of token t at once: their maximum, then each sum
+    // rescaled to it (independent exponentials), and the lowest column among
+    // the partials that reach the maximum; an empty partial has max -inf
+    float pm[NW], ps[NW];
+    int pi[NW];
 #pragma unroll
-    for (int q = 1; q < NW; q++) mrg_bf(m, idx, s, xm[q][t], xi[q][t], xs[q][t]);
+    for (int q = 0; q < NW; q++) {
+      pm[q] = xm[q][t];
+      ps[q] = xs[q][t];
+      pi[q] = xi[q][t];
+    }
+    float M = pm[0];
+#pragma unroll
+    for (int q = 1; q < NW; q++) M = fmax_sel(M, pm[q]);
+    constexpr float L2E = 1.4426950408889634f;
+    float s = 0.f;
+    int idx = 0x7fffffff;
+#pragma unroll
+    for (int q = 0; q < NW; q++) {
+      const float e = __builtin_amdgcn_exp2f((pm[q] - M) * L2E);
+      s += pm[q] == -INFINITY ? 0.f : ps[q] * e;
+      idx = pm[q] == M ? min(idx, pi[q]) : idx;
+    }
     const size_t o = (size_t)(m0 + t) * a.ntiles + nt;
-    a.pmax[o] = m;
+    a.pmax[o] = M;
     a.pidx[o] = idx;
-    a.psum[o] = s;
+    a.psum[o] = M == -INFINITY ? 0.f : s;
   }
 }
 
