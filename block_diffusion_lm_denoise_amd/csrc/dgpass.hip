@@ -376,6 +376,14 @@ dg_status dg_kv_prefill(const dg_model* m, dg_kv* kv, const int32_t* tokens, int
                     at<void>(c, c.L.u), s);
   for (int l = 0; l < cf.L; l++) {
     const dg_layer_weights& w = m->w.layers[l];
+    if (l == cf.L - 1 && !(taps && taps->qkv)) {
+      // nothing downstream reads the last layer's queries or output: its K
+      // and V columns only, straight into the cache
+      CacheDst cd{kv->k[l], kv->v[l], kv->cap, T, 0, KD, cf.hd, cf.Hkv, lens};
+      dense_gemm(c, GEMM_QKV_CACHE, at<void>(c, c.L.u), R, cf.D, w.wk, KD, w.wv, KD, nullptr, 2 * KD,
+                 at<void>(c, c.L.qkv), 2 * KD, nullptr, &cd);
+      break;
+    }
     CacheDst cd{kv->k[l], kv->v[l], kv->cap, T, QD, KD, cf.hd, cf.Hkv, lens};
     dense_gemm(c, GEMM_QKV_CACHE, at<void>(c, c.L.u), R, cf.D, w.wq, QD, w.wk, KD, w.wv, QKV,
                at<void>(c, c.L.qkv), QKV, nullptr, &cd);
