@@ -37,15 +37,15 @@ def _gateup_source_hash():
     return h.hexdigest()[:16]
 
 
-def _traffic(per_launch_alg_bytes):
+def _traffic(workload):
     """HBM bytes per gate/up launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "gateup_layer_p1024_pmc.json")
+    if it was taken on this workload and the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"gateup_{workload}_pmc.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         d = json.load(fh)
-    if d.get("source_hash") != _gateup_source_hash():
+    if d.get("source_hash") != _gateup_source_hash() or not str(d.get("workload", "")).startswith(workload):
         return None
     return d.get("hbm_bytes_per_launch")
 
@@ -147,7 +147,7 @@ def main():
     mean_touched = float(cov.mean())
     gu_bytes, gu_flops = roofline.gateup_work(cfg, mean_touched, B * N * cfg.k)
     achieved = gu_bytes / gateup_avg_s
-    traffic = _traffic(gu_bytes)
+    traffic = _traffic(wl.name)
     work = roofline.denoise_pass_work(cfg, B, N, [P] * B, cov.mean(axis=0))
     t_roof = roofline.roof_time(work.total_bytes, work.total_flops, roofline.HBM_BYTES_PER_S,
                                 roofline.MFMA_PEAK["bf16"])
