@@ -63,8 +63,9 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
                                                 // of a wave are contiguous in LDS
   constexpr int VCH = (NVG + 255) / 256;        // V groups per thread
   static_assert(KT * CPR % 256 == 0, "K staging");
-  __shared__ __attribute__((aligned(16))) TA ks[KT * KLD];
-  __shared__ __attribute__((aligned(16))) TA vt[HD * VLD];
+  // two LDS buffers: tile t+1 is stored while tile t is read
+  __shared__ __attribute__((aligned(16))) TA ks2[2][KT * KLD];
+  __shared__ __attribute__((aligned(16))) TA vt2[2][HD * VLD];
 
   // 1-D grid: the query tiles that share one (request, kv head, key split)
   // -- and so read the same K/V -- have ids 8 apart and run on one XCD,
@@ -112,6 +113,8 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
   const TA* const kn = a.mode == 0 ? (const TA*)a.kn + (size_t)b * a.T * a.ldq + gh * HD : kc;
   const TA* const vn = a.mode == 0 ? (const TA*)a.vn + (size_t)b * a.T * a.ldq + gh * HD : vc;
   const int fresh0 = a.mode == 0 ? P : 0x7fffffff;   // first key read from the qkv rows
+  // last key every query of the block may see (the tile's first query in prefill mode)
+  const int qlim_all = a.mode == 0 ? 0x7fffffff : P + qt * a.QT;
   const size_t ldq = (size_t)a.ldq;
   auto kptr = [&](int kk, const TA* cache, const TA* fresh) -> const TA* {
     const int k = kk < kend ? kk : kbeg;
@@ -121,7 +124,32 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
   // register ring of two tiles (K chunks and V 4-key groups): the loads of
   // the next two tiles are in flight while a tile is used
   u32x4 rk[2][KCH], rv[2][VCH][4];
+  // A tile wholly inside the key range and wholly in the cache (or wholly in
+  // the canvas rows) is addressed as a uniform base plus this thread's fixed
+  // row offsets; other tiles take the per-key selects.
   auto gload = [&](int buf, int k0) {
+    const bool in_range = k0 + KT <= kend;
+    const bool all_cache = in_range && k0 + KT <= fresh0;
+    const bool all_fresh = in_range && k0 >= fresh0;
+    if (all_cache || all_fresh) {
+      const size_t rs = all_cache ? (size_t)HD : ldq;
+      const TA* kb = all_cache ? kc + (size_t)k0 * HD : kn + (size_t)(k0 - fresh0) * ldq;
+      const TA* vb = all_cache ? vc + (size_t)k0 * HD : vn + (size_t)(k0 - fresh0) * ldq;
+#pragma unroll
+      for (int u = 0; u < KCH; u++) {
+        const int id = t + 256 * u, j = id / CPR, q = id % CPR;
+        rk[buf][u] = *reinterpret_cast<const u32x4*>(kb + j * rs + q * EPC);
+      }
+#pragma unroll
+      for (int u = 0; u < VCH; u++) {
+        const int id = t + 256 * u;
+        const int jg = (id < NVG ? id : 0) % NKG, dq = (id < NVG ? id : 0) / NKG;
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++)
+          rv[buf][u][jj] = *reinterpret_cast<const u32x4*>(vb + (4 * jg + jj) * rs + dq * EPC);
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < KCH; u++) {
       const int id = t + 256 * u, j = id / CPR, q = id % CPR;
@@ -138,7 +166,9 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
   };
   auto word = [](u32x4 v, int k) -> uint32_t { return v[k]; };
   // LDS: K row-major; V transposed (vt[d][key]), 4 keys of one d per store
-  auto sstore = [&](int buf) {
+  auto sstore = [&](int buf, int lb) {
+    TA* ks = ks2[lb];
+    TA* vt = vt2[lb];
 #pragma unroll
     for (int u = 0; u < KCH; u++) {
       const int id = t + 256 * u, j = id / CPR, q = id % CPR;
@@ -166,48 +196,80 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
     }
   };
 
-  // one key tile: S, online softmax, O update (K and V tiles in LDS)
-  auto compute = [&](int k0) {
+  // one key tile: S, online softmax, O update (K and V tiles in LDS buffer
+  // lb).  MFMAs are issued so that consecutive ones use different
+  // accumulators (a dependent one would wait for the previous result).
+  auto compute = [&](int k0, int lb, bool full) {
+    const TA* ks = ks2[lb];
+    const TA* vt = vt2[lb];
     // ---- S^T = K Q^T: lane holds keys 16*mt + 4*g4 + i for query row l16 ----
     f32x4_t s[KT / 16];
 #pragma unroll
-    for (int mt = 0; mt < KT / 16; mt++) {
-      s[mt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < KT / 16; mt++) s[mt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ss = 0; ss < HD / 32; ss++) {
-        Frag kf;
-        load_frag(kf, ks + (16 * mt + l16) * KLD + 32 * ss + 8 * g4);
-        mma(s[mt], kf, qf[ss]);
-      }
+    for (int ss = 0; ss < HD / 32; ss++) {
+      Frag kf[KT / 16];
+#pragma unroll
+      for (int mt = 0; mt < KT / 16; mt++) load_frag(kf[mt], ks + (16 * mt + l16) * KLD + 32 * ss + 8 * g4);
+#pragma unroll
+      for (int mt = 0; mt < KT / 16; mt++) mma(s[mt], kf[mt], qf[ss]);
     }
+    // full: every key of the tile is in range and visible to every query of
+    // the block, so no masks; the row maximum is taken on the raw scores (the
+    // scale is positive) and the scale folds into the exponent's FMA.  Rows
+    // past the queries need no mask either: a lane's statistics are its own
+    // row's, and those rows are never stored.
     float tmax = -INFINITY;
+    if (full) {
+      float x = max3_nn(s[0][0], s[0][1], s[0][2]);
 #pragma unroll
-    for (int mt = 0; mt < KT / 16; mt++)
+      for (int mt = 0; mt < KT / 16; mt++)
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int kk = k0 + 16 * mt + 4 * g4 + i;
-        const bool ok = (kk < kend) & (kk <= qlimit) & qvalid;
-        const float v = ok ? s[mt][i] * a.scale_log2 : -INFINITY;
-        s[mt][i] = v;
-        tmax = fmaxf(tmax, v);
-      }
-    tmax = fmaxf(tmax, lane_xor16(tmax));
-    tmax = fmaxf(tmax, lane_xor32(tmax));
+        for (int i = (mt == 0 ? 3 : 0); i < 4; i += 2)
+          x = i + 1 < 4 ? max3_nn(x, s[mt][i], s[mt][i + 1]) : max_nn(x, s[mt][i]);
+      tmax = x * a.scale_log2;
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < KT / 16; mt++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int kk = k0 + 16 * mt + 4 * g4 + i;
+          const bool ok = (kk < kend) & (kk <= qlimit) & qvalid;
+          const float v = ok ? s[mt][i] * a.scale_log2 : -INFINITY;
+          s[mt][i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+    }
+    tmax = pair_max16(tmax);
+    tmax = pair_max32(tmax);
     const float mnew = fmaxf(mrow, tmax);
     const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mrow - mnew);
     float psum = 0.f;
+    if (full) {
 #pragma unroll
-    for (int mt = 0; mt < KT / 16; mt++)
+      for (int mt = 0; mt < KT / 16; mt++)
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const float p = mnew == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[mt][i] - mnew);
-        s[mt][i] = p;
-        psum += p;
-      }
+        for (int i = 0; i < 4; i++) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[mt][i], a.scale_log2, -mnew));
+          s[mt][i] = p;
+          psum += p;
+        }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < KT / 16; mt++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const float p = mnew == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[mt][i] - mnew);
+          s[mt][i] = p;
+          psum += p;
+        }
+    }
     lsum = lsum * alpha + psum;
     mrow = mnew;
+    if (__ballot(alpha != 1.f)) {   // no row's maximum moved: nothing to rescale
 #pragma unroll
-    for (int u = 0; u < HD / 16; u++) o[u] *= alpha;
+      for (int u = 0; u < HD / 16; u++) o[u] *= alpha;
+    }
 
     // ---- O^T += V^T P^T: key slot 8*g4 + 4*t + i <-> key 32*c + 16*t + 4*g4 + i ----
     // bf16: P is split into hi + lo bf16 parts (two MFMAs), so the products
@@ -234,17 +296,28 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; i++) pf.v[4 * tt + i] = s[2 * c + tt][i];
       }
+      if constexpr (ES == 2) {
+        // four head-dim tiles at a time: their hi products, then their lo products
 #pragma unroll
-      for (int ht = 0; ht < HD / 16; ht++) {
-        const TA* vrow = vt + (16 * ht + l16) * VLD + 32 * c + 4 * g4;
-        Frag vf;
-        if constexpr (ES == 2) {
-          uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-          uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
-          vf.v = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-          mma(o[ht], vf, pf);
-          mma(o[ht], vf, pl);
-        } else {
+        for (int h4 = 0; h4 < HD / 64; h4++) {
+          Frag vf[4];
+#pragma unroll
+          for (int x = 0; x < 4; x++) {
+            const TA* vrow = vt + (16 * (4 * h4 + x) + l16) * VLD + 32 * c + 4 * g4;
+            const uint2 lo = *reinterpret_cast<const uint2*>(vrow);
+            const uint2 hi = *reinterpret_cast<const uint2*>(vrow + 16);
+            vf[x].v = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+          }
+#pragma unroll
+          for (int x = 0; x < 4; x++) mma(o[4 * h4 + x], vf[x], pf);
+#pragma unroll
+          for (int x = 0; x < 4; x++) mma(o[4 * h4 + x], vf[x], pl);
+        }
+      } else {
+#pragma unroll
+        for (int ht = 0; ht < HD / 16; ht++) {
+          const TA* vrow = vt + (16 * ht + l16) * VLD + 32 * c + 4 * g4;
+          Frag vf;
           float4 lo = *reinterpret_cast<const float4*>(vrow);
           float4 hi = *reinterpret_cast<const float4*>(vrow + 16);
           vf.v[0] = lo.x; vf.v[1] = lo.y; vf.v[2] = lo.z; vf.v[3] = lo.w;
@@ -256,27 +329,31 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
   };
 
   // tiles past the split load key kbeg (clamped) and are never computed, so
-  // every load is issued unconditionally and the ring indices are constants
+  // every load is issued unconditionally and the ring indices are constants.
+  // Iteration t stores tile t+1 (registers loaded two iterations earlier) in
+  // the other LDS buffer, refills those registers with tile t+3 and computes
+  // tile t; one barrier per tile makes tile t+1 visible and frees buffer t.
   const int ntile = kend > kbeg ? (kend - kbeg + KT - 1) / KT : 0;
   gload(0, kbeg);
   gload(1, kbeg + KT);
+  sstore(0, 0);
+  gload(0, kbeg + 2 * KT);
+  __syncthreads();
   int it = 0;
   for (; it + 2 <= ntile; it += 2) {
 #pragma unroll
     for (int buf = 0; buf < 2; buf++) {
       const int k0 = kbeg + (it + buf) * KT;
-      __syncthreads();   // the previous tile's readers are done with LDS
-      sstore(buf);
+      const int nb = buf ^ 1;          // registers (and LDS buffer) of tile it+buf+1
+      sstore(nb, nb);
+      gload(nb, k0 + 3 * KT);
+      compute(k0, buf, k0 + KT <= kend && k0 + KT - 1 <= qlim_all);
       __syncthreads();
-      gload(buf, k0 + 2 * KT);
-      compute(k0);
     }
   }
   if (it < ntile) {
-    __syncthreads();
-    sstore(0);
-    __syncthreads();
-    compute(kbeg + it * KT);
+    const int k0 = kbeg + it * KT;
+    compute(k0, 0, k0 + KT <= kend && k0 + KT - 1 <= qlim_all);
   }
 
   lsum += lane_xor16(lsum);
