@@ -5,7 +5,8 @@ Tolerances (per tensor, max|gpu - oracle| / max|oracle|): 1e-4 for fp32
 storage, 2e-2 for bf16 storage with fp32 accumulation.  Integer outputs
 (routing ids, permutation, counts, re-noise tokens) are bit-exact when both
 sides route on the same fp32 logits; argmax must agree wherever the oracle's
-top-2 logit gap exceeds 1e-2.
+top-2 logit gap exceeds 1e-2, or twice the largest measured logit difference
+when that is larger (no smaller gap can be decided by logits that far apart).
 """
 import numpy as np
 import torch
@@ -147,7 +148,11 @@ def compare_pass(cfg, o, g, inject_used, label="", head_scale=1.0):
     excluded from that layer's float comparisons, and later layers (and the
     head, unless it was the last layer) are not compared, since every later
     value mixes in that token.  argmax must agree wherever the oracle's top-2
-    gap exceeds 1e-2 x head_scale (head_scale: factor a test scaled the head by)."""
+    gap exceeds max(1e-2 x head_scale, 2 delta), delta the largest absolute
+    logit difference measured on the compared rows: with every logit within
+    delta of the oracle's, a row whose top-2 gap exceeds 2 delta cannot change
+    its argmax (head_scale: factor a test scaled the head by).  delta itself is
+    held to the logits' max-rel tolerance."""
     act = cfg.act
     tol = TOL[act]
     oam, ocf, ot = o
@@ -198,6 +203,7 @@ def compare_pass(cfg, o, g, inject_used, label="", head_scale=1.0):
                 gt[n] = a
             if "gates" in gt:
                 rep["gates"] = max_rel(gt["gates"][:L_ok][:, rows_ok], ot["gates"][:L_ok][:, rows_ok])
+    rep["layers_compared"] = L_ok
     rep["rows_compared"] = int(rows_ok.sum())
     if "router" in gt:
         rep["router"] = max_rel(gt["router"][:L_ok][:, rows_ok], ot["router"][:L_ok][:, rows_ok])
@@ -214,6 +220,7 @@ def compare_pass(cfg, o, g, inject_used, label="", head_scale=1.0):
         if "logits" in gt:
             rep["logits"] = max_rel(gt["logits"][rows_ok], ot["logits"][rows_ok])
             rep["logits_abs"] = float(np.abs(gt["logits"][rows_ok] - ot["logits"][rows_ok]).max())
+            thr = max(thr, 2.0 * rep["logits_abs"])
             gap = top2_gap(ot["logits"])
             clear = (gap > thr) & rows_ok
             bad = clear & (gam.ravel() != oam.ravel())

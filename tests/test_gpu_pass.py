@@ -115,6 +115,19 @@ def test_moe_layer_prefix8192_full_size_synthetic_cache():
     _run(pair, 1, [wl.P], wl.N, wl.seed, synthetic=True, inject=False, scale_note="layer_p8192")
 
 
+def test_stack8_full_size_one_pass_synthetic_cache():
+    """The 8-layer stack at its full size: one teacher-forced pass (identical
+    synthetic 4096-token caches in every layer on both sides); with the
+    oracle's router logits injected the routing is identical, so every
+    layer's taps and the head are compared (free routing diverges at near-tied
+    logits after a layer or two); the prompt prefill itself is covered at
+    smaller sizes."""
+    wl = WORKLOADS["stack8_chain4"]
+    pair = Pair(wl.model, wl.seed, gain="ones")
+    reps, _ = _run(pair, 1, [wl.P], wl.N, wl.seed, synthetic=True, inject=True, scale_note="stack8_chain4")
+    assert reps["inject"]["layers_compared"] == wl.model.L
+
+
 def test_batch8_fp8_full_size_sampled_requests():
     """Eight requests in one pass on the GPU; requests are independent, so the
     oracle checks a sample of them one at a time."""
