@@ -23,6 +23,12 @@ __device__ __forceinline__ const char* packed_group(const void* base, size_t row
   return (const char*)base + (row >> 4) * (size_t)nkb * 2048;
 }
 
+// contraction tiles in flight in registers in the LDS-tiled GEMMs (one more
+// than the tile being stored, so a tile's loads have P - 1 steps to land)
+#ifndef GEMM_P
+#define GEMM_P 2
+#endif
+
 template <typename TA, typename TW, int BM, int BN, int P = 1>
 struct Mainloop {
   static constexpr int BK = 128 / (int)sizeof(TA);            // elements per staged row
@@ -184,7 +190,7 @@ struct DenseArgs {
 
 template <typename TA, int BM, int BN>
 __global__ __launch_bounds__(256) void gemm_dense_k(DenseArgs a) {
-  typedef Mainloop<TA, TA, BM, BN> ML;
+  typedef Mainloop<TA, TA, BM, BN, GEMM_P> ML;
   __shared__ __attribute__((aligned(16))) TA smem[ML::SMEM];
   const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
   const TA* ap[ML::A_LD];
@@ -264,7 +270,7 @@ struct GroupArgs {
 // groups [gate f..f+15, up f..f+15] so each wave holds matching gate and up tiles.
 template <typename TA, typename TW, int BM, int BN>
 __global__ __launch_bounds__(256) void gateup_lds_k(GroupArgs a) {
-  typedef Mainloop<TA, TW, BM, BN> ML;
+  typedef Mainloop<TA, TW, BM, BN, GEMM_P> ML;
   __shared__ __attribute__((aligned(16))) TA smem[ML::SMEM];
   const int tile_id = blockIdx.x;
   if (tile_id >= *a.ntiles) return;
@@ -314,7 +320,7 @@ __global__ __launch_bounds__(256) void gateup_lds_k(GroupArgs a) {
 
 template <typename TA, typename TW, int BM, int BN>
 __global__ __launch_bounds__(256) void down_lds_k(GroupArgs a) {
-  typedef Mainloop<TA, TW, BM, BN> ML;
+  typedef Mainloop<TA, TW, BM, BN, GEMM_P> ML;
   __shared__ __attribute__((aligned(16))) TA smem[ML::SMEM];
   const int tile_id = blockIdx.x;
   if (tile_id >= *a.ntiles) return;
