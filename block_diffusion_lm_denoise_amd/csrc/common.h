@@ -97,13 +97,13 @@ __device__ __forceinline__ void mask_frag(FragF32& f, bool ok) {
   for (int j = 0; j < 8; j++) f.v[j] = ok ? f.v[j] : 0.f;
 }
 
-// OCP e4m3 byte pair -> two floats (hardware conversion), then bf16 bits.
-// Every e4m3 value is exact in bf16 (4 significant bits, exponent range
-// 2^-9 .. 448), so taking the top half of the fp32 pattern is exact.
+// OCP e4m3 byte pair (low or high half-word of w) -> packed bf16 pair in one
+// hardware conversion (the scaled form with scale 1).  Every e4m3 value is
+// exact in bf16 (4 significant bits, exponent range 2^-9 .. 448), so the
+// conversion rounds nothing.
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
-  auto f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
-  return (__float_as_uint(f[0]) >> 16) | (__float_as_uint(f[1]) & 0xffff0000u);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint2 u) {
   uint4 r;

@@ -39,6 +39,9 @@ struct Mainloop {
   static constexpr int B_LD = BN / B_ROWS_PER_PASS;
   static constexpr int RT = BM / 32, CT = BN / 32;             // 16x16 tiles per wave
   static constexpr int SMEM = 2 * (BM + BN) * LDK;             // elements of TA
+  static constexpr int NT = 256, WN = BN / 2;
+  static __device__ __forceinline__ int wave_m() { return threadIdx.x >> 7; }
+  static __device__ __forceinline__ int wave_n() { return (threadIdx.x >> 6) & 1; }
   typedef typename FragOf<TA>::type Frag;
 
   // thread -> chunk assignment
@@ -169,6 +172,124 @@ struct Mainloop {
   }
 };
 
+// Variant for bf16 activations whose weight operand goes straight from the
+// packed layout into MFMA fragments: a 1 KB wave load is one 16 x 32 bf16
+// fragment, or for fp8 weights two fragments decoded in registers (lane g
+// then holds contraction elements 16g .. 16g+15 of the 64-element k-tile, so
+// the activation fragments read the same elements: offset 16g + 8ks instead
+// of 32ks + 8g -- one consistent permutation of the contraction).  Only the
+// activation tile is staged through LDS, which halves the LDS traffic of the
+// two-operand form.  Waves: 2 along the rows x BN/WN along the columns, each
+// a (BM/2) x WN tile (WN = 64 from BN = 128 on; the accumulator layout of
+// Mainloop); a wider block reads each activation row fewer times from L2.
+template <typename TW, int BM, int BN, int P>
+struct MainloopD {
+  typedef uint16_t TA;
+  static constexpr int BK = 64, LDK = 80;   // 160-byte LDS rows
+  static constexpr bool FP8 = sizeof(TW) == 1;
+  static constexpr int WN = BN >= 128 ? 64 : BN / 2;      // columns per wave
+  static constexpr int NWN = BN / WN, NT = 128 * NWN;     // waves along the columns, threads
+  static constexpr int A_LD = BM * 8 / NT;  // 16-byte A chunks per thread
+  static constexpr int RT = BM / 32, CT = WN / 16;
+  static_assert(BM * 8 % NT == 0, "A staging");
+  static constexpr int NB = FP8 ? 1 : 2;    // 16-byte weight loads per column tile and k-tile
+  static constexpr int SMEM = 2 * BM * LDK;
+  static_assert(P >= 2, "a step stores the next tile's activations from another stage");
+  static __device__ __forceinline__ int a_row(int p) { return (threadIdx.x >> 3) + (NT / 8) * p; }
+  static __device__ __forceinline__ int a_col() { return (threadIdx.x & 7) * 8; }
+  static __device__ __forceinline__ int wave_m() { return (threadIdx.x >> 6) / NWN; }
+  static __device__ __forceinline__ int wave_n() { return (threadIdx.x >> 6) % NWN; }
+
+  // bq[ct]: byte address of this lane's 16 bytes of the wave's column tile ct
+  // in contraction piece 0 (row group base + 16 * lane)
+  static __device__ __forceinline__ void run(const TA* const (&ap)[A_LD], const bool (&aok)[A_LD],
+                                             const char* const (&bq)[CT], int K, TA* smem,
+                                             f32x4_t (&acc)[RT][CT]) {
+    const int lane = threadIdx.x & 63;
+    const int wm = wave_m(), l16 = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+      for (int ct = 0; ct < CT; ct++) acc[rt][ct] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+    u32x4 ra[P][A_LD], rb[P][CT][NB];
+    const int nk = K / BK;
+    const int nkp = (nk + P - 1) / P * P;
+    auto gload = [&](int st, int kt) {
+      const int kc = kt < nk ? kt : nk - 1;   // clamped: always issued
+#pragma unroll
+      for (int ct = 0; ct < CT; ct++)
+#pragma unroll
+        for (int h = 0; h < NB; h++)
+          rb[st][ct][h] = *reinterpret_cast<const u32x4*>(
+              bq[ct] + (FP8 ? (size_t)(kc >> 1) * 2048 + (kc & 1) * 1024 : (size_t)kc * 2048 + h * 1024));
+#pragma unroll
+      for (int p = 0; p < A_LD; p++) ra[st][p] = *reinterpret_cast<const u32x4*>(ap[p] + kc * BK + a_col());
+    };
+    auto sstore = [&](int st, int buf, bool ok) {   // tiles past the end are stored as zeros
+      TA* sa = smem + buf * BM * LDK;
+#pragma unroll
+      for (int p = 0; p < A_LD; p++) {
+        u32x4 u = ra[st][p];
+        const bool z = aok[p] && ok;
+        u.x = z ? u.x : 0u;
+        u.y = z ? u.y : 0u;
+        u.z = z ? u.z : 0u;
+        u.w = z ? u.w : 0u;
+        *reinterpret_cast<u32x4*>(sa + a_row(p) * LDK + a_col()) = u;
+      }
+    };
+    auto bfrag = [&](int st, int ct, int ks) {
+      FragBF f;
+      if constexpr (FP8) {
+        const u32x4 u = rb[st][ct][0];
+        f.v = __builtin_bit_cast(bf16x8_t, fp8x8_to_bf16x8(ks ? make_uint2(u.z, u.w) : make_uint2(u.x, u.y)));
+      } else {
+        f.v = __builtin_bit_cast(bf16x8_t, rb[st][ct][ks]);
+      }
+      return f;
+    };
+    const int aoff0 = FP8 ? 16 * g : 8 * g;   // A fragment column of ks = 0
+    const int aoffs = FP8 ? 8 : 32;           // and the step to ks = 1
+
+#pragma unroll
+    for (int st = 0; st < P; st++) gload(st, st);
+    sstore(0, 0, true);
+    __syncthreads();
+    for (int kb = 0; kb < nkp; kb += P) {
+#pragma unroll
+      for (int st = 0; st < P; st++) {
+        const int kt = kb + st;
+        const TA* sa = smem + (kt & 1) * BM * LDK;
+        FragBF af[2][RT];
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+          for (int rt = 0; rt < RT; rt++)
+            load_frag(af[ks][rt], sa + (wm * (BM / 2) + 16 * rt + l16) * LDK + aoff0 + aoffs * ks);
+#pragma unroll
+        for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+          for (int ct = 0; ct < CT; ct++) {
+            const FragBF bf = bfrag(st, ct, ks);
+#pragma unroll
+            for (int rt = 0; rt < RT; rt++) mma(acc[rt][ct], af[ks][rt], bf);
+          }
+        __builtin_amdgcn_sched_barrier(0);
+        sstore((st + 1) % P, (kt + 1) & 1, kt + 1 < nk);   // A of tile kt+1 (loaded P-1 steps ago)
+        gload(st, kt + P);                                  // stage st is consumed
+        __syncthreads();
+      }
+    }
+  }
+};
+
+// threads of a block of the LDS-tiled GEMMs: bf16 activations take MainloopD
+// (BN/WN x 2 waves), fp32 activations Mainloop (4 waves)
+template <typename TA, int BN>
+constexpr int gemm_threads() {
+  return sizeof(TA) == 2 ? 128 * (BN / (BN >= 128 ? 64 : BN / 2)) : 256;
+}
+
 // ---------------------------------------------------------------------------
 // dense GEMM with epilogues
 // ---------------------------------------------------------------------------
@@ -189,13 +310,14 @@ struct DenseArgs {
 };
 
 template <typename TA, int BM, int BN>
-__global__ __launch_bounds__(256) void gemm_dense_k(DenseArgs a) {
-  typedef Mainloop<TA, TA, BM, BN, GEMM_P> ML;
+__global__ __launch_bounds__((gemm_threads<TA, BN>())) void gemm_dense_k(DenseArgs a) {
+  // bf16: weights straight into fragments; fp32: both operands through LDS
+  typedef typename std::conditional<sizeof(TA) == 2, MainloopD<TA, BM, BN, GEMM_P>,
+                                    Mainloop<TA, TA, BM, BN, GEMM_P>>::type ML;
   __shared__ __attribute__((aligned(16))) TA smem[ML::SMEM];
   const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
   const TA* ap[ML::A_LD];
-  const char* bp[ML::B_LD];
-  bool aok[ML::A_LD], bok[ML::B_LD];
+  bool aok[ML::A_LD];
   const int nkb = a.K * (int)sizeof(TA) / 128;
 #pragma unroll
   for (int p = 0; p < ML::A_LD; p++) {
@@ -203,22 +325,34 @@ __global__ __launch_bounds__(256) void gemm_dense_k(DenseArgs a) {
     aok[p] = r < a.M;
     ap[p] = (const TA*)a.A + (size_t)(aok[p] ? r : 0) * a.K;
   }
-#pragma unroll
-  for (int p = 0; p < ML::B_LD; p++) {
-    const int n = n0 + ML::b_row(p);
-    bok[p] = n < a.N;
-    const int nn = bok[p] ? n : 0;
-    const char* q;
-    if (nn < a.n1) q = packed_group(a.B0, nn, nkb);
-    else if (nn < a.n1 + a.n2) q = packed_group(a.B1, nn - a.n1, nkb);
-    else q = packed_group(a.B2, nn - a.n1 - a.n2, nkb);
-    bp[p] = q + ML::b_lane();
-  }
+  // weight row n: from B0, B1 or B2 by range; rows past N read row 0 (never stored)
+  auto wrow = [&](int n) -> const char* {
+    const int nn = n < a.N ? n : 0;
+    if (nn < a.n1) return packed_group(a.B0, nn, nkb);
+    if (nn < a.n1 + a.n2) return packed_group(a.B1, nn - a.n1, nkb);
+    return packed_group(a.B2, nn - a.n1 - a.n2, nkb);
+  };
   f32x4_t acc[ML::RT][ML::CT];
-  ML::run(ap, aok, bp, bok, a.K, smem, acc);
+  if constexpr (sizeof(TA) == 2) {
+    const int wn = ML::wave_n(), lane = threadIdx.x & 63;
+    const char* bq[ML::CT];
+#pragma unroll
+    for (int ct = 0; ct < ML::CT; ct++) bq[ct] = wrow(n0 + wn * ML::WN + 16 * ct) + 16 * lane;
+    ML::run(ap, aok, bq, a.K, smem, acc);
+  } else {
+    const char* bp[ML::B_LD];
+    bool bok[ML::B_LD];
+#pragma unroll
+    for (int p = 0; p < ML::B_LD; p++) {
+      const int n = n0 + ML::b_row(p);
+      bok[p] = n < a.N;
+      bp[p] = wrow(n) + ML::b_lane();
+    }
+    ML::run(ap, aok, bp, bok, a.K, smem, acc);
+  }
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int wm = w >> 1, wn = w & 1, l16 = lane & 15, g = lane >> 4;
+  const int lane = threadIdx.x & 63;
+  const int wm = ML::wave_m(), wn = ML::wave_n(), l16 = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int rt = 0; rt < ML::RT; rt++)
 #pragma unroll
@@ -226,7 +360,7 @@ __global__ __launch_bounds__(256) void gemm_dense_k(DenseArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const int r = m0 + wm * (BM / 2) + 16 * rt + 4 * g + i;
-        const int n = n0 + wn * (BN / 2) + 16 * ct + l16;
+        const int n = n0 + wn * ML::WN + 16 * ct + l16;
         if (r >= a.M || n >= a.N) continue;
         float v = acc[rt][ct][i];
         const size_t o = (size_t)r * a.ldc + n;
@@ -264,22 +398,40 @@ struct GroupArgs {
   const int32_t* ntiles;
   int K, NW, ldo;
   void* out;
+  int max_tiles, ncol;   // row tiles the grid was sized for; column blocks per row tile
 };
+
+// The grouped GEMMs run on a 1-D grid of 8 * ceil(max_tiles * ncol / 8) blocks.
+// Work items (row tile, column block) are numbered row-tile-major, and the
+// XCD that runs block b (b mod 8, the round-robin dispatch order) takes the
+// contiguous range [x * per, (x + 1) * per) of the ntiles * ncol live items:
+// the column blocks of one row tile, and the row tiles of one expert, run
+// side by side on one XCD and share its L2 copy of the activation rows and of
+// the expert's weights (a column-major grid spreads them over all 8 L2s).
+__device__ __forceinline__ bool group_item(const GroupArgs& a, int& tile, int& col) {
+  const int nt = min(*a.ntiles, a.max_tiles);
+  const int total = nt * a.ncol, per = (total + 7) >> 3;
+  const int j = blockIdx.x >> 3, w = (blockIdx.x & 7) * per + j;
+  if (j >= per || w >= total) return false;
+  tile = w / a.ncol;
+  col = w - tile * a.ncol;
+  return true;
+}
 
 // gate/up: BN weight rows = BN/2 SwiGLU outputs, rows ordered in 32-row
 // groups [gate f..f+15, up f..f+15] so each wave holds matching gate and up tiles.
 template <typename TA, typename TW, int BM, int BN>
-__global__ __launch_bounds__(256) void gateup_lds_k(GroupArgs a) {
-  typedef Mainloop<TA, TW, BM, BN, GEMM_P> ML;
+__global__ __launch_bounds__((gemm_threads<TA, BN>())) void gateup_lds_k(GroupArgs a) {
+  typedef typename std::conditional<sizeof(TA) == 2, MainloopD<TW, BM, BN, GEMM_P>,
+                                    Mainloop<TA, TW, BM, BN, GEMM_P>>::type ML;
   __shared__ __attribute__((aligned(16))) TA smem[ML::SMEM];
-  const int tile_id = blockIdx.x;
-  if (tile_id >= *a.ntiles) return;
+  int tile_id, col;
+  if (!group_item(a, tile_id, col)) return;
   const int4 tl = a.tiles[tile_id];
   const int e = tl.x, row0 = tl.y, nrows = tl.z;
-  const int f0 = blockIdx.y * (BN / 2);
+  const int f0 = col * (BN / 2);
   const TA* ap[ML::A_LD];
-  const char* bp[ML::B_LD];
-  bool aok[ML::A_LD], bok[ML::B_LD];
+  bool aok[ML::A_LD];
   const int nkb = a.K * (int)sizeof(TW) / 128;
 #pragma unroll
   for (int p = 0; p < ML::A_LD; p++) {
@@ -287,18 +439,31 @@ __global__ __launch_bounds__(256) void gateup_lds_k(GroupArgs a) {
     aok[p] = r < nrows;
     ap[p] = (const TA*)a.A + (size_t)(a.perm[row0 + (aok[p] ? r : 0)] / a.k) * a.K;
   }
-#pragma unroll
-  for (int p = 0; p < ML::B_LD; p++) {
-    const int n = ML::b_row(p);
+  // tile row n (of BN): 32-row groups [gate f .. f+15, up f .. f+15]
+  auto wrow = [&](int n) -> const char* {
     const int f = f0 + 16 * (n >> 5) + (n & 15);
-    bp[p] = packed_group(((n >> 4) & 1) ? a.W2 : a.W1, (size_t)e * a.NW + f, nkb) + ML::b_lane();
-    bok[p] = true;
-  }
+    return packed_group(((n >> 4) & 1) ? a.W2 : a.W1, (size_t)e * a.NW + f, nkb);
+  };
   f32x4_t acc[ML::RT][ML::CT];
-  ML::run(ap, aok, bp, bok, a.K, smem, acc);
+  if constexpr (sizeof(TA) == 2) {
+    const int wn = ML::wave_n(), lane = threadIdx.x & 63;
+    const char* bq[ML::CT];
+#pragma unroll
+    for (int ct = 0; ct < ML::CT; ct++) bq[ct] = wrow(wn * ML::WN + 16 * ct) + 16 * lane;
+    ML::run(ap, aok, bq, a.K, smem, acc);
+  } else {
+    const char* bp[ML::B_LD];
+    bool bok[ML::B_LD];
+#pragma unroll
+    for (int p = 0; p < ML::B_LD; p++) {
+      bp[p] = wrow(ML::b_row(p)) + ML::b_lane();
+      bok[p] = true;
+    }
+    ML::run(ap, aok, bp, bok, a.K, smem, acc);
+  }
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int wm = w >> 1, wn = w & 1, l16 = lane & 15, g = lane >> 4;
+  const int lane = threadIdx.x & 63;
+  const int wm = ML::wave_m(), wn = ML::wave_n(), l16 = lane & 15, g = lane >> 4;
   float sg = 1.f, su = 1.f;
   if (a.escale) {
     sg = a.escale[e * 3 + 0];
@@ -313,23 +478,23 @@ __global__ __launch_bounds__(256) void gateup_lds_k(GroupArgs a) {
         const int r = wm * (BM / 2) + 16 * rt + 4 * g + i;
         if (r >= nrows) continue;
         const float gv = acc[rt][2 * p][i] * sg, uv = acc[rt][2 * p + 1][i] * su;
-        const int f = f0 + wn * (BN / 4) + 16 * p + l16;
+        const int f = f0 + wn * (ML::WN / 2) + 16 * p + l16;
         stx((TA*)a.out, (size_t)(row0 + r) * a.ldo + f, gv / (1.f + expf(-gv)) * uv);
       }
 }
 
 template <typename TA, typename TW, int BM, int BN>
-__global__ __launch_bounds__(256) void down_lds_k(GroupArgs a) {
-  typedef Mainloop<TA, TW, BM, BN, GEMM_P> ML;
+__global__ __launch_bounds__((gemm_threads<TA, BN>())) void down_lds_k(GroupArgs a) {
+  typedef typename std::conditional<sizeof(TA) == 2, MainloopD<TW, BM, BN, GEMM_P>,
+                                    Mainloop<TA, TW, BM, BN, GEMM_P>>::type ML;
   __shared__ __attribute__((aligned(16))) TA smem[ML::SMEM];
-  const int tile_id = blockIdx.x;
-  if (tile_id >= *a.ntiles) return;
+  int tile_id, col;
+  if (!group_item(a, tile_id, col)) return;
   const int4 tl = a.tiles[tile_id];
   const int e = tl.x, row0 = tl.y, nrows = tl.z;
-  const int n0 = blockIdx.y * BN;
+  const int n0 = col * BN;
   const TA* ap[ML::A_LD];
-  const char* bp[ML::B_LD];
-  bool aok[ML::A_LD], bok[ML::B_LD];
+  bool aok[ML::A_LD];
   const int nkb = a.K * (int)sizeof(TW) / 128;
 #pragma unroll
   for (int p = 0; p < ML::A_LD; p++) {
@@ -337,16 +502,27 @@ __global__ __launch_bounds__(256) void down_lds_k(GroupArgs a) {
     aok[p] = r < nrows;
     ap[p] = (const TA*)a.A + (size_t)(row0 + (aok[p] ? r : 0)) * a.K;
   }
-#pragma unroll
-  for (int p = 0; p < ML::B_LD; p++) {
-    bp[p] = packed_group(a.W1, (size_t)e * a.NW + n0 + ML::b_row(p), nkb) + ML::b_lane();
-    bok[p] = true;
-  }
   f32x4_t acc[ML::RT][ML::CT];
-  ML::run(ap, aok, bp, bok, a.K, smem, acc);
+  if constexpr (sizeof(TA) == 2) {
+    const int wn = ML::wave_n(), lane = threadIdx.x & 63;
+    const char* bq[ML::CT];
+#pragma unroll
+    for (int ct = 0; ct < ML::CT; ct++)
+      bq[ct] = packed_group(a.W1, (size_t)e * a.NW + n0 + wn * ML::WN + 16 * ct, nkb) + 16 * lane;
+    ML::run(ap, aok, bq, a.K, smem, acc);
+  } else {
+    const char* bp[ML::B_LD];
+    bool bok[ML::B_LD];
+#pragma unroll
+    for (int p = 0; p < ML::B_LD; p++) {
+      bp[p] = packed_group(a.W1, (size_t)e * a.NW + n0 + ML::b_row(p), nkb) + ML::b_lane();
+      bok[p] = true;
+    }
+    ML::run(ap, aok, bp, bok, a.K, smem, acc);
+  }
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int wm = w >> 1, wn = w & 1, l16 = lane & 15, g = lane >> 4;
+  const int lane = threadIdx.x & 63;
+  const int wm = ML::wave_m(), wn = ML::wave_n(), l16 = lane & 15, g = lane >> 4;
   const float sd = a.escale ? a.escale[e * 3 + 2] : 1.f;
 #pragma unroll
   for (int rt = 0; rt < ML::RT; rt++)
@@ -356,7 +532,7 @@ __global__ __launch_bounds__(256) void down_lds_k(GroupArgs a) {
       for (int i = 0; i < 4; i++) {
         const int r = wm * (BM / 2) + 16 * rt + 4 * g + i;
         if (r >= nrows) continue;
-        const int n = n0 + wn * (BN / 2) + 16 * ct + l16;
+        const int n = n0 + wn * ML::WN + 16 * ct + l16;
         stx((TA*)a.out, (size_t)(row0 + r) * a.ldo + n, acc[rt][ct][i] * sd);
       }
 }
@@ -725,11 +901,11 @@ void launch_gemm(int act, int mode, const void* A, int M, int K, const void* B0,
   if (cache) a.cache = *cache;
   if (M > 1024) {
     dim3 grid((M + 127) / 128, (N + 127) / 128);
-    if (act == ACT_BF16) gemm_dense_k<uint16_t, 128, 128><<<grid, 256, 0, s>>>(a);
+    if (act == ACT_BF16) gemm_dense_k<uint16_t, 128, 128><<<grid, gemm_threads<uint16_t, 128>(), 0, s>>>(a);
     else gemm_dense_k<float, 128, 128><<<grid, 256, 0, s>>>(a);
   } else {
     dim3 grid((M + 63) / 64, (N + 63) / 64);
-    if (act == ACT_BF16) gemm_dense_k<uint16_t, 64, 64><<<grid, 256, 0, s>>>(a);
+    if (act == ACT_BF16) gemm_dense_k<uint16_t, 64, 64><<<grid, gemm_threads<uint16_t, 64>(), 0, s>>>(a);
     else gemm_dense_k<float, 64, 64><<<grid, 256, 0, s>>>(a);
   }
 }
@@ -737,20 +913,42 @@ void launch_gemm(int act, int mode, const void* A, int M, int K, const void* B0,
 void launch_gateup_lds(int act, const void* u2, const int32_t* perm, int k, const MoeW& w,
                        const int4* tiles, const int32_t* ntiles, int max_tiles, int D, int F,
                        void* H, hipStream_t s) {
-  GroupArgs a{u2, perm, k, w.wg, w.wu, w.escale, tiles, ntiles, D, F, F, H};
-  dim3 grid(max_tiles, F / 64);   // 128 weight rows = 64 SwiGLU outputs per block
-  if (act == ACT_F32) gateup_lds_k<float, float, 128, 128><<<grid, 256, 0, s>>>(a);
-  else if (w.wdt == DG_FP8E4M3) gateup_lds_k<uint16_t, uint8_t, 128, 128><<<grid, 256, 0, s>>>(a);
-  else gateup_lds_k<uint16_t, uint16_t, 128, 128><<<grid, 256, 0, s>>>(a);
+  GroupArgs a{u2, perm, k, w.wg, w.wu, w.escale, tiles, ntiles, D, F, F, H, max_tiles, 0};
+  auto grid = [&](int ncol) {
+    a.ncol = ncol;
+    return dim3((unsigned)(((size_t)max_tiles * ncol + 7) / 8 * 8));
+  };
+  if (act == ACT_F32) {   // 128 weight rows = 64 SwiGLU outputs per block
+    gateup_lds_k<float, float, 128, 128><<<grid(F / 64), 256, 0, s>>>(a);
+  } else if (F % 128 == 0) {   // 256 weight rows: each routed row is read F/128 times
+    constexpr int nt = gemm_threads<uint16_t, 256>();
+    if (w.wdt == DG_FP8E4M3) gateup_lds_k<uint16_t, uint8_t, 128, 256><<<grid(F / 128), nt, 0, s>>>(a);
+    else gateup_lds_k<uint16_t, uint16_t, 128, 256><<<grid(F / 128), nt, 0, s>>>(a);
+  } else {
+    constexpr int nt = gemm_threads<uint16_t, 128>();
+    if (w.wdt == DG_FP8E4M3) gateup_lds_k<uint16_t, uint8_t, 128, 128><<<grid(F / 64), nt, 0, s>>>(a);
+    else gateup_lds_k<uint16_t, uint16_t, 128, 128><<<grid(F / 64), nt, 0, s>>>(a);
+  }
 }
 
 void launch_down_lds(int act, const void* H, const MoeW& w, const int4* tiles,
                      const int32_t* ntiles, int max_tiles, int D, int F, void* Y, hipStream_t s) {
-  GroupArgs a{H, nullptr, 0, w.wd, nullptr, w.escale, tiles, ntiles, F, D, D, Y};
-  dim3 grid(max_tiles, D / 128);
-  if (act == ACT_F32) down_lds_k<float, float, 128, 128><<<grid, 256, 0, s>>>(a);
-  else if (w.wdt == DG_FP8E4M3) down_lds_k<uint16_t, uint8_t, 128, 128><<<grid, 256, 0, s>>>(a);
-  else down_lds_k<uint16_t, uint16_t, 128, 128><<<grid, 256, 0, s>>>(a);
+  GroupArgs a{H, nullptr, 0, w.wd, nullptr, w.escale, tiles, ntiles, F, D, D, Y, max_tiles, 0};
+  auto grid = [&](int ncol) {
+    a.ncol = ncol;
+    return dim3((unsigned)(((size_t)max_tiles * ncol + 7) / 8 * 8));
+  };
+  if (act == ACT_F32) {
+    down_lds_k<float, float, 128, 128><<<grid(D / 128), 256, 0, s>>>(a);
+  } else if (D % 256 == 0) {
+    constexpr int nt = gemm_threads<uint16_t, 256>();
+    if (w.wdt == DG_FP8E4M3) down_lds_k<uint16_t, uint8_t, 128, 256><<<grid(D / 256), nt, 0, s>>>(a);
+    else down_lds_k<uint16_t, uint16_t, 128, 256><<<grid(D / 256), nt, 0, s>>>(a);
+  } else {
+    constexpr int nt = gemm_threads<uint16_t, 128>();
+    if (w.wdt == DG_FP8E4M3) down_lds_k<uint16_t, uint8_t, 128, 128><<<grid(D / 128), nt, 0, s>>>(a);
+    else down_lds_k<uint16_t, uint16_t, 128, 128><<<grid(D / 128), nt, 0, s>>>(a);
+  }
 }
 
 // contraction tiles in flight in the bf16 LM head, and its waves per block
