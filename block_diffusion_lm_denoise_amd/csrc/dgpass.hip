@@ -15,7 +15,6 @@ size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 int esize(int dt) { return dt == DG_F32 ? 4 : dt == DG_BF16 ? 2 : 1; }
 
 constexpr int MIN_TILE = 32;      // smallest expert row tile (sizes the tile list)
-constexpr int FAT_TILE = 128;     // row tile of the LDS-tiled expert kernels
 constexpr int STREAM_MAX_ROWS = 1024;  // dense projections: weight streaming up to this many rows
 constexpr int ROUTE_MIN_ROWS = 2048;   // fused routing kernel from this many token rows
 
@@ -236,7 +235,7 @@ void moe_block(const Ctx& c, int l, const float* gnext) {
   // permutation and row tiles
   const int avg = (int)(R * k / E);
   const bool stream = avg <= 64;
-  const int tile_rows = stream ? stream_tile_rows(act, cf.expert_dtype) : FAT_TILE;
+  const int tile_rows = stream ? stream_tile_rows(act, cf.expert_dtype) : group_tile_rows(act);
   const int max_tiles = (int)((R * k + tile_rows - 1) / tile_rows) + (int)E;
   int32_t* counts = c.pass ? at<int32_t>(c, c.L.cov) + l * E : at<int32_t>(c, c.L.counts);
   launch_plan(at<int32_t>(c, c.L.ids), c.R, cf.k, cf.E, tile_rows, counts, at<int32_t>(c, c.L.offsets),

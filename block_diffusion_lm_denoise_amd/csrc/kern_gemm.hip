@@ -39,7 +39,7 @@ struct Mainloop {
   static constexpr int B_LD = BN / B_ROWS_PER_PASS;
   static constexpr int RT = BM / 32, CT = BN / 32;             // 16x16 tiles per wave
   static constexpr int SMEM = 2 * (BM + BN) * LDK;             // elements of TA
-  static constexpr int NT = 256, WN = BN / 2;
+  static constexpr int NT = 256, WN = BN / 2, WM = BM / 2;
   static __device__ __forceinline__ int wave_m() { return threadIdx.x >> 7; }
   static __device__ __forceinline__ int wave_n() { return (threadIdx.x >> 6) & 1; }
   typedef typename FragOf<TA>::type Frag;
@@ -179,22 +179,29 @@ struct Mainloop {
 // the activation fragments read the same elements: offset 16g + 8ks instead
 // of 32ks + 8g -- one consistent permutation of the contraction).  Only the
 // activation tile is staged through LDS, which halves the LDS traffic of the
-// two-operand form.  Waves: 2 along the rows x BN/WN along the columns, each
-// a (BM/2) x WN tile (WN = 64 from BN = 128 on; the accumulator layout of
-// Mainloop); a wider block reads each activation row fewer times from L2.
-template <typename TW, int BM, int BN, int P>
+// two-operand form.  Waves: NWM along the rows x BN/WN along the columns,
+// each a (BM/NWM) x WN tile; a wider block reads each activation row fewer
+// times from L2, and one wave along the rows reads each weight once per block
+// (at twice the LDS reads of two).  An LDS buffer holds S consecutive 64-wide
+// k-tiles, so the block meets at a barrier once per S k-tiles: each barrier
+// holds every wave until the slowest has stored its share of the next tiles,
+// and with one barrier per k-tile that wait, not the matrix cores, set the
+// pace.  Registers hold a ring of P >= 2S k-tiles.
+template <typename TW, int BM, int BN, int P, int NWM, int WN_, int S>
 struct MainloopD {
   typedef uint16_t TA;
-  static constexpr int BK = 64, LDK = 80;   // 160-byte LDS rows
+  static constexpr int WN = WN_;            // columns per wave
+  static constexpr int BK = 64;
+  static constexpr int LDK = 64 * S + 16;   // LDS row: 128 S + 32 bytes (32 mod 64: conflict-free reads)
   static constexpr bool FP8 = sizeof(TW) == 1;
-  static constexpr int WN = BN >= 128 ? 64 : BN / 2;      // columns per wave
-  static constexpr int NWN = BN / WN, NT = 128 * NWN;     // waves along the columns, threads
+  static constexpr int NWN = BN / WN, NT = 64 * NWM * NWN;   // waves along the columns, threads
+  static constexpr int WM = BM / NWM;       // rows per wave
   static constexpr int A_LD = BM * 8 / NT;  // 16-byte A chunks per thread
-  static constexpr int RT = BM / 32, CT = WN / 16;
+  static constexpr int RT = WM / 16, CT = WN / 16;
   static_assert(BM * 8 % NT == 0, "A staging");
   static constexpr int NB = FP8 ? 1 : 2;    // 16-byte weight loads per column tile and k-tile
   static constexpr int SMEM = 2 * BM * LDK;
-  static_assert(P >= 2, "a step stores the next tile's activations from another stage");
+  static_assert(P % S == 0 && P >= 2 * S, "the tiles a barrier step stores were loaded at least S steps before");
   static __device__ __forceinline__ int a_row(int p) { return (threadIdx.x >> 3) + (NT / 8) * p; }
   static __device__ __forceinline__ int a_col() { return (threadIdx.x & 7) * 8; }
   static __device__ __forceinline__ int wave_m() { return (threadIdx.x >> 6) / NWN; }
@@ -225,8 +232,8 @@ struct MainloopD {
 #pragma unroll
       for (int p = 0; p < A_LD; p++) ra[st][p] = *reinterpret_cast<const u32x4*>(ap[p] + kc * BK + a_col());
     };
-    auto sstore = [&](int st, int buf, bool ok) {   // tiles past the end are stored as zeros
-      TA* sa = smem + buf * BM * LDK;
+    auto sstore = [&](int st, int buf, int j, bool ok) {   // tiles past the end are stored as zeros
+      TA* sa = smem + buf * BM * LDK + j * BK;
 #pragma unroll
       for (int p = 0; p < A_LD; p++) {
         u32x4 u = ra[st][p];
@@ -253,19 +260,20 @@ struct MainloopD {
 
 #pragma unroll
     for (int st = 0; st < P; st++) gload(st, st);
-    sstore(0, 0, true);
+#pragma unroll
+    for (int j = 0; j < S; j++) sstore(j, 0, j, j < nk);
     __syncthreads();
     for (int kb = 0; kb < nkp; kb += P) {
 #pragma unroll
       for (int st = 0; st < P; st++) {
-        const int kt = kb + st;
-        const TA* sa = smem + (kt & 1) * BM * LDK;
+        const int kt = kb + st;   // kt mod S = st mod S (P is a multiple of S)
+        const TA* sa = smem + ((kt / S) & 1) * BM * LDK + (st % S) * BK;
         FragBF af[2][RT];
 #pragma unroll
         for (int ks = 0; ks < 2; ks++)
 #pragma unroll
           for (int rt = 0; rt < RT; rt++)
-            load_frag(af[ks][rt], sa + (wm * (BM / 2) + 16 * rt + l16) * LDK + aoff0 + aoffs * ks);
+            load_frag(af[ks][rt], sa + (wm * WM + 16 * rt + l16) * LDK + aoff0 + aoffs * ks);
 #pragma unroll
         for (int ks = 0; ks < 2; ks++)
 #pragma unroll
@@ -275,19 +283,50 @@ struct MainloopD {
             for (int rt = 0; rt < RT; rt++) mma(acc[rt][ct], af[ks][rt], bf);
           }
         __builtin_amdgcn_sched_barrier(0);
-        sstore((st + 1) % P, (kt + 1) & 1, kt + 1 < nk);   // A of tile kt+1 (loaded P-1 steps ago)
-        gload(st, kt + P);                                  // stage st is consumed
-        __syncthreads();
+        if (st % S == S - 1) {   // A of tiles kt+1 .. kt+S (loaded P-S .. P-1 steps ago)
+#pragma unroll
+          for (int j = 0; j < S; j++) sstore((st + 1 + j) % P, ((kt + 1) / S) & 1, j, kt + 1 + j < nk);
+        }
+        gload(st, kt + P);   // stage st is consumed
+        if (st % S == S - 1) __syncthreads();
       }
     }
   }
 };
 
-// threads of a block of the LDS-tiled GEMMs: bf16 activations take MainloopD
-// (BN/WN x 2 waves), fp32 activations Mainloop (4 waves)
-template <typename TA, int BN>
+// Main loop of the LDS-tiled GEMMs: bf16 activations take MainloopD with NWM
+// waves along the rows (2: 64-column wave tiles from BN = 128 on; 1: 8 waves
+// of BN/8 columns), fp32 activations Mainloop (2 x 2 waves).
+// The grouped GEMMs (one wave along the rows) stage GROUP_S k-tiles per LDS
+// buffer with a GROUP_P-deep register ring; the dense ones one k-tile and
+// GEMM_P.  Expert tiles of 64 rows keep a block under 128 VGPRs, so two blocks
+// share a CU and one block's barrier waits are filled by the other's MFMAs
+// (batch-8 fp8 gate/up: 176 us at 128-row tiles with one block per CU, 143 at
+// 64; 2 k-tiles per LDS buffer gained nothing at 64 rows).
+#ifndef GROUP_NWM
+#define GROUP_NWM 1
+#endif
+#ifndef GROUP_S
+#define GROUP_S 1
+#endif
+#ifndef GROUP_P
+#define GROUP_P 2
+#endif
+#ifndef GROUP_WPE
+#define GROUP_WPE 1   // minimum waves per SIMD the grouped GEMMs are compiled for
+#endif
+#ifndef GROUP_BM
+#define GROUP_BM 64   // rows of a bf16-activation expert tile
+#endif
+template <typename TA, typename TW, int BM, int BN, int NWM>
+using GemmML = typename std::conditional<
+    sizeof(TA) == 2,
+    typename std::conditional<NWM == 1, MainloopD<TW, BM, BN, GROUP_P, 1, BN / 8, GROUP_S>,
+                              MainloopD<TW, BM, BN, GEMM_P, 2, (BN >= 128 ? 64 : BN / 2), 1>>::type,
+    Mainloop<TA, TW, BM, BN, GEMM_P>>::type;
+template <typename TA, typename TW, int BM, int BN, int NWM>
 constexpr int gemm_threads() {
-  return sizeof(TA) == 2 ? 128 * (BN / (BN >= 128 ? 64 : BN / 2)) : 256;
+  return GemmML<TA, TW, BM, BN, NWM>::NT;
 }
 
 // ---------------------------------------------------------------------------
@@ -310,10 +349,9 @@ struct DenseArgs {
 };
 
 template <typename TA, int BM, int BN>
-__global__ __launch_bounds__((gemm_threads<TA, BN>())) void gemm_dense_k(DenseArgs a) {
+__global__ __launch_bounds__((gemm_threads<TA, TA, BM, BN, 2>())) void gemm_dense_k(DenseArgs a) {
   // bf16: weights straight into fragments; fp32: both operands through LDS
-  typedef typename std::conditional<sizeof(TA) == 2, MainloopD<TA, BM, BN, GEMM_P>,
-                                    Mainloop<TA, TA, BM, BN, GEMM_P>>::type ML;
+  typedef GemmML<TA, TA, BM, BN, 2> ML;
   __shared__ __attribute__((aligned(16))) TA smem[ML::SMEM];
   const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
   const TA* ap[ML::A_LD];
@@ -359,7 +397,7 @@ __global__ __launch_bounds__((gemm_threads<TA, BN>())) void gemm_dense_k(DenseAr
     for (int ct = 0; ct < ML::CT; ct++)
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        const int r = m0 + wm * (BM / 2) + 16 * rt + 4 * g + i;
+        const int r = m0 + wm * ML::WM + 16 * rt + 4 * g + i;
         const int n = n0 + wn * ML::WN + 16 * ct + l16;
         if (r >= a.M || n >= a.N) continue;
         float v = acc[rt][ct][i];
@@ -420,10 +458,9 @@ __device__ __forceinline__ bool group_item(const GroupArgs& a, int& tile, int& c
 
 // gate/up: BN weight rows = BN/2 SwiGLU outputs, rows ordered in 32-row
 // groups [gate f..f+15, up f..f+15] so each wave holds matching gate and up tiles.
-template <typename TA, typename TW, int BM, int BN>
-__global__ __launch_bounds__((gemm_threads<TA, BN>())) void gateup_lds_k(GroupArgs a) {
-  typedef typename std::conditional<sizeof(TA) == 2, MainloopD<TW, BM, BN, GEMM_P>,
-                                    Mainloop<TA, TW, BM, BN, GEMM_P>>::type ML;
+template <typename TA, typename TW, int BM, int BN, int NWM>
+__global__ __launch_bounds__((gemm_threads<TA, TW, BM, BN, NWM>()), (NWM == 1 ? GROUP_WPE : 1)) void gateup_lds_k(GroupArgs a) {
+  typedef GemmML<TA, TW, BM, BN, NWM> ML;
   __shared__ __attribute__((aligned(16))) TA smem[ML::SMEM];
   int tile_id, col;
   if (!group_item(a, tile_id, col)) return;
@@ -475,7 +512,7 @@ __global__ __launch_bounds__((gemm_threads<TA, BN>())) void gateup_lds_k(GroupAr
     for (int p = 0; p < ML::CT / 2; p++)
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        const int r = wm * (BM / 2) + 16 * rt + 4 * g + i;
+        const int r = wm * ML::WM + 16 * rt + 4 * g + i;
         if (r >= nrows) continue;
         const float gv = acc[rt][2 * p][i] * sg, uv = acc[rt][2 * p + 1][i] * su;
         const int f = f0 + wn * (ML::WN / 2) + 16 * p + l16;
@@ -483,10 +520,9 @@ __global__ __launch_bounds__((gemm_threads<TA, BN>())) void gateup_lds_k(GroupAr
       }
 }
 
-template <typename TA, typename TW, int BM, int BN>
-__global__ __launch_bounds__((gemm_threads<TA, BN>())) void down_lds_k(GroupArgs a) {
-  typedef typename std::conditional<sizeof(TA) == 2, MainloopD<TW, BM, BN, GEMM_P>,
-                                    Mainloop<TA, TW, BM, BN, GEMM_P>>::type ML;
+template <typename TA, typename TW, int BM, int BN, int NWM>
+__global__ __launch_bounds__((gemm_threads<TA, TW, BM, BN, NWM>()), (NWM == 1 ? GROUP_WPE : 1)) void down_lds_k(GroupArgs a) {
+  typedef GemmML<TA, TW, BM, BN, NWM> ML;
   __shared__ __attribute__((aligned(16))) TA smem[ML::SMEM];
   int tile_id, col;
   if (!group_item(a, tile_id, col)) return;
@@ -530,7 +566,7 @@ __global__ __launch_bounds__((gemm_threads<TA, BN>())) void down_lds_k(GroupArgs
     for (int ct = 0; ct < ML::CT; ct++)
 #pragma unroll
       for (int i = 0; i < 4; i++) {
-        const int r = wm * (BM / 2) + 16 * rt + 4 * g + i;
+        const int r = wm * ML::WM + 16 * rt + 4 * g + i;
         if (r >= nrows) continue;
         const int n = n0 + wn * ML::WN + 16 * ct + l16;
         stx((TA*)a.out, (size_t)(row0 + r) * a.ldo + n, acc[rt][ct][i] * sd);
@@ -901,14 +937,16 @@ void launch_gemm(int act, int mode, const void* A, int M, int K, const void* B0,
   if (cache) a.cache = *cache;
   if (M > 1024) {
     dim3 grid((M + 127) / 128, (N + 127) / 128);
-    if (act == ACT_BF16) gemm_dense_k<uint16_t, 128, 128><<<grid, gemm_threads<uint16_t, 128>(), 0, s>>>(a);
+    if (act == ACT_BF16) gemm_dense_k<uint16_t, 128, 128><<<grid, gemm_threads<uint16_t, uint16_t, 128, 128, 2>(), 0, s>>>(a);
     else gemm_dense_k<float, 128, 128><<<grid, 256, 0, s>>>(a);
   } else {
     dim3 grid((M + 63) / 64, (N + 63) / 64);
-    if (act == ACT_BF16) gemm_dense_k<uint16_t, 64, 64><<<grid, gemm_threads<uint16_t, 64>(), 0, s>>>(a);
+    if (act == ACT_BF16) gemm_dense_k<uint16_t, 64, 64><<<grid, gemm_threads<uint16_t, uint16_t, 64, 64, 2>(), 0, s>>>(a);
     else gemm_dense_k<float, 64, 64><<<grid, 256, 0, s>>>(a);
   }
 }
+
+int group_tile_rows(int act) { return act == ACT_F32 ? 128 : GROUP_BM; }
 
 void launch_gateup_lds(int act, const void* u2, const int32_t* perm, int k, const MoeW& w,
                        const int4* tiles, const int32_t* ntiles, int max_tiles, int D, int F,
@@ -919,15 +957,17 @@ void launch_gateup_lds(int act, const void* u2, const int32_t* perm, int k, cons
     return dim3((unsigned)(((size_t)max_tiles * ncol + 7) / 8 * 8));
   };
   if (act == ACT_F32) {   // 128 weight rows = 64 SwiGLU outputs per block
-    gateup_lds_k<float, float, 128, 128><<<grid(F / 64), 256, 0, s>>>(a);
+    gateup_lds_k<float, float, 128, 128, 2><<<grid(F / 64), 256, 0, s>>>(a);
   } else if (F % 128 == 0) {   // 256 weight rows: each routed row is read F/128 times
-    constexpr int nt = gemm_threads<uint16_t, 256>();
-    if (w.wdt == DG_FP8E4M3) gateup_lds_k<uint16_t, uint8_t, 128, 256><<<grid(F / 128), nt, 0, s>>>(a);
-    else gateup_lds_k<uint16_t, uint16_t, 128, 256><<<grid(F / 128), nt, 0, s>>>(a);
+    constexpr int N8 = gemm_threads<uint16_t, uint8_t, GROUP_BM, 256, GROUP_NWM>();
+    constexpr int N16 = gemm_threads<uint16_t, uint16_t, GROUP_BM, 256, GROUP_NWM>();
+    if (w.wdt == DG_FP8E4M3) gateup_lds_k<uint16_t, uint8_t, GROUP_BM, 256, GROUP_NWM><<<grid(F / 128), N8, 0, s>>>(a);
+    else gateup_lds_k<uint16_t, uint16_t, GROUP_BM, 256, GROUP_NWM><<<grid(F / 128), N16, 0, s>>>(a);
   } else {
-    constexpr int nt = gemm_threads<uint16_t, 128>();
-    if (w.wdt == DG_FP8E4M3) gateup_lds_k<uint16_t, uint8_t, 128, 128><<<grid(F / 64), nt, 0, s>>>(a);
-    else gateup_lds_k<uint16_t, uint16_t, 128, 128><<<grid(F / 64), nt, 0, s>>>(a);
+    constexpr int N8 = gemm_threads<uint16_t, uint8_t, GROUP_BM, 128, 2>();
+    constexpr int N16 = gemm_threads<uint16_t, uint16_t, GROUP_BM, 128, 2>();
+    if (w.wdt == DG_FP8E4M3) gateup_lds_k<uint16_t, uint8_t, GROUP_BM, 128, 2><<<grid(F / 64), N8, 0, s>>>(a);
+    else gateup_lds_k<uint16_t, uint16_t, GROUP_BM, 128, 2><<<grid(F / 64), N16, 0, s>>>(a);
   }
 }
 
@@ -939,15 +979,17 @@ void launch_down_lds(int act, const void* H, const MoeW& w, const int4* tiles,
     return dim3((unsigned)(((size_t)max_tiles * ncol + 7) / 8 * 8));
   };
   if (act == ACT_F32) {
-    down_lds_k<float, float, 128, 128><<<grid(D / 128), 256, 0, s>>>(a);
+    down_lds_k<float, float, 128, 128, 2><<<grid(D / 128), 256, 0, s>>>(a);
   } else if (D % 256 == 0) {
-    constexpr int nt = gemm_threads<uint16_t, 256>();
-    if (w.wdt == DG_FP8E4M3) down_lds_k<uint16_t, uint8_t, 128, 256><<<grid(D / 256), nt, 0, s>>>(a);
-    else down_lds_k<uint16_t, uint16_t, 128, 256><<<grid(D / 256), nt, 0, s>>>(a);
+    constexpr int N8 = gemm_threads<uint16_t, uint8_t, GROUP_BM, 256, GROUP_NWM>();
+    constexpr int N16 = gemm_threads<uint16_t, uint16_t, GROUP_BM, 256, GROUP_NWM>();
+    if (w.wdt == DG_FP8E4M3) down_lds_k<uint16_t, uint8_t, GROUP_BM, 256, GROUP_NWM><<<grid(D / 256), N8, 0, s>>>(a);
+    else down_lds_k<uint16_t, uint16_t, GROUP_BM, 256, GROUP_NWM><<<grid(D / 256), N16, 0, s>>>(a);
   } else {
-    constexpr int nt = gemm_threads<uint16_t, 128>();
-    if (w.wdt == DG_FP8E4M3) down_lds_k<uint16_t, uint8_t, 128, 128><<<grid(D / 128), nt, 0, s>>>(a);
-    else down_lds_k<uint16_t, uint16_t, 128, 128><<<grid(D / 128), nt, 0, s>>>(a);
+    constexpr int N8 = gemm_threads<uint16_t, uint8_t, GROUP_BM, 128, 2>();
+    constexpr int N16 = gemm_threads<uint16_t, uint16_t, GROUP_BM, 128, 2>();
+    if (w.wdt == DG_FP8E4M3) down_lds_k<uint16_t, uint8_t, GROUP_BM, 128, 2><<<grid(D / 128), N8, 0, s>>>(a);
+    else down_lds_k<uint16_t, uint16_t, GROUP_BM, 128, 2><<<grid(D / 128), N16, 0, s>>>(a);
   }
 }
 

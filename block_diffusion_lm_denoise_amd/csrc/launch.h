@@ -104,6 +104,9 @@ struct CacheDst {
 void launch_gemm(int act, int mode, const void* A, int M, int K, const void* B0, int n1,
                  const void* B1, int n2, const void* B2, int N, void* C, int ldc, const void* R,
                  const CacheDst* cache, hipStream_t s);
+// rows of an expert tile of the LDS-tiled grouped GEMMs (the tile plan's tile
+// height when they run)
+int group_tile_rows(int act);
 void launch_gateup_lds(int act, const void* u2, const int32_t* perm, int k, const MoeW& w,
                        const int4* tiles, const int32_t* ntiles, int max_tiles, int D, int F,
                        void* H, hipStream_t s);
