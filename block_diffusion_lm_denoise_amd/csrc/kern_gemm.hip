@@ -295,8 +295,8 @@ struct MainloopD {
 };
 
 // Main loop of the LDS-tiled GEMMs: bf16 activations take MainloopD with NWM
-// waves along the rows (2: 64-column wave tiles from BN = 128 on; 1: 8 waves
-// of BN/8 columns), fp32 activations Mainloop (2 x 2 waves).
+// waves along the rows (2: 64-column wave tiles from BN = 128 on; 1: BN/32
+// waves of 32 columns side by side), fp32 activations Mainloop (2 x 2 waves).
 // The grouped GEMMs (one wave along the rows) stage GROUP_S k-tiles per LDS
 // buffer with a GROUP_P-deep register ring; the dense ones one k-tile and
 // GEMM_P.  Expert tiles of 64 rows keep a block under 128 VGPRs, so two blocks
@@ -318,10 +318,13 @@ struct MainloopD {
 #ifndef GROUP_BM
 #define GROUP_BM 64   // rows of a bf16-activation expert tile
 #endif
+#ifndef DENSE_WIDE
+#define DENSE_WIDE 1  // dense bf16 GEMMs from 1024 rows: 64-row tiles, waves side by side
+#endif
 template <typename TA, typename TW, int BM, int BN, int NWM>
 using GemmML = typename std::conditional<
     sizeof(TA) == 2,
-    typename std::conditional<NWM == 1, MainloopD<TW, BM, BN, GROUP_P, 1, BN / 8, GROUP_S>,
+    typename std::conditional<NWM == 1, MainloopD<TW, BM, BN, GROUP_P, 1, 32, GROUP_S>,
                               MainloopD<TW, BM, BN, GEMM_P, 2, (BN >= 128 ? 64 : BN / 2), 1>>::type,
     Mainloop<TA, TW, BM, BN, GEMM_P>>::type;
 template <typename TA, typename TW, int BM, int BN, int NWM>
@@ -348,10 +351,10 @@ struct DenseArgs {
   CacheDst cache;
 };
 
-template <typename TA, int BM, int BN>
-__global__ __launch_bounds__((gemm_threads<TA, TA, BM, BN, 2>())) void gemm_dense_k(DenseArgs a) {
+template <typename TA, int BM, int BN, int NWM>
+__global__ __launch_bounds__((gemm_threads<TA, TA, BM, BN, NWM>())) void gemm_dense_k(DenseArgs a) {
   // bf16: weights straight into fragments; fp32: both operands through LDS
-  typedef GemmML<TA, TA, BM, BN, 2> ML;
+  typedef GemmML<TA, TA, BM, BN, NWM> ML;
   __shared__ __attribute__((aligned(16))) TA smem[ML::SMEM];
   const int m0 = blockIdx.x * BM, n0 = blockIdx.y * BN;
   const TA* ap[ML::A_LD];
@@ -935,14 +938,22 @@ void launch_gemm(int act, int mode, const void* A, int M, int K, const void* B0,
                  const CacheDst* cache, hipStream_t s) {
   DenseArgs a{A, M, K, B0, n1, B1, n2, B2, N, C, ldc, R, mode, CacheDst{}};
   if (cache) a.cache = *cache;
-  if (M > 1024) {
+  if (act == ACT_BF16 && M > 1024 && DENSE_WIDE) {
+    // 64-row tiles, waves of 32 columns side by side: 256 columns per block
+    // when that still gives two blocks per CU, else 128
+    constexpr int N8 = gemm_threads<uint16_t, uint16_t, 64, 256, 1>();
+    constexpr int N4 = gemm_threads<uint16_t, uint16_t, 64, 128, 1>();
+    const long b256 = (long)((M + 63) / 64) * ((N + 255) / 256);
+    if (b256 >= 512) gemm_dense_k<uint16_t, 64, 256, 1><<<dim3((M + 63) / 64, (N + 255) / 256), N8, 0, s>>>(a);
+    else gemm_dense_k<uint16_t, 64, 128, 1><<<dim3((M + 63) / 64, (N + 127) / 128), N4, 0, s>>>(a);
+  } else if (M > 1024) {
     dim3 grid((M + 127) / 128, (N + 127) / 128);
-    if (act == ACT_BF16) gemm_dense_k<uint16_t, 128, 128><<<grid, gemm_threads<uint16_t, uint16_t, 128, 128, 2>(), 0, s>>>(a);
-    else gemm_dense_k<float, 128, 128><<<grid, 256, 0, s>>>(a);
+    if (act == ACT_BF16) gemm_dense_k<uint16_t, 128, 128, 2><<<grid, gemm_threads<uint16_t, uint16_t, 128, 128, 2>(), 0, s>>>(a);
+    else gemm_dense_k<float, 128, 128, 2><<<grid, 256, 0, s>>>(a);
   } else {
     dim3 grid((M + 63) / 64, (N + 63) / 64);
-    if (act == ACT_BF16) gemm_dense_k<uint16_t, 64, 64><<<grid, gemm_threads<uint16_t, uint16_t, 64, 64, 2>(), 0, s>>>(a);
-    else gemm_dense_k<float, 64, 64><<<grid, 256, 0, s>>>(a);
+    if (act == ACT_BF16) gemm_dense_k<uint16_t, 64, 64, 2><<<grid, gemm_threads<uint16_t, uint16_t, 64, 64, 2>(), 0, s>>>(a);
+    else gemm_dense_k<float, 64, 64, 2><<<grid, 256, 0, s>>>(a);
   }
 }
 
