@@ -80,6 +80,16 @@ def test_many_rows_per_expert_uses_tiled_expert_path(act, expert):
     _run(pair, 2, [30, 5], 100, 15)
 
 
+@pytest.mark.parametrize("expert,D,F", [("bf16", 384, 192), ("fp8", 384, 384)])
+def test_tiled_expert_path_narrow_column_blocks(expert, D, F):
+    # ~100 rows per expert take the LDS-tiled grouped GEMMs; D % 256 != 0 (and
+    # for bf16 F % 128 != 0) selects their 128-column blocks, with 3 column
+    # blocks and ragged 64-row expert tiles
+    cfg = _cfg(E=4, k=2, expert=expert, V=384, D=D, F=F)
+    pair = Pair(cfg, 17)
+    _run(pair, 2, [30, 5], 100, 17)
+
+
 def test_injected_router_ties_are_bit_exact():
     cfg = _cfg(E=8, k=3)
     pair = Pair(cfg, 16)
