@@ -182,17 +182,16 @@ struct Mainloop {
 // two-operand form.  Waves: NWM along the rows x BN/WN along the columns,
 // each a (BM/NWM) x WN tile; a wider block reads each activation row fewer
 // times from L2, and one wave along the rows reads each weight once per block
-// (at twice the LDS reads of two).  An LDS buffer holds S consecutive 64-wide
-// k-tiles, so the block meets at a barrier once per S k-tiles: each barrier
-// holds every wave until the slowest has stored its share of the next tiles,
-// and with one barrier per k-tile that wait, not the matrix cores, set the
-// pace.  Registers hold a ring of P >= 2S k-tiles.
-template <typename TW, int BM, int BN, int P, int NWM, int WN_, int S>
+// (at twice the LDS reads of two).  Each k-tile ends at a block barrier
+// after the next tile's activations are stored, which holds every wave until
+// the slowest has stored its share; with one block per CU nothing fills the
+// matrix cores meanwhile, so the grouped GEMMs keep a block under 128 VGPRs
+// (two per CU).  Registers hold a ring of P k-tiles.
+template <typename TW, int BM, int BN, int P, int NWM, int WN_>
 struct MainloopD {
   typedef uint16_t TA;
   static constexpr int WN = WN_;            // columns per wave
-  static constexpr int BK = 64;
-  static constexpr int LDK = 64 * S + 16;   // LDS row: 128 S + 32 bytes (32 mod 64: conflict-free reads)
+  static constexpr int BK = 64, LDK = 80;   // 160-byte LDS rows (32 mod 64: conflict-free reads)
   static constexpr bool FP8 = sizeof(TW) == 1;
   static constexpr int NWN = BN / WN, NT = 64 * NWM * NWN;   // waves along the columns, threads
   static constexpr int WM = BM / NWM;       // rows per wave
@@ -201,7 +200,7 @@ struct MainloopD {
   static_assert(BM * 8 % NT == 0, "A staging");
   static constexpr int NB = FP8 ? 1 : 2;    // 16-byte weight loads per column tile and k-tile
   static constexpr int SMEM = 2 * BM * LDK;
-  static_assert(P % S == 0 && P >= 2 * S, "the tiles a barrier step stores were loaded at least S steps before");
+  static_assert(P >= 2, "a step stores the next tile's activations from another stage");
   static __device__ __forceinline__ int a_row(int p) { return (threadIdx.x >> 3) + (NT / 8) * p; }
   static __device__ __forceinline__ int a_col() { return (threadIdx.x & 7) * 8; }
   static __device__ __forceinline__ int wave_m() { return (threadIdx.x >> 6) / NWN; }
@@ -232,8 +231,8 @@ struct MainloopD {
 #pragma unroll
       for (int p = 0; p < A_LD; p++) ra[st][p] = *reinterpret_cast<const u32x4*>(ap[p] + kc * BK + a_col());
     };
-    auto sstore = [&](int st, int buf, int j, bool ok) {   // tiles past the end are stored as zeros
-      TA* sa = smem + buf * BM * LDK + j * BK;
+    auto sstore = [&](int st, int buf, bool ok) {   // tiles past the end are stored as zeros
+      TA* sa = smem + buf * BM * LDK;
 #pragma unroll
       for (int p = 0; p < A_LD; p++) {
         u32x4 u = ra[st][p];
@@ -260,14 +259,13 @@ struct MainloopD {
 
 #pragma unroll
     for (int st = 0; st < P; st++) gload(st, st);
-#pragma unroll
-    for (int j = 0; j < S; j++) sstore(j, 0, j, j < nk);
+    sstore(0, 0, true);
     __syncthreads();
     for (int kb = 0; kb < nkp; kb += P) {
 #pragma unroll
       for (int st = 0; st < P; st++) {
-        const int kt = kb + st;   // kt mod S = st mod S (P is a multiple of S)
-        const TA* sa = smem + ((kt / S) & 1) * BM * LDK + (st % S) * BK;
+        const int kt = kb + st;
+        const TA* sa = smem + (kt & 1) * BM * LDK;
         FragBF af[2][RT];
 #pragma unroll
         for (int ks = 0; ks < 2; ks++)
@@ -283,12 +281,9 @@ struct MainloopD {
             for (int rt = 0; rt < RT; rt++) mma(acc[rt][ct], af[ks][rt], bf);
           }
         __builtin_amdgcn_sched_barrier(0);
-        if (st % S == S - 1) {   // A of tiles kt+1 .. kt+S (loaded P-S .. P-1 steps ago)
-#pragma unroll
-          for (int j = 0; j < S; j++) sstore((st + 1 + j) % P, ((kt + 1) / S) & 1, j, kt + 1 + j < nk);
-        }
-        gload(st, kt + P);   // stage st is consumed
-        if (st % S == S - 1) __syncthreads();
+        sstore((st + 1) % P, (kt + 1) & 1, kt + 1 < nk);   // A of tile kt+1 (loaded P-1 steps ago)
+        gload(st, kt + P);                                  // stage st is consumed
+        __syncthreads();
       }
     }
   }
@@ -297,23 +292,13 @@ struct MainloopD {
 // Main loop of the LDS-tiled GEMMs: bf16 activations take MainloopD with NWM
 // waves along the rows (2: 64-column wave tiles from BN = 128 on; 1: BN/32
 // waves of 32 columns side by side), fp32 activations Mainloop (2 x 2 waves).
-// The grouped GEMMs (one wave along the rows) stage GROUP_S k-tiles per LDS
-// buffer with a GROUP_P-deep register ring; the dense ones one k-tile and
-// GEMM_P.  Expert tiles of 64 rows keep a block under 128 VGPRs, so two blocks
+// Register rings: GROUP_P k-tiles for one wave along the rows, GEMM_P for
+// two.  Expert tiles of 64 rows keep a block under 128 VGPRs, so two blocks
 // share a CU and one block's barrier waits are filled by the other's MFMAs
 // (batch-8 fp8 gate/up: 176 us at 128-row tiles with one block per CU, 143 at
-// 64; 2 k-tiles per LDS buffer gained nothing at 64 rows).
-#ifndef GROUP_NWM
-#define GROUP_NWM 1
-#endif
-#ifndef GROUP_S
-#define GROUP_S 1
-#endif
+// 64).
 #ifndef GROUP_P
 #define GROUP_P 2
-#endif
-#ifndef GROUP_WPE
-#define GROUP_WPE 1   // minimum waves per SIMD the grouped GEMMs are compiled for
 #endif
 #ifndef GROUP_BM
 #define GROUP_BM 64   // rows of a bf16-activation expert tile
@@ -324,8 +309,8 @@ struct MainloopD {
 template <typename TA, typename TW, int BM, int BN, int NWM>
 using GemmML = typename std::conditional<
     sizeof(TA) == 2,
-    typename std::conditional<NWM == 1, MainloopD<TW, BM, BN, GROUP_P, 1, 32, GROUP_S>,
-                              MainloopD<TW, BM, BN, GEMM_P, 2, (BN >= 128 ? 64 : BN / 2), 1>>::type,
+    typename std::conditional<NWM == 1, MainloopD<TW, BM, BN, GROUP_P, 1, 32>,
+                              MainloopD<TW, BM, BN, GEMM_P, 2, (BN >= 128 ? 64 : BN / 2)>>::type,
     Mainloop<TA, TW, BM, BN, GEMM_P>>::type;
 template <typename TA, typename TW, int BM, int BN, int NWM>
 constexpr int gemm_threads() {
@@ -462,7 +447,7 @@ __device__ __forceinline__ bool group_item(const GroupArgs& a, int& tile, int& c
 // gate/up: BN weight rows = BN/2 SwiGLU outputs, rows ordered in 32-row
 // groups [gate f..f+15, up f..f+15] so each wave holds matching gate and up tiles.
 template <typename TA, typename TW, int BM, int BN, int NWM>
-__global__ __launch_bounds__((gemm_threads<TA, TW, BM, BN, NWM>()), (NWM == 1 ? GROUP_WPE : 1)) void gateup_lds_k(GroupArgs a) {
+__global__ __launch_bounds__((gemm_threads<TA, TW, BM, BN, NWM>())) void gateup_lds_k(GroupArgs a) {
   typedef GemmML<TA, TW, BM, BN, NWM> ML;
   __shared__ __attribute__((aligned(16))) TA smem[ML::SMEM];
   int tile_id, col;
@@ -524,7 +509,7 @@ __global__ __launch_bounds__((gemm_threads<TA, TW, BM, BN, NWM>()), (NWM == 1 ? 
 }
 
 template <typename TA, typename TW, int BM, int BN, int NWM>
-__global__ __launch_bounds__((gemm_threads<TA, TW, BM, BN, NWM>()), (NWM == 1 ? GROUP_WPE : 1)) void down_lds_k(GroupArgs a) {
+__global__ __launch_bounds__((gemm_threads<TA, TW, BM, BN, NWM>())) void down_lds_k(GroupArgs a) {
   typedef GemmML<TA, TW, BM, BN, NWM> ML;
   __shared__ __attribute__((aligned(16))) TA smem[ML::SMEM];
   int tile_id, col;
@@ -970,10 +955,10 @@ void launch_gateup_lds(int act, const void* u2, const int32_t* perm, int k, cons
   if (act == ACT_F32) {   // 128 weight rows = 64 SwiGLU outputs per block
     gateup_lds_k<float, float, 128, 128, 2><<<grid(F / 64), 256, 0, s>>>(a);
   } else if (F % 128 == 0) {   // 256 weight rows: each routed row is read F/128 times
-    constexpr int N8 = gemm_threads<uint16_t, uint8_t, GROUP_BM, 256, GROUP_NWM>();
-    constexpr int N16 = gemm_threads<uint16_t, uint16_t, GROUP_BM, 256, GROUP_NWM>();
-    if (w.wdt == DG_FP8E4M3) gateup_lds_k<uint16_t, uint8_t, GROUP_BM, 256, GROUP_NWM><<<grid(F / 128), N8, 0, s>>>(a);
-    else gateup_lds_k<uint16_t, uint16_t, GROUP_BM, 256, GROUP_NWM><<<grid(F / 128), N16, 0, s>>>(a);
+    constexpr int N8 = gemm_threads<uint16_t, uint8_t, GROUP_BM, 256, 1>();
+    constexpr int N16 = gemm_threads<uint16_t, uint16_t, GROUP_BM, 256, 1>();
+    if (w.wdt == DG_FP8E4M3) gateup_lds_k<uint16_t, uint8_t, GROUP_BM, 256, 1><<<grid(F / 128), N8, 0, s>>>(a);
+    else gateup_lds_k<uint16_t, uint16_t, GROUP_BM, 256, 1><<<grid(F / 128), N16, 0, s>>>(a);
   } else {
     constexpr int N8 = gemm_threads<uint16_t, uint8_t, GROUP_BM, 128, 2>();
     constexpr int N16 = gemm_threads<uint16_t, uint16_t, GROUP_BM, 128, 2>();
@@ -992,10 +977,10 @@ void launch_down_lds(int act, const void* H, const MoeW& w, const int4* tiles,
   if (act == ACT_F32) {
     down_lds_k<float, float, 128, 128, 2><<<grid(D / 128), 256, 0, s>>>(a);
   } else if (D % 256 == 0) {
-    constexpr int N8 = gemm_threads<uint16_t, uint8_t, GROUP_BM, 256, GROUP_NWM>();
-    constexpr int N16 = gemm_threads<uint16_t, uint16_t, GROUP_BM, 256, GROUP_NWM>();
-    if (w.wdt == DG_FP8E4M3) down_lds_k<uint16_t, uint8_t, GROUP_BM, 256, GROUP_NWM><<<grid(D / 256), N8, 0, s>>>(a);
-    else down_lds_k<uint16_t, uint16_t, GROUP_BM, 256, GROUP_NWM><<<grid(D / 256), N16, 0, s>>>(a);
+    constexpr int N8 = gemm_threads<uint16_t, uint8_t, GROUP_BM, 256, 1>();
+    constexpr int N16 = gemm_threads<uint16_t, uint16_t, GROUP_BM, 256, 1>();
+    if (w.wdt == DG_FP8E4M3) down_lds_k<uint16_t, uint8_t, GROUP_BM, 256, 1><<<grid(D / 256), N8, 0, s>>>(a);
+    else down_lds_k<uint16_t, uint16_t, GROUP_BM, 256, 1><<<grid(D / 256), N16, 0, s>>>(a);
   } else {
     constexpr int N8 = gemm_threads<uint16_t, uint8_t, GROUP_BM, 128, 2>();
     constexpr int N16 = gemm_threads<uint16_t, uint16_t, GROUP_BM, 128, 2>();
