@@ -129,8 +129,15 @@ __global__ __launch_bounds__(256) void plan_k(const int32_t* __restrict__ ids, i
   auto load_row = [&](int r, int (&v)[8]) {   // clamped loads, then a select: no branches
     const bool rok = r < rows;
     const size_t base = (size_t)(rok ? r : 0) * k;
+    if (k == 8) {   // uniform: a row's ids are 32 aligned bytes, two 16-byte loads
+      const int4 lo = *reinterpret_cast<const int4*>(ids + base);
+      const int4 hi = *reinterpret_cast<const int4*>(ids + base + 4);
+      v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+      v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+    } else {
 #pragma unroll
-    for (int j = 0; j < 8; j++) v[j] = ids[base + (j < k ? j : 0)];
+      for (int j = 0; j < 8; j++) v[j] = ids[base + (j < k ? j : 0)];
+    }
 #pragma unroll
     for (int j = 0; j < 8; j++) v[j] = rok && j < k ? v[j] : -1;
   };
