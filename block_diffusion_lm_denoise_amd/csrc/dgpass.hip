@@ -21,8 +21,10 @@ constexpr int ROUTE_MIN_ROWS = 2048;   // fused routing kernel from this many to
 struct Layout {
   size_t cov;       // [L][E] int32 expert counts of the last pass (offset 0)
   size_t x, u, qkv, o, x1, u2, rl, ids, gates, counts, offsets, perm, inv, tiles, ntiles, H, Y;
-  size_t po, pml, lpm, lpi, lps, total;
-  long part_cap;
+  size_t lpm, lpi, lps;
+  size_t fixed;     // bytes before the attention split partials
+  size_t po, pml, total;
+  long part_cap;    // (row, head) entries of split partials the workspace holds
   int max_tiles;
 };
 
@@ -44,7 +46,13 @@ size_t router_floats(const dg_config& c, int rows) {
   return (size_t)rows * c.E * router_split(c, rows);
 }
 
-Layout layout(const dg_config& c, int rows) {
+// bytes of one (row, head) entry of the attention split partials: O and (m, l)
+size_t part_entry_bytes(const dg_config& c) { return (size_t)c.hd * 4 + 2 * 4; }
+
+// Workspace carve for `rows` token rows with room for `part_entries` (row,
+// head) entries of attention split partials, which come last so that a
+// call can use whatever room the caller's workspace leaves for them.
+Layout layout(const dg_config& c, int rows, long part_entries) {
   Layout L{};
   const size_t a = esize(c.act_dtype);
   const size_t R = rows > 0 ? rows : 1;
@@ -75,15 +83,27 @@ Layout layout(const dg_config& c, int rows) {
   L.ntiles = take(4);
   L.H = take(slots * c.F * a);
   L.Y = take(slots * c.D * a);
-  L.part_cap = attn_partial_entries((int)R, c.Hq);
-  L.po = take((size_t)L.part_cap * c.hd * 4);
-  L.pml = take((size_t)L.part_cap * 2 * 4);
   const size_t nt = (c.V + 63) / 64;  // LM-head partials per row (64-column chunks)
   L.lpm = take(R * nt * 4);
   L.lpi = take(R * nt * 4);
   L.lps = take(R * nt * 4);
+  L.fixed = off;
+  L.part_cap = part_entries > 0 ? part_entries : 0;
+  L.po = take((size_t)L.part_cap * c.hd * 4);
+  L.pml = take((size_t)L.part_cap * 2 * 4);
   L.total = off;
   return L;
+}
+
+// the carve a call uses: the split partials it would like (its key counts),
+// cut to what the caller's workspace holds beyond the fixed part
+Layout call_layout(const dg_config& c, int rows, int max_keys, size_t ws_bytes) {
+  Layout L = layout(c, rows, 0);
+  long want = attn_partial_entries(rows, c.Hq, max_keys);
+  const size_t room = ws_bytes > L.fixed ? ws_bytes - L.fixed : 0;
+  // po and pml are each rounded up to 256 bytes
+  const long fit = room > 512 ? (long)((room - 512) / part_entry_bytes(c)) : 0;
+  return layout(c, rows, want < fit ? want : fit);
 }
 
 bool valid_cfg(const dg_config* c) {
@@ -134,6 +154,25 @@ T* at(const Ctx& c, size_t off) {
 
 void tap_copy(void* dst, const void* src, size_t bytes, hipStream_t s) {
   if (dst && bytes) (void)hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, s);
+}
+
+// record stage event [l][stage][which] of the caller's stage_events, if any
+void stage_event(const dg_taps* t, int l, int stage, int which, hipStream_t s) {
+  if (!t || !t->stage_events) return;
+  void* e = t->stage_events[((size_t)l * DG_NSTAGES + stage) * 2 + which];
+  if (e) (void)hipEventRecord((hipEvent_t)e, s);
+}
+
+// layer l's input rows replaced by the caller's (x and its first RMSNorm)
+void inject_layer_input(const Ctx& c, int l) {
+  const dg_taps* t = c.taps;
+  if (!t || !t->inject_x) return;
+  const dg_config& cf = c.m->cfg;
+  const size_t a = esize(cf.act_dtype), bytes = (size_t)c.R * cf.D * a;
+  (void)hipMemcpyAsync(at<void>(c, c.L.x), (const char*)t->inject_x + (size_t)l * bytes, bytes,
+                       hipMemcpyDeviceToDevice, c.s);
+  launch_rmsnorm(cf.act_dtype == DG_BF16 ? ACT_BF16 : ACT_F32, at<void>(c, c.L.x),
+                 c.m->w.layers[l].g1, c.R, cf.D, cf.eps, at<void>(c, c.L.u), c.s);
 }
 
 // waves splitting the contraction: 4, or 2 when 4 would leave each wave an odd
@@ -255,7 +294,7 @@ void moe_block(const Ctx& c, int l, const float* gnext) {
   g.escale = w.escale;
   g.tiles = at<int4>(c, c.L.tiles);
   g.ntiles = at<int32_t>(c, c.L.ntiles);
-  if (t && t->ev_gateup && t->ev_gateup[2 * l]) (void)hipEventRecord((hipEvent_t)t->ev_gateup[2 * l], s);
+  stage_event(t, l, DG_STAGE_GATEUP, 0, s);
   if (stream) {
     g.A = at<void>(c, c.L.u2);
     g.K = cf.D;
@@ -272,11 +311,11 @@ void moe_block(const Ctx& c, int l, const float* gnext) {
                       at<int4>(c, c.L.tiles), at<int32_t>(c, c.L.ntiles), max_tiles, cf.D, cf.F,
                       at<void>(c, c.L.H), s);
   }
-  if (t && t->ev_gateup && t->ev_gateup[2 * l + 1])
-    (void)hipEventRecord((hipEvent_t)t->ev_gateup[2 * l + 1], s);
+  stage_event(t, l, DG_STAGE_GATEUP, 1, s);
   if (t && t->hmid)
     launch_unpermute(act, at<void>(c, c.L.H), at<int32_t>(c, c.L.inv), (int)(R * k), cf.F,
                      (char*)t->hmid + l * R * k * cf.F * a, s);
+  stage_event(t, l, DG_STAGE_DOWN, 0, s);
   if (stream) {
     g.A = at<void>(c, c.L.H);
     g.K = cf.F;
@@ -293,6 +332,7 @@ void moe_block(const Ctx& c, int l, const float* gnext) {
     launch_down_lds(act, at<void>(c, c.L.H), mw, at<int4>(c, c.L.tiles), at<int32_t>(c, c.L.ntiles),
                     max_tiles, cf.D, cf.F, at<void>(c, c.L.Y), s);
   }
+  stage_event(t, l, DG_STAGE_DOWN, 1, s);
   if (t && t->yexp)
     launch_unpermute(act, at<void>(c, c.L.Y), at<int32_t>(c, c.L.inv), (int)(R * k), cf.D,
                      (char*)t->yexp + l * R * k * D * a, s);
@@ -345,7 +385,7 @@ dg_status dg_model_init(dg_model* m, const dg_config* cfg, const dg_weights* w) 
 
 size_t dg_workspace_bytes(const dg_config* cfg, int32_t max_rows, int32_t max_keys) {
   if (!valid_cfg(cfg) || max_rows < 1 || max_keys < 0) return 0;
-  return layout(*cfg, max_rows).total;
+  return layout(*cfg, max_rows, attn_partial_entries(max_rows, cfg->Hq, max_keys)).total;
 }
 
 dg_status dg_kv_prefill(const dg_model* m, dg_kv* kv, const int32_t* tokens, int32_t B, int32_t T,
@@ -356,14 +396,16 @@ dg_status dg_kv_prefill(const dg_model* m, dg_kv* kv, const int32_t* tokens, int
   for (int l = 0; l < cf.L; l++)
     if (!kv->k[l] || !kv->v[l]) return DG_ERR_INVALID;
   Lens lens{};
+  int maxkeys = 0;
   for (int b = 0; b < B; b++) {
     if (kv->len[b] < 0 || kv->len[b] > kv->cap) return DG_ERR_INVALID;
     if ((long)kv->len[b] + T > kv->cap) return DG_ERR_CAPACITY;
     lens.v[b] = kv->len[b];
+    maxkeys = kv->len[b] + T > maxkeys ? kv->len[b] + T : maxkeys;
   }
   if ((long)B * T > (1L << 20)) return DG_ERR_UNSUPPORTED;
   const int R = B * T;
-  Ctx c{m, (char*)ws, layout(cf, R), R, taps, (hipStream_t)stream, false};
+  Ctx c{m, (char*)ws, call_layout(cf, R, maxkeys, ws_bytes), R, taps, (hipStream_t)stream, false};
   if (c.L.total > ws_bytes) return DG_ERR_WORKSPACE;
 
   (void)hipGetLastError();  // clear a stale error so the status below is ours
@@ -375,6 +417,7 @@ dg_status dg_kv_prefill(const dg_model* m, dg_kv* kv, const int32_t* tokens, int
                     at<void>(c, c.L.u), s);
   for (int l = 0; l < cf.L; l++) {
     const dg_layer_weights& w = m->w.layers[l];
+    inject_layer_input(c, l);
     if (l == cf.L - 1 && !(taps && taps->qkv)) {
       // nothing downstream reads the last layer's queries or output: its K
       // and V columns only, straight into the cache
@@ -392,7 +435,9 @@ dg_status dg_kv_prefill(const dg_model* m, dg_kv* kv, const int32_t* tokens, int
     AttnArgsHost ah{act, at<void>(c, c.L.qkv), QKV, kv->k[l], kv->v[l], kv->cap, nullptr, nullptr,
                     B, T, cf.Hq, cf.Hkv, cf.hd, 1, lens, at<void>(c, c.L.o), at<float>(c, c.L.po),
                     at<float>(c, c.L.pml), c.L.part_cap};
+    stage_event(taps, l, DG_STAGE_ATTN, 0, s);
     launch_attention(ah, s);
+    stage_event(taps, l, DG_STAGE_ATTN, 1, s);
     if (taps) tap_copy(taps->attn ? (char*)taps->attn + (size_t)l * R * QD * a : nullptr,
                        at<void>(c, c.L.o), (size_t)R * QD * a, s);
     moe_block(c, l, m->w.layers[l + 1].g1);
@@ -412,17 +457,19 @@ static dg_status denoise(const dg_model* m, const dg_kv* kv, const int32_t* canv
   const dg_config& cf = m->cfg;
   Lens lens{};
   bool any_prefix = false;
+  int maxkeys = 0;
   for (int b = 0; b < B; b++) {
     if (kv->len[b] < 0 || (kv->len[b] > 0 && kv->len[b] > kv->cap)) return DG_ERR_INVALID;
     lens.v[b] = kv->len[b];
     any_prefix |= kv->len[b] > 0;
+    maxkeys = kv->len[b] + N > maxkeys ? kv->len[b] + N : maxkeys;
   }
   if (any_prefix)
     for (int l = 0; l < cf.L; l++)
       if (!kv->k[l] || !kv->v[l]) return DG_ERR_INVALID;
   if ((long)B * N > (1L << 20)) return DG_ERR_UNSUPPORTED;
   const int R = B * N;
-  Ctx c{m, (char*)ws, layout(cf, R), R, taps, (hipStream_t)stream, true};
+  Ctx c{m, (char*)ws, call_layout(cf, R, maxkeys, ws_bytes), R, taps, (hipStream_t)stream, true};
   if (c.L.total > ws_bytes) return DG_ERR_WORKSPACE;
 
   (void)hipGetLastError();
@@ -434,6 +481,7 @@ static dg_status denoise(const dg_model* m, const dg_kv* kv, const int32_t* canv
                     at<void>(c, c.L.u), s);
   for (int l = 0; l < cf.L; l++) {
     const dg_layer_weights& w = m->w.layers[l];
+    inject_layer_input(c, l);
     dense_gemm(c, GEMM_STORE, at<void>(c, c.L.u), R, cf.D, w.wq, QD, w.wk, KD, w.wv, QKV,
                at<void>(c, c.L.qkv), QKV, nullptr, nullptr);
     if (taps) tap_copy(taps->qkv ? (char*)taps->qkv + (size_t)l * R * QKV * a : nullptr,
@@ -442,15 +490,20 @@ static dg_status denoise(const dg_model* m, const dg_kv* kv, const int32_t* canv
     AttnArgsHost ah{act, qkv, QKV, kv->k[l], kv->v[l], kv->cap, qkv + QD * a, qkv + (QD + KD) * a,
                     B, N, cf.Hq, cf.Hkv, cf.hd, 0, lens, at<void>(c, c.L.o), at<float>(c, c.L.po),
                     at<float>(c, c.L.pml), c.L.part_cap};
+    stage_event(taps, l, DG_STAGE_ATTN, 0, s);
     launch_attention(ah, s);
+    stage_event(taps, l, DG_STAGE_ATTN, 1, s);
     if (taps) tap_copy(taps->attn ? (char*)taps->attn + (size_t)l * R * QD * a : nullptr,
                        at<void>(c, c.L.o), (size_t)R * QD * a, s);
     moe_block(c, l, l + 1 < cf.L ? m->w.layers[l + 1].g1 : m->w.gf);
   }
   // head: logits tiles reduced to (max, argmax, sum exp), merged per row
-  const int nparts = launch_lmhead(act, at<void>(c, c.L.u), R, cf.D, m->w.lm, cf.V, at<float>(c, c.L.lpm),
+  const void* head_in = (taps && taps->inject_uf) ? taps->inject_uf : at<void>(c, c.L.u);
+  stage_event(taps, cf.L - 1, DG_STAGE_HEAD, 0, s);
+  const int nparts = launch_lmhead(act, head_in, R, cf.D, m->w.lm, cf.V, at<float>(c, c.L.lpm),
                                    at<int32_t>(c, c.L.lpi), at<float>(c, c.L.lps),
                                    taps ? taps->logits : nullptr, s);
+  stage_event(taps, cf.L - 1, DG_STAGE_HEAD, 1, s);
   if (taps) tap_copy(taps->uf, at<void>(c, c.L.u), (size_t)R * cf.D * a, s);
   nx.counts = at<int32_t>(c, c.L.cov);
   nx.L = cf.L;

@@ -47,6 +47,32 @@ struct AttnArgs {
   int nqt, groups;   // query tiles; (request, kv head, split) groups
 };
 
+// Block id -> (request b, kv head gh, key split, query tile qt).  The query
+// tiles that share one (request, kv head, key split) -- and so read the same
+// K/V -- have ids 8 apart and run on one XCD, whose L2 then serves the K/V
+// tiles after the first read.  False for the padding ids of the last group.
+__host__ __device__ inline bool attn_block(int id, int nqt, int groups, int nsplit, int Hkv,
+                                           int& b, int& gh, int& split, int& qt) {
+  const int g = (id / (8 * nqt)) * 8 + id % 8;
+  qt = (id % (8 * nqt)) / 8;
+  if (g >= groups) return false;
+  const int bh = g / nsplit;
+  split = g % nsplit;
+  b = bh / Hkv;
+  gh = bh % Hkv;
+  return true;
+}
+
+// The key a block addresses for key index kk of its staged tiles.  Keys of
+// the split [kbeg, kend) are read as they are; the staged tiles run past the
+// split end (the pipeline loads whole tiles, and two tiles ahead), and those
+// slots read a key of the same request that holds data: kbeg when the split
+// has keys, else key 0 (a request always has at least one key: T >= 1).
+// Their scores are masked to -inf, so the data only has to be finite.
+__host__ __device__ inline int attn_key_index(int kk, int kbeg, int kend) {
+  return kk < kend ? kk : (kbeg < kend ? kbeg : 0);
+}
+
 template <typename TA, int HD>
 __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
   typedef typename FragOf<TA>::type Frag;
@@ -67,14 +93,8 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) TA ks2[2][KT * KLD];
   __shared__ __attribute__((aligned(16))) TA vt2[2][HD * VLD];
 
-  // 1-D grid: the query tiles that share one (request, kv head, key split)
-  // -- and so read the same K/V -- have ids 8 apart and run on one XCD,
-  // whose L2 then serves the K/V tiles after the first read
-  const int id = blockIdx.x, nqt = a.nqt;
-  const int g = (id / (8 * nqt)) * 8 + id % 8, qt = (id % (8 * nqt)) / 8;
-  if (g >= a.groups) return;
-  const int bh = g / a.nsplit, split = g % a.nsplit;
-  const int b = bh / a.Hkv, gh = bh % a.Hkv;
+  int b, gh, split, qt;
+  if (!attn_block(blockIdx.x, a.nqt, a.groups, a.nsplit, a.Hkv, b, gh, split, qt)) return;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, l16 = lane & 15, g4 = lane >> 4;
   const int P = a.len.v[b];
 
@@ -105,8 +125,8 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
   float mrow = -INFINITY, lsum = 0.f;
 
   // K/V of key kk: the cache, or in mode 0 the canvas rows of the qkv buffer
-  // for kk >= P.  Keys past the split end read key kbeg (a valid key, so the
-  // data is finite): their scores are masked to -inf, so they add nothing.
+  // for kk >= P.  Slots past the split end read a key of this request
+  // (attn_key_index): their scores are masked to -inf, so they add nothing.
   // Straight-line selects keep the loads of the next tile in flight.
   const TA* const kc = (const TA*)a.kc + ((size_t)b * a.Hkv + gh) * a.cap * HD;
   const TA* const vc = (const TA*)a.vc + ((size_t)b * a.Hkv + gh) * a.cap * HD;
@@ -117,7 +137,7 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
   const int qlim_all = a.mode == 0 ? 0x7fffffff : P + qt * a.QT;
   const size_t ldq = (size_t)a.ldq;
   auto kptr = [&](int kk, const TA* cache, const TA* fresh) -> const TA* {
-    const int k = kk < kend ? kk : kbeg;
+    const int k = attn_key_index(kk, kbeg, kend);
     const bool f = k >= fresh0;
     return (f ? fresh : cache) + (size_t)(f ? k - fresh0 : k) * (f ? ldq : (size_t)HD);
   };
@@ -440,20 +460,60 @@ __global__ __launch_bounds__(256) void attn_merge_k(const float* __restrict__ po
 // ---------------------------------------------------------------------------
 // key splits: enough blocks to fill the chip several times over (each block
 // is a short latency chain), at least ATTN_MIN_SPLIT_KEYS keys per split
-#ifndef ATTN_TARGET_BLOCKS
-#define ATTN_TARGET_BLOCKS 512
-#endif
-#ifndef ATTN_MIN_SPLIT_KEYS
-#define ATTN_MIN_SPLIT_KEYS 128
-#endif
+constexpr int ATTN_TARGET_BLOCKS = 512;
+constexpr int ATTN_MIN_SPLIT_KEYS = 128;
+constexpr int ATTN_MAX_SPLIT = 16;
+constexpr long ATTN_MAX_PART_ENTRIES = 1L << 18;
 
-long attn_partial_entries(int rows, int Hq) {
-  // bounded split buffer: at most 2^18 (row, head) entries across all splits
-  long full = (long)rows * Hq * 16;
-  return full < (1L << 18) ? full : (1L << 18);
+long attn_partial_entries(int rows, int Hq, int max_keys) {
+  // bounded split buffer: at most 2^18 (row, head) entries across all splits;
+  // no more splits than the key count allows (max_keys 0: not known)
+  int splits = ATTN_MAX_SPLIT;
+  if (max_keys > 0) {
+    const int by_keys = (max_keys + ATTN_MIN_SPLIT_KEYS - 1) / ATTN_MIN_SPLIT_KEYS;
+    splits = by_keys < splits ? by_keys : splits;
+  }
+  if (splits <= 1) return 0;
+  const long full = (long)rows * Hq * splits;
+  return full < ATTN_MAX_PART_ENTRIES ? full : ATTN_MAX_PART_ENTRIES;
+}
+
+struct AttnPlan {
+  int G, QT, nqt, nsplit, split_len, groups;
+  unsigned grid;
+};
+
+AttnPlan plan_attention(int B, int T, const Lens& len, int Hq, int Hkv, long part_cap) {
+  AttnPlan p{};
+  p.G = Hq / Hkv;
+  p.QT = 64 / p.G;
+  int maxkeys = 0;
+  for (int b = 0; b < B; b++) maxkeys = maxkeys > len.v[b] + T ? maxkeys : len.v[b] + T;
+  p.nqt = (T + p.QT - 1) / p.QT;
+  const long base = (long)p.nqt * B * Hkv;
+  int nsplit = 1;
+  if (base < ATTN_TARGET_BLOCKS) {
+    nsplit = (int)((ATTN_TARGET_BLOCKS + base - 1) / base);
+    const int by_keys = (maxkeys + ATTN_MIN_SPLIT_KEYS - 1) / ATTN_MIN_SPLIT_KEYS;
+    if (nsplit > by_keys) nsplit = by_keys;
+    if (nsplit > ATTN_MAX_SPLIT) nsplit = ATTN_MAX_SPLIT;
+    const long entries = (long)B * T * Hq;
+    while (nsplit > 1 && entries * nsplit > part_cap) nsplit--;
+    if (nsplit < 1) nsplit = 1;
+  }
+  int split_len = (maxkeys + nsplit - 1) / nsplit;
+  split_len = (split_len + KT - 1) / KT * KT;
+  nsplit = (maxkeys + split_len - 1) / split_len;
+  if (nsplit < 1) nsplit = 1;
+  p.split_len = split_len;
+  p.nsplit = nsplit;
+  p.groups = B * Hkv * nsplit;
+  p.grid = (unsigned)(((p.groups + 7) / 8) * 8 * p.nqt);
+  return p;
 }
 
 void launch_attention(const AttnArgsHost& h, hipStream_t s) {
+  const AttnPlan p = plan_attention(h.B, h.T, h.len, h.Hq, h.Hkv, h.part_cap);
   AttnArgs a{};
   a.q = h.q;
   a.ldq = h.ldq;
@@ -465,8 +525,8 @@ void launch_attention(const AttnArgsHost& h, hipStream_t s) {
   a.T = h.T;
   a.Hq = h.Hq;
   a.Hkv = h.Hkv;
-  a.G = h.Hq / h.Hkv;
-  a.QT = 64 / a.G;
+  a.G = p.G;
+  a.QT = p.QT;
   a.mode = h.mode;
   a.len = h.len;
   a.scale_log2 = 1.4426950408889634f / sqrtf((float)h.hd);
@@ -474,30 +534,11 @@ void launch_attention(const AttnArgsHost& h, hipStream_t s) {
   a.po = h.po;
   a.pml = h.pml;
   a.rows = h.B * h.T;
-
-  int maxkeys = 0;
-  for (int b = 0; b < h.B; b++) maxkeys = maxkeys > h.len.v[b] + h.T ? maxkeys : h.len.v[b] + h.T;
-  const int nqt = (h.T + a.QT - 1) / a.QT;
-  const long base = (long)nqt * h.B * h.Hkv;
-  int nsplit = 1;
-  if (base < ATTN_TARGET_BLOCKS) {
-    nsplit = (int)((ATTN_TARGET_BLOCKS + base - 1) / base);
-    const int by_keys = (maxkeys + ATTN_MIN_SPLIT_KEYS - 1) / ATTN_MIN_SPLIT_KEYS;
-    if (nsplit > by_keys) nsplit = by_keys;
-    const long entries = (long)a.rows * h.Hq;
-    while (nsplit > 1 && entries * nsplit > h.part_cap) nsplit--;
-    if (nsplit < 1) nsplit = 1;
-  }
-  int split_len = (maxkeys + nsplit - 1) / nsplit;
-  split_len = (split_len + KT - 1) / KT * KT;
-  nsplit = (maxkeys + split_len - 1) / split_len;
-  if (nsplit < 1) nsplit = 1;
-  a.split_len = split_len;
-  a.nsplit = nsplit;
-
-  a.nqt = nqt;
-  a.groups = h.B * h.Hkv * nsplit;
-  const dim3 grid((unsigned)(((a.groups + 7) / 8) * 8 * nqt));
+  a.split_len = p.split_len;
+  a.nsplit = p.nsplit;
+  a.nqt = p.nqt;
+  a.groups = p.groups;
+  const dim3 grid(p.grid);
   if (h.act == ACT_BF16) {
     if (h.hd == 128) attn_k<uint16_t, 128><<<grid, 256, 0, s>>>(a);
     else attn_k<uint16_t, 64><<<grid, 256, 0, s>>>(a);
@@ -505,17 +546,60 @@ void launch_attention(const AttnArgsHost& h, hipStream_t s) {
     if (h.hd == 128) attn_k<float, 128><<<grid, 256, 0, s>>>(a);
     else attn_k<float, 64><<<grid, 256, 0, s>>>(a);
   }
-  if (nsplit > 1) {
+  if (p.nsplit > 1) {
     const int entries = a.rows * h.Hq;
     const int blocks = (int)(((long)entries * (h.hd / 8) + 255) / 256);
     if (h.act == ACT_BF16) {
-      if (h.hd == 128) attn_merge_k<uint16_t, 128><<<blocks, 256, 0, s>>>(h.po, h.pml, nsplit, entries, (uint16_t*)h.out);
-      else attn_merge_k<uint16_t, 64><<<blocks, 256, 0, s>>>(h.po, h.pml, nsplit, entries, (uint16_t*)h.out);
+      if (h.hd == 128) attn_merge_k<uint16_t, 128><<<blocks, 256, 0, s>>>(h.po, h.pml, p.nsplit, entries, (uint16_t*)h.out);
+      else attn_merge_k<uint16_t, 64><<<blocks, 256, 0, s>>>(h.po, h.pml, p.nsplit, entries, (uint16_t*)h.out);
     } else {
-      if (h.hd == 128) attn_merge_k<float, 128><<<blocks, 256, 0, s>>>(h.po, h.pml, nsplit, entries, (float*)h.out);
-      else attn_merge_k<float, 64><<<blocks, 256, 0, s>>>(h.po, h.pml, nsplit, entries, (float*)h.out);
+      if (h.hd == 128) attn_merge_k<float, 128><<<blocks, 256, 0, s>>>(h.po, h.pml, p.nsplit, entries, (float*)h.out);
+      else attn_merge_k<float, 64><<<blocks, 256, 0, s>>>(h.po, h.pml, p.nsplit, entries, (float*)h.out);
     }
   }
 }
 
+// Host replica of every K/V address the attention kernel issues for one
+// launch (the plan, the block decode and the key index of each staged slot,
+// with the tile schedule of the kernel: tiles 0, 1, 2 in the prologue, then
+// tile i+3 while tile i is computed).  Returns the number of addressed keys
+// that are not keys of the block's own request: in mode 0 a cache row must
+// lie in [0, len[b]) and a canvas row in [0, T); in mode 1 a cache row in
+// [0, len[b] + T) (the new keys are written before the attention runs).
+// Also checks the partial entries the launch writes against part_cap.
+long attn_check_addresses(int B, int T, const Lens& len, int Hq, int Hkv, int mode,
+                          long part_cap, long* nslots) {
+  const AttnPlan p = plan_attention(B, T, len, Hq, Hkv, part_cap);
+  long bad = 0, n = 0;
+  if (p.nsplit > 1 && (long)B * T * Hq * p.nsplit > part_cap) bad++;
+  for (unsigned id = 0; id < p.grid; id++) {
+    int b, gh, split, qt;
+    if (!attn_block((int)id, p.nqt, p.groups, p.nsplit, Hkv, b, gh, split, qt)) continue;
+    const int P = len.v[b];
+    const int nkeys = mode == 0 ? P + T : P + (((qt + 1) * p.QT) < T ? (qt + 1) * p.QT : T);
+    const int kbeg = split * p.split_len;
+    const int kend = nkeys < kbeg + p.split_len ? nkeys : kbeg + p.split_len;
+    const int ntile = kend > kbeg ? (kend - kbeg + KT - 1) / KT : 0;
+    // tiles loaded: 0, 1, 2, then it+3 for it = 0 .. (ntile rounded down to even) - 1
+    int last = 2;
+    for (int it = 0; it + 2 <= ntile; it += 2) last = it + 1 + 3 > last ? it + 1 + 3 : last;
+    for (int tl = 0; tl <= last; tl++)
+      for (int j = 0; j < KT; j++) {
+        const int k = attn_key_index(kbeg + tl * KT + j, kbeg, kend);
+        n++;
+        bad += !(k >= 0 && k < P + T);
+      }
+  }
+  if (nslots) *nslots = n;
+  return bad;
+}
+
 }  // namespace dg
+
+extern "C" long dg_check_attention_addresses(int B, int T, const int32_t* lens, int Hq, int Hkv,
+                                         int mode, long part_cap, long* nslots) {
+  dg::Lens l{};
+  if (B < 1 || B > DG_MAX_BATCH || T < 1 || Hkv < 1 || Hq % Hkv) return -1;
+  for (int b = 0; b < B; b++) l.v[b] = lens[b];
+  return dg::attn_check_addresses(B, T, l, Hq, Hkv, mode, part_cap, nslots);
+}

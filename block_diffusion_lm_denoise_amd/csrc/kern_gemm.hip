@@ -25,9 +25,7 @@ __device__ __forceinline__ const char* packed_group(const void* base, size_t row
 
 // contraction tiles in flight in registers in the LDS-tiled GEMMs (one more
 // than the tile being stored, so a tile's loads have P - 1 steps to land)
-#ifndef GEMM_P
-#define GEMM_P 2
-#endif
+constexpr int GEMM_P = 2;
 
 template <typename TA, typename TW, int BM, int BN, int P = 1>
 struct Mainloop {
@@ -297,15 +295,9 @@ struct MainloopD {
 // share a CU and one block's barrier waits are filled by the other's MFMAs
 // (batch-8 fp8 gate/up: 176 us at 128-row tiles with one block per CU, 143 at
 // 64).
-#ifndef GROUP_P
-#define GROUP_P 2
-#endif
-#ifndef GROUP_BM
-#define GROUP_BM 64   // rows of a bf16-activation expert tile
-#endif
-#ifndef DENSE_WIDE
-#define DENSE_WIDE 1  // dense bf16 GEMMs from 1024 rows: 64-row tiles, waves side by side
-#endif
+constexpr int GROUP_P = 2;
+constexpr int GROUP_BM = 64;   // rows of a bf16-activation expert tile
+constexpr int DENSE_WIDE = 1;  // dense bf16 GEMMs from 1024 rows: 64-row tiles, waves side by side
 template <typename TA, typename TW, int BM, int BN, int NWM>
 using GemmML = typename std::conditional<
     sizeof(TA) == 2,
@@ -990,18 +982,10 @@ void launch_down_lds(int act, const void* H, const MoeW& w, const int4* tiles,
 }
 
 // contraction tiles in flight in the bf16 LM head, and its waves per block
-#ifndef LMHEAD_P
-#define LMHEAD_P 4
-#endif
-#ifndef LMHEAD_NW
-#define LMHEAD_NW 8
-#endif
-#ifndef LMHEAD_BN
-#define LMHEAD_BN 256
-#endif
-#ifndef LMHEAD_MINB
-#define LMHEAD_MINB 1
-#endif
+constexpr int LMHEAD_P = 4;
+constexpr int LMHEAD_NW = 8;
+constexpr int LMHEAD_BN = 256;
+constexpr int LMHEAD_MINB = 1;
 
 int launch_lmhead(int act, const void* uf, int M, int D, const void* lm, int V, float* pmax,
                   int32_t* pidx, float* psum, float* logits, hipStream_t s) {

@@ -115,12 +115,8 @@ __device__ __forceinline__ void piece_mma(f32x4_t (&acc)[RT][4], const u32x4 (&w
 // expert weights are read once per expert tile: nontemporal loads (streamed,
 // not kept); the dense projections' weights are shared by several row tiles
 // (and read again every pass), so they are loaded normally
-#ifndef STREAM_NT_DENSE
-#define STREAM_NT_DENSE 0
-#endif
-#ifndef STREAM_NT
-#define STREAM_NT 1
-#endif
+constexpr int STREAM_NT_DENSE = 0;
+constexpr int STREAM_NT = 1;
 
 // KW waves split the contraction; the 4/KW wave groups take different 64-row
 // weight column groups (a block covers 64 * 4/KW weight rows).  A row tile
@@ -378,30 +374,16 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
 
 // register buffers (pieces in flight) per wave, chosen by measurement: bf16
 // gate/up, bf16 down and dense projections, fp8 experts
-#ifndef STREAM_NB_GATEUP
-#define STREAM_NB_GATEUP 2
-#endif
-#ifndef STREAM_NB
-#define STREAM_NB 2
-#endif
-#ifndef STREAM_NB_FP8
-#define STREAM_NB_FP8 2
-#endif
+constexpr int STREAM_NB_GATEUP = 2;
+constexpr int STREAM_NB = 2;
+constexpr int STREAM_NB_FP8 = 2;
 // register buffers of the dense bf16 projections (64- and 32-row tiles)
-#ifndef STREAM_NB_DENSE4
-#define STREAM_NB_DENSE4 2
-#endif
-#ifndef STREAM_NB_DENSE2
-#define STREAM_NB_DENSE2 2
-#endif
+constexpr int STREAM_NB_DENSE4 = 2;
+constexpr int STREAM_NB_DENSE2 = 2;
 // blocks a dense bf16 launch needs to take 64-row tiles
-#ifndef STREAM_DENSE_RT4_BLOCKS
-#define STREAM_DENSE_RT4_BLOCKS 256
-#endif
+constexpr int STREAM_DENSE_RT4_BLOCKS = 256;
 // 16-row tiles per expert tile of the bf16 grouped GEMMs
-#ifndef STREAM_RT_BF16
-#define STREAM_RT_BF16 4
-#endif
+constexpr int STREAM_RT_BF16 = 4;
 
 // rows per expert tile of the grouped modes (the plan cuts tiles this size)
 int stream_tile_rows(int act, int wdt) {

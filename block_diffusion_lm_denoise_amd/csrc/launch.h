@@ -168,6 +168,6 @@ struct AttnArgsHost {
   long part_cap;   // capacity of the partial buffers in (row, head) entries
 };
 void launch_attention(const AttnArgsHost& a, hipStream_t s);
-long attn_partial_entries(int rows, int Hq);
+long attn_partial_entries(int rows, int Hq, int max_keys);
 
 }  // namespace dg

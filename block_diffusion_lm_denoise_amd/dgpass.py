@@ -58,8 +58,14 @@ class dg_kv(C.Structure):
 
 
 class dg_taps(C.Structure):
-    _fields_ = [(n, C.c_void_p) for n in TAP_FIELDS] + [("inject_router", C.c_void_p),
-                                                         ("ev_gateup", C.c_void_p)]
+    _fields_ = [(n, C.c_void_p) for n in TAP_FIELDS] + [
+        ("inject_router", C.c_void_p), ("inject_x", C.c_void_p), ("inject_uf", C.c_void_p),
+        ("stage_events", C.c_void_p)]
+
+
+# stages a call can bracket with HIP events (dg_taps.stage_events)
+STAGE_ATTN, STAGE_GATEUP, STAGE_DOWN, STAGE_HEAD = 0, 1, 2, 3
+NSTAGES = 4
 
 
 class dg_renoise_args(C.Structure):
@@ -69,7 +75,7 @@ class dg_renoise_args(C.Structure):
 
 EXPORTS = ("dg_model_init", "dg_workspace_bytes", "dg_kv_prefill", "dg_denoise_pass",
            "dg_denoise_pass_next", "dg_renoise", "dg_expert_coverage", "dg_packed_bytes",
-           "dg_pack_weight", "dg_status_str")
+           "dg_pack_weight", "dg_status_str", "dg_check_attention_addresses")
 
 _lib = None
 
@@ -103,6 +109,9 @@ def lib():
         L.dg_pack_weight.restype = i32
         L.dg_status_str.argtypes = [i32]
         L.dg_status_str.restype = C.c_char_p
+        L.dg_check_attention_addresses.argtypes = [i32, i32, vp, i32, i32, i32, C.c_long,
+                                                   C.POINTER(C.c_long)]
+        L.dg_check_attention_addresses.restype = C.c_long
         _lib = L
     return _lib
 
@@ -170,19 +179,34 @@ def make_taps(cfg: ModelConfig, rows: int, names, device="cuda") -> dict:
     return {n: torch.zeros(*shapes[n][0], dtype=shapes[n][1], device=device) for n in names}
 
 
-def _taps_struct(taps, inject_router=None, events=None):
-    if not taps and inject_router is None and events is None:
+def _taps_struct(taps, inject_router=None, inject_x=None, inject_uf=None, stage_events=None):
+    """dg_taps for the given device tensors; stage_events: flat list of
+    torch.cuda.Event (or None) indexed [l][stage][0/1]."""
+    if not taps and inject_router is None and inject_x is None and inject_uf is None \
+            and stage_events is None:
         return None, None
     t = dg_taps()
     for n, v in (taps or {}).items():
         setattr(t, n, v.data_ptr())
-    if inject_router is not None:
-        t.inject_router = inject_router.data_ptr()
+    t.inject_router = _ptr(inject_router)
+    t.inject_x = _ptr(inject_x)
+    t.inject_uf = _ptr(inject_uf)
     keep = None
-    if events is not None:
-        keep = (C.c_void_p * len(events))(*[e.cuda_event for e in events])
-        t.ev_gateup = C.cast(keep, C.c_void_p)
+    if stage_events is not None:
+        keep = (C.c_void_p * len(stage_events))(
+            *[None if e is None else e.cuda_event for e in stage_events])
+        t.stage_events = C.cast(keep, C.c_void_p)
     return t, keep
+
+
+def check_attention_addresses(B, T, lens, Hq, Hkv, mode, part_cap):
+    """Host replay of the attention's K/V addresses (dg_check_attention_addresses):
+    (slots addressing a key outside the block's request, slots checked)."""
+    ln = np.ascontiguousarray(lens, dtype=np.int32)
+    n = C.c_long(0)
+    bad = lib().dg_check_attention_addresses(int(B), int(T), ln.ctypes.data_as(C.c_void_p), int(Hq),
+                                             int(Hkv), int(mode), int(part_cap), C.byref(n))
+    return int(bad), int(n.value)
 
 
 def packed_bytes(rows: int, cols: int, dtype: str) -> int:
@@ -248,20 +272,22 @@ class Model:
         return KVCache(self.cfg, B, cap, device)
 
     def kv_prefill(self, kv: KVCache, tokens: torch.Tensor, ws: torch.Tensor, taps=None,
-                   inject_router=None, stream=None):
+                   inject_router=None, inject_x=None, stage_events=None, stream=None):
         B, T = tokens.shape
         s = kv.struct()
-        ts, _ = _taps_struct(taps, inject_router)
+        ts, keep = _taps_struct(taps, inject_router, inject_x, None, stage_events)
         st = lib().dg_kv_prefill(C.byref(self._m), C.byref(s), tokens.data_ptr(), B, T,
                                  None if ts is None else C.byref(ts), ws.data_ptr(), ws.numel(),
                                  _stream(stream))
+        del keep
         _check(st, "dg_kv_prefill")
 
     def denoise_pass(self, kv: KVCache, canvas: torch.Tensor, argmax: torch.Tensor, conf: torch.Tensor,
-                     ws: torch.Tensor, taps=None, inject_router=None, events=None, stream=None):
+                     ws: torch.Tensor, taps=None, inject_router=None, inject_x=None, inject_uf=None,
+                     stage_events=None, stream=None):
         B, N = canvas.shape
         s = kv.struct()
-        ts, keep = _taps_struct(taps, inject_router, events)
+        ts, keep = _taps_struct(taps, inject_router, inject_x, inject_uf, stage_events)
         st = lib().dg_denoise_pass(C.byref(self._m), C.byref(s), canvas.data_ptr(), B, N,
                                    argmax.data_ptr(), conf.data_ptr(),
                                    None if ts is None else C.byref(ts), ws.data_ptr(), ws.numel(),
@@ -271,13 +297,14 @@ class Model:
 
     def denoise_pass_next(self, kv: KVCache, canvas: torch.Tensor, argmax: torch.Tensor,
                           conf: torch.Tensor, ws: torch.Tensor, touched=None, renoise=None, taps=None,
-                          inject_router=None, events=None, stream=None):
+                          inject_router=None, inject_x=None, inject_uf=None, stage_events=None,
+                          stream=None):
         """A pass whose last kernel also writes the expert coverage (touched:
         device [L] int32, or None) and, with renoise = dict(tau, seed,
         pass_tag, pos0[, req_id]), re-noises canvas in place for the next pass."""
         B, N = canvas.shape
         s = kv.struct()
-        ts, keep = _taps_struct(taps, inject_router, events)
+        ts, keep = _taps_struct(taps, inject_router, inject_x, inject_uf, stage_events)
         nx, arrs = None, None
         if renoise is not None:
             p0 = np.ascontiguousarray(renoise["pos0"], dtype=np.int32)

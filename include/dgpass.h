@@ -132,9 +132,28 @@ typedef struct dg_kv {
   int32_t* len;
 } dg_kv;
 
-/* Optional device outputs (debug taps) of a pass or prefill; every field may
- * be NULL.  BN = B*N (or B*T for a prefill).  Token-major, slots in top-k
- * order.  Writing taps adds work; leave them NULL when timing. */
+/* Stages a pass or prefill can bracket with HIP events (dg_taps.stage_events). */
+#define DG_STAGE_ATTN 0     /* attention (and the merge of its key splits) */
+#define DG_STAGE_GATEUP 1   /* grouped gate/up expert GEMM + SwiGLU */
+#define DG_STAGE_DOWN 2     /* grouped down expert GEMM */
+#define DG_STAGE_HEAD 3     /* LM head + argmax/confidence partials (pass only; layer L-1's slots) */
+#define DG_NSTAGES 4
+
+/* Optional device outputs (debug taps), injected inputs and stage events of a
+ * pass or prefill; every field may be NULL.  BN = B*N (or B*T for a prefill).
+ * Token-major, slots in top-k order.  Writing taps adds work; leave them NULL
+ * when timing.
+ *
+ * Injected inputs replace a value the call would compute by one given by the
+ * caller, so that a stage can be checked on inputs identical to another
+ * implementation's (the taps still record what this call computed):
+ *  - inject_x: layer l starts from inject_x[l] instead of the previous
+ *    layer's output (layer 0: instead of the embedding rows); its first
+ *    RMSNorm is taken of the injected rows;
+ *  - inject_router: routing of layer l uses inject_router[l] instead of the
+ *    router logits (the router GEMM is skipped);
+ *  - inject_uf: the LM head reads inject_uf instead of the final RMSNorm
+ *    output (pass only). */
 typedef struct dg_taps {
   void* qkv;                 /* [L][BN][(Hq+2Hkv)*hd] act */
   void* attn;                /* [L][BN][Hq*hd] act: attention output before Wo */
@@ -148,13 +167,17 @@ typedef struct dg_taps {
   int32_t* perm;             /* [L][BN*k]: entries t*k+j sorted by (expert, t, j) */
   void* hmid;                /* [L][BN][k][F] act: SwiGLU output per slot */
   void* yexp;                /* [L][BN][k][D] act: expert output per slot */
-  void* xout;                /* [L][BN][D] act: layer output */
-  void* uf;                  /* [BN][D] act (pass only) */
+  void* xout;                /* [L][BN][D] act: layer output (computed, not injected) */
+  void* uf;                  /* [BN][D] act: final RMSNorm output (pass only; computed) */
   float* logits;             /* [BN][V] f32 (pass only) */
-  const float* inject_router;/* input [L][BN][E] f32: route on these logits instead */
-  void* const* ev_gateup;    /* host array of 2*L hipEvent_t: recorded on `stream`
-                                just before and after each layer's gate/up expert
-                                launch (for timing that kernel); NULL = none */
+  const float* inject_router;/* input [L][BN][E] f32 */
+  const void* inject_x;      /* input [L][BN][D] act */
+  const void* inject_uf;     /* input [BN][D] act (pass only) */
+  void* const* stage_events; /* host array [L][DG_NSTAGES][2] of hipEvent_t: entry
+                                [l][s][0] is recorded on `stream` just before the
+                                launches of stage s of layer l, [l][s][1] just
+                                after them (timing of one stage); NULL entries and
+                                stages a call does not run are skipped */
 } dg_taps;
 
 /* Fill *m after validating cfg and the weight pointers.  No device work. */
@@ -162,13 +185,19 @@ dg_status dg_model_init(dg_model* m, const dg_config* cfg, const dg_weights* w);
 
 /* Bytes of workspace a call needs for up to max_rows token rows (B*N of a
  * pass or B*T of a prefill) and up to max_keys keys per request (prefix +
- * rows of that request).  0 when cfg is invalid.  Host arithmetic only. */
+ * rows of that request; 0 = not known: room for the most key splits).
+ * max_keys sizes the partial results of the attention's key splits; a call
+ * whose requests hold more keys still runs, with fewer splits.  0 when cfg
+ * is invalid.  Host arithmetic only. */
 size_t dg_workspace_bytes(const dg_config* cfg, int32_t max_rows, int32_t max_keys);
 
 /* Causal prefill ("Prefill mode"): appends T tokens per request (device
  * tokens [B][T] int32 in [0, V)) to every layer's cache at positions
  * [len[b], len[b]+T) and, on success, advances kv->len[b] by T (host).  Query
  * i sees keys 0 .. len[b]+i.  The last layer stops after its cache write.
+ * Token ids are not checked on the host (they live in device memory): an id
+ * outside [0, V) is clamped into that range by the embedding kernel, with no
+ * error reported; the same holds for the canvas of a pass.
  * Errors: INVALID, CAPACITY (len[b]+T > cap), UNSUPPORTED, WORKSPACE, HIP. */
 dg_status dg_kv_prefill(const dg_model* m, dg_kv* kv, const int32_t* tokens, int32_t B, int32_t T,
                         const dg_taps* taps, void* ws, size_t ws_bytes, void* stream);

@@ -4,9 +4,12 @@ seeded inputs and compare them.
 Tolerances (per tensor, max|gpu - oracle| / max|oracle|): 1e-4 for fp32
 storage, 2e-2 for bf16 storage with fp32 accumulation.  Integer outputs
 (routing ids, permutation, counts, re-noise tokens) are bit-exact when both
-sides route on the same fp32 logits; argmax must agree wherever the oracle's
-top-2 logit gap exceeds 1e-2, or twice the largest measured logit difference
-when that is larger (no smaller gap can be decided by logits that far apart).
+sides route on the same fp32 logits.  The argmax must agree wherever the
+oracle's top-2 logit gap exceeds 1e-2 (absolute), asserted where the LM head
+reads the same input on both sides (the oracle's final-norm rows injected into
+the GPU's head) and in fp32 end to end; bf16 runs without that injection
+report how many rows with a gap above 1e-2 changed their argmax (bf16 rounding
+differences upstream move the logits by up to a few 1e-2).
 """
 import numpy as np
 import torch
@@ -123,19 +126,64 @@ class Pair:
         torch.cuda.synchronize()
         return oks, ovs, oln, kv
 
-    def gpu_pass(self, kv, canvas, taps=ALL_TAPS, inject=None):
+    def gpu_pass(self, kv, canvas, taps=ALL_TAPS, inject=None, inject_x=None, inject_uf=None):
+        """One GPU pass.  inject: oracle router logits [L][BN][E]; inject_x:
+        layer inputs [L][BN][D] (oracle representation); inject_uf: final-norm
+        rows [BN][D] for the LM head."""
         B, N = canvas.shape
         ws = self.gm.workspace(B * N, int(kv.lens.max()) + N, device=DEV)
         tp = dgpass.make_taps(self.cfg, B * N, taps, device=DEV)
         am = torch.empty(B, N, dtype=torch.int32, device=DEV)
         cf = torch.empty(B, N, dtype=torch.float32, device=DEV)
         inj = None if inject is None else torch.from_numpy(np.ascontiguousarray(inject, np.float32)).to(DEV)
-        self.gm.denoise_pass(kv, torch.from_numpy(canvas).to(DEV), am, cf, ws, taps=tp, inject_router=inj)
+        ix = None if inject_x is None else to_torch_act(inject_x, self.cfg.act).to(DEV)
+        iu = None if inject_uf is None else to_torch_act(inject_uf, self.cfg.act).to(DEV)
+        self.gm.denoise_pass(kv, torch.from_numpy(canvas).to(DEV), am, cf, ws, taps=tp, inject_router=inj,
+                             inject_x=ix, inject_uf=iu)
         torch.cuda.synchronize()
         return host(am), host(cf), {n: host(t) for n, t in tp.items()}, ws
 
+    def layer_inputs(self, tokens, ot):
+        """Oracle layer inputs [L][rows][D] of a call over `tokens` [B][T]: the
+        embedding rows (a gather of the input weights) for layer 0 and the
+        oracle's output of layer l-1 (its xout tap) for layer l."""
+        cfg = self.cfg
+        emb = self.om_np("emb")[np.asarray(tokens).reshape(-1)]
+        xs = [emb] + [ot["xout"][l] for l in range(cfg.L - 1)]
+        return np.ascontiguousarray(np.stack(xs))
 
-def compare_pass(cfg, o, g, inject_used, label="", head_scale=1.0):
+    def om_np(self, name):
+        t = self.w[name].contiguous()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        return t.numpy()
+
+
+def argmax_report(rep, fails, oam, ocf, gam, gcf, ot, gt, rows_ok, assert_argmax, label_note=""):
+    """Argmax / confidence comparison of the head on rows rows_ok.  Rows whose
+    oracle top-2 gap exceeds 1e-2 must keep their argmax when assert_argmax;
+    the count of such rows that changed is reported either way."""
+    thr = ARGMAX_GAP
+    if "logits" in gt:
+        rep["logits"] = max_rel(gt["logits"][rows_ok], ot["logits"][rows_ok])
+        rep["logits_abs"] = float(np.abs(gt["logits"][rows_ok] - ot["logits"][rows_ok]).max())
+    if "logits" in ot:
+        gap = top2_gap(ot["logits"])
+        clear = (gap > thr) & rows_ok
+        flips = clear & (gam.ravel() != oam.ravel())
+        rep["argmax_rows_gap_le_1e-2"] = int(((gap <= thr) & rows_ok).sum())
+        rep["argmax_flips_gap_gt_1e-2"] = int(flips.sum())
+        rep["argmax_equal"] = float((gam.ravel() == oam.ravel())[rows_ok].mean())
+        if assert_argmax and flips.any():
+            fails.append(f"argmax differs on {int(flips.sum())} rows with a top-2 gap > 1e-2 "
+                         f"(gaps {np.sort(gap[flips])[:5]}){label_note}")
+    rep["conf"] = max_rel(gcf.ravel()[rows_ok], ocf.ravel()[rows_ok])
+
+
+ARGMAX_GAP = 1e-2
+
+
+def compare_pass(cfg, o, g, inject_used, label="", head_injected=False):
     """o, g: (argmax, conf, taps) of the oracle and the GPU.  Asserts the bars and
     returns a report.
 
@@ -147,12 +195,10 @@ def compare_pass(cfg, o, g, inject_used, label="", head_scale=1.0):
     before comparing per-slot taps); a token routed to a different set is
     excluded from that layer's float comparisons, and later layers (and the
     head, unless it was the last layer) are not compared, since every later
-    value mixes in that token.  argmax must agree wherever the oracle's top-2
-    gap exceeds max(1e-2 x head_scale, 2 delta), delta the largest absolute
-    logit difference measured on the compared rows: with every logit within
-    delta of the oracle's, a row whose top-2 gap exceeds 2 delta cannot change
-    its argmax (head_scale: factor a test scaled the head by).  delta itself is
-    held to the logits' max-rel tolerance."""
+    value mixes in that token.  The argmax must agree wherever the oracle's
+    top-2 logit gap exceeds 1e-2 when the GPU's head read the oracle's
+    final-norm rows (head_injected) or the storage is fp32; otherwise the
+    number of such rows that changed is reported."""
     act = cfg.act
     tol = TOL[act]
     oam, ocf, ot = o
@@ -213,22 +259,12 @@ def compare_pass(cfg, o, g, inject_used, label="", head_scale=1.0):
             continue
         a, b = f64(gt[n], act)[:L_ok][:, rows_ok], f64(ot[n], act)[:L_ok][:, rows_ok]
         rep[n] = max_rel(a, b)
-    if head_ok:
-        if "uf" in gt:
+    if head_ok or head_injected:
+        if "uf" in gt and head_ok:
             rep["uf"] = max_rel(f64(gt["uf"], act)[rows_ok], f64(ot["uf"], act)[rows_ok])
-        thr = 1e-2 * head_scale
-        if "logits" in gt:
-            rep["logits"] = max_rel(gt["logits"][rows_ok], ot["logits"][rows_ok])
-            rep["logits_abs"] = float(np.abs(gt["logits"][rows_ok] - ot["logits"][rows_ok]).max())
-            thr = max(thr, 2.0 * rep["logits_abs"])
-            gap = top2_gap(ot["logits"])
-            clear = (gap > thr) & rows_ok
-            bad = clear & (gam.ravel() != oam.ravel())
-            rep["argmax_exempt"] = int((gap <= thr).sum())
-            rep["argmax_equal"] = float((gam.ravel() == oam.ravel())[rows_ok].mean())
-            if bad.any():
-                fails.append(f"argmax differs on {int(bad.sum())} clear rows (gaps {np.sort(gap[bad])[:5]})")
-        rep["conf"] = max_rel(gcf.ravel()[rows_ok], ocf.ravel()[rows_ok])
+        hrows = np.ones(BN, bool) if head_injected else rows_ok
+        argmax_report(rep, fails, oam, ocf, gam, gcf, ot, gt, hrows,
+                      assert_argmax=head_injected or act == "f32")
     else:
         rep["head"] = "skipped (routing differed before the last layer)"
     for n in ("router", "conf", "logits", "gates") + FLOAT_TAPS:

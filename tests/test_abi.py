@@ -11,16 +11,19 @@ from block_diffusion_lm_denoise_amd import dgpass
 from block_diffusion_lm_denoise_amd.configs import WORKLOADS, ModelConfig
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "dgpass.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(dgpass.LIB_PATH),
                                 reason="libdgpass.so not built (run __graft_entry__.build())")
 
 
 def _declared():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(dg_\w+)\s*\(", src, flags=re.M)))
+    names = set()
+    for h in HEADERS:
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(dg_\w+)\s*\(", src, flags=re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():

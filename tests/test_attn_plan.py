@@ -1,0 +1,48 @@
+"""Host replay of every K/V address the attention kernel issues (no GPU).
+
+Course page "Module 12. Diffusion Language Models", block-mask exercise:
+every query of the active block reads the complete prefix and the block of
+its own request.  The library replays its launch plan on the CPU (the same
+plan, block decode and key-index functions the kernel is compiled from) and
+counts staged K/V slots that would address a key outside the block's request;
+ragged prefixes whose key splits start past a short request's keys are the
+case that matters.
+"""
+import os
+
+import pytest
+
+from block_diffusion_lm_denoise_amd import dgpass
+
+pytestmark = pytest.mark.skipif(not os.path.exists(dgpass.LIB_PATH),
+                                reason="libdgpass.so not built (run __graft_entry__.build())")
+
+CASES = [
+    # (B, T, lens, Hq, Hkv, mode)
+    (1, 256, [1024], 16, 8, 0),           # one request, 1024-token prefix
+    (1, 256, [8192], 16, 8, 0),           # 8192-token prefix
+    (8, 256, [2048] * 8, 16, 8, 0),       # batch of eight equal prefixes
+    (2, 256, [2048, 0], 16, 8, 0),        # ragged: the second request has no prefix
+    (2, 256, [32768, 0], 16, 8, 0),
+    (3, 37, [50, 0, 13], 8, 4, 0),
+    (4, 100, [5000, 1, 0, 300], 16, 8, 0),
+    (2, 1, [4000, 0], 16, 8, 0),          # one-slot canvas
+    (1, 4096, [0], 16, 8, 1),             # prompt prefill
+    (1, 256, [4096], 16, 8, 1),           # append prefill
+    (2, 256, [4096, 0], 16, 8, 1),        # ragged append
+    (3, 400, [0, 0, 0], 4, 2, 1),
+    (2, 33, [40, 3], 4, 2, 1),
+]
+
+
+@pytest.mark.parametrize("B,T,lens,Hq,Hkv,mode", CASES)
+@pytest.mark.parametrize("part_cap", [0, 1 << 12, 1 << 18])
+def test_every_staged_key_belongs_to_the_blocks_request(B, T, lens, Hq, Hkv, mode, part_cap):
+    bad, n = dgpass.check_attention_addresses(B, T, lens, Hq, Hkv, mode, part_cap)
+    assert n > 0
+    assert bad == 0, f"{bad} of {n} staged K/V slots address another request's keys"
+
+
+def test_invalid_arguments_are_rejected():
+    assert dgpass.check_attention_addresses(0, 4, [], 4, 2, 0, 0)[0] == -1
+    assert dgpass.check_attention_addresses(1, 4, [3], 3, 2, 0, 0)[0] == -1

@@ -136,3 +136,33 @@ def test_large_prefill_uses_tiled_dense_gemm(act, expert):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(kv.lens, oln)
     print(act, expert, "cache max-rel", _compare_caches(cfg, kv, oks, ovs, oln, "large"))
+
+
+def test_prefill_ragged_lengths_with_key_splits_full_width():
+    """Append 256 tokens to two requests holding 2048 and 0 keys at the
+    1024-prefix layer's width (two layers): the causal attention splits the
+    keys, and the short request's late splits are empty.  Routing on the
+    oracle's logits; caches compared with the oracle."""
+    from block_diffusion_lm_denoise_amd.configs import WORKLOADS, scaled
+    wl = scaled(WORKLOADS["layer_p1024"], L=2)
+    cfg = wl.model
+    pair = Pair(cfg, 32)
+    cap, T = 2048 + 256, 256
+    ks, vs = synth.kv_cache_values(cfg, 2, cap, 2048, 32)
+    for l in range(cfg.L):
+        ks[l][1] = 0
+        vs[l][1] = 0
+    kv = pair.gm.kv_cache(2, cap, device=DEV)
+    for l in range(cfg.L):
+        kv.k[l].copy_(ks[l])
+        kv.v[l].copy_(vs[l])
+    kv.lens[:] = [2048, 0]
+    oks, ovs = [host(k) for k in ks], [host(v) for v in vs]
+    oln = np.array([2048, 0], np.int32)
+    toks = synth.tokens(cfg.V, (2, T), 32, "append")
+    ro = pair.om.kv_prefill(oks, ovs, oln, toks.numpy(), taps=("router",))["router"]
+    ws = pair.gm.workspace(2 * T, cap, device=DEV)
+    pair.gm.kv_prefill(kv, toks.to(DEV), ws, inject_router=torch.from_numpy(ro).to(DEV))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(kv.lens, oln)
+    print("ragged split prefill cache max-rel", _compare_caches(cfg, kv, oks, ovs, oln, "ragged-split"))
