@@ -99,10 +99,13 @@ Layout layout(const dg_config& c, int rows, long part_entries) {
 // cut to what the caller's workspace holds beyond the fixed part
 Layout call_layout(const dg_config& c, int rows, int max_keys, size_t ws_bytes) {
   Layout L = layout(c, rows, 0);
-  long want = attn_partial_entries(rows, c.Hq, max_keys);
+  const long want = attn_partial_entries(rows, c.Hq, max_keys);
   const size_t room = ws_bytes > L.fixed ? ws_bytes - L.fixed : 0;
-  // po and pml are each rounded up to 256 bytes
-  const long fit = room > 512 ? (long)((room - 512) / part_entry_bytes(c)) : 0;
+  // the most entries whose two buffers (each rounded up to 256 bytes) fit the
+  // room: a workspace sized by dg_workspace_bytes for these keys holds `want`
+  auto need = [&](long n) { return al((size_t)n * c.hd * 4) + al((size_t)n * 2 * 4); };
+  long fit = (long)(room / part_entry_bytes(c));
+  while (fit > 0 && need(fit) > room) fit--;
   return layout(c, rows, want < fit ? want : fit);
 }
 
