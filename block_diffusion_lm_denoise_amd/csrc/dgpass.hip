@@ -3,6 +3,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "launch.h"
 
 using namespace dg;
@@ -352,6 +354,38 @@ dg_status check_hip() {
   return e == hipSuccess ? DG_OK : DG_ERR_HIP;
 }
 
+// Workspace of the allocation-free pass: a file-scope device array (each GPU
+// the library runs on holds its own copy until the process ends).  Host code
+// never passes the array's name to a kernel: it is a host-side stand-in, not
+// a device address.  The device address is looked up once per device with
+// that device current, and that pointer is what the kernels receive.
+static __device__ __align__(256) char scratch[DG_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES];
+
+// the current device's copy of `scratch`, or null with *st set
+void* scratch_for_current_device(dg_status* st) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) {
+    *st = DG_ERR_HIP;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      *st = DG_ERR_HIP;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *st = DG_OK;
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -547,6 +581,21 @@ dg_status dg_denoise_pass_next(const dg_model* m, const dg_kv* kv, int32_t* canv
     nx.rn.tag = next->pass_tag;
   }
   return denoise(m, kv, canvas, B, N, argmax, conf, taps, ws, ws_bytes, stream, nx);
+}
+
+dg_status dg_denoise_pass_next_noalloc(const dg_model* m, const dg_kv* kv, int32_t* canvas, int32_t B,
+                                       int32_t N, int32_t* argmax, float* conf, int32_t* touched,
+                                       const dg_renoise_args* next, const dg_taps* taps, void* stream) {
+  if (!model_ok(m) || !kv || !kv->len || B < 1 || B > DG_MAX_BATCH || N < 1) return DG_ERR_INVALID;
+  // reject, before touching the device, what the scratch cannot hold: the
+  // fixed part of the carve (the attention split partials take what is left)
+  if ((long)B * N > (1L << 20)) return DG_ERR_UNSUPPORTED;
+  if (layout(m->cfg, B * N, 0).fixed > (size_t)DG_NOALLOC_SCRATCH_BYTES) return DG_ERR_WORKSPACE;
+  dg_status st = DG_OK;
+  void* ws = scratch_for_current_device(&st);
+  if (!ws) return st;
+  return dg_denoise_pass_next(m, kv, canvas, B, N, argmax, conf, touched, next, taps, ws,
+                              (size_t)DG_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 dg_status dg_renoise(int32_t* canvas, const int32_t* argmax, const float* conf, float tau,

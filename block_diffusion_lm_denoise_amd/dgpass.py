@@ -75,7 +75,9 @@ class dg_renoise_args(C.Structure):
 
 EXPORTS = ("dg_model_init", "dg_workspace_bytes", "dg_kv_prefill", "dg_denoise_pass",
            "dg_denoise_pass_next", "dg_renoise", "dg_expert_coverage", "dg_packed_bytes",
-           "dg_pack_weight", "dg_status_str", "dg_check_attention_addresses")
+           "dg_pack_weight", "dg_status_str", "dg_check_attention_addresses",
+           "dg_denoise_pass_next_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -98,6 +100,8 @@ def lib():
         L.dg_denoise_pass.restype = i32
         L.dg_denoise_pass_next.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.dg_denoise_pass_next.restype = i32
+        L.dg_denoise_pass_next_noalloc.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp]
+        L.dg_denoise_pass_next_noalloc.restype = i32
         L.dg_renoise.argtypes = [vp, vp, vp, C.c_float, C.c_uint64, C.c_uint32, vp, vp, i32, i32, i32,
                                  vp]
         L.dg_renoise.restype = i32
@@ -197,6 +201,20 @@ def _taps_struct(taps, inject_router=None, inject_x=None, inject_uf=None, stage_
             *[None if e is None else e.cuda_event for e in stage_events])
         t.stage_events = C.cast(keep, C.c_void_p)
     return t, keep
+
+
+def _renoise_struct(renoise):
+    """dg_renoise_args for dict(tau, seed, pass_tag, pos0[, req_id]) (or None),
+    with the host arrays it points to (kept alive by the caller)."""
+    if renoise is None:
+        return None, None
+    p0 = np.ascontiguousarray(renoise["pos0"], dtype=np.int32)
+    rq = renoise.get("req_id")
+    rq = None if rq is None else np.ascontiguousarray(rq, dtype=np.uint32)
+    nx = dg_renoise_args(float(renoise["tau"]), int(renoise["seed"]) & (2**64 - 1),
+                         int(renoise["pass_tag"]) & 0xFFFFFFFF, p0.ctypes.data_as(C.c_void_p),
+                         None if rq is None else rq.ctypes.data_as(C.c_void_p))
+    return nx, (p0, rq)
 
 
 def check_attention_addresses(B, T, lens, Hq, Hkv, mode, part_cap):
@@ -305,15 +323,7 @@ class Model:
         B, N = canvas.shape
         s = kv.struct()
         ts, keep = _taps_struct(taps, inject_router, inject_x, inject_uf, stage_events)
-        nx, arrs = None, None
-        if renoise is not None:
-            p0 = np.ascontiguousarray(renoise["pos0"], dtype=np.int32)
-            rq = renoise.get("req_id")
-            rq = None if rq is None else np.ascontiguousarray(rq, dtype=np.uint32)
-            arrs = (p0, rq)
-            nx = dg_renoise_args(float(renoise["tau"]), int(renoise["seed"]) & (2**64 - 1),
-                                 int(renoise["pass_tag"]) & 0xFFFFFFFF, p0.ctypes.data_as(C.c_void_p),
-                                 None if rq is None else rq.ctypes.data_as(C.c_void_p))
+        nx, arrs = _renoise_struct(renoise)
         st = lib().dg_denoise_pass_next(C.byref(self._m), C.byref(s), canvas.data_ptr(), B, N,
                                         argmax.data_ptr(), conf.data_ptr(), _ptr(touched),
                                         None if nx is None else C.byref(nx),
@@ -321,6 +331,21 @@ class Model:
                                         _stream(stream))
         del keep, arrs
         _check(st, "dg_denoise_pass_next")
+
+    def denoise_pass_next_noalloc(self, kv: KVCache, canvas: torch.Tensor, argmax: torch.Tensor,
+                                  conf: torch.Tensor, touched=None, renoise=None, taps=None,
+                                  inject_router=None, inject_x=None, inject_uf=None, stream=None):
+        """denoise_pass_next on the library's static per-GPU scratch (no workspace)."""
+        B, N = canvas.shape
+        s = kv.struct()
+        ts, keep = _taps_struct(taps, inject_router, inject_x, inject_uf, None)
+        nx, arrs = _renoise_struct(renoise)
+        st = lib().dg_denoise_pass_next_noalloc(C.byref(self._m), C.byref(s), canvas.data_ptr(), B, N,
+                                                argmax.data_ptr(), conf.data_ptr(), _ptr(touched),
+                                                None if nx is None else C.byref(nx),
+                                                None if ts is None else C.byref(ts), _stream(stream))
+        del keep, arrs
+        _check(st, "dg_denoise_pass_next_noalloc")
 
     def expert_coverage(self, ws: torch.Tensor, touched: torch.Tensor, counts=None, stream=None):
         st = lib().dg_expert_coverage(C.byref(self._m), ws.data_ptr(), ws.numel(), touched.data_ptr(),

@@ -253,6 +253,28 @@ dg_status dg_denoise_pass_next(const dg_model* m, const dg_kv* kv, int32_t* canv
                                const dg_renoise_args* next, const dg_taps* taps, void* ws,
                                size_t ws_bytes, void* stream);
 
+/* Bytes of the device scratch of dg_denoise_pass_next_noalloc (one per GPU). */
+#define DG_NOALLOC_SCRATCH_BYTES (64 << 20)
+
+/* dg_denoise_pass_next without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Arguments, results and errors are those
+ * of dg_denoise_pass_next; the call allocates nothing.  Its workspace is a
+ * static device array of DG_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each GPU it runs on until the process ends (looked up once per device on the
+ * first call there).  Limit: the pass's fixed workspace (every buffer but the
+ * attention split partials, which take the room that is left and so bound the
+ * number of key splits) must fit the scratch, about 256 canvas rows of a
+ * model with 2048-wide layers and a 32768-token vocabulary; larger calls
+ * return DG_ERR_WORKSPACE before any device work.  Every call on one GPU
+ * shares that GPU's scratch: calls that overlap on one GPU (different streams
+ * or host threads without ordering) race; calls on one stream are ordered.
+ * The expert counts of the pass stay in the scratch only until the next call
+ * on that GPU, so read the coverage through `touched`. */
+dg_status dg_denoise_pass_next_noalloc(const dg_model* m, const dg_kv* kv, int32_t* canvas, int32_t B,
+                                       int32_t N, int32_t* argmax, float* conf, int32_t* touched,
+                                       const dg_renoise_args* next, const dg_taps* taps, void* stream);
+
 /* Experts touched per layer by the last pass run with this workspace: device
  * touched [L] int32 = #{e : count[l][e] > 0} (the union over the batch), and
  * optionally device counts [L][E] int32. */

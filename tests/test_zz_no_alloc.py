@@ -1,0 +1,70 @@
+"""The allocation-free pass (dg_denoise_pass_next_noalloc, for callers that
+cannot allocate) against the same pass with a caller workspace
+(dg_denoise_pass_next): identical outputs on two calls in a row, the second
+with a smaller input, and the size limit rejected before any device work."""
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_lm_denoise_amd import dgpass, synth
+from block_diffusion_lm_denoise_amd.configs import WORKLOADS, ModelConfig
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _both(model, kv, canvas, tau, seed, tag):
+    """(outputs with a workspace, outputs on the static scratch) of one pass
+    with the fused coverage and re-noise, from the same canvas."""
+    cfg = model.cfg
+    B, N = canvas.shape
+    res = []
+    for noalloc in (False, True):
+        cv = canvas.clone()
+        am = torch.full((B, N), -1, dtype=torch.int32, device=DEV)
+        cf = torch.full((B, N), -1.0, dtype=torch.float32, device=DEV)
+        tch = torch.full((cfg.L,), -1, dtype=torch.int32, device=DEV)
+        nxt = dict(tau=tau, seed=seed, pass_tag=tag, pos0=kv.lens.copy())
+        if noalloc:
+            model.denoise_pass_next_noalloc(kv, cv, am, cf, touched=tch, renoise=nxt)
+        else:
+            ws = model.workspace(B * N, int(kv.lens.max()) + N, device=DEV)
+            model.denoise_pass_next(kv, cv, am, cf, ws, touched=tch, renoise=nxt)
+        torch.cuda.synchronize()
+        res.append((am.cpu(), cf.cpu(), tch.cpu(), cv.cpu()))
+    return res
+
+
+def test_noalloc_pass_equals_workspace_pass_twice():
+    wl = WORKLOADS["layer_p1024"]
+    cfg = wl.model
+    model = dgpass.Model(cfg, synth.make_weights(cfg, 41, device=DEV))
+    kv = model.kv_cache(1, wl.P + wl.N, device=DEV)
+    ws = model.workspace(wl.P, wl.P + wl.N, device=DEV)
+    model.kv_prefill(kv, synth.tokens(cfg.V, (1, wl.P), 41, device=DEV), ws)
+    torch.cuda.synchronize()
+    # call 1: the full canvas over the 1024-token prefix
+    canvas = synth.tokens(cfg.V, (1, wl.N), 41, "canvas", device=DEV)
+    a, b = _both(model, kv, canvas, 0.5, 41, 1)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    assert int(a[2][0]) > 0 and (a[0] >= 0).all()
+    # call 2: a smaller canvas over a shorter prefix (the scratch keeps call
+    # 1's contents; nothing of it may leak into this pass)
+    kv.lens[:] = 300
+    canvas2 = synth.tokens(cfg.V, (1, 100), 42, "canvas", device=DEV)
+    a, b = _both(model, kv, canvas2, 0.5, 42, 2)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_noalloc_rejects_a_pass_beyond_the_scratch():
+    cfg = ModelConfig(L=1, D=2048, Hq=16, Hkv=8, hd=128, E=128, k=8, F=768, V=32768)
+    model = dgpass.Model(cfg, synth.make_weights(cfg, 43, device=DEV))
+    kv = model.kv_cache(8, 16, device=DEV)
+    canvas = torch.zeros(8, 512, dtype=torch.int32, device=DEV)   # 4096 rows
+    am = torch.zeros(8, 512, dtype=torch.int32, device=DEV)
+    cf = torch.zeros(8, 512, dtype=torch.float32, device=DEV)
+    with pytest.raises(dgpass.DgError) as e:
+        model.denoise_pass_next_noalloc(kv, canvas, am, cf)
+    assert e.value.status == -4
