@@ -19,6 +19,8 @@
 // combines in split order.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -404,6 +406,326 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 attention (gfx950).  Block = NW waves x 32 rows = 32 NW (query, head)
+// rows of one (request, kv head, key split): G query heads sharing the kv head
+// x 32 NW / G consecutive queries.  K and V tiles of 64 keys go from memory straight
+// into LDS (global_load_lds, 16 bytes per lane: a wave load fills 1 KB of LDS
+// with 4 (hd 128) or 8 (hd 64) key rows); the 16-byte chunks of a key row are
+// stored XOR-swizzled by the key index, so both the K fragment reads (16 keys
+// x 64 bytes) and the transposing V reads (16 keys x 32 bytes) spread over
+// all LDS banks.  NBUF tile buffers: NBUF-1 tiles are in flight while one is
+// used, one barrier per tile; the tile loop is unrolled NBUF times so that
+// every LDS address is a lane offset plus a constant.
+//   S^T = K Q^T: keys on the MFMA row axis, queries on the column axis, so a
+//   lane's softmax statistics belong to one query row (two per lane: the
+//   wave's two 16-row tiles).
+//   O^T += V^T P^T: the V^T operand comes from the row-major V tile through
+//   the gfx950 transposing LDS read (ds_read_b64_tr_b16: 16 lanes read 4 key
+//   rows x 16 dims and each lane receives one dim of the 4 keys), with the
+//   key order of a lane's S^T accumulators, so P is used in place (one bf16
+//   rounding of the probabilities).
+// Online softmax in fp32 (base-2 exponent with the scale folded in).  The
+// running maximum is moved (and O and the sum rescaled) only when a tile's
+// maximum exceeds it by more than 2^8: until then the probabilities of a
+// tile are at most 256 times larger than with the exact maximum, which fp32
+// sums and bf16 probabilities hold exactly as well, and the final division
+// by the sum uses the same reference.
+// ---------------------------------------------------------------------------
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+// wait until at most n vector-memory loads of this wave are outstanding (gfx9
+// s_waitcnt encoding: vmcnt low bits [3:0] and high bits [15:14]; expcnt and
+// lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+constexpr float ATTN_RESCALE_LOG2 = 8.f;   // move the running maximum past this margin
+
+template <int HD, int NBUF, int NW>
+__global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void attn_bf16_k(AttnArgs a) {
+  constexpr int KT = 64;                 // keys per tile
+  constexpr int RBY = HD * 2;            // bytes of one key row
+  constexpr int CPK = RBY / 16;          // 16-byte chunks per key row (16 or 8)
+  constexpr int TB = KT * RBY;           // bytes of a K (or V) tile
+  constexpr int KPI = 1024 / RBY;        // key rows per 1 KB wave load
+  constexpr int NIW = TB / 1024 / NW;    // wave loads per wave per K (or V) tile
+  constexpr int NSS = HD / 32;           // contraction steps of S
+  constexpr int NHT = HD / 16;           // 16-dim tiles of O
+  static_assert(NIW >= 1, "tile");
+  __shared__ __attribute__((aligned(1024))) char lds[NBUF][2][TB];   // [buffer][K, V]
+
+  int b, gh, split, qt;
+  if (!attn_block(blockIdx.x, a.nqt, a.groups, a.nsplit, a.Hkv, b, gh, split, qt)) return;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, l16 = lane & 15, g4 = lane >> 4;
+  const int P = a.len.v[b];
+
+  // the wave's two 16-row tiles; this lane's query row in each
+  int qi[2], head[2];
+  bool qv[2];
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    const int r = 32 * w + 16 * j + l16;
+    qi[j] = qt * a.QT + r % a.QT;
+    qv[j] = qi[j] < a.T;
+    head[j] = gh * a.G + r / a.QT;
+  }
+  const int nkeys = a.mode == 0 ? P + a.T : P + min((qt + 1) * a.QT, a.T);
+  const int kbeg = split * a.split_len;
+  const int kend = min(nkeys, kbeg + a.split_len);
+  const int qlim0 = a.mode == 0 ? 0x7fffffff : P + qi[0];
+  const int qlim1 = a.mode == 0 ? 0x7fffffff : P + qi[1];
+  // last key every query of the block may see (the tile's first query in prefill mode)
+  const int qlim_all = a.mode == 0 ? 0x7fffffff : P + qt * a.QT;
+
+  FragBF qf[2][NSS];
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    const uint16_t* qp = (const uint16_t*)a.q + (size_t)(b * a.T + (qv[j] ? qi[j] : 0)) * a.ldq + head[j] * HD;
+#pragma unroll
+    for (int ss = 0; ss < NSS; ss++) {
+      load_frag(qf[j][ss], qp + 32 * ss + 8 * g4);
+      mask_frag(qf[j][ss], qv[j]);
+    }
+  }
+
+  const uint16_t* const kc = (const uint16_t*)a.kc + ((size_t)b * a.Hkv + gh) * a.cap * HD;
+  const uint16_t* const vc = (const uint16_t*)a.vc + ((size_t)b * a.Hkv + gh) * a.cap * HD;
+  const uint16_t* const kn = a.mode == 0 ? (const uint16_t*)a.kn + (size_t)b * a.T * a.ldq + gh * HD : kc;
+  const uint16_t* const vn = a.mode == 0 ? (const uint16_t*)a.vn + (size_t)b * a.T * a.ldq + gh * HD : vc;
+  const int fresh0 = a.mode == 0 ? P : 0x7fffffff;   // first key read from the qkv rows
+  const size_t ldq = (size_t)a.ldq;
+
+  // this lane's slot of each wave load: key row lkey[u] of the tile, global
+  // chunk lq[u] (stored at slot lane % CPK = lq ^ (key % CPK))
+  int lkey[NIW], lq[NIW];
+#pragma unroll
+  for (int u = 0; u < NIW; u++) {
+    lkey[u] = (w * NIW + u) * KPI + lane / CPK;
+    lq[u] = (lane % CPK) ^ (lkey[u] & (CPK - 1));
+  }
+  // K and V tile at key k0 into LDS buffer nb.  A tile wholly inside the key
+  // range and wholly in the cache (or in the canvas rows) is addressed from a
+  // uniform base; other tiles take per-key sources (attn_key_index keeps the
+  // slots past the split end on keys of this request).
+  auto issue = [&](int nb, int k0) __attribute__((always_inline)) {
+    const bool in_range = k0 + KT <= kend;
+    const bool all_cache = in_range && k0 + KT <= fresh0;
+    const bool all_fresh = in_range && k0 >= fresh0;
+#pragma unroll
+    for (int u = 0; u < NIW; u++) {
+      const uint16_t *kp, *vp;
+      if (all_cache) {
+        kp = kc + (size_t)(k0 + lkey[u]) * HD;
+        vp = vc + (size_t)(k0 + lkey[u]) * HD;
+      } else if (all_fresh) {
+        kp = kn + (size_t)(k0 + lkey[u] - fresh0) * ldq;
+        vp = vn + (size_t)(k0 + lkey[u] - fresh0) * ldq;
+      } else {
+        // per-key source, as integer selects (a select between two pointer
+        // pairs is otherwise lowered to a table in private memory)
+        const int k = attn_key_index(k0 + lkey[u], kbeg, kend);
+        const bool f = k >= fresh0;
+        const size_t off = f ? (size_t)(k - fresh0) * ldq : (size_t)k * HD;
+        const uint64_t kb = f ? (uint64_t)(uintptr_t)kn : (uint64_t)(uintptr_t)kc;
+        const uint64_t vb = f ? (uint64_t)(uintptr_t)vn : (uint64_t)(uintptr_t)vc;
+        kp = (const uint16_t*)(uintptr_t)(kb + off * 2);
+        vp = (const uint16_t*)(uintptr_t)(vb + off * 2);
+      }
+      const int ii = w * NIW + u;
+      lds_dma16(kp + lq[u] * 8, &lds[nb][0][ii * 1024]);
+      lds_dma16(vp + lq[u] * 8, &lds[nb][1][ii * 1024]);
+    }
+  };
+
+  f32x4_t o[2][NHT];
+#pragma unroll
+  for (int j = 0; j < 2; j++)
+#pragma unroll
+    for (int u = 0; u < NHT; u++) o[j][u] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  float mrow[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+
+  // LDS byte offsets of this lane's reads (tile-independent)
+  int koff[4][NSS];     // K fragment: key 16 mt + l16, chunk 4 ss + g4
+#pragma unroll
+  for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+    for (int ss = 0; ss < NSS; ss++) {
+      const int r = 16 * mt + l16, q = 4 * ss + g4;
+      koff[mt][ss] = r * RBY + 16 * (q ^ (r & (CPK - 1)));
+    }
+  // V^T operand: keys 32 c + 16 h + 4 g4 + l16 / 4, dims 16 ht + 4 (l16 % 4)
+  auto voff = [&](int c, int h, int ht) __attribute__((always_inline)) {
+    const int r = 32 * c + 16 * h + 4 * g4 + (l16 >> 2);
+    const int byte = 32 * ht + 8 * (l16 & 3);
+    return r * RBY + 16 * ((byte >> 4) ^ (r & (CPK - 1))) + (byte & 15);
+  };
+
+  auto compute = [&](int k0, int nb, bool full) __attribute__((always_inline)) {
+    const char* ks = lds[nb][0];
+    const char* vs = lds[nb][1];
+    f32x4_t s[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++) s[j][mt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ss = 0; ss < NSS; ss++) {
+      FragBF kf[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++)
+        kf[mt].v = *reinterpret_cast<const bf16x8_t*>(ks + koff[mt][ss]);
+#pragma unroll
+      for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+        for (int j = 0; j < 2; j++) mma(s[j][mt], kf[mt], qf[j][ss]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      float tmax;
+      if (full) {
+        float x = max3_nn(s[j][0][0], s[j][0][1], s[j][0][2]);
+        x = max3_nn(x, s[j][0][3], s[j][1][0]);
+        x = max3_nn(x, s[j][1][1], s[j][1][2]);
+        x = max3_nn(x, s[j][1][3], s[j][2][0]);
+        x = max3_nn(x, s[j][2][1], s[j][2][2]);
+        x = max3_nn(x, s[j][2][3], s[j][3][0]);
+        x = max3_nn(x, s[j][3][1], s[j][3][2]);
+        tmax = max_nn(x, s[j][3][3]) * a.scale_log2;
+      } else {
+        const int ql = j == 0 ? qlim0 : qlim1;
+        tmax = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const int kk = k0 + 16 * mt + 4 * g4 + i;
+            const bool ok = (kk < kend) & (kk <= ql) & qv[j];
+            const float v = ok ? s[j][mt][i] * a.scale_log2 : -INFINITY;
+            s[j][mt][i] = v;
+            tmax = fmaxf(tmax, v);
+          }
+      }
+      tmax = pair_max16(tmax);
+      tmax = pair_max32(tmax);
+      // move the reference only past the margin (a row's first keys always
+      // move it: the reference starts at -inf)
+      const bool move = tmax > mrow[j] + ATTN_RESCALE_LOG2;
+      if (__ballot(move)) {
+        const float alpha = move ? (mrow[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrow[j] - tmax)) : 1.f;
+        mrow[j] = move ? tmax : mrow[j];
+        lsum[j] *= alpha;
+#pragma unroll
+        for (int u = 0; u < NHT; u++) o[j][u] *= alpha;
+      }
+      const float mref = mrow[j];
+      float psum = 0.f;
+      if (full) {
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][mt][i], a.scale_log2, -mref));
+            s[j][mt][i] = p;
+            psum += p;
+          }
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < 4; mt++)
+#pragma unroll
+          for (int i = 0; i < 4; i++) {
+            const float p = mref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[j][mt][i] - mref);
+            s[j][mt][i] = p;
+            psum += p;
+          }
+      }
+      lsum[j] += psum;
+    }
+    // O^T += V^T P^T over the two 32-key chunks of the tile
+#pragma unroll
+    for (int c = 0; c < KT / 32; c++) {
+      FragBF pf[2];
+#pragma unroll
+      for (int j = 0; j < 2; j++)
+        pf[j].v = __builtin_bit_cast(bf16x8_t, make_uint4(f2bf2(s[j][2 * c][0], s[j][2 * c][1]),
+                                                          f2bf2(s[j][2 * c][2], s[j][2 * c][3]),
+                                                          f2bf2(s[j][2 * c + 1][0], s[j][2 * c + 1][1]),
+                                                          f2bf2(s[j][2 * c + 1][2], s[j][2 * c + 1][3])));
+#pragma unroll
+      for (int ht = 0; ht < NHT; ht++) {
+        const s16x4_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vs + voff(c, 0, ht)));
+        const s16x4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vs + voff(c, 1, ht)));
+        FragBF vf;
+        vf.v = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int j = 0; j < 2; j++) mma(o[j][ht], vf, pf[j]);
+      }
+    }
+  };
+
+  // NBUF-1 tiles in flight: tile t+NBUF-1 is issued into the buffer that
+  // held tile t-1 once the barrier shows every wave is done with it
+  constexpr int LPT = 2 * NIW;   // wave loads per tile
+  const int ntile = kend > kbeg ? (kend - kbeg + KT - 1) / KT : 0;
+#pragma unroll
+  for (int pb = 0; pb < NBUF - 1; pb++)
+    if (pb < ntile) issue(pb, kbeg + pb * KT);
+  auto step = [&](auto bc, int tl) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(bc)::value;
+    // this wave's loads of tile tl have landed (the later tiles' may not have)
+    const int later = min(NBUF - 2, ntile - 1 - tl);
+    if (NBUF >= 4 && later >= 2) wait_vmcnt<(NBUF >= 4 ? 2 * LPT : 0)>();
+    else if (NBUF >= 3 && later >= 1) wait_vmcnt<(NBUF >= 3 ? LPT : 0)>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    if (tl + NBUF - 1 < ntile) issue((BUF + NBUF - 1) % NBUF, kbeg + (tl + NBUF - 1) * KT);
+    const int k0 = kbeg + tl * KT;
+    compute(k0, BUF, k0 + KT <= kend && k0 + KT - 1 <= qlim_all);
+  };
+  for (int it = 0; it < ntile; it += NBUF) {
+    step(std::integral_constant<int, 0>(), it);
+    if (it + 1 < ntile) step(std::integral_constant<int, 1>(), it + 1);
+    if (NBUF >= 3 && it + 2 < ntile) step(std::integral_constant<int, (NBUF >= 3 ? 2 : 0)>(), it + 2);
+    if (NBUF >= 4 && it + 3 < ntile) step(std::integral_constant<int, (NBUF >= 4 ? 3 : 0)>(), it + 3);
+  }
+
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    float l = lsum[j];
+    l += lane_xor16(l);
+    l += lane_xor32(l);
+    const size_t row = (size_t)b * a.T + qi[j];
+    if (!qv[j]) {
+      // rows past the request's queries are not stored
+    } else if (a.nsplit == 1) {
+      const float inv = 1.f / l;
+      uint16_t* out = (uint16_t*)a.out + row * (a.Hq * HD) + head[j] * HD + 4 * g4;
+#pragma unroll
+      for (int ht = 0; ht < NHT; ht++)
+        *reinterpret_cast<uint2*>(out + 16 * ht) =
+            make_uint2(f2bf2(o[j][ht][0] * inv, o[j][ht][1] * inv), f2bf2(o[j][ht][2] * inv, o[j][ht][3] * inv));
+    } else {
+      // key splits: unnormalised partials (O, m, l), merged by attn_merge_k
+      const size_t e = split * (size_t)a.rows * a.Hq + row * a.Hq + head[j];
+      float* po = a.po + e * HD + 4 * g4;
+#pragma unroll
+      for (int ht = 0; ht < NHT; ht++)
+        *reinterpret_cast<float4*>(po + 16 * ht) = make_float4(o[j][ht][0], o[j][ht][1], o[j][ht][2], o[j][ht][3]);
+      if (g4 == 0) {
+        a.pml[2 * e] = mrow[j];
+        a.pml[2 * e + 1] = l;
+      }
+    }
+  }
+}
+
 // combine key splits in split order: o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
 // A thread owns 8 consecutive head-dimension elements of one (row, head)
 // entry; the partial loads of several splits are in flight together.
@@ -483,10 +805,21 @@ struct AttnPlan {
   unsigned grid;
 };
 
-AttnPlan plan_attention(int B, int T, const Lens& len, int Hq, int Hkv, long part_cap) {
+// bf16 kernel: waves per block and tile buffers (4 waves x 32 rows, two 32 KB
+// K+V tile buffers: 64 KB of LDS at hd 128, two blocks per CU).  Measured at
+// the 8192-prefix and batch-8 workloads: 8 waves with three buffers (one block
+// per CU, two tiles in flight) took 42 and 81 us against 44 and 73 us.
+constexpr int ATTN_NW = 4;
+constexpr int ATTN_NBUF = 2;
+
+// rows per block: 32 per wave for the bf16 kernel, 64 for the fp32 kernel
+// (4 waves x 16 rows)
+int attn_block_rows(int act) { return act == ACT_BF16 ? 32 * ATTN_NW : 64; }
+
+AttnPlan plan_attention(int act, int B, int T, const Lens& len, int Hq, int Hkv, long part_cap) {
   AttnPlan p{};
   p.G = Hq / Hkv;
-  p.QT = 64 / p.G;
+  p.QT = attn_block_rows(act) / p.G;
   int maxkeys = 0;
   for (int b = 0; b < B; b++) maxkeys = maxkeys > len.v[b] + T ? maxkeys : len.v[b] + T;
   p.nqt = (T + p.QT - 1) / p.QT;
@@ -513,7 +846,7 @@ AttnPlan plan_attention(int B, int T, const Lens& len, int Hq, int Hkv, long par
 }
 
 void launch_attention(const AttnArgsHost& h, hipStream_t s) {
-  const AttnPlan p = plan_attention(h.B, h.T, h.len, h.Hq, h.Hkv, h.part_cap);
+  const AttnPlan p = plan_attention(h.act, h.B, h.T, h.len, h.Hq, h.Hkv, h.part_cap);
   AttnArgs a{};
   a.q = h.q;
   a.ldq = h.ldq;
@@ -540,8 +873,8 @@ void launch_attention(const AttnArgsHost& h, hipStream_t s) {
   a.groups = p.groups;
   const dim3 grid(p.grid);
   if (h.act == ACT_BF16) {
-    if (h.hd == 128) attn_k<uint16_t, 128><<<grid, 256, 0, s>>>(a);
-    else attn_k<uint16_t, 64><<<grid, 256, 0, s>>>(a);
+    if (h.hd == 128) attn_bf16_k<128, ATTN_NBUF, ATTN_NW><<<grid, ATTN_NW * 64, 0, s>>>(a);
+    else attn_bf16_k<64, ATTN_NBUF, ATTN_NW><<<grid, ATTN_NW * 64, 0, s>>>(a);
   } else {
     if (h.hd == 128) attn_k<float, 128><<<grid, 256, 0, s>>>(a);
     else attn_k<float, 64><<<grid, 256, 0, s>>>(a);
@@ -559,17 +892,19 @@ void launch_attention(const AttnArgsHost& h, hipStream_t s) {
   }
 }
 
-// Host replica of every K/V address the attention kernel issues for one
+// Host replica of every K/V address the attention kernels issue for one
 // launch (the plan, the block decode and the key index of each staged slot,
-// with the tile schedule of the kernel: tiles 0, 1, 2 in the prologue, then
-// tile i+3 while tile i is computed).  Returns the number of addressed keys
-// that are not keys of the block's own request: in mode 0 a cache row must
-// lie in [0, len[b]) and a canvas row in [0, T); in mode 1 a cache row in
-// [0, len[b] + T) (the new keys are written before the attention runs).
-// Also checks the partial entries the launch writes against part_cap.
-long attn_check_addresses(int B, int T, const Lens& len, int Hq, int Hkv, int mode,
+// with each kernel's tile schedule: the bf16 kernel loads tiles 0 ..
+// ntile-1 only; the fp32 kernel loads tiles 0, 1, 2 in its prologue, then tile
+// i+3 while tile i is computed, so it stages tiles past the split end).
+// Returns the number of addressed keys that are not keys of the block's own
+// request: in mode 0 a cache row must lie in [0, len[b]) and a canvas row in
+// [0, T); in mode 1 a cache row in [0, len[b] + T) (the new keys are written
+// before the attention runs).  Also counts a launch whose partials would
+// overflow part_cap.
+long attn_check_addresses(int act, int B, int T, const Lens& len, int Hq, int Hkv, int mode,
                           long part_cap, long* nslots) {
-  const AttnPlan p = plan_attention(B, T, len, Hq, Hkv, part_cap);
+  const AttnPlan p = plan_attention(act, B, T, len, Hq, Hkv, part_cap);
   long bad = 0, n = 0;
   if (p.nsplit > 1 && (long)B * T * Hq * p.nsplit > part_cap) bad++;
   for (unsigned id = 0; id < p.grid; id++) {
@@ -580,9 +915,11 @@ long attn_check_addresses(int B, int T, const Lens& len, int Hq, int Hkv, int mo
     const int kbeg = split * p.split_len;
     const int kend = nkeys < kbeg + p.split_len ? nkeys : kbeg + p.split_len;
     const int ntile = kend > kbeg ? (kend - kbeg + KT - 1) / KT : 0;
-    // tiles loaded: 0, 1, 2, then it+3 for it = 0 .. (ntile rounded down to even) - 1
-    int last = 2;
-    for (int it = 0; it + 2 <= ntile; it += 2) last = it + 1 + 3 > last ? it + 1 + 3 : last;
+    int last = ntile - 1;
+    if (act != ACT_BF16) {
+      last = 2;
+      for (int it = 0; it + 2 <= ntile; it += 2) last = it + 1 + 3 > last ? it + 1 + 3 : last;
+    }
     for (int tl = 0; tl <= last; tl++)
       for (int j = 0; j < KT; j++) {
         const int k = attn_key_index(kbeg + tl * KT + j, kbeg, kend);
@@ -596,10 +933,12 @@ long attn_check_addresses(int B, int T, const Lens& len, int Hq, int Hkv, int mo
 
 }  // namespace dg
 
-extern "C" long dg_check_attention_addresses(int B, int T, const int32_t* lens, int Hq, int Hkv,
-                                         int mode, long part_cap, long* nslots) {
+extern "C" long dg_check_attention_addresses(int act_dtype, int B, int T, const int32_t* lens, int Hq,
+                                             int Hkv, int mode, long part_cap, long* nslots) {
   dg::Lens l{};
   if (B < 1 || B > DG_MAX_BATCH || T < 1 || Hkv < 1 || Hq % Hkv) return -1;
+  if (act_dtype != DG_F32 && act_dtype != DG_BF16) return -1;
   for (int b = 0; b < B; b++) l.v[b] = lens[b];
-  return dg::attn_check_addresses(B, T, l, Hq, Hkv, mode, part_cap, nslots);
+  return dg::attn_check_addresses(act_dtype == DG_BF16 ? dg::ACT_BF16 : dg::ACT_F32, B, T, l, Hq,
+                                  Hkv, mode, part_cap, nslots);
 }

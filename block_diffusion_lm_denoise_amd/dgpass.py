@@ -113,7 +113,7 @@ def lib():
         L.dg_pack_weight.restype = i32
         L.dg_status_str.argtypes = [i32]
         L.dg_status_str.restype = C.c_char_p
-        L.dg_check_attention_addresses.argtypes = [i32, i32, vp, i32, i32, i32, C.c_long,
+        L.dg_check_attention_addresses.argtypes = [i32, i32, i32, vp, i32, i32, i32, C.c_long,
                                                    C.POINTER(C.c_long)]
         L.dg_check_attention_addresses.restype = C.c_long
         _lib = L
@@ -217,13 +217,13 @@ def _renoise_struct(renoise):
     return nx, (p0, rq)
 
 
-def check_attention_addresses(B, T, lens, Hq, Hkv, mode, part_cap):
+def check_attention_addresses(act, B, T, lens, Hq, Hkv, mode, part_cap):
     """Host replay of the attention's K/V addresses (dg_check_attention_addresses):
     (slots addressing a key outside the block's request, slots checked)."""
     ln = np.ascontiguousarray(lens, dtype=np.int32)
     n = C.c_long(0)
-    bad = lib().dg_check_attention_addresses(int(B), int(T), ln.ctypes.data_as(C.c_void_p), int(Hq),
-                                             int(Hkv), int(mode), int(part_cap), C.byref(n))
+    bad = lib().dg_check_attention_addresses(_DT[act], int(B), int(T), ln.ctypes.data_as(C.c_void_p),
+                                             int(Hq), int(Hkv), int(mode), int(part_cap), C.byref(n))
     return int(bad), int(n.value)
 
 

@@ -14,7 +14,9 @@
 extern "C" {
 #endif
 
-/* The attention of a denoising pass (mode 0) or of a prefill (mode 1) over B
+/* The attention of a denoising pass (mode 0) or of a prefill (mode 1), with
+ * activations of storage type act_dtype (DG_F32 or DG_BF16: the two use
+ * different kernels and tile schedules), over B
  * requests of T new rows each, with len[b] cached keys (host array [B]), Hq
  * query heads sharing Hkv key/value heads and room for part_cap (row, head)
  * entries of key-split partials.  Course page "Module 12. Diffusion Language
@@ -26,9 +28,10 @@ extern "C" {
  * [0, T); mode 1: cache rows [0, len[b] + T)), plus one if the partials
  * would overflow part_cap; 0 means every access is in bounds.  *nslots (may
  * be NULL) receives the number of slots checked.  Returns -1 for invalid
- * arguments (B outside [1, DG_MAX_BATCH], T < 1, Hq not a multiple of Hkv). */
-long dg_check_attention_addresses(int B, int T, const int32_t* len, int Hq, int Hkv, int mode,
-                                  long part_cap, long* nslots);
+ * arguments (B outside [1, DG_MAX_BATCH], T < 1, Hq not a multiple of Hkv,
+ * another act_dtype). */
+long dg_check_attention_addresses(int act_dtype, int B, int T, const int32_t* len, int Hq, int Hkv,
+                                  int mode, long part_cap, long* nslots);
 
 #ifdef __cplusplus
 }

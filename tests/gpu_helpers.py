@@ -4,12 +4,13 @@ seeded inputs and compare them.
 Tolerances (per tensor, max|gpu - oracle| / max|oracle|): 1e-4 for fp32
 storage, 2e-2 for bf16 storage with fp32 accumulation.  Integer outputs
 (routing ids, permutation, counts, re-noise tokens) are bit-exact when both
-sides route on the same fp32 logits.  The argmax must agree wherever the
-oracle's top-2 logit gap exceeds 1e-2 (absolute), asserted where the LM head
-reads the same input on both sides (the oracle's final-norm rows injected into
-the GPU's head) and in fp32 end to end; bf16 runs without that injection
-report how many rows with a gap above 1e-2 changed their argmax (bf16 rounding
-differences upstream move the logits by up to a few 1e-2).
+sides route on the same fp32 logits (end to end, bf16 runs report the tokens
+routed differently at k-th logit gaps above 1e-2).  The argmax must agree
+wherever the oracle's top-2 logit gap exceeds 1e-2 (absolute), asserted where
+the LM head reads the same input on both sides (the oracle's final-norm rows
+injected into the GPU's head) and in fp32 end to end; bf16 runs without that
+injection report how many rows with a gap above 1e-2 changed their argmax
+(bf16 rounding differences upstream move the logits by up to a few 1e-2).
 """
 import numpy as np
 import torch
@@ -189,13 +190,15 @@ def compare_pass(cfg, o, g, inject_used, label="", head_injected=False):
 
     With injected router logits both sides route on identical fp32 logits, so
     ids, gates order, permutation and counts must be bit-exact and every tap is
-    compared.  With free routing each token's set of experts must agree
-    wherever the oracle's k-th vs (k+1)-th logit gap exceeds 1e-2 (the order
-    inside the set may differ at near-ties, so slots are aligned by expert id
-    before comparing per-slot taps); a token routed to a different set is
-    excluded from that layer's float comparisons, and later layers (and the
-    head, unless it was the last layer) are not compared, since every later
-    value mixes in that token.  The argmax must agree wherever the oracle's
+    compared.  With free routing each token's set of experts is compared (the
+    order inside the set may differ at near-ties, so slots are aligned by
+    expert id before comparing per-slot taps); tokens whose set differs where
+    the oracle's k-th vs (k+1)-th logit gap exceeds 1e-2 are counted (an
+    error in fp32, reported for bf16: the router logits themselves are held to
+    the max-rel bar, and bf16 rounding upstream moves them by ~1e-2); a token
+    routed to a different set is excluded from that layer's float comparisons,
+    and later layers (and the head, unless it was the last layer) are not
+    compared, since every later value mixes in that token.  The argmax must agree wherever the oracle's
     top-2 logit gap exceeds 1e-2 when the GPU's head read the oracle's
     final-norm rows (head_injected) or the storage is fp32; otherwise the
     number of such rows that changed is reported."""
@@ -235,7 +238,8 @@ def compare_pass(cfg, o, g, inject_used, label="", head_injected=False):
             rep["route_exempt"] = int((gap <= 1e-2).sum())
             rep["route_order_differs"] = int((same[:L_ok] & np.any(gt["ids"][:L_ok] != ot["ids"][:L_ok], -1)).sum())
             rep["layers_compared"] = L_ok
-            if bad.any():
+            rep["route_flips_gap_gt_1e-2"] = int(bad.sum())
+            if bad.any() and act == "f32":
                 fails.append(f"routing differs on {int(bad.sum())} clear tokens")
             # align the GPU's slots to the oracle's order (same expert sets)
             for n in ("gates", "hmid", "yexp"):

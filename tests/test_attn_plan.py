@@ -37,12 +37,14 @@ CASES = [
 
 @pytest.mark.parametrize("B,T,lens,Hq,Hkv,mode", CASES)
 @pytest.mark.parametrize("part_cap", [0, 1 << 12, 1 << 18])
-def test_every_staged_key_belongs_to_the_blocks_request(B, T, lens, Hq, Hkv, mode, part_cap):
-    bad, n = dgpass.check_attention_addresses(B, T, lens, Hq, Hkv, mode, part_cap)
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_every_staged_key_belongs_to_the_blocks_request(act, B, T, lens, Hq, Hkv, mode, part_cap):
+    bad, n = dgpass.check_attention_addresses(act, B, T, lens, Hq, Hkv, mode, part_cap)
     assert n > 0
     assert bad == 0, f"{bad} of {n} staged K/V slots address another request's keys"
 
 
 def test_invalid_arguments_are_rejected():
-    assert dgpass.check_attention_addresses(0, 4, [], 4, 2, 0, 0)[0] == -1
-    assert dgpass.check_attention_addresses(1, 4, [3], 3, 2, 0, 0)[0] == -1
+    assert dgpass.check_attention_addresses("bf16", 0, 4, [], 4, 2, 0, 0)[0] == -1
+    assert dgpass.check_attention_addresses("bf16", 1, 4, [3], 3, 2, 0, 0)[0] == -1
+    assert dgpass.check_attention_addresses("fp8", 1, 4, [3], 4, 2, 0, 0)[0] == -1
