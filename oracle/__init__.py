@@ -56,6 +56,7 @@ def lib():
         L.or_kv_prefill.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, i32, vp, i32]
         L.or_denoise_pass.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, i32, vp, vp, vp, i32]
         L.or_renoise.argtypes = [vp, vp, vp, C.c_float, C.c_uint64, C.c_uint32, vp, vp, i32, i32, i32]
+        L.or_unmask.argtypes = [vp, vp, vp, C.c_float, C.c_int32, i32, i32, i32, vp, vp]
         L.or_philox4x64_10.argtypes = [vp, vp, vp]
         L.or_round_to.argtypes = [i32, C.c_double]
         L.or_round_to.restype = C.c_double
@@ -201,6 +202,22 @@ def renoise(canvas, argmax, conf, tau, seed, pass_tag, pos0, V, req_id=None):
     if rc != 0:
         raise ValueError(f"or_renoise failed: {rc}")
     return cv
+
+
+def unmask(canvas, argmax, conf, tau, mask_id, final_pass=False):
+    """Masked-diffusion update of a copy of canvas [B, N]: returns (canvas,
+    changed [B], masked_left [B])."""
+    cv = np.array(canvas, dtype=np.int32, copy=True, order="C")
+    B, N = cv.shape
+    am = np.ascontiguousarray(argmax, dtype=np.int32)
+    cf = np.ascontiguousarray(conf, dtype=np.float32)
+    ch = np.zeros(B, np.int32)
+    ml = np.zeros(B, np.int32)
+    rc = lib().or_unmask(_ptr(cv), _ptr(am), _ptr(cf), float(tau), int(mask_id), int(bool(final_pass)),
+                         B, N, _ptr(ch), _ptr(ml))
+    if rc != 0:
+        raise ValueError(f"or_unmask failed: {rc}")
+    return cv, ch, ml
 
 
 def philox4x64_10(ctr, key):

@@ -143,6 +143,34 @@ int or_renoise(int32_t* canvas, const int32_t* argmax, const float* conf, float 
 }
 
 /* ------------------------------------------------------------------------ */
+/* masked ("absorbing") diffusion, the earlier sampler the explainer        */
+/* contrasts with uniform-state noise ("First attempt: masked diffusion"):   */
+/* slots start as a [MASK] token; a pass's prediction fills a masked slot,   */
+/* and a filled slot is locked in for good.  Reading: a masked slot is      */
+/* filled when its confidence reaches tau (the same rule that keeps a slot  */
+/* under uniform-state noise); the canvas's last pass fills every slot.     */
+/* ------------------------------------------------------------------------ */
+
+int or_unmask(int32_t* canvas, const int32_t* argmax, const float* conf, float tau, int32_t mask_id,
+              int final_pass, int B, int N, int32_t* changed, int32_t* masked_left) {
+  if (!canvas || !argmax || !conf || B < 0 || N < 0) return -1;
+  for (int b = 0; b < B; b++) {
+    int nchanged = 0, nleft = 0;
+    for (int i = 0; i < N; i++) {
+      size_t t = (size_t)b * N + i;
+      if (canvas[t] == mask_id && (final_pass || conf[t] >= tau)) {
+        if (argmax[t] != canvas[t]) nchanged++;
+        canvas[t] = argmax[t];
+      }
+      if (canvas[t] == mask_id) nleft++;
+    }
+    if (changed) changed[b] = nchanged;
+    if (masked_left) masked_left[b] = nleft;
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* layer pieces                                                             */
 /* ------------------------------------------------------------------------ */
 

@@ -117,6 +117,15 @@ int or_renoise(int32_t* canvas, const int32_t* argmax, const float* conf, float 
                uint64_t seed, uint32_t pass_tag, const int32_t* pos0, const uint32_t* req_id,
                int B, int N, int V);
 
+/* Masked ("absorbing") diffusion update of canvases [B][N] in place: a slot
+ * holding mask_id takes argmax when conf >= tau (every masked slot when
+ * final_pass is set); any other slot is left as it is (filled slots are
+ * locked in).  changed[b] (may be NULL) receives the number of slots of
+ * request b whose token changed, masked_left[b] (may be NULL) the number
+ * still holding mask_id. */
+int or_unmask(int32_t* canvas, const int32_t* argmax, const float* conf, float tau, int32_t mask_id,
+              int final_pass, int B, int N, int32_t* changed, int32_t* masked_left);
+
 /* Philox4x64 with 10 rounds, exposed for the known-answer tests. */
 void or_philox4x64_10(const uint64_t ctr[4], const uint64_t key[2], uint64_t out[4]);
 

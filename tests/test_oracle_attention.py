@@ -179,3 +179,38 @@ def test_batch_requests_are_independent_with_ragged_prefixes():
         np.testing.assert_array_equal(a1[0], am[b])
         np.testing.assert_array_equal(c1[0], cf[b])
         np.testing.assert_array_equal(t1["logits"], t["logits"][b * 6:(b + 1) * 6])
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_decode_step_is_a_one_slot_pass_plus_one_token_prefill(act):
+    """An autoregressive step over the oracle's own functions: the head of a
+    one-slot canvas pass (its query sees the prefix and itself) is the last
+    row of a joint causal forward, and a one-token prefill writes the same K/V
+    the pass computed for that slot.  Checked against a joint pass over the
+    whole sequence whose last row is the new token (course page, block-mask
+    exercise: a prefix row is causal, so the new row is the last causal row)."""
+    cfg = tiny_cfg(act=act, expert=act, L=2)
+    model, w = oracle_model(cfg, seed=5)
+    P = 9
+    ks, vs, ln = prefilled(model, cfg, 1, P, cap=P + 2, seed=5)
+    tok = np.array([[17]], np.int32)
+    am, cf, t = model.denoise_pass(ks, vs, ln, tok, taps=("qkv", "logits"))
+    ks2 = [k.copy() for k in ks]
+    vs2 = [v.copy() for v in vs]
+    ln2 = ln.copy()
+    model.kv_prefill(ks2, vs2, ln2, tok)
+    assert ln2[0] == P + 1
+    QD, KD = cfg.Hq * cfg.hd, cfg.Hkv * cfg.hd
+    for l in range(cfg.L):
+        k_pass = t["qkv"][l, 0, QD:QD + KD].reshape(cfg.Hkv, cfg.hd)
+        v_pass = t["qkv"][l, 0, QD + KD:].reshape(cfg.Hkv, cfg.hd)
+        np.testing.assert_array_equal(ks2[l][0, :, P], k_pass)
+        np.testing.assert_array_equal(vs2[l][0, :, P], v_pass)
+    # the same step as the last query of a causal prefill of the whole
+    # sequence: prefill P tokens, then a one-slot pass is what a step sees
+    prompt = synth.tokens(cfg.V, (1, P), 5, name="prompt0").numpy()
+    ks3, vs3 = model.new_cache(1, P + 2)
+    ln3 = np.zeros(1, np.int32)
+    model.kv_prefill(ks3, vs3, ln3, np.concatenate([prompt, tok], 1))
+    for l in range(cfg.L):
+        np.testing.assert_array_equal(ks3[l][0, :, :P + 1], ks2[l][0, :, :P + 1])

@@ -106,3 +106,62 @@ def test_threshold_invariants():
     np.testing.assert_array_equal(oracle.renoise(canvas, am, conf, 1.5, 11, 4, pos0, V), noise)
     # the old canvas content never matters
     np.testing.assert_array_equal(oracle.renoise(canvas * 0, am, conf, tau, 11, 4, pos0, V), out)
+
+
+# ---- masked ("absorbing") diffusion: explainer "DiffusionGemma", "First
+# attempt: masked diffusion" -- a filled [MASK] slot locks in ----
+
+def _masked_case(seed=3, B=3, N=50, V=100, mask_id=99):
+    rng = np.random.default_rng(seed)
+    canvas = rng.integers(0, V - 1, (B, N)).astype(np.int32)
+    canvas[rng.random((B, N)) < 0.6] = mask_id
+    argmax = rng.integers(0, V - 1, (B, N)).astype(np.int32)
+    conf = rng.random((B, N)).astype(np.float32)
+    return canvas, argmax, conf
+
+
+def test_unmask_fills_confident_masked_slots_and_locks_the_rest():
+    canvas, argmax, conf = _masked_case()
+    out, ch, ml = oracle.unmask(canvas, argmax, conf, 0.5, 99)
+    masked = canvas == 99
+    fill = masked & (conf >= 0.5)
+    np.testing.assert_array_equal(out[fill], argmax[fill])
+    np.testing.assert_array_equal(out[~masked], canvas[~masked])        # filled slots never change
+    assert (out[masked & ~fill] == 99).all()                            # the rest stay masked
+    np.testing.assert_array_equal(ch, (out != canvas).sum(1))           # brute-force counts
+    np.testing.assert_array_equal(ml, (out == 99).sum(1))
+
+
+def test_unmask_special_thresholds_and_final_pass():
+    canvas, argmax, conf = _masked_case(seed=4)
+    masked = canvas == 99
+    out, _, ml = oracle.unmask(canvas, argmax, conf, 0.0, 99)           # tau 0: every masked slot fills
+    np.testing.assert_array_equal(out[masked], argmax[masked])
+    assert (ml == 0).all()
+    out, ch, _ = oracle.unmask(canvas, argmax, conf, 1.5, 99)           # tau > 1: none fills
+    np.testing.assert_array_equal(out, canvas)
+    assert (ch == 0).all()
+    out, _, ml = oracle.unmask(canvas, argmax, conf, 1.5, 99, final_pass=True)
+    np.testing.assert_array_equal(out[masked], argmax[masked])          # the last pass fills all
+    np.testing.assert_array_equal(out[~masked], canvas[~masked])
+    assert (ml == 0).all()
+    # an argmax equal to the mask token keeps the slot masked (and unchanged)
+    am2 = argmax.copy()
+    am2[masked] = 99
+    out, ch, ml = oracle.unmask(canvas, am2, conf, 0.0, 99)
+    np.testing.assert_array_equal(out, canvas)
+    assert (ch == 0).all() and (ml == masked.sum(1)).all()
+
+
+def test_uniform_update_fixed_point():
+    """Uniform-state re-noise has converged once every slot is confident and
+    already holds its prediction: the update then changes nothing (explainer,
+    "Uniform State Diffusion": after several passes the canvas converges)."""
+    rng = np.random.default_rng(6)
+    canvas = rng.integers(0, 1000, (2, 30)).astype(np.int32)
+    conf = (0.6 + 0.4 * rng.random((2, 30))).astype(np.float32)
+    out = oracle.renoise(canvas, canvas, conf, 0.6, 9, 3, np.array([0, 100], np.int32), 1000)
+    np.testing.assert_array_equal(out, canvas)
+    conf[1, 7] = 0.1                                                    # one unsure slot moves
+    out = oracle.renoise(canvas, canvas, conf, 0.6, 9, 3, np.array([0, 100], np.int32), 1000)
+    assert (out != canvas).sum() <= 1 and (out[0] == canvas[0]).all()

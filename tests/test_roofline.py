@@ -59,3 +59,19 @@ def test_moe_layer_pass_work_is_expert_dominated():
     t = R.roof_time(work.total_bytes, work.total_flops, R.HBM_BYTES_PER_S, R.MFMA_PEAK["bf16"])
     assert t == pytest.approx(work.total_bytes / R.HBM_BYTES_PER_S)
     assert 165e-6 < t < 180e-6
+
+
+def test_decode_step_work_is_a_one_slot_canvas_pass():
+    """One autoregressive step of a token over prefix P does the work of a
+    denoising pass over a one-slot canvas (its query sees the prefix and
+    itself); both read the touched experts, the attention weights and the
+    head once."""
+    cfg = WORKLOADS["layer_p1024"].model
+    for P, touched in ((1024, 8), (0, 8), (4096, 3)):
+        a = R.decode_step_work(cfg, 1, [P], [touched])
+        b = R.denoise_pass_work(cfg, 1, 1, [P], [touched])
+        assert a.total_bytes == b.total_bytes
+        assert a.total_flops == b.total_flops
+    # weights dominate the step: at the 1024 prefix it reads ~0.24 GB
+    w = R.decode_step_work(cfg, 1, [1024], [8])
+    assert 0.2e9 < w.total_bytes < 0.3e9
