@@ -77,6 +77,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sampler", choices=("uniform", "masked"), default="uniform",
+                    help="update between passes: uniform-state noise, or masked (absorbing) diffusion")
+    ap.add_argument("--early-exit", action="store_true",
+                    help="stop a canvas once it has converged (reads two counts per pass to the host)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 4 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -124,20 +128,37 @@ def main():
         lst[i], lst[i + 1] = ev_pair
         return lst
 
+    masked = args.sampler == "masked"
+    counts = torch.zeros(2, B, dtype=torch.int32, device=dev)
+    passes_run = []
+
     def canvas_loop(c, events=None, marks=None):
         pos0 = kv.lens.copy()
-        dgpass.renoise(canvas, None, None, wl.tau, wl.seed, 0, pos0, cfg.V)
+        base = dict(sampler=args.sampler, mask_id=cfg.V - 1, tau=wl.tau, seed=wl.seed, pos0=pos0,
+                    changed=counts[0] if args.early_exit else None,
+                    masked_left=counts[1] if args.early_exit else None)
+        dgpass.canvas_update(canvas, None, None, dict(base, pass_tag=0), cfg.V)
+        ran = S
         for p in range(S):
             # one mid-canvas pass of each timed step carries the stage events of
             # the dominant kernel (an event record costs a few us of GPU time)
             se = None if events is None or p != S // 2 else stage_list(events, stage_id, ev_layer)
-            # coverage and the re-noise for the next pass run in the pass's last kernel
-            nxt = dict(tau=wl.tau, seed=wl.seed, pass_tag=p + 1, pos0=pos0) if p < S - 1 else None
+            # coverage and the update for the next pass run in the pass's last
+            # kernel (uniform: none after the last pass; masked: the last update
+            # fills every masked slot)
+            last = p == S - 1
+            nxt = None if (last and not masked) else dict(base, pass_tag=p + 1, final_pass=last)
             model.denoise_pass_next(kv, canvas, argmax, conf, ws, touched=touched[c, p], renoise=nxt,
                                     stage_events=se)
+            if args.early_exit and not last:
+                torch.cuda.synchronize()
+                if int(counts[1 if masked else 0].max()) == 0:
+                    ran = p + 1
+                    break
+        passes_run.append(ran)
         if marks is not None:
             marks[0].record()
-        model.kv_prefill(kv, argmax, ws)   # append the committed canvas
+        model.kv_prefill(kv, canvas if masked else argmax, ws)   # append the committed canvas
         if marks is not None:
             marks[1].record()
 
@@ -243,7 +264,31 @@ def main():
               "steady_state_pass_us": pass_us,
               "output_tokens_per_s": B * N * C / (request_ms / 1e3)}
 
+    # autoregressive baseline (course page, break-even solution): decoding
+    # steps over the same prefix, one new token per request per step
+    ar_tok = torch.zeros(B, dtype=torch.int32, device=dev)
+    ar_am = torch.empty(B, dtype=torch.int32, device=dev)
+    ar_cf = torch.empty(B, dtype=torch.float32, device=dev)
+    kv.lens[:] = pass_lens
+    nar = 16 if cap - int(kv.lens.max()) >= 20 else max(1, cap - int(kv.lens.max()) - 4)
+    model.decode_step(kv, ar_tok, ar_am, ar_cf, ws)
+    kv.lens[:] = pass_lens
+    torch.cuda.synchronize()
+    a0, a1 = ev_pair()
+    a0.record()
+    for _ in range(nar):
+        model.decode_step(kv, ar_am, ar_am, ar_cf, ws)   # greedy: each step feeds its own output
+    a1.record()
+    torch.cuda.synchronize()
+    ar_us = a0.elapsed_time(a1) / nar * 1e3
+    kv.lens[:] = pass_lens
+    ar_work = roofline.decode_step_work(cfg, B, list(pass_lens), [min(cfg.E, B * cfg.k)] * cfg.L)
+    ar_roof = roofline.roof_time(ar_work.total_bytes, ar_work.total_flops, roofline.HBM_BYTES_PER_S,
+                                 roofline.MFMA_PEAK["bf16"])
+
     passes_per_step = S * C
+    if args.early_exit:   # the passes the timed steps actually ran
+        passes_per_step = float(np.mean(passes_run[-args.steps * C:])) * C
     value = B * N * passes_per_step / (ms_step / 1e3)
     if dom_stage == "gateup":
         dom_work, _ = roofline.gateup_work(cfg, mean_touched, B * N * cfg.k)
@@ -277,6 +322,7 @@ def main():
         "config": {"workload": wl.name, "B": B, "canvas": N, "prefix": P, "passes": S,
                    "canvases": C, "layers": cfg.L, "d_model": cfg.D, "experts": cfg.E,
                    "top_k": cfg.k, "expert_ffn": cfg.F, "vocab": cfg.V, "expert_dtype": cfg.expert,
+                   "sampler": args.sampler, "early_exit": bool(args.early_exit),
                    "step": ("prompt prefill + " if chained else "") +
                            f"{C} x (init noise + {S} x (pass + coverage + re-noise, fused tail) + "
                            "append prefill)"},
@@ -289,6 +335,12 @@ def main():
         "experts_touched_per_pass": mean_touched,
         "experts_touched_per_layer": [float(x) for x in cov_layer],
     }
+    out["ar_baseline"] = {
+        "step_us": ar_us, "tok_s": B / (ar_us / 1e6), "roof_us": ar_roof * 1e6,
+        "frac": ar_roof * 1e6 / ar_us, "steps_timed": nar,
+        "breakeven_passes": N * ar_us / pass_us,
+        "breakeven_passes_at_roofline": N * ar_roof / t_roof,
+        "note": "a canvas of N tokens in S passes beats N decoding steps iff S < N * step / pass"}
     if c3 is not None:
         out["request"] = c3
 

@@ -425,9 +425,14 @@ size_t dg_workspace_bytes(const dg_config* cfg, int32_t max_rows, int32_t max_ke
   return layout(*cfg, max_rows, attn_partial_entries(max_rows, cfg->Hq, max_keys)).total;
 }
 
-dg_status dg_kv_prefill(const dg_model* m, dg_kv* kv, const int32_t* tokens, int32_t B, int32_t T,
-                        const dg_taps* taps, void* ws, size_t ws_bytes, void* stream) {
+// causal prefill of T tokens per request; with argmax/conf set (a decoding
+// step) the last layer runs in full and the LM head reads its output
+static dg_status prefill(const dg_model* m, dg_kv* kv, const int32_t* tokens, int32_t B, int32_t T,
+                         const dg_taps* taps, void* ws, size_t ws_bytes, void* stream,
+                         int32_t* argmax, float* conf) {
+  const bool head = argmax != nullptr;
   if (!model_ok(m) || !kv || !kv->len || !tokens || !ws) return DG_ERR_INVALID;
+  if (head && !conf) return DG_ERR_INVALID;
   if (B < 1 || B > DG_MAX_BATCH || T < 1 || kv->cap < 1) return DG_ERR_INVALID;
   const dg_config& cf = m->cfg;
   for (int l = 0; l < cf.L; l++)
@@ -455,7 +460,7 @@ dg_status dg_kv_prefill(const dg_model* m, dg_kv* kv, const int32_t* tokens, int
   for (int l = 0; l < cf.L; l++) {
     const dg_layer_weights& w = m->w.layers[l];
     inject_layer_input(c, l);
-    if (l == cf.L - 1 && !(taps && taps->qkv)) {
+    if (l == cf.L - 1 && !head && !(taps && taps->qkv)) {
       // nothing downstream reads the last layer's queries or output: its K
       // and V columns only, straight into the cache
       CacheDst cd{kv->k[l], kv->v[l], kv->cap, T, 0, KD, cf.hd, cf.Hkv, lens};
@@ -468,7 +473,7 @@ dg_status dg_kv_prefill(const dg_model* m, dg_kv* kv, const int32_t* tokens, int
                at<void>(c, c.L.qkv), QKV, nullptr, &cd);
     if (taps) tap_copy(taps->qkv ? (char*)taps->qkv + (size_t)l * R * QKV * a : nullptr,
                        at<void>(c, c.L.qkv), (size_t)R * QKV * a, s);
-    if (l == cf.L - 1) break;  // nothing downstream reads the last layer's output
+    if (l == cf.L - 1 && !head) break;  // nothing downstream reads the last layer's output
     AttnArgsHost ah{act, at<void>(c, c.L.qkv), QKV, kv->k[l], kv->v[l], kv->cap, nullptr, nullptr,
                     B, T, cf.Hq, cf.Hkv, cf.hd, 1, lens, at<void>(c, c.L.o), at<float>(c, c.L.po),
                     at<float>(c, c.L.pml), c.L.part_cap};
@@ -477,12 +482,36 @@ dg_status dg_kv_prefill(const dg_model* m, dg_kv* kv, const int32_t* tokens, int
     stage_event(taps, l, DG_STAGE_ATTN, 1, s);
     if (taps) tap_copy(taps->attn ? (char*)taps->attn + (size_t)l * R * QD * a : nullptr,
                        at<void>(c, c.L.o), (size_t)R * QD * a, s);
-    moe_block(c, l, m->w.layers[l + 1].g1);
+    moe_block(c, l, l + 1 < cf.L ? m->w.layers[l + 1].g1 : m->w.gf);
+  }
+  if (head) {
+    // next token of every row: the LM head over the final RMSNorm output
+    const void* head_in = (taps && taps->inject_uf) ? taps->inject_uf : at<void>(c, c.L.u);
+    stage_event(taps, cf.L - 1, DG_STAGE_HEAD, 0, s);
+    const int nparts = launch_lmhead(act, head_in, R, cf.D, m->w.lm, cf.V, at<float>(c, c.L.lpm),
+                                     at<int32_t>(c, c.L.lpi), at<float>(c, c.L.lps),
+                                     taps ? taps->logits : nullptr, s);
+    stage_event(taps, cf.L - 1, DG_STAGE_HEAD, 1, s);
+    if (taps) tap_copy(taps->uf, at<void>(c, c.L.u), (size_t)R * cf.D * a, s);
+    launch_lm_merge(at<float>(c, c.L.lpm), at<int32_t>(c, c.L.lpi), at<float>(c, c.L.lps), R, nparts,
+                    argmax, conf, MergeNext{}, s);
   }
   dg_status st = check_hip();
   if (st != DG_OK) return st;
   for (int b = 0; b < B; b++) kv->len[b] += T;
   return DG_OK;
+}
+
+dg_status dg_kv_prefill(const dg_model* m, dg_kv* kv, const int32_t* tokens, int32_t B, int32_t T,
+                        const dg_taps* taps, void* ws, size_t ws_bytes, void* stream) {
+  return prefill(m, kv, tokens, B, T, taps, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+dg_status dg_decode_step(const dg_model* m, dg_kv* kv, const int32_t* tokens, int32_t B,
+                         int32_t* argmax, float* conf, const dg_taps* taps, void* ws, size_t ws_bytes,
+                         void* stream) {
+  if (!argmax || !conf) return DG_ERR_INVALID;
+  return prefill(m, kv, tokens, B, 1, taps, ws, ws_bytes, stream, argmax, conf);
 }
 
 // one pass; nx carries the between-pass work its last kernel takes over
@@ -515,7 +544,8 @@ static dg_status denoise(const dg_model* m, const dg_kv* kv, const int32_t* canv
   const int QD = cf.Hq * cf.hd, KD = cf.Hkv * cf.hd, QKV = QD + 2 * KD;
   hipStream_t s = c.s;
   launch_embed_norm(act, canvas, m->w.emb, m->w.layers[0].g1, R, cf.D, cf.V, cf.eps, at<void>(c, c.L.x),
-                    at<void>(c, c.L.u), s);
+                    at<void>(c, c.L.u), s, nx.rn.canvas ? nx.rn.changed : nullptr, B,
+                    nx.rn.canvas ? nx.rn.masked_left : nullptr, B);
   for (int l = 0; l < cf.L; l++) {
     const dg_layer_weights& w = m->w.layers[l];
     inject_layer_input(c, l);
@@ -568,17 +598,25 @@ dg_status dg_denoise_pass_next(const dg_model* m, const dg_kv* kv, int32_t* canv
   MergeNext nx{};
   nx.touched = touched;
   if (next) {
-    if (!next->pos0 || B < 1 || B > DG_MAX_BATCH) return DG_ERR_INVALID;
+    if (next->mode != DG_SAMPLER_UNIFORM && next->mode != DG_SAMPLER_MASKED) return DG_ERR_INVALID;
+    // positions key the noise draws: required by uniform-state noise only
+    if ((next->mode == DG_SAMPLER_UNIFORM && !next->pos0) || B < 1 || B > DG_MAX_BATCH)
+      return DG_ERR_INVALID;
     if (!canvas || canvas == argmax || (const void*)canvas == (const void*)conf) return DG_ERR_INVALID;
     for (int b = 0; b < B; b++) {
-      if (next->pos0[b] < 0) return DG_ERR_INVALID;
-      nx.rn.pos0.v[b] = next->pos0[b];
+      if (next->pos0 && next->pos0[b] < 0) return DG_ERR_INVALID;
+      nx.rn.pos0.v[b] = next->pos0 ? next->pos0[b] : 0;
       nx.rn.req.v[b] = next->req_id ? next->req_id[b] : (uint32_t)b;
     }
     nx.rn.canvas = canvas;
     nx.rn.tau = next->tau;
     nx.rn.seed = next->seed;
     nx.rn.tag = next->pass_tag;
+    nx.rn.mode = next->mode;
+    nx.rn.mask_id = next->mask_id;
+    nx.rn.final_pass = next->final_pass;
+    nx.rn.changed = next->changed;
+    nx.rn.masked_left = next->masked_left;
   }
   return denoise(m, kv, canvas, B, N, argmax, conf, taps, ws, ws_bytes, stream, nx);
 }
@@ -612,6 +650,37 @@ dg_status dg_renoise(int32_t* canvas, const int32_t* argmax, const float* conf, 
   }
   (void)hipGetLastError();
   launch_renoise(canvas, argmax, conf, tau, seed, pass_tag, p, r, B, N, V, (hipStream_t)stream);
+  return check_hip();
+}
+
+dg_status dg_canvas_update(int32_t* canvas, const int32_t* argmax, const float* conf,
+                           const dg_renoise_args* a, int32_t B, int32_t N, int32_t V, void* stream) {
+  if (!canvas || !a || B < 1 || B > DG_MAX_BATCH || N < 1 || V < 1) return DG_ERR_INVALID;
+  if (conf && !argmax) return DG_ERR_INVALID;
+  if (a->mode != DG_SAMPLER_UNIFORM && a->mode != DG_SAMPLER_MASKED) return DG_ERR_INVALID;
+  RenoiseArgs r{};
+  if (a->mode == DG_SAMPLER_UNIFORM && !a->pos0) return DG_ERR_INVALID;
+  for (int b = 0; b < B; b++) {
+    if (a->pos0 && a->pos0[b] < 0) return DG_ERR_INVALID;
+    r.pos0.v[b] = a->pos0 ? a->pos0[b] : 0;
+    r.req.v[b] = a->req_id ? a->req_id[b] : (uint32_t)b;
+  }
+  r.canvas = canvas;
+  r.argmax = argmax;
+  r.conf = conf;
+  r.tau = a->tau;
+  r.seed = a->seed;
+  r.tag = a->pass_tag;
+  r.B = B;
+  r.N = N;
+  r.V = (uint32_t)V;
+  r.mode = a->mode;
+  r.mask_id = a->mask_id;
+  r.final_pass = a->final_pass;
+  r.changed = a->changed;
+  r.masked_left = a->masked_left;
+  (void)hipGetLastError();
+  launch_canvas_update(r, (hipStream_t)stream);
   return check_hip();
 }
 

@@ -20,9 +20,16 @@ __global__ __launch_bounds__(256) void embed_norm_k(const int32_t* __restrict__ 
                                                     const TA* __restrict__ emb,
                                                     const float* __restrict__ g, int D, int V,
                                                     float eps, TA* __restrict__ x,
-                                                    TA* __restrict__ u) {
+                                                    TA* __restrict__ u, int32_t* zero0, int nzero0,
+                                                    int32_t* zero1, int nzero1) {
   __shared__ float red[4];
   const size_t row = blockIdx.x;
+  // counters the pass's last kernel adds to start at zero: cleared here, by
+  // the pass's first kernel
+  if (row == 0) {
+    if (zero0 && (int)threadIdx.x < nzero0) zero0[threadIdx.x] = 0;
+    if (zero1 && (int)threadIdx.x < nzero1) zero1[threadIdx.x] = 0;
+  }
   const int tk = min(max(tok[row], 0), V - 1);
   const TA* src = emb + (size_t)tk * D;
   float v[ROWC][8], gv[ROWC][8];
@@ -233,6 +240,48 @@ __device__ __forceinline__ int32_t renoise_token(const RenoiseArgs& a, int b, in
   return keep ? am : noise;
 }
 
+// The token of slot (b, i) after the between-pass update, from its current
+// token `old` and this pass's prediction (am, cf):
+//  - uniform-state noise: the prediction where cf >= tau, else a fresh draw;
+//  - masked ("absorbing") diffusion: a slot holding the [MASK] token takes the
+//    prediction where cf >= tau (every masked slot on the last pass); any other
+//    slot keeps its token (a filled slot is locked in).
+__device__ __forceinline__ int32_t update_token(const RenoiseArgs& a, int b, int i, int32_t old,
+                                                int32_t am, float cf) {
+  if (a.mode == DG_SAMPLER_MASKED)
+    return (old == a.mask_id && (a.final_pass || cf >= a.tau)) ? am : old;
+  return renoise_token(a, b, i, cf >= a.tau, am);
+}
+
+// One block per request: every slot's update, then the request's counts.  No
+// confidence: initialisation (uniform noise, or the [MASK] token everywhere).
+__global__ __launch_bounds__(256) void canvas_update_k(RenoiseArgs a) {
+  __shared__ int red[2][4];
+  const int b = blockIdx.x;
+  int nch = 0, nleft = 0;
+  for (int i = threadIdx.x; i < a.N; i += 256) {
+    const size_t idx = (size_t)b * a.N + i;
+    const int32_t old = a.canvas[idx];
+    int32_t t;
+    if (!a.conf) t = a.mode == DG_SAMPLER_MASKED ? a.mask_id : renoise_token(a, b, i, false, 0);
+    else t = update_token(a, b, i, old, a.argmax[idx], a.conf[idx]);
+    a.canvas[idx] = t;
+    nch += t != old;
+    nleft += a.mode == DG_SAMPLER_MASKED && t == a.mask_id;
+  }
+  // counts of at most 2^24 slots: exact in fp32
+  const float c0 = wave_sum((float)nch), c1 = wave_sum((float)nleft);
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = (int)c0;
+    red[1][threadIdx.x >> 6] = (int)c1;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (a.changed) a.changed[b] = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+    if (a.masked_left) a.masked_left[b] = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  }
+}
+
 __global__ __launch_bounds__(256) void renoise_k(RenoiseArgs a) {
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= a.B * a.N) return;
@@ -335,7 +384,13 @@ __global__ __launch_bounds__(256) void lm_merge_k(const float* __restrict__ pmax
     conf[row] = cf;
     if (nx.rn.canvas) {
       const int b = (int)row / nx.rn.N, p = (int)row % nx.rn.N;
-      nx.rn.canvas[row] = renoise_token(nx.rn, b, p, cf >= nx.rn.tau, i);
+      const int32_t old = nx.rn.canvas[row];
+      const int32_t t = update_token(nx.rn, b, p, old, i, cf);
+      nx.rn.canvas[row] = t;
+      // the counters were cleared by the pass's first kernel
+      if (nx.rn.changed && t != old) atomicAdd(nx.rn.changed + b, 1);
+      if (nx.rn.masked_left && nx.rn.mode == DG_SAMPLER_MASKED && t == nx.rn.mask_id)
+        atomicAdd(nx.rn.masked_left + b, 1);
     }
   }
 }
@@ -363,13 +418,15 @@ __global__ __launch_bounds__(256) void pack_k(const uint8_t* __restrict__ src, u
 
 // ---------------------------------------------------------------------------
 void launch_embed_norm(int act, const int32_t* tok, const void* emb, const float* g, int rows, int D,
-                       int V, float eps, void* x, void* u, hipStream_t s) {
+                       int V, float eps, void* x, void* u, hipStream_t s, int32_t* zero0, int nzero0,
+                       int32_t* zero1, int nzero1) {
   if (act == ACT_BF16)
     embed_norm_k<uint16_t><<<rows, 256, 0, s>>>(tok, (const uint16_t*)emb, g, D, V, eps,
-                                                 (uint16_t*)x, (uint16_t*)u);
+                                                 (uint16_t*)x, (uint16_t*)u, zero0, nzero0, zero1,
+                                                 nzero1);
   else
     embed_norm_k<float><<<rows, 256, 0, s>>>(tok, (const float*)emb, g, D, V, eps, (float*)x,
-                                              (float*)u);
+                                              (float*)u, zero0, nzero0, zero1, nzero1);
 }
 
 void launch_rmsnorm(int act, const void* x, const float* g, int rows, int D, float eps, void* u,
@@ -394,10 +451,15 @@ void launch_combine_norm(int act, const void* x1, const void* Y, const float* ga
 void launch_renoise(int32_t* canvas, const int32_t* argmax, const float* conf, float tau,
                     uint64_t seed, uint32_t tag, const Lens& pos0, const ReqIds& req, int B, int N,
                     int V, hipStream_t s) {
-  RenoiseArgs a{canvas, argmax, conf, tau, seed, tag, B, N, (uint32_t)V, pos0, req};
+  RenoiseArgs a{canvas, argmax, conf, tau, seed, tag, B, N, (uint32_t)V, pos0, req,
+                DG_SAMPLER_UNIFORM, 0, 0, nullptr, nullptr};
   const int n = B * N;
   if (n == 0) return;
   renoise_k<<<(n + 255) / 256, 256, 0, s>>>(a);
+}
+
+void launch_canvas_update(const RenoiseArgs& a, hipStream_t s) {
+  if (a.B > 0 && a.N > 0) canvas_update_k<<<a.B, 256, 0, s>>>(a);
 }
 
 void launch_coverage(const int32_t* counts, int L, int E, int32_t* touched, int32_t* counts_out,

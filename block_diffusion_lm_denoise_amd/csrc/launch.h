@@ -19,8 +19,10 @@ struct ReqIds {
 };
 
 // ---- elementwise / reductions (kern_elem.hip) ----
+// zero: optional device ints cleared by the same launch (n <= 256 each)
 void launch_embed_norm(int act, const int32_t* tok, const void* emb, const float* g, int rows, int D,
-                       int V, float eps, void* x, void* u, hipStream_t s);
+                       int V, float eps, void* x, void* u, hipStream_t s, int32_t* zero0 = nullptr,
+                       int nzero0 = 0, int32_t* zero1 = nullptr, int nzero1 = 0);
 void launch_rmsnorm(int act, const void* x, const float* g, int rows, int D, float eps, void* u,
                     hipStream_t s);
 void launch_combine_norm(int act, const void* x1, const void* Y, const float* gates,
@@ -48,7 +50,15 @@ struct RenoiseArgs {
   uint32_t V;
   Lens pos0;
   ReqIds req;
+  int mode;              // DG_SAMPLER_UNIFORM or DG_SAMPLER_MASKED
+  int32_t mask_id;       // masked sampler: the [MASK] token
+  int final_pass;        // masked sampler: fill every masked slot
+  int32_t* changed;      // optional [B]: slots whose token changed
+  int32_t* masked_left;  // optional [B]: slots holding mask_id afterwards
 };
+// the between-pass update of either sampler as its own launch (one block per
+// request, so the counts need no atomics); a.conf == nullptr initialises
+void launch_canvas_update(const RenoiseArgs& a, hipStream_t s);
 struct MergeNext {
   RenoiseArgs rn;
   const int32_t* counts;

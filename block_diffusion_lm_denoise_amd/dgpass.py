@@ -70,13 +70,19 @@ NSTAGES = 4
 
 class dg_renoise_args(C.Structure):
     _fields_ = [("tau", C.c_float), ("seed", C.c_uint64), ("pass_tag", C.c_uint32),
-                ("pos0", C.c_void_p), ("req_id", C.c_void_p)]
+                ("pos0", C.c_void_p), ("req_id", C.c_void_p), ("mode", C.c_int32),
+                ("mask_id", C.c_int32), ("final_pass", C.c_int32), ("changed", C.c_void_p),
+                ("masked_left", C.c_void_p)]
+
+
+SAMPLER_UNIFORM, SAMPLER_MASKED = 0, 1
+_SAMPLER = {"uniform": SAMPLER_UNIFORM, "masked": SAMPLER_MASKED}
 
 
 EXPORTS = ("dg_model_init", "dg_workspace_bytes", "dg_kv_prefill", "dg_denoise_pass",
            "dg_denoise_pass_next", "dg_renoise", "dg_expert_coverage", "dg_packed_bytes",
            "dg_pack_weight", "dg_status_str", "dg_check_attention_addresses",
-           "dg_denoise_pass_next_noalloc")
+           "dg_denoise_pass_next_noalloc", "dg_decode_step", "dg_canvas_update")
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
@@ -96,6 +102,10 @@ def lib():
         L.dg_workspace_bytes.restype = sz
         L.dg_kv_prefill.argtypes = [vp, vp, vp, i32, i32, vp, vp, sz, vp]
         L.dg_kv_prefill.restype = i32
+        L.dg_canvas_update.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp]
+        L.dg_canvas_update.restype = i32
+        L.dg_decode_step.argtypes = [vp, vp, vp, i32, vp, vp, vp, vp, sz, vp]
+        L.dg_decode_step.restype = i32
         L.dg_denoise_pass.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, vp, sz, vp]
         L.dg_denoise_pass.restype = i32
         L.dg_denoise_pass_next.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -204,17 +214,36 @@ def _taps_struct(taps, inject_router=None, inject_x=None, inject_uf=None, stage_
 
 
 def _renoise_struct(renoise):
-    """dg_renoise_args for dict(tau, seed, pass_tag, pos0[, req_id]) (or None),
-    with the host arrays it points to (kept alive by the caller)."""
+    """dg_renoise_args for dict(tau, seed, pass_tag, pos0[, req_id, sampler,
+    mask_id, final_pass, changed, masked_left]) (or None), with the host
+    arrays it points to (kept alive by the caller).  sampler: "uniform" or
+    "masked"; changed / masked_left: device int32 tensors [B] or None."""
     if renoise is None:
         return None, None
-    p0 = np.ascontiguousarray(renoise["pos0"], dtype=np.int32)
+    p0 = renoise.get("pos0")
+    p0 = None if p0 is None else np.ascontiguousarray(p0, dtype=np.int32)
     rq = renoise.get("req_id")
     rq = None if rq is None else np.ascontiguousarray(rq, dtype=np.uint32)
-    nx = dg_renoise_args(float(renoise["tau"]), int(renoise["seed"]) & (2**64 - 1),
-                         int(renoise["pass_tag"]) & 0xFFFFFFFF, p0.ctypes.data_as(C.c_void_p),
-                         None if rq is None else rq.ctypes.data_as(C.c_void_p))
+    nx = dg_renoise_args(float(renoise.get("tau", 0.0)), int(renoise.get("seed", 0)) & (2**64 - 1),
+                         int(renoise.get("pass_tag", 0)) & 0xFFFFFFFF,
+                         None if p0 is None else p0.ctypes.data_as(C.c_void_p),
+                         None if rq is None else rq.ctypes.data_as(C.c_void_p),
+                         _SAMPLER[renoise.get("sampler", "uniform")], int(renoise.get("mask_id", 0)),
+                         int(bool(renoise.get("final_pass", False))), _ptr(renoise.get("changed")),
+                         _ptr(renoise.get("masked_left")))
     return nx, (p0, rq)
+
+
+def canvas_update(canvas: torch.Tensor, argmax, conf, args: dict, V: int, stream=None):
+    """The between-pass update of device canvases [B][N] in place
+    (dg_canvas_update); args as for denoise_pass_next's renoise; conf None:
+    initialise the canvas."""
+    B, N = canvas.shape
+    nx, keep = _renoise_struct(args)
+    st = lib().dg_canvas_update(canvas.data_ptr(), _ptr(argmax), _ptr(conf), C.byref(nx), B, N, V,
+                                _stream(stream))
+    del keep
+    _check(st, "dg_canvas_update")
 
 
 def check_attention_addresses(act, B, T, lens, Hq, Hkv, mode, part_cap):
@@ -299,6 +328,19 @@ class Model:
                                  _stream(stream))
         del keep
         _check(st, "dg_kv_prefill")
+
+    def decode_step(self, kv: KVCache, tokens: torch.Tensor, argmax: torch.Tensor, conf: torch.Tensor,
+                    ws: torch.Tensor, taps=None, inject_uf=None, stage_events=None, stream=None):
+        """One autoregressive step: append tokens [B] and write the next token
+        and its confidence per request."""
+        B = tokens.shape[0]
+        s = kv.struct()
+        ts, keep = _taps_struct(taps, None, None, inject_uf, stage_events)
+        st = lib().dg_decode_step(C.byref(self._m), C.byref(s), tokens.data_ptr(), B, argmax.data_ptr(),
+                                  conf.data_ptr(), None if ts is None else C.byref(ts), ws.data_ptr(),
+                                  ws.numel(), _stream(stream))
+        del keep
+        _check(st, "dg_decode_step")
 
     def denoise_pass(self, kv: KVCache, canvas: torch.Tensor, argmax: torch.Tensor, conf: torch.Tensor,
                      ws: torch.Tensor, taps=None, inject_router=None, inject_x=None, inject_uf=None,

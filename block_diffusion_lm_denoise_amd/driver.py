@@ -9,6 +9,20 @@ canvases").  Plain readings where the pages are silent: the committed
 canvas is the last pass's argmax (no re-noise after the last pass); RNG
 pass tags are 0 for the initial noise and p+1 for the re-noise after pass
 p; positions are absolute, so chained canvases draw different noise.
+
+Two variants of the same loop (the kernels are the same; only the update
+between passes changes):
+  - sampler="masked": masked ("absorbing") diffusion, the earlier scheme the
+    explainer contrasts with ("First attempt: masked diffusion"): the canvas
+    starts as the [MASK] token, a masked slot takes the prediction once its
+    confidence reaches tau and is then locked in; after the last pass every
+    slot still masked takes its prediction, and the canvas is committed;
+  - early_exit: stop a canvas once it has converged ("Uniform State
+    Diffusion": after several passes the canvas converges) -- under uniform
+    noise when a pass's update changed no slot (every slot kept, each equal to
+    its prediction: the next pass would see the same canvas), under masked
+    diffusion when no slot is masked any more.  Each check reads two counts
+    per request back to the host after the pass.
 """
 from dataclasses import dataclass, field
 
@@ -22,31 +36,59 @@ class GenerateResult:
     canvases: list                       # committed canvases, [B][N] int32 each
     touched: torch.Tensor                # [canvases][S][L] experts touched per pass
     lens: list = field(default_factory=list)
+    passes: list = field(default_factory=list)   # passes run per canvas
 
 
 def generate(model: dgpass.Model, kv: dgpass.KVCache, prompt: torch.Tensor, n_canvases: int, N: int,
              S: int, tau: float, seed: int, ws: torch.Tensor, prefill_prompt: bool = True,
-             stream=None) -> GenerateResult:
+             stream=None, sampler: str = "uniform", mask_id: int = None,
+             early_exit: bool = False) -> GenerateResult:
     cfg = model.cfg
     B = kv.B
+    if sampler not in ("uniform", "masked"):
+        raise ValueError(f"unknown sampler {sampler}")
+    if sampler == "masked":
+        mask_id = cfg.V - 1 if mask_id is None else int(mask_id)
+        if not 0 <= mask_id < cfg.V:
+            raise ValueError("mask_id must be a vocabulary id")
     dev = prompt.device if prompt is not None else kv.k[0].device
     if prefill_prompt and prompt is not None:
         model.kv_prefill(kv, prompt, ws, stream=stream)
     canvas = torch.empty(B, N, dtype=torch.int32, device=dev)
     argmax = torch.empty(B, N, dtype=torch.int32, device=dev)
     conf = torch.empty(B, N, dtype=torch.float32, device=dev)
+    changed = torch.zeros(B, dtype=torch.int32, device=dev)
+    masked_left = torch.zeros(B, dtype=torch.int32, device=dev)
     touched = torch.zeros(n_canvases, S, cfg.L, dtype=torch.int32, device=dev)
-    out = []
+    out, used = [], []
     for c in range(n_canvases):
         pos0 = kv.lens.copy()
-        dgpass.renoise(canvas, None, None, tau, seed, 0, pos0, cfg.V, stream=stream)
+        base = dict(sampler=sampler, mask_id=mask_id or 0, tau=tau, seed=seed, pos0=pos0)
+        dgpass.canvas_update(canvas, None, None, dict(base, pass_tag=0), cfg.V, stream=stream)
+        ran = S
         for p in range(S):
-            # the pass's last kernel writes the coverage and, before every pass
-            # but the last, re-noises the canvas for the next one
-            nxt = dict(tau=tau, seed=seed, pass_tag=p + 1, pos0=pos0) if p < S - 1 else None
+            last = p == S - 1
+            # the pass's last kernel writes the coverage and the update for the
+            # next pass (uniform: none after the last pass; masked: the last
+            # update fills every masked slot)
+            if sampler == "uniform" and last:
+                nxt = None
+            else:
+                nxt = dict(base, pass_tag=p + 1, final_pass=last, changed=changed,
+                           masked_left=masked_left)
             model.denoise_pass_next(kv, canvas, argmax, conf, ws, touched=touched[c, p], renoise=nxt,
                                     stream=stream)
-        committed = argmax.clone()
+            if early_exit and not last:
+                left = masked_left if sampler == "masked" else changed
+                if stream is not None:
+                    stream.synchronize()
+                else:
+                    torch.cuda.synchronize(dev)
+                if int(left.cpu().max()) == 0:
+                    ran = p + 1
+                    break
+        committed = (argmax if sampler == "uniform" else canvas).clone()
         model.kv_prefill(kv, committed, ws, stream=stream)
         out.append(committed)
-    return GenerateResult(out, touched, [int(x) for x in kv.lens])
+        used.append(ran)
+    return GenerateResult(out, touched, [int(x) for x in kv.lens], used)

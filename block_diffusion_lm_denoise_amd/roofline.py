@@ -109,3 +109,28 @@ def down_work(cfg, touched: int, rows: int):
     b = touched * cfg.F * cfg.D * we + rows * (cfg.D + cfg.F) * w
     f = 2.0 * rows * cfg.F * cfg.D
     return b, f
+
+
+def decode_step_work(cfg, B: int, prefix_lens, experts_per_layer) -> PassWork:
+    """Algorithmic bytes and flops of one autoregressive decoding step of B
+    requests (one new token each, attending its prefix and itself):
+    experts_per_layer distinct experts read per layer (at most B*k)."""
+    w = _BYTES[cfg.act]
+    we = _BYTES[cfg.expert]
+    D, F = cfg.D, cfg.F
+    attn_w = (cfg.Hq * cfg.hd * D * 2 + cfg.Hkv * cfg.hd * D * 2)
+    by = {"embed": B * D * w + B * 4, "attn_proj": 0.0, "attention": 0.0, "router": 0.0,
+          "experts": 0.0, "head": V_bytes(cfg) + D * 4 + B * 8}
+    fl = {"attn_proj": 0.0, "attention": 0.0, "router": 0.0, "experts": 0.0,
+          "head": 2.0 * B * cfg.V * D}
+    for l in range(cfg.L):
+        by["attn_proj"] += attn_w * w + 2 * D * 4
+        by["attention"] += sum(int(p) for p in prefix_lens) * cfg.Hkv * cfg.hd * 2 * w
+        by["router"] += cfg.E * D * w
+        scales = 12 if cfg.expert == "fp8" else 0
+        by["experts"] += int(experts_per_layer[l]) * (3 * D * F * we + scales)
+        fl["attn_proj"] += 2.0 * B * attn_w
+        fl["attention"] += sum(4.0 * (int(p) + 1) * cfg.Hq * cfg.hd for p in prefix_lens)
+        fl["router"] += 2.0 * B * cfg.E * D
+        fl["experts"] += 2.0 * B * cfg.k * 3 * D * F
+    return PassWork(by, fl)

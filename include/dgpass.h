@@ -153,7 +153,7 @@ typedef struct dg_kv {
  *  - inject_router: routing of layer l uses inject_router[l] instead of the
  *    router logits (the router GEMM is skipped);
  *  - inject_uf: the LM head reads inject_uf instead of the final RMSNorm
- *    output (pass only). */
+ *    output (pass or decoding step). */
 typedef struct dg_taps {
   void* qkv;                 /* [L][BN][(Hq+2Hkv)*hd] act */
   void* attn;                /* [L][BN][Hq*hd] act: attention output before Wo */
@@ -168,11 +168,11 @@ typedef struct dg_taps {
   void* hmid;                /* [L][BN][k][F] act: SwiGLU output per slot */
   void* yexp;                /* [L][BN][k][D] act: expert output per slot */
   void* xout;                /* [L][BN][D] act: layer output (computed, not injected) */
-  void* uf;                  /* [BN][D] act: final RMSNorm output (pass only; computed) */
-  float* logits;             /* [BN][V] f32 (pass only) */
+  void* uf;                  /* [BN][D] act: final RMSNorm output (pass or decoding step; computed) */
+  float* logits;             /* [BN][V] f32 (pass or decoding step) */
   const float* inject_router;/* input [L][BN][E] f32 */
   const void* inject_x;      /* input [L][BN][D] act */
-  const void* inject_uf;     /* input [BN][D] act (pass only) */
+  const void* inject_uf;     /* input [BN][D] act (pass or decoding step) */
   void* const* stage_events; /* host array [L][DG_NSTAGES][2] of hipEvent_t: entry
                                 [l][s][0] is recorded on `stream` just before the
                                 launches of stage s of layer l, [l][s][1] just
@@ -202,6 +202,21 @@ size_t dg_workspace_bytes(const dg_config* cfg, int32_t max_rows, int32_t max_ke
 dg_status dg_kv_prefill(const dg_model* m, dg_kv* kv, const int32_t* tokens, int32_t B, int32_t T,
                         const dg_taps* taps, void* ws, size_t ws_bytes, void* stream);
 
+/* One autoregressive decoding step, the baseline a canvas pass is weighed
+ * against (course page "Module 12. Diffusion Language Models", break-even
+ * solution: autoregressive decoding emits one token per pass over the
+ * weights).  Appends one token per request (device tokens [B] int32) at
+ * position len[b] as dg_kv_prefill with T = 1 does, runs every layer in full
+ * on that row (query len[b] sees keys 0 .. len[b]) and the LM head, and writes
+ * the next token (lowest index of the maximum logit) and its softmax
+ * probability to device argmax [B] int32 and conf [B] f32.  Advances
+ * kv->len[b] by 1 on success.  Taps as for a prefill; inject_uf, uf and
+ * logits apply to the head.  Errors: those of dg_kv_prefill, INVALID for a
+ * null argmax or conf. */
+dg_status dg_decode_step(const dg_model* m, dg_kv* kv, const int32_t* tokens, int32_t B,
+                         int32_t* argmax, float* conf, const dg_taps* taps, void* ws, size_t ws_bytes,
+                         void* stream);
+
 /* One denoising pass ("Denoising mode") over device canvases [B][N] int32.
  * Request b's canvas queries see its whole cached prefix kv->len[b] and its
  * whole canvas (bidirectional).  The cache is only read.  Outputs device
@@ -224,15 +239,46 @@ dg_status dg_renoise(int32_t* canvas, const int32_t* argmax, const float* conf, 
                      uint64_t seed, uint32_t pass_tag, const int32_t* pos0,
                      const uint32_t* req_id, int32_t B, int32_t N, int32_t V, void* stream);
 
-/* Parameters of a re-noise, as the arguments of dg_renoise: pos0 host [B],
- * req_id host [B] or NULL for b. */
+/* Samplers of the between-pass update. */
+#define DG_SAMPLER_UNIFORM 0  /* uniform-state noise (explainer "DiffusionGemma", "Uniform
+                                 State Diffusion"): slots below tau take a fresh random token */
+#define DG_SAMPLER_MASKED 1   /* masked ("absorbing") diffusion (same page, "First attempt:
+                                 masked diffusion"): a [MASK] slot takes the prediction once its
+                                 confidence reaches tau and is then locked in */
+
+/* Parameters of the update between two passes of a canvas.  tau, seed,
+ * pass_tag, pos0 (host [B]) and req_id (host [B] or NULL for b) are the
+ * arguments of dg_renoise.  mode: DG_SAMPLER_UNIFORM (what dg_renoise does)
+ * or DG_SAMPLER_MASKED: a slot holding mask_id takes the pass's argmax when its
+ * conf >= tau, or in any case when final_pass is set (the canvas's last
+ * pass); any other slot keeps its token.  changed and masked_left: device [B]
+ * int32 or NULL, receive per request the number of slots whose token changed
+ * and (masked mode) the number still holding mask_id afterwards -- the canvas
+ * has converged when nothing changed (uniform) or nothing is masked (masked;
+ * explainer, "Uniform State Diffusion": after several passes the canvas
+ * converges). */
 typedef struct dg_renoise_args {
   float tau;
   uint64_t seed;
   uint32_t pass_tag;
   const int32_t* pos0;
   const uint32_t* req_id;
+  int32_t mode;
+  int32_t mask_id;
+  int32_t final_pass;
+  int32_t* changed;
+  int32_t* masked_left;
 } dg_renoise_args;
+
+/* The between-pass update of device canvases [B][N] in place as its own call:
+ * from this pass's device argmax [B][N] and conf [B][N] under a->mode, with
+ * the counts of a->changed / a->masked_left.  conf == NULL initialises a
+ * canvas: uniform noise (pass tag a->pass_tag, as dg_renoise with conf NULL)
+ * or mask_id in every slot.  Errors: INVALID (null canvas or a, null pos0 in
+ * uniform mode, a negative pos0[b], conf without argmax, a bad mode, B
+ * outside [1, DG_MAX_BATCH], N or V < 1), HIP. */
+dg_status dg_canvas_update(int32_t* canvas, const int32_t* argmax, const float* conf,
+                           const dg_renoise_args* a, int32_t B, int32_t N, int32_t V, void* stream);
 
 /* A denoising pass (arguments and results as dg_denoise_pass) whose last
  * kernel also does the work that follows a pass inside a canvas ("Uniform
@@ -242,12 +288,12 @@ typedef struct dg_renoise_args {
  *  - touched: device [L] int32, or NULL; receives what dg_expert_coverage
  *    would write after this pass (the counts stay in the workspace as well);
  *  - next: or NULL; the canvas (device [B][N], read by this pass) is then
- *    re-noised in place from this pass's argmax and conf, with the same
- *    tokens dg_renoise(canvas, argmax, conf, next->tau, next->seed,
- *    next->pass_tag, next->pos0, next->req_id, B, N, V) gives after the pass.
+ *    updated in place from this pass's argmax and conf, with the same tokens
+ *    and counts dg_canvas_update(canvas, argmax, conf, next, B, N, V) gives
+ *    after the pass (uniform mode: those of dg_renoise).
  * With both NULL this is dg_denoise_pass.  Errors: those of dg_denoise_pass;
- * INVALID also for a null next->pos0, a negative next->pos0[b], or a canvas
- * that aliases argmax or conf. */
+ * INVALID also for a bad next->mode, a null next->pos0 in uniform mode, a
+ * negative next->pos0[b], or a canvas that aliases argmax or conf. */
 dg_status dg_denoise_pass_next(const dg_model* m, const dg_kv* kv, int32_t* canvas, int32_t B,
                                int32_t N, int32_t* argmax, float* conf, int32_t* touched,
                                const dg_renoise_args* next, const dg_taps* taps, void* ws,
