@@ -9,7 +9,7 @@ requests with fp8 expert weights.
 from dataclasses import dataclass, field, replace
 
 ACT_DTYPES = ("f32", "bf16")
-EXPERT_DTYPES = ("f32", "bf16", "fp8")
+EXPERT_DTYPES = ("f32", "bf16", "fp8", "mxfp4")
 
 
 @dataclass(frozen=True)
@@ -32,6 +32,8 @@ class ModelConfig:
             raise ValueError(f"unsupported dtypes act={self.act} expert={self.expert}")
         if self.Hq % self.Hkv:
             raise ValueError("Hq must be a multiple of Hkv")
+        if self.expert == "mxfp4" and self.act != "bf16":
+            raise ValueError("MXFP4 expert weights go with bf16 activations")
 
     @property
     def qkv_dim(self) -> int:

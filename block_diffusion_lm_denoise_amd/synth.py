@@ -37,6 +37,35 @@ def quantize_fp8(w: torch.Tensor):
     return q, s.to(torch.float32)
 
 
+# E2M1 magnitudes and the midpoints between neighbours, with the neighbour a
+# tie rounds to (the one with an even code)
+_FP4_GRID = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+_FP4_MIDS = ((0.25, False), (0.75, True), (1.25, False), (1.75, True), (2.5, False), (3.5, True),
+             (5.0, False))   # (midpoint, a tie goes up)
+
+
+def quantize_mxfp4(w: torch.Tensor):
+    """OCP microscaling FP4 of w [..., cols] (cols a multiple of 32): per block
+    of 32 consecutive elements of a row an E8M0 scale 2^(floor(log2 amax) - 2)
+    (2 is E2M1's largest exponent) and E2M1 codes of w / scale, rounded to
+    nearest (ties to even), saturating at 6.  Returns (codes packed two per
+    byte, element 2i in the low nibble: uint8 [..., cols/2]; scales uint8
+    [..., cols/32])."""
+    shp = w.shape
+    blocks = w.reshape(*shp[:-1], shp[-1] // 32, 32).to(torch.float64)
+    amax = blocks.abs().amax(-1).clamp_min(2.0 ** -126)
+    e = torch.floor(torch.log2(amax)) - 2
+    y = (blocks / torch.pow(2.0, e)[..., None]).clamp(-6.0, 6.0)
+    a = y.abs()
+    idx = torch.zeros_like(a, dtype=torch.int64)
+    for mid, up in _FP4_MIDS:
+        idx += (a >= mid if up else a > mid).to(torch.int64)
+    codes = (idx | ((y < 0).to(torch.int64) << 3)).reshape(*shp[:-1], shp[-1])
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).to(torch.uint8)
+    scales = (e + 127).to(torch.uint8)
+    return packed.contiguous(), scales.contiguous()
+
+
 def make_weights(cfg: ModelConfig, seed: int, device="cpu", gain: str = "ones") -> dict:
     """All weights of a model.
 
@@ -70,7 +99,15 @@ def make_weights(cfg: ModelConfig, seed: int, device="cpu", gain: str = "ones") 
         mats = {"wg": (cfg.E, cfg.F, cfg.D), "wu": (cfg.E, cfg.F, cfg.D), "wd": (cfg.E, cfg.D, cfg.F)}
         scales = []
         for name, shape in mats.items():
-            if cfg.expert == "fp8":
+            if cfg.expert == "mxfp4":
+                codes, mx = [], []
+                for e in range(cfg.E):
+                    q, sc = quantize_mxfp4(normal(shape[1:], seed, f"{p}{name}.{e}", device=device))
+                    codes.append(q)
+                    mx.append(sc)
+                lw[name] = torch.stack(codes)          # [E, rows, cols/2] uint8
+                lw[name + "_mx"] = torch.stack(mx)     # [E, rows, cols/32] uint8
+            elif cfg.expert == "fp8":
                 # one expert at a time keeps the fp32 staging small
                 codes, sc = [], []
                 for e in range(cfg.E):

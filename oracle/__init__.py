@@ -14,8 +14,8 @@ import torch
 
 from .build import LIB, build
 
-OR_F32, OR_BF16, OR_FP8 = 0, 1, 2
-_DT = {"f32": OR_F32, "bf16": OR_BF16, "fp8": OR_FP8}
+OR_F32, OR_BF16, OR_FP8, OR_MXFP4 = 0, 1, 2, 3
+_DT = {"f32": OR_F32, "bf16": OR_BF16, "fp8": OR_FP8, "mxfp4": OR_MXFP4}
 _NP = {OR_F32: np.float32, OR_BF16: np.uint16}
 
 
@@ -27,7 +27,8 @@ class _Config(C.Structure):
 class _Layer(C.Structure):
     _fields_ = [("g1", C.c_void_p), ("wq", C.c_void_p), ("wk", C.c_void_p), ("wv", C.c_void_p),
                 ("wo", C.c_void_p), ("g2", C.c_void_p), ("wr", C.c_void_p), ("wg", C.c_void_p),
-                ("wu", C.c_void_p), ("wd", C.c_void_p), ("escale", C.c_void_p)]
+                ("wu", C.c_void_p), ("wd", C.c_void_p), ("escale", C.c_void_p),
+                ("wg_mx", C.c_void_p), ("wu_mx", C.c_void_p), ("wd_mx", C.c_void_p)]
 
 
 class _Weights(C.Structure):
@@ -62,6 +63,10 @@ def lib():
         L.or_round_to.restype = C.c_double
         L.or_fp8e4m3_decode.argtypes = [C.c_uint8]
         L.or_fp8e4m3_decode.restype = C.c_double
+        L.or_fp4e2m1_decode.argtypes = [C.c_uint8]
+        L.or_fp4e2m1_decode.restype = C.c_double
+        L.or_e8m0_decode.argtypes = [C.c_uint8]
+        L.or_e8m0_decode.restype = C.c_double
         L.or_bf16_bits.argtypes = [C.c_double]
         L.or_bf16_bits.restype = C.c_uint16
         _lib = L
@@ -103,7 +108,8 @@ class Model:
         layers = (_Layer * cfg.L)()
         for l, lw in enumerate(weights["layers"]):
             arrs = {}
-            for n in ("g1", "wq", "wk", "wv", "wo", "g2", "wr", "wg", "wu", "wd", "escale"):
+            for n in ("g1", "wq", "wk", "wv", "wo", "g2", "wr", "wg", "wu", "wd", "escale", "wg_mx",
+                      "wu_mx", "wd_mx"):
                 a = _np(lw.get(n))
                 arrs[n] = a
                 self._keep.append(a)
@@ -234,6 +240,14 @@ def round_to(dt: str, x: float) -> float:
 
 def fp8_decode(code: int) -> float:
     return lib().or_fp8e4m3_decode(code)
+
+
+def fp4_decode(code: int) -> float:
+    return lib().or_fp4e2m1_decode(code)
+
+
+def e8m0_decode(code: int) -> float:
+    return lib().or_e8m0_decode(code)
 
 
 def bf16_bits(x: float) -> int:

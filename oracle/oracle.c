@@ -34,6 +34,20 @@ double or_fp8e4m3_decode(uint8_t code) {
   return s ? -v : v;
 }
 
+/* OCP FP4 E2M1: 1 sign bit, 2 exponent bits with bias 1, 1 mantissa bit;
+ * exponent field 0 is subnormal with value m * 2^-1.  No infinities or NaN. */
+double or_fp4e2m1_decode(uint8_t code) {
+  int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+  double v = e == 0 ? 0.5 * m : ldexp(1.0 + m / 2.0, e - 1);
+  return s ? -v : v;
+}
+
+/* OCP E8M0 block scale: 2^(e - 127); the all-ones code is NaN. */
+double or_e8m0_decode(uint8_t code) {
+  if (code == 0xFF) return NAN;
+  return ldexp(1.0, (int)code - 127);
+}
+
 static double bf16_bits_to_double(uint16_t h) {
   uint32_t b = (uint32_t)h << 16;
   float f;
@@ -70,6 +84,16 @@ static double ld(const void* p, int dt, size_t i) {
   if (dt == OR_F32) return (double)((const float*)p)[i];
   if (dt == OR_BF16) return bf16_bits_to_double(((const uint16_t*)p)[i]);
   return or_fp8e4m3_decode(((const uint8_t*)p)[i]);
+}
+
+/* element i of a row-major expert matrix in storage type dt; MXFP4 codes
+ * take their block's scale (rows hold a multiple of 32 elements, so the block
+ * of flat element i is i / 32) */
+static double ldw(const void* p, const uint8_t* mx, int dt, size_t i) {
+  if (dt != OR_MXFP4) return ld(p, dt, i);
+  uint8_t byte = ((const uint8_t*)p)[i >> 1];
+  uint8_t code = (i & 1) ? (byte >> 4) : (byte & 15);
+  return or_fp4e2m1_decode(code) * or_e8m0_decode(mx[i >> 5]);
 }
 
 static void st(void* p, int dt, size_t i, double x) {
@@ -419,8 +443,8 @@ static void layer_forward(const ctx* X, const or_layer* lw, int li, double* x, i
         for (int f = 0; f < F; f++) {
           double a = 0.0, cc = 0.0;
           size_t base = ((size_t)e * F + f) * D;
-          for (int d = 0; d < D; d++) a += a_in[d] * ld(lw->wg, edt, base + d);
-          for (int d = 0; d < D; d++) cc += a_in[d] * ld(lw->wu, edt, base + d);
+          for (int d = 0; d < D; d++) a += a_in[d] * ldw(lw->wg, lw->wg_mx, edt, base + d);
+          for (int d = 0; d < D; d++) cc += a_in[d] * ldw(lw->wu, lw->wu_mx, edt, base + d);
           a *= sg;
           cc *= su;
           hcol[f] = or_round_to(adt, silu(a) * cc);
@@ -429,7 +453,7 @@ static void layer_forward(const ctx* X, const or_layer* lw, int li, double* x, i
         for (int d = 0; d < D; d++) {
           double acc = 0.0;
           size_t base = ((size_t)e * D + d) * F;
-          for (int f = 0; f < F; f++) acc += hcol[f] * ld(lw->wd, edt, base + f);
+          for (int f = 0; f < F; f++) acc += hcol[f] * ldw(lw->wd, lw->wd_mx, edt, base + f);
           yj[d] = or_round_to(adt, acc * sd);
         }
         if (tp && tp->hmid)
@@ -468,7 +492,9 @@ static int check_cfg(const or_config* c) {
     return 0;
   if (c->Hq % c->Hkv) return 0;
   if (c->act_dt != OR_F32 && c->act_dt != OR_BF16) return 0;
-  if (c->exp_dt != OR_F32 && c->exp_dt != OR_BF16 && c->exp_dt != OR_FP8E4M3) return 0;
+  if (c->exp_dt != OR_F32 && c->exp_dt != OR_BF16 && c->exp_dt != OR_FP8E4M3 && c->exp_dt != OR_MXFP4)
+    return 0;
+  if (c->exp_dt == OR_MXFP4 && (c->D % 32 || c->F % 32)) return 0;
   return 1;
 }
 

@@ -42,13 +42,13 @@ extern "C" {
 #endif
 
 /* storage types */
-enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8E4M3 = 2 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_FP8E4M3 = 2, OR_MXFP4 = 3 };
 
 typedef struct or_config {
   int L, D, Hq, Hkv, hd, E, k, F, V;
   double eps;       /* RMSNorm epsilon */
   int act_dt;       /* OR_F32 or OR_BF16: embeddings, attention/router/head weights, activations, KV cache */
-  int exp_dt;       /* OR_F32, OR_BF16 or OR_FP8E4M3: expert weights */
+  int exp_dt;       /* OR_F32, OR_BF16, OR_FP8E4M3 or OR_MXFP4: expert weights */
 } or_config;
 
 typedef struct or_layer {
@@ -63,6 +63,13 @@ typedef struct or_layer {
   const void* wu;       /* [E, F, D] exp_dt up */
   const void* wd;       /* [E, D, F] exp_dt down */
   const float* escale;  /* [E, 3] (gate, up, down) dequant scales, fp8 only; NULL otherwise */
+  /* MXFP4 (OCP microscaling FP4): wg, wu, wd hold 4-bit E2M1 codes, two per
+   * byte (element 2i in the low nibble), of the row-major matrices above; the
+   * scales are one E8M0 byte per 32 consecutive elements of a row, [E, rows,
+   * cols/32]; NULL otherwise */
+  const uint8_t* wg_mx;
+  const uint8_t* wu_mx;
+  const uint8_t* wd_mx;
 } or_layer;
 
 typedef struct or_weights {
@@ -132,6 +139,8 @@ void or_philox4x64_10(const uint64_t ctr[4], const uint64_t key[2], uint64_t out
 /* Conversions, exposed for the exhaustive tests. */
 double or_round_to(int dt, double x);          /* RNE to the storage type, returned as double */
 double or_fp8e4m3_decode(uint8_t code);
+double or_fp4e2m1_decode(uint8_t code);        /* low 4 bits */
+double or_e8m0_decode(uint8_t code);
 uint16_t or_bf16_bits(double x);               /* RNE bf16 bit pattern of x */
 
 #ifdef __cplusplus
