@@ -118,6 +118,8 @@ def main():
     conf = torch.empty(B, N, dtype=torch.float32, device=dev)
     touched = torch.zeros(C, S, cfg.L, dtype=torch.int32, device=dev)
     dom_stage, dom_bound, dom_kernel, dom_files = DOMINANT[cfg.expert if cfg.expert == "fp8" else "bf16"]
+    if cfg.expert == "mxfp4":
+        dom_kernel = "dg::wstream_k<bf16, mxfp4, 4, 4, 2, 2> (grouped gate/up + SwiGLU, 4-bit experts)"
     stage_id = {"gateup": dgpass.STAGE_GATEUP, "head": dgpass.STAGE_HEAD}[dom_stage]
     ev_layer = cfg.L - 1 if dom_stage == "head" else 0
 

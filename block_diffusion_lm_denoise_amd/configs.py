@@ -75,6 +75,12 @@ WORKLOADS = {
                            N=256, S=8, tau=0.5, seed=4),
 }
 
+# The 1024-prefix layer with 4-bit (MXFP4) expert weights: the same pass with
+# a quarter of the expert bytes (course page, dense-8B solution: four-bit
+# packing).
+WORKLOADS["layer_p1024_mxfp4"] = Workload("layer_p1024_mxfp4", ModelConfig(L=1, expert="mxfp4", **_LAYER),
+                                          B=1, P=1024, N=256, S=8, tau=0.5, seed=1)
+
 # The workload the benchmark times on one GPU.
 BENCH_WORKLOAD = "layer_p1024"
 

@@ -45,6 +45,29 @@ __device__ __forceinline__ float rnd(float v, const uint16_t*) { return bf2f(f2b
 // v_mfma_f32_16x16x4_f32, element j of each lane feeding the j-th.
 // The accumulator (4 floats) of lane l holds rows 4*(l/16)+i, column l%16.
 // ---------------------------------------------------------------------------
+// tag type of MXFP4 weights (4-bit E2M1 codes, two per byte, with E8M0 block
+// scales): selects the decoding code paths
+struct mxfp4_t {
+  uint8_t codes;
+};
+
+// E8M0 scale byte -> the fp32 power of two 2^(e - 127) (code 0: the fp32
+// subnormal 2^-127)
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  return __uint_as_float(e ? (e << 23) : 0x00400000u);
+}
+// eight MXFP4 codes (one 32-bit word, element 2i in the low nibble of byte i)
+// times their block scale -> eight bf16, exact (two significant bits times a
+// power of two), four hardware conversions
+__device__ __forceinline__ uint4 fp4x8_to_bf16x8(uint32_t w, float scale) {
+  uint4 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+  return r;
+}
+
 struct FragBF {
   bf16x8_t v;
 };

@@ -15,6 +15,8 @@ constexpr uint32_t MODEL_MAGIC = 0x44475041u;  // "DGPA"
 
 size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 int esize(int dt) { return dt == DG_F32 ? 4 : dt == DG_BF16 ? 2 : 1; }
+// bytes of n elements of storage type dt (MXFP4: two codes per byte)
+size_t nbytes(size_t n, int dt) { return dt == DG_MXFP4 ? n / 2 : n * esize(dt); }
 
 constexpr int MIN_TILE = 32;      // smallest expert row tile (sizes the tile list)
 constexpr int STREAM_MAX_ROWS = 1024;  // dense projections: weight streaming up to this many rows
@@ -122,6 +124,7 @@ bool valid_cfg(const dg_config* c) {
 dg_status supported_cfg(const dg_config* c) {
   if (c->D % 128 || c->F % 64) return DG_ERR_UNSUPPORTED;
   if (c->expert_dtype == DG_FP8E4M3 && c->F % 128) return DG_ERR_UNSUPPORTED;   // packed fp8 rows
+  if (c->expert_dtype == DG_MXFP4 && (c->F % 256 || c->D % 256)) return DG_ERR_UNSUPPORTED;
   if (c->hd != 64 && c->hd != 128) return DG_ERR_UNSUPPORTED;
   if (c->Hq % c->Hkv) return DG_ERR_UNSUPPORTED;
   const int G = c->Hq / c->Hkv;
@@ -131,7 +134,8 @@ dg_status supported_cfg(const dg_config* c) {
   if (c->act_dtype == DG_F32) {
     if (c->expert_dtype != DG_F32) return DG_ERR_UNSUPPORTED;
   } else if (c->act_dtype == DG_BF16) {
-    if (c->expert_dtype != DG_BF16 && c->expert_dtype != DG_FP8E4M3) return DG_ERR_UNSUPPORTED;
+    if (c->expert_dtype != DG_BF16 && c->expert_dtype != DG_FP8E4M3 && c->expert_dtype != DG_MXFP4)
+      return DG_ERR_UNSUPPORTED;
   } else {
     return DG_ERR_UNSUPPORTED;
   }
@@ -183,7 +187,8 @@ void inject_layer_input(const Ctx& c, int l) {
 // waves splitting the contraction: 4, or 2 when 4 would leave each wave an odd
 // number of pieces (128 bytes of each weight row; the pipeline works on pairs)
 int stream_kw(int K, int wdt) {
-  const int nch = K * esize(wdt) / 128, per4 = (nch + 3) / 4;
+  // pieces of the contraction (MXFP4: half pieces of 128 elements)
+  const int nch = wdt == DG_MXFP4 ? K / 128 : (int)(nbytes(K, wdt) / 128), per4 = (nch + 3) / 4;
   return (per4 % 2 == 1 && nch % 2 == 0) ? 2 : 4;
 }
 
@@ -278,7 +283,9 @@ void moe_block(const Ctx& c, int l, const float* gnext) {
 
   // permutation and row tiles
   const int avg = (int)(R * k / E);
-  const bool stream = avg <= 64;
+  // weight streaming for few rows per expert; MXFP4 experts always stream
+  // (the LDS-tiled grouped GEMMs take bf16 and fp8 weights)
+  const bool stream = avg <= 64 || cf.expert_dtype == DG_MXFP4;
   const int tile_rows = stream ? stream_tile_rows(act, cf.expert_dtype) : group_tile_rows(act);
   const int max_tiles = (int)((R * k + tile_rows - 1) / tile_rows) + (int)E;
   int32_t* counts = c.pass ? at<int32_t>(c, c.L.cov) + l * E : at<int32_t>(c, c.L.counts);
@@ -297,6 +304,8 @@ void moe_block(const Ctx& c, int l, const float* gnext) {
   g.perm = at<int32_t>(c, c.L.perm);
   g.k = cf.k;
   g.escale = w.escale;
+  g.S0 = w.wg_mx;
+  g.S1 = w.wu_mx;
   g.tiles = at<int4>(c, c.L.tiles);
   g.ntiles = at<int32_t>(c, c.L.ntiles);
   stage_event(t, l, DG_STAGE_GATEUP, 0, s);
@@ -326,6 +335,8 @@ void moe_block(const Ctx& c, int l, const float* gnext) {
     g.K = cf.F;
     g.W0 = w.wd;
     g.W1 = nullptr;
+    g.S0 = w.wd_mx;
+    g.S1 = nullptr;
     g.NW = cf.D;
     g.N = cf.D;
     const int kw = stream_kw(cf.F, cf.expert_dtype);
@@ -412,6 +423,9 @@ dg_status dg_model_init(dg_model* m, const dg_config* cfg, const dg_weights* w) 
     if (!x.g1 || !x.wq || !x.wk || !x.wv || !x.wo || !x.g2 || !x.wr || !x.wg || !x.wu || !x.wd)
       return DG_ERR_INVALID;
     if ((cfg->expert_dtype == DG_FP8E4M3) != (x.escale != nullptr)) return DG_ERR_INVALID;
+    const bool mx = cfg->expert_dtype == DG_MXFP4;
+    if (mx != (x.wg_mx != nullptr) || mx != (x.wu_mx != nullptr) || mx != (x.wd_mx != nullptr))
+      return DG_ERR_INVALID;
   }
   memset(m, 0, sizeof(*m));
   m->cfg = *cfg;
@@ -685,19 +699,35 @@ dg_status dg_canvas_update(int32_t* canvas, const int32_t* argmax, const float* 
 }
 
 size_t dg_packed_bytes(int32_t rows, int32_t cols, int32_t dtype) {
-  if (rows < 1 || cols < 1 || (dtype != DG_F32 && dtype != DG_BF16 && dtype != DG_FP8E4M3)) return 0;
-  const size_t rowbytes = (size_t)cols * esize(dtype);
+  if (rows < 1 || cols < 1 ||
+      (dtype != DG_F32 && dtype != DG_BF16 && dtype != DG_FP8E4M3 && dtype != DG_MXFP4))
+    return 0;
+  if (dtype == DG_MXFP4 && cols % 2) return 0;
+  const size_t rowbytes = nbytes((size_t)cols, dtype);
   if (rowbytes % 128) return 0;
   return (size_t)((rows + 15) / 16) * 16 * rowbytes;
+}
+
+size_t dg_packed_mx_scale_bytes(int32_t rows, int32_t cols) {
+  if (rows < 1 || cols < 1 || cols % 256) return 0;
+  return (size_t)((rows + 15) / 16) * 16 * (cols / 32);
+}
+
+dg_status dg_pack_mx_scales(const void* src, void* dst, int32_t rows, int32_t cols, void* stream) {
+  if (!src || !dst || src == dst) return DG_ERR_INVALID;
+  if (dg_packed_mx_scale_bytes(rows, cols) == 0) return DG_ERR_INVALID;
+  (void)hipGetLastError();
+  launch_pack_mx_scales(src, dst, rows, cols / 32, (hipStream_t)stream);
+  return check_hip();
 }
 
 dg_status dg_pack_weight(const void* src, void* dst, int32_t rows, int32_t cols, int32_t dtype,
                          void* stream) {
   if (!src || !dst || src == dst) return DG_ERR_INVALID;
   if (dg_packed_bytes(rows, cols, dtype) == 0) return DG_ERR_INVALID;
-  if ((size_t)cols * esize(dtype) > (size_t)INT32_MAX) return DG_ERR_UNSUPPORTED;
+  if (nbytes((size_t)cols, dtype) > (size_t)INT32_MAX) return DG_ERR_UNSUPPORTED;
   (void)hipGetLastError();
-  launch_pack(src, dst, rows, cols * esize(dtype), (hipStream_t)stream);
+  launch_pack(src, dst, rows, (int)nbytes((size_t)cols, dtype), (hipStream_t)stream);
   return check_hip();
 }
 

@@ -416,6 +416,25 @@ __global__ __launch_bounds__(256) void pack_k(const uint8_t* __restrict__ src, u
   }
 }
 
+// MXFP4 scale packing: byte q of the packed scales is tile q/128 (row group
+// rg, code column block kb of 8 scale blocks), half h = (q/64) % 2, lane l =
+// q % 64; it holds the scale of row 16 rg + l%16, block 8 kb + 4 h + l/16;
+// rows past the source get scale 1 (code 127).
+__global__ __launch_bounds__(256) void pack_mx_k(const uint8_t* __restrict__ src,
+                                                 uint8_t* __restrict__ dst, int rows, int nblk,
+                                                 size_t n) {
+  const int nkb = nblk / 8;
+  for (size_t q = (size_t)blockIdx.x * 256 + threadIdx.x; q < n; q += (size_t)gridDim.x * 256) {
+    const size_t tile = q >> 7;
+    const int h = (int)(q >> 6) & 1, l = (int)q & 63;
+    const size_t rg = tile / nkb;
+    const int kb = (int)(tile % nkb);
+    const size_t row = rg * 16 + (l & 15);
+    const int blk = 8 * kb + 4 * h + (l >> 4);
+    dst[q] = row < (size_t)rows ? src[row * nblk + blk] : (uint8_t)127;
+  }
+}
+
 // ---------------------------------------------------------------------------
 void launch_embed_norm(int act, const int32_t* tok, const void* emb, const float* g, int rows, int D,
                        int V, float eps, void* x, void* u, hipStream_t s, int32_t* zero0, int nzero0,
@@ -479,6 +498,13 @@ void launch_lm_merge(const float* pmax, const int32_t* pidx, const float* psum, 
                      int ntiles, int32_t* argmax, float* conf, const MergeNext& nx, hipStream_t s) {
   lm_merge_k<<<rows + (nx.touched ? nx.L : 0), 256, 0, s>>>(pmax, pidx, psum, ntiles, rows, argmax,
                                                             conf, nx);
+}
+
+void launch_pack_mx_scales(const void* src, void* dst, int rows, int nblk, hipStream_t s) {
+  const size_t n = (size_t)((rows + 15) / 16) * 16 * nblk;
+  const size_t blocks = (n + 255) / 256;
+  pack_mx_k<<<(unsigned)(blocks < 65536 ? blocks : 65536), 256, 0, s>>>((const uint8_t*)src,
+                                                                      (uint8_t*)dst, rows, nblk, n);
 }
 
 void launch_pack(const void* src, void* dst, int rows, int rowbytes, hipStream_t s) {

@@ -18,6 +18,8 @@
 // tiles is served from that XCD's L2 after the first read.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -36,6 +38,13 @@ template <> struct Piece<uint16_t, uint16_t> {
 template <> struct Piece<uint16_t, uint8_t> {
   static constexpr int EP = 128, NA = 4;
   static __device__ __forceinline__ int a_off(int j, int g) { return 64 * (j >> 1) + 16 * g + 8 * (j & 1); }
+};
+template <> struct Piece<uint16_t, mxfp4_t> {
+  // MXFP4 works on half pieces: one 1 KB wave load of 64 code bytes per row =
+  // 128 elements; lane g's 16 bytes are the 32 elements 32 g .. +31 (one MX
+  // block), four MFMA groups of 8
+  static constexpr int EP = 128, NA = 4;
+  static __device__ __forceinline__ int a_off(int j, int g) { return 32 * g + 8 * j; }
 };
 template <> struct Piece<float, float> {
   static constexpr int EP = 32, NA = 2;
@@ -87,6 +96,28 @@ __device__ __forceinline__ void piece_mma(f32x4_t (&acc)[RT][4], const u32x4 (&w
         }
     }
 }
+// MXFP4: each 16-byte weight load is one MX block of 32 codes with its scale
+// byte sr[ct][h]; its four 8-code words decode (scaled, exactly) into the
+// bf16 operands of four MFMA groups
+template <int RT>
+__device__ __forceinline__ void piece_mma_mx(f32x4_t (&acc)[RT][4], const u32x4 (&wr)[4][2],
+                                             const u32x4 (&ar)[RT][4], const uint32_t (&sr)[4][2],
+                                             int nrt) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ks++)
+#pragma unroll
+    for (int ct = 0; ct < 4; ct++) {
+      FragBF y;
+      y.v = __builtin_bit_cast(bf16x8_t, fp4x8_to_bf16x8(wr[ct][0][ks], e8m0_to_f32(sr[ct][0])));
+#pragma unroll
+      for (int rt = 0; rt < RT; rt++)
+        if (rt < 2 || rt < nrt) {
+          FragBF x;
+          x.v = __builtin_bit_cast(bf16x8_t, ar[rt][ks]);
+          mma(acc[rt][ct], x, y);
+        }
+    }
+}
 template <int RT>
 __device__ __forceinline__ void piece_mma(f32x4_t (&acc)[RT][4], const u32x4 (&wr)[4][2],
                                           const u32x4 (&ar)[RT][2], int nrt, float*, float*) {
@@ -126,6 +157,7 @@ template <typename TA, typename TW, int MODE, int KW, int NB, int RT>
 __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
   typedef Piece<TA, TW> PC;
   constexpr int NA = PC::NA;
+  constexpr bool MX = std::is_same<TW, mxfp4_t>::value;
   constexpr int CWG = 4 / KW;          // column groups per block
   __shared__ float red[4][4][64][4];   // [wave][col tile][lane][i], one 16-row tile at a time
   constexpr bool GROUPED = MODE == SG_GATEUP || MODE == SG_DOWN;
@@ -153,7 +185,9 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l16 = lane & 15, g = lane >> 4;
   const int kw = w % KW, cg = w / KW;  // contraction share, column group of this wave
   const int K = a.K;
-  const int nch_all = K / PC::EP;      // pieces (packed column blocks) per weight row
+  const int nch_all = K / PC::EP;      // pieces (packed column blocks; MXFP4: halves) per weight row
+  // bytes from one 16-row group of the packed weights to the next
+  const size_t rg_bytes = (size_t)(MX ? K / 256 : nch_all) * 2048;
   // contraction split: this block takes pieces [pbeg, pbeg + nch)
   const int nsp = MODE == SG_F32 && a.ksplit > 1 ? a.ksplit : 1;
   const int nch = nch_all / nsp, pbeg = split * nch;
@@ -161,18 +195,22 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
   // packed weight tiles of this wave's 4 column tiles: byte address of row
   // group rg, piece c, load h, this lane = base + (rg * nch_all + c) * 2048 + h * 1024 + 16 * lane
   const char* wtile[4];
+  const uint8_t* stile[4];   // MXFP4: this lane's scale byte of the tile, piece 0, load 0
   const int n0 = (chunk * CWG + cg) * 64;   // first weight row (dense/down) of this wave
 #pragma unroll
   for (int ct = 0; ct < 4; ct++) {
     const char* base;
+    const uint8_t* sbase = nullptr;
     size_t row;   // first row of the 16-row group in its matrix
     if (MODE == SG_GATEUP) {
       // 32 SwiGLU outputs per column group: tiles [gate f, up f, gate f+16, up f+16]
       row = (size_t)e * a.NW + (chunk * CWG + cg) * 32 + 16 * (ct >> 1);
       base = (const char*)((ct & 1) ? a.W1 : a.W0);
+      sbase = (ct & 1) ? a.S1 : a.S0;
     } else if (MODE == SG_DOWN) {
       row = (size_t)e * a.NW + n0 + 16 * ct;
       base = (const char*)a.W0;
+      sbase = a.S0;
     } else {
       // groups past N read group 0: their output columns are never stored
       const int n = n0 + 16 * ct;
@@ -181,7 +219,8 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
       else if (nn < a.n1 + a.n2) { base = (const char*)a.W1; row = nn - a.n1; }
       else { base = (const char*)a.W2; row = nn - a.n1 - a.n2; }
     }
-    wtile[ct] = base + (row / 16) * nch_all * 2048 + 16 * lane;
+    wtile[ct] = base + (row / 16) * rg_bytes + 16 * lane;
+    stile[ct] = MX ? sbase + (row / 16) * (rg_bytes / 16) + lane : nullptr;
   }
 
   // residual values of this thread's outputs (stored by thread (w, lane) in
@@ -211,13 +250,24 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
   // NB register buffers of one piece each: the loads of NB-1 later pieces are
   // in flight while a piece is multiplied
   u32x4 wbuf[NB][4][2], abuf[NB][RT][NA];
+  uint32_t sbuf[NB][4][2];   // MXFP4 scale bytes of each buffer's weight loads
   auto load_w = [&](u32x4(&wr)[4][2], int c) {
 #pragma unroll
-    for (int h = 0; h < 2; h++)
+    for (int h = 0; h < (MX ? 1 : 2); h++)
 #pragma unroll
-      for (int ct = 0; ct < 4; ct++)
-        wr[ct][h] = (GROUPED ? STREAM_NT : STREAM_NT_DENSE) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wtile[ct] + (size_t)c * 2048 + h * 1024))
-                              : *reinterpret_cast<const u32x4*>(wtile[ct] + (size_t)c * 2048 + h * 1024);
+      for (int ct = 0; ct < 4; ct++) {
+        // MXFP4 half piece c: load c % 2 of 128-byte piece c / 2
+        const size_t off = MX ? (size_t)(c >> 1) * 2048 + (c & 1) * 1024 : (size_t)c * 2048 + h * 1024;
+        wr[ct][h] = (GROUPED ? STREAM_NT : STREAM_NT_DENSE)
+                        ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wtile[ct] + off))
+                        : *reinterpret_cast<const u32x4*>(wtile[ct] + off);
+      }
+  };
+  auto load_s = [&](uint32_t(&sr)[4][2], int c) {
+    if constexpr (MX) {
+#pragma unroll
+      for (int ct = 0; ct < 4; ct++) sr[ct][0] = stile[ct][(size_t)(c >> 1) * 128 + (c & 1) * 64];
+    }
   };
   const TA* arow[RT];
   auto load_a = [&](u32x4(&ar)[RT][NA], int c) {
@@ -227,21 +277,23 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
       for (int rt = 0; rt < RT; rt++)
         ar[rt][j] = *reinterpret_cast<const u32x4*>(arow[rt] + c * PC::EP + PC::a_off(j, g));
   };
-  auto load = [&](u32x4(&wr)[4][2], u32x4(&ar)[RT][NA], int c) {
-    load_w(wr, c);
-    load_a(ar, c);
+  auto load = [&](int b, int c) {
+    load_w(wbuf[b], c);
+    load_s(sbuf[b], c);
+    load_a(abuf[b], c);
   };
-  auto comp = [&](u32x4(&wr)[4][2], u32x4(&ar)[RT][NA]) {
-    piece_mma<RT>(acc, wr, ar, nrt, (TA*)nullptr, (TW*)nullptr);
+  auto comp = [&](int b) {
+    if constexpr (MX) piece_mma_mx<RT>(acc, wbuf[b], abuf[b], sbuf[b], nrt);
+    else piece_mma<RT>(acc, wbuf[b], abuf[b], nrt, (TA*)nullptr, (TW*)nullptr);
   };
   // ok = false: the piece is past the contraction (a clamped load of the last
   // piece), so its A is zeroed
-  auto comp_masked = [&](u32x4(&wr)[4][2], u32x4(&ar)[RT][NA], bool ok) {
+  auto comp_masked = [&](int b, bool ok) {
 #pragma unroll
     for (int rt = 0; rt < RT; rt++)
 #pragma unroll
-      for (int j = 0; j < NA; j++) zero_unless(ar[rt][j], ok);
-    piece_mma<RT>(acc, wr, ar, nrt, (TA*)nullptr, (TW*)nullptr);
+      for (int j = 0; j < NA; j++) zero_unless(abuf[b][rt][j], ok);
+    comp(b);
   };
 
   // wave takes pieces kw, kw+KW, ...; indices past the end are clamped and
@@ -272,27 +324,28 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
   }
   __builtin_amdgcn_sched_barrier(0);
   load_w(wbuf[0], cidx(0));
+  load_s(sbuf[0], cidx(0));
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int rt = 0; rt < RT; rt++)
     arow[rt] = (const TA*)a.A + (size_t)(MODE == SG_GATEUP ? src[rt] / a.k : src[rt]) * K;
   load_a(abuf[0], cidx(0));
 #pragma unroll
-  for (int b = 1; b < NB; b++) load(wbuf[b], abuf[b], cidx(b));
+  for (int b = 1; b < NB; b++) load(b, cidx(b));
   int ib = 0;
   for (; ib + NB < nper; ib += NB) {
 #pragma unroll
     for (int b = 0; b < NB; b++) {
       __builtin_amdgcn_sched_barrier(0);
-      comp(wbuf[b], abuf[b]);
+      comp(b);
       __builtin_amdgcn_sched_barrier(0);
-      load(wbuf[b], abuf[b], cidx(ib + NB + b));
+      load(b, cidx(ib + NB + b));
     }
   }
 #pragma unroll
   for (int b = 0; b < NB; b++) {   // last group: nothing left to load
     __builtin_amdgcn_sched_barrier(0);
-    comp_masked(wbuf[b], abuf[b], cok(ib + b));
+    comp_masked(b, cok(ib + b));
   }
 
   // ---- reduce the four waves' partial tiles, one 16-row tile at a time ----
@@ -403,6 +456,11 @@ static void dispatch(int act, int wdt, const StreamGemm& a, int ntiles_max, hipS
   } else if (wdt == DG_FP8E4M3) {
     const int nb = a.nchunks * (GROUPED ? ntiles_max : (a.M + 31) / 32) * nsp;
     if (nb > 0) wstream_k<uint16_t, uint8_t, MODE, KW, STREAM_NB_FP8, 2><<<nb, 256, 0, s>>>(a);
+  } else if (wdt == DG_MXFP4) {
+    if constexpr (GROUPED) {
+      const int nb = a.nchunks * ntiles_max;
+      if (nb > 0) wstream_k<uint16_t, mxfp4_t, MODE, KW, 2, 2><<<nb, 256, 0, s>>>(a);
+    }
   } else if constexpr (GROUPED) {
     const int nb = a.nchunks * ntiles_max;
     if (nb > 0)

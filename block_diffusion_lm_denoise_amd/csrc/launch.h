@@ -126,6 +126,8 @@ void launch_down_lds(int act, const void* H, const MoeW& w, const int4* tiles,
 // row-major [rows][rowbytes] -> packed weight layout (rowbytes % 128 == 0,
 // rows padded to a multiple of 16 with zeros)
 void launch_pack(const void* src, void* dst, int rows, int rowbytes, hipStream_t s);
+// MXFP4 scales [rows][nblk] (nblk a multiple of 8) -> the packed scale layout
+void launch_pack_mx_scales(const void* src, void* dst, int rows, int nblk, hipStream_t s);
 
 // returns the number of per-row partials written (one per vocabulary tile)
 int launch_lmhead(int act, const void* uf, int M, int D, const void* lm, int V, float* pmax,
@@ -145,6 +147,8 @@ struct StreamGemm {
   int n1, n2, N;          // dense / head output columns
   int NW;                 // grouped: rows per expert of W0
   const float* escale;    // grouped fp8: [E][3]
+  const uint8_t* S0;      // grouped MXFP4: packed scales of W0 (gate / down)
+  const uint8_t* S1;      //   and of W1 (up)
   const int4* tiles;      // grouped: (expert, first row, rows)
   const int32_t* ntiles;
   int nchunks;            // 64-weight-row chunks per row tile (gate/up: F/32)

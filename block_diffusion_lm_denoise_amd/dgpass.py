@@ -17,8 +17,8 @@ LIB_PATH = os.path.join(HERE, "libdgpass.so")
 MAX_LAYERS = 64
 MAX_BATCH = 64
 
-DG_F32, DG_BF16, DG_FP8E4M3 = 0, 1, 2
-_DT = {"f32": DG_F32, "bf16": DG_BF16, "fp8": DG_FP8E4M3}
+DG_F32, DG_BF16, DG_FP8E4M3, DG_MXFP4 = 0, 1, 2, 3
+_DT = {"f32": DG_F32, "bf16": DG_BF16, "fp8": DG_FP8E4M3, "mxfp4": DG_MXFP4}
 TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float8_e4m3fn}
 
 TAP_FIELDS = ("qkv", "attn", "x1", "u2", "router", "ids", "gates", "counts", "offsets", "perm",
@@ -40,7 +40,7 @@ class dg_config(C.Structure):
 
 class dg_layer_weights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in ("g1", "wq", "wk", "wv", "wo", "g2", "wr", "wg", "wu",
-                                          "wd", "escale")]
+                                          "wd", "escale", "wg_mx", "wu_mx", "wd_mx")]
 
 
 class dg_weights(C.Structure):
@@ -82,7 +82,8 @@ _SAMPLER = {"uniform": SAMPLER_UNIFORM, "masked": SAMPLER_MASKED}
 EXPORTS = ("dg_model_init", "dg_workspace_bytes", "dg_kv_prefill", "dg_denoise_pass",
            "dg_denoise_pass_next", "dg_renoise", "dg_expert_coverage", "dg_packed_bytes",
            "dg_pack_weight", "dg_status_str", "dg_check_attention_addresses",
-           "dg_denoise_pass_next_noalloc", "dg_decode_step", "dg_canvas_update")
+           "dg_denoise_pass_next_noalloc", "dg_decode_step", "dg_canvas_update",
+           "dg_packed_mx_scale_bytes", "dg_pack_mx_scales")
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
@@ -121,6 +122,10 @@ def lib():
         L.dg_packed_bytes.restype = sz
         L.dg_pack_weight.argtypes = [vp, vp, i32, i32, i32, vp]
         L.dg_pack_weight.restype = i32
+        L.dg_packed_mx_scale_bytes.argtypes = [i32, i32]
+        L.dg_packed_mx_scale_bytes.restype = sz
+        L.dg_pack_mx_scales.argtypes = [vp, vp, i32, i32, vp]
+        L.dg_pack_mx_scales.restype = i32
         L.dg_status_str.argtypes = [i32]
         L.dg_status_str.restype = C.c_char_p
         L.dg_check_attention_addresses.argtypes = [i32, i32, i32, vp, i32, i32, i32, C.c_long,
@@ -271,6 +276,18 @@ def pack_weight(src: torch.Tensor, rows: int, cols: int, dtype: str, stream=None
     return dst
 
 
+def pack_mx_scales(src: torch.Tensor, rows: int, cols: int, stream=None) -> torch.Tensor:
+    """Packed copy (a new uint8 device tensor) of the E8M0 scales src
+    [rows][cols/32] of an MXFP4 matrix [rows][cols]."""
+    n = lib().dg_packed_mx_scale_bytes(int(rows), int(cols))
+    if n == 0:
+        raise DgError(-1, "dg_packed_mx_scale_bytes")
+    dst = torch.empty(n, dtype=torch.uint8, device=src.device)
+    _check(lib().dg_pack_mx_scales(src.data_ptr(), dst.data_ptr(), int(rows), int(cols), _stream(stream)),
+           "dg_pack_mx_scales")
+    return dst
+
+
 # streamed weight matrices: name -> (rows, cols, dtype field of the config)
 def _packed_shapes(cfg: ModelConfig):
     QD, KD = cfg.Hq * cfg.hd, cfg.Hkv * cfg.hd
@@ -299,12 +316,17 @@ class Model:
         for l, lw in enumerate(weights["layers"]):
             L = w.layers[l]
             pk = {n: pack_weight(lw[n], *shapes[n]) for n in shapes}
+            if cfg.expert == "mxfp4":
+                for n in ("wg", "wu", "wd"):
+                    pk[n + "_mx"] = pack_mx_scales(lw[n + "_mx"], shapes[n][0], shapes[n][1])
             self.packed["layers"].append(pk)
             for n in ("g1", "g2"):
                 setattr(L, n, lw[n].data_ptr())
             for n in shapes:
                 setattr(L, n, pk[n].data_ptr())
             L.escale = _ptr(lw.get("escale"))
+            for n in ("wg_mx", "wu_mx", "wd_mx"):
+                setattr(L, n, _ptr(pk.get(n)))
         self._c = make_config(cfg)
         self._m = dg_model()
         _check(lib().dg_model_init(C.byref(self._m), C.byref(self._c), C.byref(w)), "dg_model_init")

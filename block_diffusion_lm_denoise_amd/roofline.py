@@ -17,7 +17,8 @@ from dataclasses import dataclass
 HBM_BYTES_PER_S = 8.0e12
 MFMA_PEAK = {"bf16": 2.5e15, "fp16": 2.5e15, "fp8": 5.0e15, "f32": 157.3e12, "f64": 78.6e12}
 
-_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
+# bytes per element; MXFP4 adds one E8M0 scale byte per 32 elements
+_BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "mxfp4": 0.5 + 1 / 32}
 
 
 def roof_time(bytes_moved: float, flops: float, bw: float, peak: float) -> float:

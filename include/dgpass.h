@@ -66,14 +66,18 @@ typedef int32_t dg_status;
 #define DG_F32 0
 #define DG_BF16 1
 #define DG_FP8E4M3 2   /* OCP e4m3 (max 448, no infinities), expert weights only */
+#define DG_MXFP4 3     /* OCP microscaling FP4, expert weights only: 4-bit E2M1 codes, two
+                          per byte (element 2i in the low nibble), and one E8M0 scale byte
+                          (2^(s-127)) per 32 consecutive elements of a row */
 
 #define DG_MAX_LAYERS 64
 #define DG_MAX_BATCH 64
 
 /* Model shape.  Supported: act_dtype F32 with expert_dtype F32, or act_dtype
- * BF16 with expert_dtype BF16 or FP8E4M3; hd in {64, 128}; Hq/Hkv in
+ * BF16 with expert_dtype BF16, FP8E4M3 or MXFP4; hd in {64, 128}; Hq/Hkv in
  * {1, 2, 4, 8, 16}; D a multiple of 128; F and Hq*hd multiples of 64 (F of
- * 128 with FP8E4M3 experts); 1 <= k <= 8; k <= E <= 256. */
+ * 128 with FP8E4M3 experts; D and F of 256 with MXFP4 experts); 1 <= k <= 8;
+ * k <= E <= 256. */
 typedef struct dg_config {
   int32_t L, D, Hq, Hkv, hd, E, k, F, V;
   float eps;               /* RMSNorm epsilon */
@@ -91,7 +95,12 @@ typedef struct dg_config {
  * zero.  One 64-lane load of 16 bytes per lane then reads 1 KB of contiguous
  * memory and leaves every lane with its matrix-core operand fragment.  An
  * expert tensor [E][F][D] is packed as one [E*F][D] matrix (F is a multiple
- * of 16, so no tile straddles two experts). */
+ * of 16, so no tile straddles two experts).  MXFP4 codes are packed the same
+ * way (rb = cols / 2).  Their E8M0 scales ([rows][cols/32] bytes) are packed
+ * to match: the 128 bytes at offset (rg * cols/256 + kb) * 128 belong to code
+ * tile (rg, kb), and byte 64 h + l holds the scale of row 16 rg + l % 16,
+ * block 8 kb + 4 h + l / 16 -- the block of the 32 codes that lane l of load
+ * h of that tile reads. */
 
 /* Device pointers of one layer. */
 typedef struct dg_layer_weights {
@@ -107,6 +116,9 @@ typedef struct dg_layer_weights {
   const void* wd;      /* [E][D][F] expert dtype, packed as [E*D][F] */
   const float* escale; /* [E][3] f32 (gate, up, down) multipliers of the
                           accumulated fp8 products; NULL unless FP8E4M3 */
+  const uint8_t* wg_mx; /* MXFP4: E8M0 scales of wg, wu, wd, packed (above); */
+  const uint8_t* wu_mx; /* NULL unless MXFP4 */
+  const uint8_t* wd_mx;
 } dg_layer_weights;
 
 typedef struct dg_weights {
@@ -339,6 +351,16 @@ size_t dg_packed_bytes(int32_t rows, int32_t cols, int32_t dtype);
  * rejects), UNSUPPORTED, HIP. */
 dg_status dg_pack_weight(const void* src, void* dst, int32_t rows, int32_t cols, int32_t dtype,
                          void* stream);
+
+/* Bytes of the packed MXFP4 scales of a [rows][cols] matrix (cols a multiple
+ * of 256): ceil(rows/16)*16 * cols/32; 0 otherwise.  Host arithmetic only. */
+size_t dg_packed_mx_scale_bytes(int32_t rows, int32_t cols);
+
+/* Write the packed layout of the row-major device E8M0 scales src
+ * [rows][cols/32] of an MXFP4 matrix [rows][cols] to device dst
+ * (dg_packed_mx_scale_bytes bytes, not overlapping src); rows past the matrix
+ * get scale 1 (code 127).  Errors: INVALID, HIP. */
+dg_status dg_pack_mx_scales(const void* src, void* dst, int32_t rows, int32_t cols, void* stream);
 
 const char* dg_status_str(dg_status s);
 

@@ -107,6 +107,24 @@ def test_ragged_prefixes_with_key_splits_full_width():
     _run(pair, 2, [2048, 0], wl.N, 31, synthetic=True, scale_note="ragged [2048, 0]")
 
 
+@pytest.mark.parametrize("E,k,N", [(16, 4, 33), (4, 2, 100)])
+def test_mxfp4_experts(E, k, N):
+    """4-bit (MXFP4) expert weights decoded in registers by the streamed
+    grouped GEMMs (few rows per expert, and ~100 rows per expert over several
+    32-row tiles); ragged requests, two layers."""
+    cfg = _cfg(L=2, E=E, k=k, D=256, F=256, expert="mxfp4", V=384)
+    pair = Pair(cfg, 18, scale_lm=10.0)
+    _run(pair, 2, [30, 5], N, 18, scale_note=f"mxfp4 E{E} k{k}")
+
+
+def test_mxfp4_layer_prefix1024_full_size():
+    """The 1024-prefix layer with MXFP4 experts at its full size (synthetic
+    cache given to both sides)."""
+    wl = WORKLOADS["layer_p1024_mxfp4"]
+    pair = Pair(wl.model, wl.seed, gain="ones")
+    _run(pair, 1, [wl.P], wl.N, wl.seed, synthetic=True, scale_note="layer_p1024_mxfp4")
+
+
 def test_injected_router_ties_are_bit_exact():
     cfg = _cfg(E=8, k=3)
     pair = Pair(cfg, 16)
