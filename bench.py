@@ -83,6 +83,8 @@ def main():
                     help="stop a canvas once it has converged (reads two counts per pass to the host)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 4 GiB device copy (counter calibration)")
+    ap.add_argument("--no-ar-baseline", action="store_true",
+                    help="skip the autoregressive-step comparison (keeps kernel traces to the pass)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the pass runs on a single MI355X (no multi-GPU path is "
@@ -266,27 +268,29 @@ def main():
               "steady_state_pass_us": pass_us,
               "output_tokens_per_s": B * N * C / (request_ms / 1e3)}
 
-    # autoregressive baseline (course page, break-even solution): decoding
-    # steps over the same prefix, one new token per request per step
-    ar_tok = torch.zeros(B, dtype=torch.int32, device=dev)
-    ar_am = torch.empty(B, dtype=torch.int32, device=dev)
-    ar_cf = torch.empty(B, dtype=torch.float32, device=dev)
-    kv.lens[:] = pass_lens
-    nar = 16 if cap - int(kv.lens.max()) >= 20 else max(1, cap - int(kv.lens.max()) - 4)
-    model.decode_step(kv, ar_tok, ar_am, ar_cf, ws)
-    kv.lens[:] = pass_lens
-    torch.cuda.synchronize()
-    a0, a1 = ev_pair()
-    a0.record()
-    for _ in range(nar):
-        model.decode_step(kv, ar_am, ar_am, ar_cf, ws)   # greedy: each step feeds its own output
-    a1.record()
-    torch.cuda.synchronize()
-    ar_us = a0.elapsed_time(a1) / nar * 1e3
-    kv.lens[:] = pass_lens
-    ar_work = roofline.decode_step_work(cfg, B, list(pass_lens), [min(cfg.E, B * cfg.k)] * cfg.L)
-    ar_roof = roofline.roof_time(ar_work.total_bytes, ar_work.total_flops, roofline.HBM_BYTES_PER_S,
-                                 roofline.MFMA_PEAK["bf16"])
+    ar_us = ar_roof = nar = None
+    if not args.no_ar_baseline:
+        # autoregressive baseline (course page, break-even solution): decoding
+        # steps over the same prefix, one new token per request per step
+        ar_tok = torch.zeros(B, dtype=torch.int32, device=dev)
+        ar_am = torch.empty(B, dtype=torch.int32, device=dev)
+        ar_cf = torch.empty(B, dtype=torch.float32, device=dev)
+        kv.lens[:] = pass_lens
+        nar = 16 if cap - int(kv.lens.max()) >= 20 else max(1, cap - int(kv.lens.max()) - 4)
+        model.decode_step(kv, ar_tok, ar_am, ar_cf, ws)
+        kv.lens[:] = pass_lens
+        torch.cuda.synchronize()
+        a0, a1 = ev_pair()
+        a0.record()
+        for _ in range(nar):
+            model.decode_step(kv, ar_am, ar_am, ar_cf, ws)   # greedy: each step feeds its own output
+        a1.record()
+        torch.cuda.synchronize()
+        ar_us = a0.elapsed_time(a1) / nar * 1e3
+        kv.lens[:] = pass_lens
+        ar_work = roofline.decode_step_work(cfg, B, list(pass_lens), [min(cfg.E, B * cfg.k)] * cfg.L)
+        ar_roof = roofline.roof_time(ar_work.total_bytes, ar_work.total_flops, roofline.HBM_BYTES_PER_S,
+                                     roofline.MFMA_PEAK["bf16"])
 
     passes_per_step = S * C
     if args.early_exit:   # the passes the timed steps actually ran
@@ -337,12 +341,13 @@ def main():
         "experts_touched_per_pass": mean_touched,
         "experts_touched_per_layer": [float(x) for x in cov_layer],
     }
-    out["ar_baseline"] = {
-        "step_us": ar_us, "tok_s": B / (ar_us / 1e6), "roof_us": ar_roof * 1e6,
-        "frac": ar_roof * 1e6 / ar_us, "steps_timed": nar,
-        "breakeven_passes": N * ar_us / pass_us,
-        "breakeven_passes_at_roofline": N * ar_roof / t_roof,
-        "note": "a canvas of N tokens in S passes beats N decoding steps iff S < N * step / pass"}
+    if ar_us is not None:
+        out["ar_baseline"] = {
+            "step_us": ar_us, "tok_s": B / (ar_us / 1e6), "roof_us": ar_roof * 1e6,
+            "frac": ar_roof * 1e6 / ar_us, "steps_timed": nar,
+            "breakeven_passes": N * ar_us / pass_us,
+            "breakeven_passes_at_roofline": N * ar_roof / t_roof,
+            "note": "a canvas of N tokens in S passes beats N decoding steps iff S < N * step / pass"}
     if c3 is not None:
         out["request"] = c3
 
