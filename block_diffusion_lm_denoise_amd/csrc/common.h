@@ -193,6 +193,10 @@ __device__ __forceinline__ int lane_xor32(int x) { return (int)lane_xor32((uint3
 // result in both: the swap of two copies of x leaves rows (0, 0, 2, 2) in one
 // and rows (1, 1, 3, 3) in the other (for 32: (0, 1, 0, 1) and (2, 3, 2, 3)),
 // so an operation on the pair needs no lane select.
+// (max_nn and max3_nn are inline assembly: the compiler does not see which
+// registers they read, so it inserts no wait states for a matrix-core result
+// read too early -- never pass them an MFMA accumulator; fmax3 below is the
+// compiler-visible form for those)
 __device__ __forceinline__ float max_nn(float a, float b) {   // non-NaN operands, no quieting
   float r;
   asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
@@ -246,6 +250,12 @@ __device__ __forceinline__ float max3_nn(float a, float b, float c) {
   float r;
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
+}
+// maximum of three floats, compiler-visible (one v_max3 for operands the
+// compiler knows are canonical, e.g. matrix-core results), so the hazard
+// recognizer orders it after the MFMAs that produce its operands
+__device__ __forceinline__ float fmax3(float a, float b, float c) {
+  return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
 }
 __device__ __forceinline__ float row16_max(float v) {
   v = fmax_sel(v, dpp_f<DPP_QUAD_1032>(v));

@@ -243,12 +243,12 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
     // row's, and those rows are never stored.
     float tmax = -INFINITY;
     if (full) {
-      float x = max3_nn(s[0][0], s[0][1], s[0][2]);
+      float x = fmax3(s[0][0], s[0][1], s[0][2]);
 #pragma unroll
       for (int mt = 0; mt < KT / 16; mt++)
 #pragma unroll
         for (int i = (mt == 0 ? 3 : 0); i < 4; i += 2)
-          x = i + 1 < 4 ? max3_nn(x, s[mt][i], s[mt][i + 1]) : max_nn(x, s[mt][i]);
+          x = i + 1 < 4 ? fmax3(x, s[mt][i], s[mt][i + 1]) : __builtin_fmaxf(x, s[mt][i]);
       tmax = x * a.scale_log2;
     } else {
 #pragma unroll
@@ -409,14 +409,12 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // bf16 attention (gfx950).  Block = NW waves x 32 rows = 32 NW (query, head)
 // rows of one (request, kv head, key split): G query heads sharing the kv head
-// x 32 NW / G consecutive queries.  K and V tiles of 64 keys go from memory straight
-// into LDS (global_load_lds, 16 bytes per lane: a wave load fills 1 KB of LDS
-// with 4 (hd 128) or 8 (hd 64) key rows); the 16-byte chunks of a key row are
-// stored XOR-swizzled by the key index, so both the K fragment reads (16 keys
-// x 64 bytes) and the transposing V reads (16 keys x 32 bytes) spread over
-// all LDS banks.  NBUF tile buffers: NBUF-1 tiles are in flight while one is
-// used, one barrier per tile; the tile loop is unrolled NBUF times so that
-// every LDS address is a lane offset plus a constant.
+// x 32 NW / G consecutive queries.  K and V tiles of 64 keys go from memory
+// straight into LDS (global_load_lds, 16 bytes per lane: a wave load fills
+// 1 KB of LDS with 4 (hd 128) or 8 (hd 64) key rows); the 16-byte chunks of a
+// key row are stored XOR-swizzled by the key index, so both the K fragment
+// reads (16 keys x 64 bytes) and the transposing V reads (16 keys x 32 bytes)
+// spread over all LDS banks.
 //   S^T = K Q^T: keys on the MFMA row axis, queries on the column axis, so a
 //   lane's softmax statistics belong to one query row (two per lane: the
 //   wave's two 16-row tiles).
@@ -425,6 +423,13 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
 //   rows x 16 dims and each lane receives one dim of the 4 keys), with the
 //   key order of a lane's S^T accumulators, so P is used in place (one bf16
 //   rounding of the probabilities).
+// Software pipeline over key tiles, one barrier per tile: step t computes the
+// scores S(t) on the matrix cores while the vector units turn S(t-1) into
+// probabilities, then accumulates P(t-1) V(t-1) (and the row sums, as a
+// product with an all-ones operand) while the vector units take the lane
+// maxima of S(t).  The K tiles run one tile ahead of the V tiles: step t
+// loads K(t+1) and V(t) (two buffers each), so a tile's loads have a whole
+// step to land.
 // Online softmax in fp32 (base-2 exponent with the scale folded in).  The
 // running maximum is moved (and O and the sum rescaled) only when a tile's
 // maximum exceeds it by more than 2^8: until then the probabilities of a
@@ -438,6 +443,13 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 __device__ __forceinline__ void lds_dma16(const void* g, void* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
+// a pointer the whole wave holds, in scalar registers
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
 // wait until at most n vector-memory loads of this wave are outstanding (gfx9
 // s_waitcnt encoding: vmcnt low bits [3:0] and high bits [15:14]; expcnt and
 // lgkmcnt left at their maxima)
@@ -449,9 +461,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 constexpr float ATTN_RESCALE_LOG2 = 8.f;   // move the running maximum past this margin
 
-template <int HD, int NBUF, int NW>
-__global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void attn_bf16_k(AttnArgs a) {
-  constexpr int KT = 64;                 // keys per tile
+template <int HD, int NW, int KT, int J>
+__global__ __launch_bounds__(NW * 64, 2) void attn_bf16_k(AttnArgs a) {
+  // J 16-row tiles per wave, NW waves: 16 J NW (query, head) rows per block;
+  // KT keys per tile
+  constexpr int MT = KT / 16;            // 16-key tiles of S
+  constexpr int NCH = KT / 32;           // 32-key chunks of P V
   constexpr int RBY = HD * 2;            // bytes of one key row
   constexpr int CPK = RBY / 16;          // 16-byte chunks per key row (16 or 8)
   constexpr int TB = KT * RBY;           // bytes of a K (or V) tile
@@ -459,35 +474,36 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void attn_bf16_k(AttnArgs
   constexpr int NIW = TB / 1024 / NW;    // wave loads per wave per K (or V) tile
   constexpr int NSS = HD / 32;           // contraction steps of S
   constexpr int NHT = HD / 16;           // 16-dim tiles of O
-  static_assert(NIW >= 1, "tile");
-  __shared__ __attribute__((aligned(1024))) char lds[NBUF][2][TB];   // [buffer][K, V]
+  static_assert(NIW >= 1 && NIW * NW * 1024 == TB, "tile");
+  // K tile buffers at 0 and TB, V tile buffers at 2 TB and 3 TB
+  __shared__ __attribute__((aligned(1024))) char lds[4 * TB];
 
   int b, gh, split, qt;
   if (!attn_block(blockIdx.x, a.nqt, a.groups, a.nsplit, a.Hkv, b, gh, split, qt)) return;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, l16 = lane & 15, g4 = lane >> 4;
   const int P = a.len.v[b];
 
-  // the wave's two 16-row tiles; this lane's query row in each
-  int qi[2], head[2];
-  bool qv[2];
+  // the wave's 16-row tiles; this lane's query row in each
+  int qi[J], head[J], qlim[J];
+  bool qv[J];
 #pragma unroll
-  for (int j = 0; j < 2; j++) {
-    const int r = 32 * w + 16 * j + l16;
+  for (int j = 0; j < J; j++) {
+    const int r = 16 * J * w + 16 * j + l16;
     qi[j] = qt * a.QT + r % a.QT;
     qv[j] = qi[j] < a.T;
     head[j] = gh * a.G + r / a.QT;
+    qlim[j] = a.mode == 0 ? 0x7fffffff : P + qi[j];   // last key the query may see
   }
   const int nkeys = a.mode == 0 ? P + a.T : P + min((qt + 1) * a.QT, a.T);
   const int kbeg = split * a.split_len;
   const int kend = min(nkeys, kbeg + a.split_len);
-  const int qlim0 = a.mode == 0 ? 0x7fffffff : P + qi[0];
-  const int qlim1 = a.mode == 0 ? 0x7fffffff : P + qi[1];
   // last key every query of the block may see (the tile's first query in prefill mode)
   const int qlim_all = a.mode == 0 ? 0x7fffffff : P + qt * a.QT;
+  const float c2 = a.scale_log2, inv_c2 = 1.f / a.scale_log2;
 
-  FragBF qf[2][NSS];
+  FragBF qf[J][NSS];
 #pragma unroll
-  for (int j = 0; j < 2; j++) {
+  for (int j = 0; j < J; j++) {
     const uint16_t* qp = (const uint16_t*)a.q + (size_t)(b * a.T + (qv[j] ? qi[j] : 0)) * a.ldq + head[j] * HD;
 #pragma unroll
     for (int ss = 0; ss < NSS; ss++) {
@@ -496,211 +512,289 @@ __global__ __launch_bounds__(NW * 64, NW >= 8 ? 1 : 2) void attn_bf16_k(AttnArgs
     }
   }
 
-  const uint16_t* const kc = (const uint16_t*)a.kc + ((size_t)b * a.Hkv + gh) * a.cap * HD;
-  const uint16_t* const vc = (const uint16_t*)a.vc + ((size_t)b * a.Hkv + gh) * a.cap * HD;
-  const uint16_t* const kn = a.mode == 0 ? (const uint16_t*)a.kn + (size_t)b * a.T * a.ldq + gh * HD : kc;
-  const uint16_t* const vn = a.mode == 0 ? (const uint16_t*)a.vn + (size_t)b * a.T * a.ldq + gh * HD : vc;
+  // key sources, uniform across the block (readfirstlane keeps them in
+  // scalar registers, so uniform tiles load with a scalar base and a 32-bit
+  // lane offset)
+  const char* const kc = uniform_ptr((const uint16_t*)a.kc + ((size_t)b * a.Hkv + gh) * a.cap * HD);
+  const char* const vc = uniform_ptr((const uint16_t*)a.vc + ((size_t)b * a.Hkv + gh) * a.cap * HD);
+  const char* const kn = a.mode == 0 ? uniform_ptr((const uint16_t*)a.kn + (size_t)b * a.T * a.ldq + gh * HD) : kc;
+  const char* const vn = a.mode == 0 ? uniform_ptr((const uint16_t*)a.vn + (size_t)b * a.T * a.ldq + gh * HD) : vc;
   const int fresh0 = a.mode == 0 ? P : 0x7fffffff;   // first key read from the qkv rows
-  const size_t ldq = (size_t)a.ldq;
+  const uint32_t ldqb = (uint32_t)a.ldq * 2;         // bytes between two qkv rows
 
   // this lane's slot of each wave load: key row lkey[u] of the tile, global
-  // chunk lq[u] (stored at slot lane % CPK = lq ^ (key % CPK))
+  // chunk lq[u] (stored at slot lane % CPK = lq ^ (key % CPK)); its byte
+  // offset from the tile's first key in the cache (coff) and in the qkv rows
+  // (foff)
   int lkey[NIW], lq[NIW];
+  uint32_t coff[NIW], foff[NIW];
 #pragma unroll
   for (int u = 0; u < NIW; u++) {
     lkey[u] = (w * NIW + u) * KPI + lane / CPK;
     lq[u] = (lane % CPK) ^ (lkey[u] & (CPK - 1));
+    coff[u] = (uint32_t)(lkey[u] * RBY + lq[u] * 16);
+    foff[u] = (uint32_t)lkey[u] * ldqb + lq[u] * 16;
   }
-  // K and V tile at key k0 into LDS buffer nb.  A tile wholly inside the key
-  // range and wholly in the cache (or in the canvas rows) is addressed from a
-  // uniform base; other tiles take per-key sources (attn_key_index keeps the
-  // slots past the split end on keys of this request).
-  auto issue = [&](int nb, int k0) __attribute__((always_inline)) {
+  // K (KV = 0) or V (KV = 1) tile at key k0 into LDS buffer NB.  A tile
+  // wholly inside the key range and wholly in the cache (or in the canvas
+  // rows) is read from a uniform base plus the lane offsets; other tiles take
+  // per-key sources (attn_key_index keeps the slots past the split end on
+  // keys of this request).
+  auto issue = [&](auto kvc, auto nbc, int k0) __attribute__((always_inline)) {
+    constexpr int KV = decltype(kvc)::value, NB = decltype(nbc)::value;
+    char* const dst = lds + (2 * KV + NB) * TB + w * NIW * 1024;
+    const char* const cb = KV ? vc : kc;
+    const char* const fb = KV ? vn : kn;
     const bool in_range = k0 + KT <= kend;
-    const bool all_cache = in_range && k0 + KT <= fresh0;
-    const bool all_fresh = in_range && k0 >= fresh0;
+    if (in_range && k0 + KT <= fresh0) {
+      const char* base = cb + (size_t)k0 * RBY;
 #pragma unroll
-    for (int u = 0; u < NIW; u++) {
-      const uint16_t *kp, *vp;
-      if (all_cache) {
-        kp = kc + (size_t)(k0 + lkey[u]) * HD;
-        vp = vc + (size_t)(k0 + lkey[u]) * HD;
-      } else if (all_fresh) {
-        kp = kn + (size_t)(k0 + lkey[u] - fresh0) * ldq;
-        vp = vn + (size_t)(k0 + lkey[u] - fresh0) * ldq;
-      } else {
-        // per-key source, as integer selects (a select between two pointer
-        // pairs is otherwise lowered to a table in private memory)
+      for (int u = 0; u < NIW; u++) lds_dma16(base + coff[u], dst + u * 1024);
+    } else if (in_range && k0 >= fresh0) {
+      const char* base = fb + (size_t)(k0 - fresh0) * ldqb;
+#pragma unroll
+      for (int u = 0; u < NIW; u++) lds_dma16(base + foff[u], dst + u * 1024);
+    } else {
+#pragma unroll
+      for (int u = 0; u < NIW; u++) {
+        // per-key source, as integer selects (a select between two pointers
+        // is otherwise lowered to a table in private memory)
         const int k = attn_key_index(k0 + lkey[u], kbeg, kend);
         const bool f = k >= fresh0;
-        const size_t off = f ? (size_t)(k - fresh0) * ldq : (size_t)k * HD;
-        const uint64_t kb = f ? (uint64_t)(uintptr_t)kn : (uint64_t)(uintptr_t)kc;
-        const uint64_t vb = f ? (uint64_t)(uintptr_t)vn : (uint64_t)(uintptr_t)vc;
-        kp = (const uint16_t*)(uintptr_t)(kb + off * 2);
-        vp = (const uint16_t*)(uintptr_t)(vb + off * 2);
+        const uint64_t off = f ? (uint64_t)(k - fresh0) * ldqb : (uint64_t)k * RBY;
+        const uint64_t base = f ? (uint64_t)(uintptr_t)fb : (uint64_t)(uintptr_t)cb;
+        lds_dma16((const char*)(uintptr_t)(base + off) + lq[u] * 16, dst + u * 1024);
       }
-      const int ii = w * NIW + u;
-      lds_dma16(kp + lq[u] * 8, &lds[nb][0][ii * 1024]);
-      lds_dma16(vp + lq[u] * 8, &lds[nb][1][ii * 1024]);
     }
   };
 
-  f32x4_t o[2][NHT];
+  f32x4_t o[J][NHT];
+  float mrow[J];    // reference maximum of the row (log2 units); -inf before its first key
+  float mneg[J];    // exponent offset -mrow (0 while mrow is -inf)
+  float thr[J];     // raw score above which the reference moves: (mrow + margin) / c2
+  f32x4_t ls[J];    // row sums of the probabilities (every element holds the sum)
 #pragma unroll
-  for (int j = 0; j < 2; j++)
+  for (int j = 0; j < J; j++) {
 #pragma unroll
     for (int u = 0; u < NHT; u++) o[j][u] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  float mrow[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+    mrow[j] = -INFINITY;
+    mneg[j] = 0.f;
+    thr[j] = -INFINITY;
+    ls[j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  }
+  FragBF ones;
+  ones.v = __builtin_bit_cast(bf16x8_t, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+  f32x4_t sa[J][MT], sb[J][MT];   // raw scores of the even and of the odd tiles
 
-  // LDS byte offsets of this lane's reads (tile-independent)
-  int koff[4][NSS];     // K fragment: key 16 mt + l16, chunk 4 ss + g4
+  // LDS byte offsets of this lane's reads within a tile buffer.  K fragment
+  // (16 mt + l16, chunk 4 ss + g4): koff[ss] + 16 mt RBY.  V^T operand (keys
+  // 32 c + 16 h + 4 g4 + l16 / 4, dims 16 ht + 4 (l16 % 4)): voff[ht] +
+  // (32 c + 16 h) RBY.  The swizzle depends on the key only modulo 16, so
+  // the key-tile parts are constants the reads carry as immediate offsets.
+  int koff[NSS], voff[NHT];
 #pragma unroll
-  for (int mt = 0; mt < 4; mt++)
+  for (int ss = 0; ss < NSS; ss++) koff[ss] = l16 * RBY + 16 * ((4 * ss + g4) ^ (l16 & (CPK - 1)));
 #pragma unroll
-    for (int ss = 0; ss < NSS; ss++) {
-      const int r = 16 * mt + l16, q = 4 * ss + g4;
-      koff[mt][ss] = r * RBY + 16 * (q ^ (r & (CPK - 1)));
-    }
-  // V^T operand: keys 32 c + 16 h + 4 g4 + l16 / 4, dims 16 ht + 4 (l16 % 4)
-  auto voff = [&](int c, int h, int ht) __attribute__((always_inline)) {
-    const int r = 32 * c + 16 * h + 4 * g4 + (l16 >> 2);
+  for (int ht = 0; ht < NHT; ht++) {
+    const int r = 4 * g4 + (l16 >> 2);
     const int byte = 32 * ht + 8 * (l16 & 3);
-    return r * RBY + 16 * ((byte >> 4) ^ (r & (CPK - 1))) + (byte & 15);
-  };
+    voff[ht] = r * RBY + 16 * ((byte >> 4) ^ (r & (CPK - 1))) + (byte & 15);
+  }
 
-  auto compute = [&](int k0, int nb, bool full) __attribute__((always_inline)) {
-    const char* ks = lds[nb][0];
-    const char* vs = lds[nb][1];
-    f32x4_t s[2][4];
-#pragma unroll
-    for (int j = 0; j < 2; j++)
-#pragma unroll
-      for (int mt = 0; mt < 4; mt++) s[j][mt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  // S^T(t) = K(t) Q^T for the wave's row tiles (K tile in buffer PB)
+  auto scores = [&](auto pbc, f32x4_t (&s)[J][MT]) __attribute__((always_inline)) {
+    constexpr int PB = decltype(pbc)::value;
 #pragma unroll
     for (int ss = 0; ss < NSS; ss++) {
-      FragBF kf[4];
+      FragBF kf[MT];
 #pragma unroll
-      for (int mt = 0; mt < 4; mt++)
-        kf[mt].v = *reinterpret_cast<const bf16x8_t*>(ks + koff[mt][ss]);
+      for (int mt = 0; mt < MT; mt++)
+        kf[mt].v = *reinterpret_cast<const bf16x8_t*>(lds + PB * TB + mt * 16 * RBY + koff[ss]);
 #pragma unroll
-      for (int mt = 0; mt < 4; mt++)
+      for (int mt = 0; mt < MT; mt++)
 #pragma unroll
-        for (int j = 0; j < 2; j++) mma(s[j][mt], kf[mt], qf[j][ss]);
+        for (int j = 0; j < J; j++) {
+          if (ss == 0) s[j][mt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+          mma(s[j][mt], kf[mt], qf[j][ss]);
+        }
     }
+  };
+  // scores of keys outside the split or past a query's causal limit -> -inf
+  auto mask = [&](f32x4_t (&s)[J][MT], int k0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-      float tmax;
-      if (full) {
-        float x = max3_nn(s[j][0][0], s[j][0][1], s[j][0][2]);
-        x = max3_nn(x, s[j][0][3], s[j][1][0]);
-        x = max3_nn(x, s[j][1][1], s[j][1][2]);
-        x = max3_nn(x, s[j][1][3], s[j][2][0]);
-        x = max3_nn(x, s[j][2][1], s[j][2][2]);
-        x = max3_nn(x, s[j][2][3], s[j][3][0]);
-        x = max3_nn(x, s[j][3][1], s[j][3][2]);
-        tmax = max_nn(x, s[j][3][3]) * a.scale_log2;
-      } else {
-        const int ql = j == 0 ? qlim0 : qlim1;
-        tmax = -INFINITY;
+    for (int j = 0; j < J; j++)
 #pragma unroll
-        for (int mt = 0; mt < 4; mt++)
+      for (int mt = 0; mt < MT; mt++)
 #pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const int kk = k0 + 16 * mt + 4 * g4 + i;
-            const bool ok = (kk < kend) & (kk <= ql) & qv[j];
-            const float v = ok ? s[j][mt][i] * a.scale_log2 : -INFINITY;
-            s[j][mt][i] = v;
-            tmax = fmaxf(tmax, v);
-          }
-      }
-      tmax = pair_max16(tmax);
-      tmax = pair_max32(tmax);
-      // move the reference only past the margin (a row's first keys always
-      // move it: the reference starts at -inf)
-      const bool move = tmax > mrow[j] + ATTN_RESCALE_LOG2;
-      if (__ballot(move)) {
-        const float alpha = move ? (mrow[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrow[j] - tmax)) : 1.f;
-        mrow[j] = move ? tmax : mrow[j];
-        lsum[j] *= alpha;
+        for (int i = 0; i < 4; i++) {
+          const int kk = k0 + 16 * mt + 4 * g4 + i;
+          const bool ok = (kk < kend) & (kk <= qlim[j]) & qv[j];
+          s[j][mt][i] = ok ? s[j][mt][i] : -INFINITY;
+        }
+  };
+  // probabilities 2^(c s - m) as bf16 B fragments of the 32-key chunks (a
+  // row that has seen no key has m = -inf and all its scores -inf: offset 0
+  // gives probabilities 0)
+  auto probs = [&](const f32x4_t (&s)[J][MT], FragBF (&pf)[J][NCH]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int u = 0; u < NHT; u++) o[j][u] *= alpha;
-      }
-      const float mref = mrow[j];
-      float psum = 0.f;
-      if (full) {
+    for (int j = 0; j < J; j++) {
+      float p[MT][4];
 #pragma unroll
-        for (int mt = 0; mt < 4; mt++)
+      for (int mt = 0; mt < MT; mt++)
 #pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][mt][i], a.scale_log2, -mref));
-            s[j][mt][i] = p;
-            psum += p;
-          }
-      } else {
+        for (int i = 0; i < 4; i++) p[mt][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][mt][i], c2, mneg[j]));
 #pragma unroll
-        for (int mt = 0; mt < 4; mt++)
-#pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const float p = mref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s[j][mt][i] - mref);
-            s[j][mt][i] = p;
-            psum += p;
-          }
-      }
-      lsum[j] += psum;
+      for (int c = 0; c < NCH; c++)
+        pf[j][c].v = __builtin_bit_cast(bf16x8_t, make_uint4(f2bf2(p[2 * c][0], p[2 * c][1]),
+                                                             f2bf2(p[2 * c][2], p[2 * c][3]),
+                                                             f2bf2(p[2 * c + 1][0], p[2 * c + 1][1]),
+                                                             f2bf2(p[2 * c + 1][2], p[2 * c + 1][3])));
     }
-    // O^T += V^T P^T over the two 32-key chunks of the tile
+  };
+  // O^T += V^T P^T over the 32-key chunks of the tile (V tile in buffer PB),
+  // and the row sums of the same bf16 probabilities on the matrix cores (an
+  // all-ones A operand: every row of the product holds the column sums)
+  auto pv = [&](auto pbc, const FragBF (&pf)[J][NCH]) __attribute__((always_inline)) {
+    constexpr int PB = decltype(pbc)::value;
 #pragma unroll
-    for (int c = 0; c < KT / 32; c++) {
-      FragBF pf[2];
-#pragma unroll
-      for (int j = 0; j < 2; j++)
-        pf[j].v = __builtin_bit_cast(bf16x8_t, make_uint4(f2bf2(s[j][2 * c][0], s[j][2 * c][1]),
-                                                          f2bf2(s[j][2 * c][2], s[j][2 * c][3]),
-                                                          f2bf2(s[j][2 * c + 1][0], s[j][2 * c + 1][1]),
-                                                          f2bf2(s[j][2 * c + 1][2], s[j][2 * c + 1][3])));
+    for (int c = 0; c < NCH; c++) {
 #pragma unroll
       for (int ht = 0; ht < NHT; ht++) {
-        const s16x4_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vs + voff(c, 0, ht)));
-        const s16x4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vs + voff(c, 1, ht)));
+        const char* vs = lds + (2 + PB) * TB + 32 * c * RBY + voff[ht];
+        const s16x4_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vs));
+        const s16x4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vs + 16 * RBY));
         FragBF vf;
         vf.v = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-        for (int j = 0; j < 2; j++) mma(o[j][ht], vf, pf[j]);
+        for (int j = 0; j < J; j++) mma(o[j][ht], vf, pf[j][c]);
+      }
+#pragma unroll
+      for (int j = 0; j < J; j++) mma(ls[j], ones, pf[j][c]);
+    }
+  };
+  // this lane's maximum raw score of each row
+  auto lanemax = [&](const f32x4_t (&s)[J][MT], float (&m)[J]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < J; j++) {
+      float x[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) x[mt] = fmax3(s[j][mt][0], s[j][mt][1], __builtin_fmaxf(s[j][mt][2], s[j][mt][3]));
+      float y = x[0];
+#pragma unroll
+      for (int mt = 1; mt + 1 < MT; mt += 2) y = fmax3(y, x[mt], x[mt + 1]);
+      m[j] = MT % 2 == 0 ? __builtin_fmaxf(y, x[MT - 1]) : y;
+    }
+  };
+  // move the reference past the margin: only when some lane of the wave
+  // holds a score above its row's threshold does the wave take the row
+  // maxima over the four lane groups (a row's first keys always move it:
+  // the threshold starts at -inf)
+  auto rescale = [&](const float (&m)[J]) __attribute__((always_inline)) {
+    bool need = false;
+#pragma unroll
+    for (int j = 0; j < J; j++) need |= m[j] > thr[j];
+    if (__ballot(need)) {
+#pragma unroll
+      for (int j = 0; j < J; j++) {
+        const float tmax = pair_max32(pair_max16(m[j])) * c2;
+        const bool move = tmax > mrow[j] + ATTN_RESCALE_LOG2;
+        const float alpha = move ? __builtin_amdgcn_exp2f(mrow[j] - tmax) : 1.f;
+        mrow[j] = move ? tmax : mrow[j];
+        mneg[j] = mrow[j] == -INFINITY ? 0.f : -mrow[j];
+        thr[j] = (mrow[j] + ATTN_RESCALE_LOG2) * inv_c2;
+        ls[j] *= alpha;
+#pragma unroll
+        for (int u = 0; u < NHT; u++) o[j][u] *= alpha;
       }
     }
   };
-
-  // NBUF-1 tiles in flight: tile t+NBUF-1 is issued into the buffer that
-  // held tile t-1 once the barrier shows every wave is done with it
-  constexpr int LPT = 2 * NIW;   // wave loads per tile
-  const int ntile = kend > kbeg ? (kend - kbeg + KT - 1) / KT : 0;
+  // instruction interleaving of the two phases (sched_group_barrier masks:
+  // 0x008 MFMA, 0x100 LDS read, 0x402 VALU or transcendental)
+  auto interleave_a = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int pb = 0; pb < NBUF - 1; pb++)
-    if (pb < ntile) issue(pb, kbeg + pb * KT);
-  auto step = [&](auto bc, int tl) __attribute__((always_inline)) {
-    constexpr int BUF = decltype(bc)::value;
-    // this wave's loads of tile tl have landed (the later tiles' may not have)
-    const int later = min(NBUF - 2, ntile - 1 - tl);
-    if (NBUF >= 4 && later >= 2) wait_vmcnt<(NBUF >= 4 ? 2 * LPT : 0)>();
-    else if (NBUF >= 3 && later >= 1) wait_vmcnt<(NBUF >= 3 ? LPT : 0)>();
-    else wait_vmcnt<0>();
-    __syncthreads();
-    if (tl + NBUF - 1 < ntile) issue((BUF + NBUF - 1) % NBUF, kbeg + (tl + NBUF - 1) * KT);
-    const int k0 = kbeg + tl * KT;
-    compute(k0, BUF, k0 + KT <= kend && k0 + KT - 1 <= qlim_all);
+    for (int i = 0; i < MT * NSS; i++) {
+      __builtin_amdgcn_sched_group_barrier(0x008, J, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x402, 2 * J + 1, 0);
+    }
   };
-  for (int it = 0; it < ntile; it += NBUF) {
-    step(std::integral_constant<int, 0>(), it);
-    if (it + 1 < ntile) step(std::integral_constant<int, 1>(), it + 1);
-    if (NBUF >= 3 && it + 2 < ntile) step(std::integral_constant<int, (NBUF >= 3 ? 2 : 0)>(), it + 2);
-    if (NBUF >= 4 && it + 3 < ntile) step(std::integral_constant<int, (NBUF >= 4 ? 3 : 0)>(), it + 3);
+  auto interleave_b = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NCH * NHT; i++) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, J, 1);
+      __builtin_amdgcn_sched_group_barrier(0x402, 1, 1);
+    }
+  };
+
+  const int ntile = kend > kbeg ? (kend - kbeg + KT - 1) / KT : 0;
+  auto full = [&](int k0) __attribute__((always_inline)) { return k0 + KT <= kend && k0 + KT - 1 <= qlim_all; };
+  // Step tl (PB = tl & 1): scores of tile tl (CUR) and the probabilities and
+  // P V product of tile tl - 1 (PREV).  K(tl) sits in K buffer PB and V(tl-1)
+  // in V buffer PB ^ 1; after the barrier (every wave is done with step
+  // tl - 1) the step loads K(tl+1) into K buffer PB ^ 1 and V(tl) into V
+  // buffer PB, which both land before the next step's wait.
+  auto step = [&](auto pbc, auto curc, auto prevc, int tl) __attribute__((always_inline)) {
+    constexpr int PB = decltype(pbc)::value;
+    constexpr bool CUR = decltype(curc)::value, PREV = decltype(prevc)::value;
+    f32x4_t(&sc)[J][MT] = PB ? sb : sa;
+    f32x4_t(&sp)[J][MT] = PB ? sa : sb;
+    wait_vmcnt<0>();
+    __syncthreads();
+    const int k0 = kbeg + tl * KT;
+    if (CUR) {
+      if (tl + 1 < ntile) issue(std::integral_constant<int, 0>(), std::integral_constant<int, PB ^ 1>(), k0 + KT);
+      issue(std::integral_constant<int, 1>(), std::integral_constant<int, PB>(), k0);
+    }
+    // phase A: S(t) on the matrix cores, the probabilities of t-1 on the
+    // vector units (one basic block, interleaved)
+    FragBF pf[J][NCH];
+    if (PREV) probs(sp, pf);
+    if (CUR) scores(pbc, sc);
+    if (PREV && CUR) {
+      // the probabilities are only used after the mask branch: an empty
+      // statement that reads them keeps their computation in this block, so
+      // that it overlaps the score MFMAs (it defines nothing, so the wait
+      // states before the MFMAs that read them still follow the conversions)
+#pragma unroll
+      for (int j = 0; j < J; j++)
+#pragma unroll
+        for (int c = 0; c < NCH; c++) asm volatile("" ::"v"(pf[j][c].v));
+      interleave_a();
+    }
+    if (CUR && !full(k0)) mask(sc, k0);
+    // phase B: P(t-1) V(t-1) and the row sums on the matrix cores, the row
+    // maxima of S(t) on the vector units
+    float m[J];
+    if (PREV) pv(std::integral_constant<int, PB ^ 1>(), pf);
+    if (CUR) lanemax(sc, m);
+    if (PREV && CUR) interleave_b();
+    if (CUR) rescale(m);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using BT = std::integral_constant<bool, true>;
+  using BF = std::integral_constant<bool, false>;
+  if (ntile > 0) {
+    issue(I0(), I0(), kbeg);
+    step(I0(), BT(), BF(), 0);
+    int tl = 1;
+    for (; tl + 1 < ntile; tl += 2) {
+      step(I1(), BT(), BT(), tl);
+      step(I0(), BT(), BT(), tl + 1);
+    }
+    if (tl < ntile) {
+      step(I1(), BT(), BT(), tl);
+      step(I0(), BF(), BT(), tl + 1);
+    } else {
+      step(I1(), BF(), BT(), tl);
+    }
   }
 
 #pragma unroll
-  for (int j = 0; j < 2; j++) {
-    float l = lsum[j];
-    l += lane_xor16(l);
-    l += lane_xor32(l);
+  for (int j = 0; j < J; j++) {
+    // ls[j]: row 4 g4 + i of the column-sum product, i.e. query l16's sum in every element
+    const float l = ls[j][0];
     const size_t row = (size_t)b * a.T + qi[j];
     if (!qv[j]) {
       // rows past the request's queries are not stored
@@ -809,12 +903,12 @@ struct AttnPlan {
 // K+V tile buffers: 64 KB of LDS at hd 128, two blocks per CU).  Measured at
 // the 8192-prefix and batch-8 workloads: 8 waves with three buffers (one block
 // per CU, two tiles in flight) took 42 and 81 us against 44 and 73 us.
-constexpr int ATTN_NW = 4;
-constexpr int ATTN_NBUF = 2;
+constexpr int ATTN_ROWS = 128;   // (query, head) rows per bf16 attention block
+constexpr int ATTN_KT = 32;   // keys per pipeline step of the bf16 kernel
 
 // rows per block: 32 per wave for the bf16 kernel, 64 for the fp32 kernel
 // (4 waves x 16 rows)
-int attn_block_rows(int act) { return act == ACT_BF16 ? 32 * ATTN_NW : 64; }
+int attn_block_rows(int act) { return act == ACT_BF16 ? ATTN_ROWS : 64; }
 
 AttnPlan plan_attention(int act, int B, int T, const Lens& len, int Hq, int Hkv, long part_cap) {
   AttnPlan p{};
@@ -873,8 +967,11 @@ void launch_attention(const AttnArgsHost& h, hipStream_t s) {
   a.groups = p.groups;
   const dim3 grid(p.grid);
   if (h.act == ACT_BF16) {
-    if (h.hd == 128) attn_bf16_k<128, ATTN_NBUF, ATTN_NW><<<grid, ATTN_NW * 64, 0, s>>>(a);
-    else attn_bf16_k<64, ATTN_NBUF, ATTN_NW><<<grid, ATTN_NW * 64, 0, s>>>(a);
+    // 4 waves of two 16-row tiles (each K and V fragment read from LDS
+    // serves both tiles)
+    static_assert(16 * 2 * 4 == ATTN_ROWS, "block rows");
+    if (h.hd == 128) attn_bf16_k<128, 4, ATTN_KT, 2><<<grid, 4 * 64, 0, s>>>(a);
+    else attn_bf16_k<64, 4, ATTN_KT, 2><<<grid, 4 * 64, 0, s>>>(a);
   } else {
     if (h.hd == 128) attn_k<float, 128><<<grid, 256, 0, s>>>(a);
     else attn_k<float, 64><<<grid, 256, 0, s>>>(a);
@@ -914,15 +1011,18 @@ long attn_check_addresses(int act, int B, int T, const Lens& len, int Hq, int Hk
     const int nkeys = mode == 0 ? P + T : P + (((qt + 1) * p.QT) < T ? (qt + 1) * p.QT : T);
     const int kbeg = split * p.split_len;
     const int kend = nkeys < kbeg + p.split_len ? nkeys : kbeg + p.split_len;
-    const int ntile = kend > kbeg ? (kend - kbeg + KT - 1) / KT : 0;
+    // the bf16 kernel loads exactly its ntile tiles of ATTN_KT keys; the
+    // fp32 kernel stages 64-key tiles up to two ahead of the last one used
+    const int kt = act == ACT_BF16 ? ATTN_KT : KT;
+    const int ntile = kend > kbeg ? (kend - kbeg + kt - 1) / kt : 0;
     int last = ntile - 1;
     if (act != ACT_BF16) {
       last = 2;
       for (int it = 0; it + 2 <= ntile; it += 2) last = it + 1 + 3 > last ? it + 1 + 3 : last;
     }
     for (int tl = 0; tl <= last; tl++)
-      for (int j = 0; j < KT; j++) {
-        const int k = attn_key_index(kbeg + tl * KT + j, kbeg, kend);
+      for (int j = 0; j < kt; j++) {
+        const int k = attn_key_index(kbeg + tl * kt + j, kbeg, kend);
         n++;
         bad += !(k >= 0 && k < P + T);
       }

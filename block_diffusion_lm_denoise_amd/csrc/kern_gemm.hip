@@ -821,8 +821,8 @@ __global__ __launch_bounds__(NW * 64, MINB) void lmhead_direct_k(HeadArgs a) {
         for (int i = 0; i < 4; i++) x[4 * ct + i] = ok[ct][i] ? acc[rt][ct][i] : -INFINITY;
       float v = x[0];
 #pragma unroll
-      for (int j = 1; j + 1 < 4 * CT; j += 2) v = max3_nn(v, x[j], x[j + 1]);
-      m[rt] = max3_nn(v, x[4 * CT - 1], x[4 * CT - 1]);
+      for (int j = 1; j + 1 < 4 * CT; j += 2) v = fmax3(v, x[j], x[j + 1]);
+      m[rt] = __builtin_fmaxf(v, x[4 * CT - 1]);
     }
 #pragma unroll
     for (int rt = 0; rt < RT; rt++) m[rt] = pair_max16(m[rt]);
