@@ -22,5 +22,25 @@ def build(force: bool = True) -> str:
     return LIB
 
 
+SANITIZED = os.path.join(HERE, "oracle_sanitized")
+
+
+def build_sanitized(selfcheck: bool = False) -> str:
+    """The oracle with AddressSanitizer and UndefinedBehaviorSanitizer linked
+    into sanitize_main.c, a driver of every entry point on tiny shapes (a
+    host-only executable; any sanitizer report ends it with a failure).
+    selfcheck builds the driver's planted out-of-bounds read instead, to show
+    that the build is instrumented."""
+    out = SANITIZED + ("_selfcheck" if selfcheck else "")
+    tmp = out + ".tmp"
+    cmd = ["gcc", *(["-DSANITIZER_SELFCHECK"] if selfcheck else []), "-std=gnu11", "-O1", "-g", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+           "-Wall", "-Wextra", "-Wno-unused-parameter", "-o", tmp,
+           os.path.join(HERE, "oracle.c"), os.path.join(HERE, "sanitize_main.c"), "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
     print(build())
