@@ -10,6 +10,13 @@ canvas is the last pass's argmax (no re-noise after the last pass); RNG
 pass tags are 0 for the initial noise and p+1 for the re-noise after pass
 p; positions are absolute, so chained canvases draw different noise.
 
+Stop and resume: the whole state between two passes is the KV cache (with
+its lengths), the canvas, the canvas and pass indices and the seed (the
+noise is a function of position, pass tag and seed alone).  stop=(c, p)
+returns before pass p of canvas c with that state in `state`; start=state
+continues from it (on the same cache, or on a copy of it) and produces what
+the uninterrupted loop would have.
+
 Two variants of the same loop (the kernels are the same; only the update
 between passes changes):
   - sampler="masked": masked ("absorbing") diffusion, the earlier scheme the
@@ -37,12 +44,13 @@ class GenerateResult:
     touched: torch.Tensor                # [canvases][S][L] experts touched per pass
     lens: list = field(default_factory=list)
     passes: list = field(default_factory=list)   # passes run per canvas
+    state: dict = None                   # set when stopped: where to resume
 
 
 def generate(model: dgpass.Model, kv: dgpass.KVCache, prompt: torch.Tensor, n_canvases: int, N: int,
              S: int, tau: float, seed: int, ws: torch.Tensor, prefill_prompt: bool = True,
              stream=None, sampler: str = "uniform", mask_id: int = None,
-             early_exit: bool = False) -> GenerateResult:
+             early_exit: bool = False, stop=None, start=None) -> GenerateResult:
     cfg = model.cfg
     B = kv.B
     if sampler not in ("uniform", "masked"):
@@ -52,6 +60,11 @@ def generate(model: dgpass.Model, kv: dgpass.KVCache, prompt: torch.Tensor, n_ca
         if not 0 <= mask_id < cfg.V:
             raise ValueError("mask_id must be a vocabulary id")
     dev = prompt.device if prompt is not None else kv.k[0].device
+    c_first, p_first = 0, 0
+    if start is not None:
+        c_first, p_first = int(start["canvas_index"]), int(start["pass_index"])
+        if not (0 <= c_first < n_canvases and 0 <= p_first < S) or prefill_prompt:
+            raise ValueError("start needs a canvas and pass inside the run, and no prompt prefill")
     if prefill_prompt and prompt is not None:
         model.kv_prefill(kv, prompt, ws, stream=stream)
     canvas = torch.empty(B, N, dtype=torch.int32, device=dev)
@@ -61,12 +74,20 @@ def generate(model: dgpass.Model, kv: dgpass.KVCache, prompt: torch.Tensor, n_ca
     masked_left = torch.zeros(B, dtype=torch.int32, device=dev)
     touched = torch.zeros(n_canvases, S, cfg.L, dtype=torch.int32, device=dev)
     out, used = [], []
-    for c in range(n_canvases):
+    for c in range(c_first, n_canvases):
         pos0 = kv.lens.copy()
         base = dict(sampler=sampler, mask_id=mask_id or 0, tau=tau, seed=seed, pos0=pos0)
-        dgpass.canvas_update(canvas, None, None, dict(base, pass_tag=0), cfg.V, stream=stream)
+        p0 = 0
+        if start is not None and c == c_first:
+            canvas.copy_(start["canvas"])
+            p0 = p_first
+        else:
+            dgpass.canvas_update(canvas, None, None, dict(base, pass_tag=0), cfg.V, stream=stream)
         ran = S
-        for p in range(S):
+        for p in range(p0, S):
+            if stop is not None and (c, p) == tuple(stop):
+                state = dict(canvas_index=c, pass_index=p, canvas=canvas.clone())
+                return GenerateResult(out, touched, [int(x) for x in kv.lens], used, state)
             last = p == S - 1
             # the pass's last kernel writes the coverage and the update for the
             # next pass (uniform: none after the last pass; masked: the last

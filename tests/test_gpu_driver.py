@@ -238,3 +238,54 @@ def test_early_exit_stops_a_converged_canvas(sampler, tau):
         np.testing.assert_array_equal(host(res.canvases[c]), commits[c])
     np.testing.assert_array_equal(host(res.touched), touched)
     print(sampler, "early exit after passes", used, flush=True)
+
+
+@pytest.mark.parametrize("sampler,stop", [("uniform", (1, 2)), ("uniform", (0, 0)), ("masked", (1, 1))])
+def test_stop_and_resume_reproduces_the_run(sampler, stop):
+    """The state between two passes is (KV cache with its lengths, canvas,
+    canvas and pass index, seed): a run stopped before pass p of canvas c
+    and resumed from a copy of that state commits the same canvases, with
+    the same coverage and the same cache, as the uninterrupted run
+    (explainer "DiffusionGemma", "Long-form text: chaining canvases": the
+    cache carries everything earlier canvases left)."""
+    cfg = ModelConfig(L=2, D=256, Hq=4, Hkv=2, hd=64, E=8, k=2, F=128, V=512, act="bf16", expert="bf16")
+    seed, tau, B, P, N, S, n_canvases = 31, 0.5, 2, 6, 16, 4, 3
+    mask_id = cfg.V - 1 if sampler == "masked" else None
+    pair = Pair(cfg, seed, scale_lm=12.0)
+    prompt = synth.tokens(cfg.V, (B, P), seed, name="prompt").to(DEV)
+    cap = P + n_canvases * N
+    ws = pair.gm.workspace(B * N, cap, device=DEV)
+    kw = dict(sampler=sampler, mask_id=mask_id)
+
+    kv = pair.gm.kv_cache(B, cap, device=DEV)
+    whole = driver.generate(pair.gm, kv, prompt, n_canvases, N, S, tau, seed, ws, **kw)
+
+    kv1 = pair.gm.kv_cache(B, cap, device=DEV)
+    first = driver.generate(pair.gm, kv1, prompt, n_canvases, N, S, tau, seed, ws, stop=stop, **kw)
+    assert first.state is not None and len(first.canvases) == stop[0]
+    # the saved state: a copy of the cache and its lengths, the canvas, (c, p)
+    kv2 = pair.gm.kv_cache(B, cap, device=DEV)
+    for l in range(cfg.L):
+        kv2.k[l].copy_(kv1.k[l])
+        kv2.v[l].copy_(kv1.v[l])
+    kv2.lens[:] = kv1.lens
+    del kv1
+    rest = driver.generate(pair.gm, kv2, None, n_canvases, N, S, tau, seed, ws, prefill_prompt=False,
+                           start=first.state, **kw)
+    torch.cuda.synchronize()
+
+    commits = first.canvases + rest.canvases
+    assert len(commits) == n_canvases
+    for c in range(n_canvases):
+        np.testing.assert_array_equal(host(commits[c]), host(whole.canvases[c]), err_msg=f"canvas {c}")
+    c0, p0 = stop
+    wt, ft, rt = host(whole.touched), host(first.touched), host(rest.touched)
+    np.testing.assert_array_equal(ft[:c0], wt[:c0])
+    np.testing.assert_array_equal(ft[c0, :p0], wt[c0, :p0])
+    np.testing.assert_array_equal(rt[c0, p0:], wt[c0, p0:])
+    np.testing.assert_array_equal(rt[c0 + 1:], wt[c0 + 1:])
+    assert rest.lens == whole.lens
+    for l in range(cfg.L):
+        n = max(whole.lens)
+        assert torch.equal(kv2.k[l][:, :, :n], kv.k[l][:, :, :n])
+        assert torch.equal(kv2.v[l][:, :, :n], kv.v[l][:, :, :n])
