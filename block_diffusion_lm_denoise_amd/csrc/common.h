@@ -320,4 +320,27 @@ __device__ __forceinline__ float block_sum256(float v, float* red) {
   return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
+// ---------------------------------------------------------------------------
+// direct loads into LDS (gfx950 global_load_lds, 16 bytes per lane: lane i
+// writes lds_wave_base + 16 i) and their waits
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+// a pointer the whole wave holds, in scalar registers
+__device__ __forceinline__ const char* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+// wait until at most n vector-memory loads of this wave are outstanding (gfx9
+// s_waitcnt encoding: vmcnt low bits [3:0] and high bits [15:14]; expcnt and
+// lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 }  // namespace dg

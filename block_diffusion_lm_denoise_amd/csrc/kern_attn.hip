@@ -440,25 +440,6 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
-__device__ __forceinline__ void lds_dma16(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
-}
-// a pointer the whole wave holds, in scalar registers
-__device__ __forceinline__ const char* uniform_ptr(const void* p) {
-  const uint64_t v = (uint64_t)(uintptr_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
-// wait until at most n vector-memory loads of this wave are outstanding (gfx9
-// s_waitcnt encoding: vmcnt low bits [3:0] and high bits [15:14]; expcnt and
-// lgkmcnt left at their maxima)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 constexpr float ATTN_RESCALE_LOG2 = 8.f;   // move the running maximum past this margin
 
 template <int HD, int NW, int KT, int J>
@@ -821,56 +802,50 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_k(AttnArgs a) {
 }
 
 // combine key splits in split order: o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-// A thread owns 8 consecutive head-dimension elements of one (row, head)
-// entry; the partial loads of several splits are in flight together.
-template <typename TA, int HD>
+// A thread owns 4 consecutive head-dimension elements of one (row, head)
+// entry and has the loads of every split in flight at once (the merge is a
+// short latency chain over 2 + nsplit loads).
+constexpr int ATTN_MAX_SPLIT = 16;
+template <typename T> struct TypeTag { using type = T; };
+template <typename TA, int HD, int NS>
 __global__ __launch_bounds__(256) void attn_merge_k(const float* __restrict__ po,
                                                     const float* __restrict__ pml, int nsplit,
                                                     int entries, TA* __restrict__ out) {
-  constexpr int TPE = HD / 8;   // threads per entry
+  constexpr int TPE = HD / 4;   // threads per entry
   const int gt = blockIdx.x * 256 + threadIdx.x;
-  const int e = gt / TPE, d0 = (gt % TPE) * 8;
+  const int e = gt / TPE, d0 = (gt % TPE) * 4;
   if (e >= entries) return;
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < nsplit; s0 += 8) {
-    float m[8];
+  // NS >= nsplit: the loads of all splits at once (splits past nsplit re-read
+  // split 0 and weigh nothing)
+  float m[NS], l[NS];
+  float4 v[NS];
 #pragma unroll
-    for (int j = 0; j < 8; j++) m[j] = s0 + j < nsplit ? pml[2 * ((size_t)(s0 + j) * entries + e)] : -INFINITY;
-#pragma unroll
-    for (int j = 0; j < 8; j++) M = fmaxf(M, m[j]);
+  for (int j = 0; j < NS; j++) {
+    const size_t ee = (size_t)(j < nsplit ? j : 0) * entries + e;
+    m[j] = pml[2 * ee];
+    l[j] = pml[2 * ee + 1];
+    v[j] = *reinterpret_cast<const float4*>(po + ee * HD + d0);
   }
-  float den = 0.f, num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < nsplit; s0 += 4) {
-    float f[4], l[4];
-    float4 v0[4], v1[4];
+  float M = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int sp = s0 + j < nsplit ? s0 + j : s0;
-      const size_t ee = (size_t)sp * entries + e;
-      const float mj = pml[2 * ee];
-      f[j] = (s0 + j < nsplit && mj != -INFINITY) ? __builtin_amdgcn_exp2f(mj - M) : 0.f;
-      l[j] = pml[2 * ee + 1];
-      v0[j] = *reinterpret_cast<const float4*>(po + ee * HD + d0);
-      v1[j] = *reinterpret_cast<const float4*>(po + ee * HD + d0 + 4);
-    }
+  for (int j = 0; j < NS; j++) M = j < nsplit ? fmaxf(M, m[j]) : M;
+  float den = 0.f, num[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      den += f[j] * l[j];
-      num[0] += f[j] * v0[j].x;
-      num[1] += f[j] * v0[j].y;
-      num[2] += f[j] * v0[j].z;
-      num[3] += f[j] * v0[j].w;
-      num[4] += f[j] * v1[j].x;
-      num[5] += f[j] * v1[j].y;
-      num[6] += f[j] * v1[j].z;
-      num[7] += f[j] * v1[j].w;
-    }
+  for (int j = 0; j < NS; j++) {
+    const float f = (j < nsplit && m[j] != -INFINITY) ? __builtin_amdgcn_exp2f(m[j] - M) : 0.f;
+    den += f * l[j];
+    num[0] += f * v[j].x;
+    num[1] += f * v[j].y;
+    num[2] += f * v[j].z;
+    num[3] += f * v[j].w;
   }
   const float inv = 1.f / den;
-  float r[8];
-#pragma unroll
-  for (int i = 0; i < 8; i++) r[i] = num[i] * inv;
-  st8(out + (size_t)e * HD + d0, r);
+  if constexpr (sizeof(TA) == 2)
+    *reinterpret_cast<uint2*>(out + (size_t)e * HD + d0) =
+        make_uint2(f2bf2(num[0] * inv, num[1] * inv), f2bf2(num[2] * inv, num[3] * inv));
+  else
+    *reinterpret_cast<float4*>(out + (size_t)e * HD + d0) =
+        make_float4(num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -878,7 +853,6 @@ __global__ __launch_bounds__(256) void attn_merge_k(const float* __restrict__ po
 // is a short latency chain), at least ATTN_MIN_SPLIT_KEYS keys per split
 constexpr int ATTN_TARGET_BLOCKS = 512;
 constexpr int ATTN_MIN_SPLIT_KEYS = 128;
-constexpr int ATTN_MAX_SPLIT = 16;
 constexpr long ATTN_MAX_PART_ENTRIES = 1L << 18;
 
 long attn_partial_entries(int rows, int Hq, int max_keys) {
@@ -978,14 +952,20 @@ void launch_attention(const AttnArgsHost& h, hipStream_t s) {
   }
   if (p.nsplit > 1) {
     const int entries = a.rows * h.Hq;
-    const int blocks = (int)(((long)entries * (h.hd / 8) + 255) / 256);
-    if (h.act == ACT_BF16) {
-      if (h.hd == 128) attn_merge_k<uint16_t, 128><<<blocks, 256, 0, s>>>(h.po, h.pml, p.nsplit, entries, (uint16_t*)h.out);
-      else attn_merge_k<uint16_t, 64><<<blocks, 256, 0, s>>>(h.po, h.pml, p.nsplit, entries, (uint16_t*)h.out);
-    } else {
-      if (h.hd == 128) attn_merge_k<float, 128><<<blocks, 256, 0, s>>>(h.po, h.pml, p.nsplit, entries, (float*)h.out);
-      else attn_merge_k<float, 64><<<blocks, 256, 0, s>>>(h.po, h.pml, p.nsplit, entries, (float*)h.out);
-    }
+    const int blocks = (int)(((long)entries * (h.hd / 4) + 255) / 256);
+    auto merge = [&](auto tac, auto nsc) {
+      using TA = typename decltype(tac)::type;
+      constexpr int NS = decltype(nsc)::value;
+      if (h.hd == 128) attn_merge_k<TA, 128, NS><<<blocks, 256, 0, s>>>(h.po, h.pml, p.nsplit, entries, (TA*)h.out);
+      else attn_merge_k<TA, 64, NS><<<blocks, 256, 0, s>>>(h.po, h.pml, p.nsplit, entries, (TA*)h.out);
+    };
+    auto by_splits = [&](auto tac) {
+      if (p.nsplit <= 4) merge(tac, std::integral_constant<int, 4>());
+      else if (p.nsplit <= 8) merge(tac, std::integral_constant<int, 8>());
+      else merge(tac, std::integral_constant<int, ATTN_MAX_SPLIT>());
+    };
+    if (h.act == ACT_BF16) by_splits(TypeTag<uint16_t>());
+    else by_splits(TypeTag<float>());
   }
 }
 
