@@ -851,7 +851,14 @@ __global__ __launch_bounds__(256) void attn_merge_k(const float* __restrict__ po
 // ---------------------------------------------------------------------------
 // key splits: enough blocks to fill the chip several times over (each block
 // is a short latency chain), at least ATTN_MIN_SPLIT_KEYS keys per split
+// About 512 blocks when requests hold many keys.  With few keys (up to 2048
+// per request) 256: more splits then add partial traffic and merge work that
+// outweigh the parallelism.  Measured for attention + merge: 20.8 against
+// 23.9 us at 1280 keys; 256 blocks were slower at 2304 keys (batch 8: 89
+// against 71 us) and at 8448 (47 against 42).
 constexpr int ATTN_TARGET_BLOCKS = 512;
+constexpr int ATTN_TARGET_BLOCKS_FEW_KEYS = 256;
+constexpr int ATTN_FEW_KEYS = 2048;
 constexpr int ATTN_MIN_SPLIT_KEYS = 128;
 constexpr long ATTN_MAX_PART_ENTRIES = 1L << 18;
 
@@ -873,10 +880,8 @@ struct AttnPlan {
   unsigned grid;
 };
 
-// bf16 kernel: waves per block and tile buffers (4 waves x 32 rows, two 32 KB
-// K+V tile buffers: 64 KB of LDS at hd 128, two blocks per CU).  Measured at
-// the 8192-prefix and batch-8 workloads: 8 waves with three buffers (one block
-// per CU, two tiles in flight) took 42 and 81 us against 44 and 73 us.
+// bf16 kernel: 4 waves x 32 rows, K and V tiles of 32 keys in two buffers
+// each (32 KB of LDS at hd 128, two blocks per CU)
 constexpr int ATTN_ROWS = 128;   // (query, head) rows per bf16 attention block
 constexpr int ATTN_KT = 32;   // keys per pipeline step of the bf16 kernel
 
@@ -893,8 +898,9 @@ AttnPlan plan_attention(int act, int B, int T, const Lens& len, int Hq, int Hkv,
   p.nqt = (T + p.QT - 1) / p.QT;
   const long base = (long)p.nqt * B * Hkv;
   int nsplit = 1;
-  if (base < ATTN_TARGET_BLOCKS) {
-    nsplit = (int)((ATTN_TARGET_BLOCKS + base - 1) / base);
+  const int target = maxkeys <= ATTN_FEW_KEYS ? ATTN_TARGET_BLOCKS_FEW_KEYS : ATTN_TARGET_BLOCKS;
+  if (base < target) {
+    nsplit = (int)((target + base - 1) / base);
     const int by_keys = (maxkeys + ATTN_MIN_SPLIT_KEYS - 1) / ATTN_MIN_SPLIT_KEYS;
     if (nsplit > by_keys) nsplit = by_keys;
     if (nsplit > ATTN_MAX_SPLIT) nsplit = ATTN_MAX_SPLIT;
