@@ -656,133 +656,18 @@ __global__ __launch_bounds__(256) void lmhead_k(HeadArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// LM head for bf16 activations and more than 64 rows.  Block tile: 128 rows x
-// 256 vocabulary entries; the 4 waves sit side by side (128 x 64 each).  Every
-// weight byte is used by exactly one wave, so the weight rows stream from HBM
-// straight into MFMA fragments; only the activation tile, which all 4 waves
-// share, goes through LDS (a ring of P contraction tiles in flight in
-// registers, LDS double buffer).  Staging both operands through LDS would make
-// the LDS write port the bottleneck.
-// ---------------------------------------------------------------------------
-template <int P, int NW, int BN, int MINB>
-__global__ __launch_bounds__(NW * 64, MINB) void lmhead_direct_k(HeadArgs a) {
-  constexpr int NT = NW * 64;                 // threads
-  constexpr int BM = 128, BK = 64, LDK = 80, RT = 8;   // 160-byte LDS rows: conflict-free fragment reads
-  constexpr int WC = BN / NW, CT = WC / 16;   // vocabulary columns per wave
-  constexpr int A_LD = BM * BK * 2 / 16 / NT;   // 16-byte A chunks staged per thread
-  constexpr int A_RSTEP = NT / 8;             // rows between a thread's chunks
-  // three LDS buffers: while tile kt is consumed, tile kt+1 is readable (its
-  // first fragments are prefetched) and tile kt+2 is being written
-  __shared__ __attribute__((aligned(16))) uint16_t sA[3][BM * LDK];
-  __shared__ float xm[NW][BM], xs[NW][BM];
-  __shared__ int xi[NW][BM];
-  const int b8 = blockIdx.x >> 3, mtiles = a.mtiles;
-  const int nt = (b8 / mtiles) * 8 + (blockIdx.x & 7), mt = b8 % mtiles;
-  if (nt >= a.ntiles) return;
-  const int n0 = nt * BN, m0 = mt * BM;
+// Epilogue of the LM head kernels.  acc[rt][ct] is the block's transposed
+// logits tile: lane (l16, g) of wave w holds vocabulary rows
+// n0 + WC w + 16 ct + 4 g + i (i = 0..3) of token m0 + 16 rt + l16, so a
+// token's WC columns of this wave sit in 4 CT registers of 4 lanes (g = 0..3).
+// Writes, per token of the tile, the maximum over the block's NW WC columns,
+// the lowest column attaining it and sum exp(l - max) to the tile's partials.
+template <int NW, int RT, int CT>
+__device__ __forceinline__ void head_tile_epilogue(const f32x4_t (&acc)[RT][CT], const HeadArgs& a,
+                                                   int n0, int m0, int nt, float (*xm)[16 * RT],
+                                                   float (*xs)[16 * RT], int (*xi)[16 * RT]) {
+  constexpr int WC = 16 * CT, BM = 16 * RT;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, l16 = lane & 15, g = lane >> 4;
-  const uint16_t* A = (const uint16_t*)a.A;
-  const uint16_t* W = (const uint16_t*)a.B;
-  const int K = a.K, nk = K / BK, nkp = (nk + P - 1) / P * P;
-
-  const uint16_t* ap[A_LD];
-  bool aok[A_LD];
-#pragma unroll
-  for (int p = 0; p < A_LD; p++) {
-    const int r = m0 + (t >> 3) + A_RSTEP * p;
-    aok[p] = r < a.M;
-    ap[p] = A + (size_t)(aok[p] ? r : 0) * K + (t & 7) * 8;
-  }
-  // packed weights: one 1 KB wave load per (column tile, k-tile, half)
-  const char* bp[CT];
-#pragma unroll
-  for (int ct = 0; ct < CT; ct++) {
-    const int n = n0 + WC * w + 16 * ct;
-    bp[ct] = packed_group(W, n < a.V ? n : 0, nk) + 16 * lane;   // groups past V: masked in the epilogue
-  }
-
-  f32x4_t acc[RT][CT];
-#pragma unroll
-  for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-    for (int ct = 0; ct < CT; ct++) acc[rt][ct] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-
-  uint4 ra[P][A_LD];
-  FragBF rb[P][2][CT];
-  auto gload = [&](int st, int kt) {
-    const int k0 = (kt < nk ? kt : nk - 1) * BK;   // clamped: always issued
-#pragma unroll
-    for (int p = 0; p < A_LD; p++) ra[st][p] = *reinterpret_cast<const uint4*>(ap[p] + k0);
-#pragma unroll
-    for (int ks = 0; ks < 2; ks++)
-#pragma unroll
-      for (int ct = 0; ct < CT; ct++)
-        rb[st][ks][ct].v = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(bp[ct] + (size_t)(k0 / BK) * 2048 + ks * 1024));
-  };
-  // tiles past the end are stored as zeros, so their MFMAs add nothing
-  auto astore = [&](int st, int buf, bool ok) {
-#pragma unroll
-    for (int p = 0; p < A_LD; p++) {
-      uint4 u = ra[st][p];
-      const bool z = aok[p] && ok;
-      u.x = z ? u.x : 0u;
-      u.y = z ? u.y : 0u;
-      u.z = z ? u.z : 0u;
-      u.w = z ? u.w : 0u;
-      *reinterpret_cast<uint4*>(&sA[buf][((t >> 3) + A_RSTEP * p) * LDK + (t & 7) * 8]) = u;
-    }
-  };
-  FragBF af[2][RT];
-  auto lload = [&](int buf, int ks) {
-#pragma unroll
-    for (int rt = 0; rt < RT; rt++) load_frag(af[ks][rt], &sA[buf][(16 * rt + l16) * LDK + 32 * ks + 8 * g]);
-  };
-  auto mmas = [&](int st, int ks) {
-#pragma unroll
-    for (int rt = 0; rt < RT; rt++)
-#pragma unroll
-      for (int ct = 0; ct < CT; ct++) mma(acc[rt][ct], rb[st][ks][ct], af[ks][rt]);   // logits^T
-  };
-
-#pragma unroll
-  for (int st = 0; st < P; st++) gload(st, st);
-  astore(0, 0, true);
-  astore(1 % P, 1, 1 < nk);
-  __syncthreads();
-  lload(0, 0);
-  int cur = 0;   // LDS buffer of tile kt
-  auto step = [&](int st, int kt, auto with_load) {
-    const int nxt = cur == 2 ? 0 : cur + 1, nn = nxt == 2 ? 0 : nxt + 1;
-    lload(cur, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    mmas(st, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    lload(nxt, 0);   // tile kt+1: written one step ago, behind the last barrier
-    __builtin_amdgcn_sched_barrier(0);
-    mmas(st, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (decltype(with_load)::value) {
-      gload(st, kt + P);   // stage st: its A tile is in LDS, its B fragments consumed
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    astore((st + 2) % P, nn, kt + 2 < nk);
-    __syncthreads();
-    cur = nxt;
-  };
-  int kb = 0;
-  for (; kb + P < nkp; kb += P) {
-#pragma unroll
-    for (int st = 0; st < P; st++) step(st, kb + st, std::integral_constant<bool, true>{});
-  }
-  // last group: every tile it needs is already loaded, so it issues no loads
-  // (loads past the end would only hold the epilogue's registers)
-#pragma unroll
-  for (int st = 0; st < P; st++) step(st, kb + st, std::integral_constant<bool, false>{});
-
-  // acc[rt][ct] is the transposed tile: lane (l16, g) holds vocabulary rows
-  // n0 + WC w + 16ct + 4g + i (i = 0..3) of token m0 + 16rt + l16, so a
-  // token's WC columns of this wave sit in 4 CT registers of 4 lanes (g = 0..3)
   if (a.logits) {   // debug tap: raw logits, 4 consecutive columns per store
 #pragma unroll
     for (int rt = 0; rt < RT; rt++)
@@ -910,6 +795,255 @@ __global__ __launch_bounds__(NW * 64, MINB) void lmhead_direct_k(HeadArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// LM head for bf16 activations and more than 64 rows.  Block tile: 128 rows x
+// 256 vocabulary entries; the 4 waves sit side by side (128 x 64 each).  Every
+// weight byte is used by exactly one wave, so the weight rows stream from HBM
+// straight into MFMA fragments; only the activation tile, which all 4 waves
+// share, goes through LDS (a ring of P contraction tiles in flight in
+// registers, LDS double buffer).  Staging both operands through LDS would make
+// the LDS write port the bottleneck.
+// ---------------------------------------------------------------------------
+template <int P, int NW, int BN, int MINB>
+__global__ __launch_bounds__(NW * 64, MINB) void lmhead_direct_k(HeadArgs a) {
+  constexpr int NT = NW * 64;                 // threads
+  constexpr int BM = 128, BK = 64, LDK = 80, RT = 8;   // 160-byte LDS rows: conflict-free fragment reads
+  constexpr int WC = BN / NW, CT = WC / 16;   // vocabulary columns per wave
+  constexpr int A_LD = BM * BK * 2 / 16 / NT;   // 16-byte A chunks staged per thread
+  constexpr int A_RSTEP = NT / 8;             // rows between a thread's chunks
+  // three LDS buffers: while tile kt is consumed, tile kt+1 is readable (its
+  // first fragments are prefetched) and tile kt+2 is being written
+  __shared__ __attribute__((aligned(16))) uint16_t sA[3][BM * LDK];
+  __shared__ float xm[NW][BM], xs[NW][BM];
+  __shared__ int xi[NW][BM];
+  const int b8 = blockIdx.x >> 3, mtiles = a.mtiles;
+  const int nt = (b8 / mtiles) * 8 + (blockIdx.x & 7), mt = b8 % mtiles;
+  if (nt >= a.ntiles) return;
+  const int n0 = nt * BN, m0 = mt * BM;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, l16 = lane & 15, g = lane >> 4;
+  const uint16_t* A = (const uint16_t*)a.A;
+  const uint16_t* W = (const uint16_t*)a.B;
+  const int K = a.K, nk = K / BK, nkp = (nk + P - 1) / P * P;
+
+  const uint16_t* ap[A_LD];
+  bool aok[A_LD];
+#pragma unroll
+  for (int p = 0; p < A_LD; p++) {
+    const int r = m0 + (t >> 3) + A_RSTEP * p;
+    aok[p] = r < a.M;
+    ap[p] = A + (size_t)(aok[p] ? r : 0) * K + (t & 7) * 8;
+  }
+  // packed weights: one 1 KB wave load per (column tile, k-tile, half)
+  const char* bp[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ct++) {
+    const int n = n0 + WC * w + 16 * ct;
+    bp[ct] = packed_group(W, n < a.V ? n : 0, nk) + 16 * lane;   // groups past V: masked in the epilogue
+  }
+
+  f32x4_t acc[RT][CT];
+#pragma unroll
+  for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+    for (int ct = 0; ct < CT; ct++) acc[rt][ct] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+  uint4 ra[P][A_LD];
+  FragBF rb[P][2][CT];
+  auto gload = [&](int st, int kt) {
+    const int k0 = (kt < nk ? kt : nk - 1) * BK;   // clamped: always issued
+#pragma unroll
+    for (int p = 0; p < A_LD; p++) ra[st][p] = *reinterpret_cast<const uint4*>(ap[p] + k0);
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+      for (int ct = 0; ct < CT; ct++)
+        rb[st][ks][ct].v = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(bp[ct] + (size_t)(k0 / BK) * 2048 + ks * 1024));
+  };
+  // tiles past the end are stored as zeros, so their MFMAs add nothing
+  auto astore = [&](int st, int buf, bool ok) {
+#pragma unroll
+    for (int p = 0; p < A_LD; p++) {
+      uint4 u = ra[st][p];
+      const bool z = aok[p] && ok;
+      u.x = z ? u.x : 0u;
+      u.y = z ? u.y : 0u;
+      u.z = z ? u.z : 0u;
+      u.w = z ? u.w : 0u;
+      *reinterpret_cast<uint4*>(&sA[buf][((t >> 3) + A_RSTEP * p) * LDK + (t & 7) * 8]) = u;
+    }
+  };
+  FragBF af[2][RT];
+  auto lload = [&](int buf, int ks) {
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++) load_frag(af[ks][rt], &sA[buf][(16 * rt + l16) * LDK + 32 * ks + 8 * g]);
+  };
+  auto mmas = [&](int st, int ks) {
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+      for (int ct = 0; ct < CT; ct++) mma(acc[rt][ct], rb[st][ks][ct], af[ks][rt]);   // logits^T
+  };
+
+#pragma unroll
+  for (int st = 0; st < P; st++) gload(st, st);
+  astore(0, 0, true);
+  astore(1 % P, 1, 1 < nk);
+  __syncthreads();
+  lload(0, 0);
+  int cur = 0;   // LDS buffer of tile kt
+  auto step = [&](int st, int kt, auto with_load) {
+    const int nxt = cur == 2 ? 0 : cur + 1, nn = nxt == 2 ? 0 : nxt + 1;
+    lload(cur, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mmas(st, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    lload(nxt, 0);   // tile kt+1: written one step ago, behind the last barrier
+    __builtin_amdgcn_sched_barrier(0);
+    mmas(st, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (decltype(with_load)::value) {
+      gload(st, kt + P);   // stage st: its A tile is in LDS, its B fragments consumed
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    astore((st + 2) % P, nn, kt + 2 < nk);
+    __syncthreads();
+    cur = nxt;
+  };
+  int kb = 0;
+  for (; kb + P < nkp; kb += P) {
+#pragma unroll
+    for (int st = 0; st < P; st++) step(st, kb + st, std::integral_constant<bool, true>{});
+  }
+  // last group: every tile it needs is already loaded, so it issues no loads
+  // (loads past the end would only hold the epilogue's registers)
+#pragma unroll
+  for (int st = 0; st < P; st++) step(st, kb + st, std::integral_constant<bool, false>{});
+
+  head_tile_epilogue<NW, RT, CT>(acc, a, n0, m0, nt, xm, xs, xi);
+}
+
+// ---------------------------------------------------------------------------
+// LM head for bf16 activations and many rows (batched canvases).  Block tile
+// 128 rows x BN vocabulary entries, NW waves side by side of 128 rows x 64
+// columns each.  Every wave reads the whole activation tile from LDS each
+// step, so twice the columns of lmhead_direct_k per wave halve the LDS
+// fragment reads per MFMA (the LDS command queue is what fills up there).
+// The 128 accumulators per lane leave room for one fragment register set and
+// two register stages: a step reads its fragments while the other wave of
+// the SIMD multiplies, and the activation tile of step kt + 1 is stored from
+// registers loaded one step earlier.
+// ---------------------------------------------------------------------------
+template <int P, int NW, int BN>
+__global__ __launch_bounds__(NW * 64, 1) void lmhead_wide_k(HeadArgs a) {
+  constexpr int NT = NW * 64;                 // threads
+  constexpr int BM = 128, BK = 64, LDK = 80, RT = 8;   // 160-byte LDS rows: conflict-free fragment reads
+  constexpr int WC = BN / NW, CT = WC / 16;   // vocabulary columns per wave
+  constexpr int A_LD = BM * BK * 2 / 16 / NT;   // 16-byte A chunks staged per thread
+  constexpr int A_RSTEP = NT / 8;             // rows between a thread's chunks
+  static_assert(A_LD >= 1 && A_LD * NT * 16 == BM * BK * 2, "activation staging");
+  // two LDS buffers: tile kt is read while tile kt + 1 is written
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * LDK];
+  __shared__ float xm[NW][BM], xs[NW][BM];
+  __shared__ int xi[NW][BM];
+  const int b8 = blockIdx.x >> 3, mtiles = a.mtiles;
+  const int nt = (b8 / mtiles) * 8 + (blockIdx.x & 7), mt = b8 % mtiles;
+  if (nt >= a.ntiles) return;
+  const int n0 = nt * BN, m0 = mt * BM;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, l16 = lane & 15, g = lane >> 4;
+  const uint16_t* A = (const uint16_t*)a.A;
+  const uint16_t* W = (const uint16_t*)a.B;
+  const int K = a.K, nk = K / BK, nkp = (nk + P - 1) / P * P;
+
+  const uint16_t* ap[A_LD];
+  bool aok[A_LD];
+#pragma unroll
+  for (int p = 0; p < A_LD; p++) {
+    const int r = m0 + (t >> 3) + A_RSTEP * p;
+    aok[p] = r < a.M;
+    ap[p] = A + (size_t)(aok[p] ? r : 0) * K + (t & 7) * 8;
+  }
+  const char* bp[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ct++) {
+    const int n = n0 + WC * w + 16 * ct;
+    bp[ct] = packed_group(W, n < a.V ? n : 0, nk) + 16 * lane;   // groups past V: masked in the epilogue
+  }
+
+  f32x4_t acc[RT][CT];
+#pragma unroll
+  for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+    for (int ct = 0; ct < CT; ct++) acc[rt][ct] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+  uint4 ra[P][A_LD];
+  FragBF rb[P][2][CT];
+  auto gload = [&](int st, int kt) {
+    const int k0 = (kt < nk ? kt : nk - 1) * BK;   // clamped: always issued
+#pragma unroll
+    for (int p = 0; p < A_LD; p++) ra[st][p] = *reinterpret_cast<const uint4*>(ap[p] + k0);
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++)
+#pragma unroll
+      for (int ct = 0; ct < CT; ct++)
+        rb[st][ks][ct].v = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(bp[ct] + (size_t)(k0 / BK) * 2048 + ks * 1024));
+  };
+  // tiles past the end are stored as zeros, so their MFMAs add nothing
+  auto astore = [&](int st, int buf, bool ok) {
+#pragma unroll
+    for (int p = 0; p < A_LD; p++) {
+      uint4 u = ra[st][p];
+      const bool z = aok[p] && ok;
+      u.x = z ? u.x : 0u;
+      u.y = z ? u.y : 0u;
+      u.z = z ? u.z : 0u;
+      u.w = z ? u.w : 0u;
+      *reinterpret_cast<uint4*>(&sA[buf][((t >> 3) + A_RSTEP * p) * LDK + (t & 7) * 8]) = u;
+    }
+  };
+  FragBF af[RT];
+  auto lload = [&](int buf, int ks) {
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++) load_frag(af[rt], &sA[buf][(16 * rt + l16) * LDK + 32 * ks + 8 * g]);
+  };
+  auto mmas = [&](int st, int ks) {
+#pragma unroll
+    for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+      for (int ct = 0; ct < CT; ct++) mma(acc[rt][ct], rb[st][ks][ct], af[rt]);   // logits^T
+  };
+
+#pragma unroll
+  for (int st = 0; st < P; st++) gload(st, st);
+  astore(0, 0, true);
+  __syncthreads();
+  auto step = [&](int st, int kt, auto with_load) {
+    const int cur = kt & 1;
+    lload(cur, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mmas(st, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    lload(cur, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mmas(st, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (decltype(with_load)::value) {
+      gload(st, kt + P);   // stage st: its A tile is in LDS, its B fragments consumed
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    astore((st + 1) % P, cur ^ 1, kt + 1 < nk);   // tile kt + 1 into the buffer of tile kt - 1
+    __syncthreads();
+  };
+  int kb = 0;
+  for (; kb + P < nkp; kb += P) {
+#pragma unroll
+    for (int st = 0; st < P; st++) step(st, kb + st, std::integral_constant<bool, true>{});
+  }
+#pragma unroll
+  for (int st = 0; st < P; st++) step(st, kb + st, std::integral_constant<bool, false>{});
+
+  head_tile_epilogue<NW, RT, CT>(acc, a, n0, m0, nt, xm, xs, xi);
+}
+
+// ---------------------------------------------------------------------------
 void launch_gemm(int act, int mode, const void* A, int M, int K, const void* B0, int n1,
                  const void* B1, int n2, const void* B2, int N, void* C, int ldc, const void* R,
                  const CacheDst* cache, hipStream_t s) {
@@ -986,9 +1120,20 @@ constexpr int LMHEAD_P = 4;
 constexpr int LMHEAD_NW = 8;
 constexpr int LMHEAD_BN = 256;
 constexpr int LMHEAD_MINB = 1;
+// from this many rows: 64 vocabulary columns per wave, 512 per block
+constexpr int LMHEAD_WIDE_MIN_ROWS = 1024;
+constexpr int LMHEAD_WIDE_P = 2;
+constexpr int LMHEAD_WIDE_BN = 512;
 
 int launch_lmhead(int act, const void* uf, int M, int D, const void* lm, int V, float* pmax,
                   int32_t* pidx, float* psum, float* logits, hipStream_t s) {
+  if (act == ACT_BF16 && M >= LMHEAD_WIDE_MIN_ROWS) {
+    const int nt = (V + LMHEAD_WIDE_BN - 1) / LMHEAD_WIDE_BN;
+    HeadArgs a{uf, M, D, lm, V, pmax, pidx, psum, logits, nt, (M + 127) / 128};
+    lmhead_wide_k<LMHEAD_WIDE_P, LMHEAD_NW, LMHEAD_WIDE_BN>
+        <<<((nt + 7) / 8) * 8 * a.mtiles, LMHEAD_NW * 64, 0, s>>>(a);
+    return nt;
+  }
   if (act == ACT_BF16 && M > 64) {
     const int nt = (V + LMHEAD_BN - 1) / LMHEAD_BN;
     HeadArgs a{uf, M, D, lm, V, pmax, pidx, psum, logits, nt, (M + 127) / 128};
