@@ -40,7 +40,7 @@ def _source_hash(files):
 DOMINANT = {
     "bf16": ("gateup", "hbm", "dg::wstream_k<bf16, bf16, 4, 4, 2, 4> (grouped gate/up + SwiGLU)",
              ("kern_stream.hip", "common.h", "launch.h")),
-    "fp8": ("head", "mfma", "dg::lmhead_direct_k (LM head + argmax/confidence partials)",
+    "fp8": ("head", "mfma", "dg::lmhead_wide_k (LM head + argmax/confidence partials, 2048 rows)",
             ("kern_gemm.hip", "common.h", "launch.h")),
 }
 
