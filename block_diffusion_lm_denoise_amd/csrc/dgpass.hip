@@ -51,7 +51,9 @@ size_t router_floats(const dg_config& c, int rows) {
 }
 
 // bytes of one (row, head) entry of the attention split partials: O and (m, l)
-size_t part_entry_bytes(const dg_config& c) { return (size_t)c.hd * 4 + 2 * 4; }
+// bytes of one (row, head) entry of the split partials: O in the activation
+// type, then (m, l) in fp32
+size_t part_entry_bytes(const dg_config& c) { return (size_t)c.hd * esize(c.act_dtype) + 2 * 4; }
 
 // Workspace carve for `rows` token rows with room for `part_entries` (row,
 // head) entries of attention split partials, which come last so that a
@@ -93,7 +95,7 @@ Layout layout(const dg_config& c, int rows, long part_entries) {
   L.lps = take(R * nt * 4);
   L.fixed = off;
   L.part_cap = part_entries > 0 ? part_entries : 0;
-  L.po = take((size_t)L.part_cap * c.hd * 4);
+  L.po = take((size_t)L.part_cap * c.hd * a);   // partial O in the activation type
   L.pml = take((size_t)L.part_cap * 2 * 4);
   L.total = off;
   return L;
@@ -107,7 +109,7 @@ Layout call_layout(const dg_config& c, int rows, int max_keys, size_t ws_bytes) 
   const size_t room = ws_bytes > L.fixed ? ws_bytes - L.fixed : 0;
   // the most entries whose two buffers (each rounded up to 256 bytes) fit the
   // room: a workspace sized by dg_workspace_bytes for these keys holds `want`
-  auto need = [&](long n) { return al((size_t)n * c.hd * 4) + al((size_t)n * 2 * 4); };
+  auto need = [&](long n) { return al((size_t)n * c.hd * esize(c.act_dtype)) + al((size_t)n * 2 * 4); };
   long fit = (long)(room / part_entry_bytes(c));
   while (fit > 0 && need(fit) > room) fit--;
   return layout(c, rows, want < fit ? want : fit);
@@ -492,7 +494,7 @@ static dg_status prefill(const dg_model* m, dg_kv* kv, const int32_t* tokens, in
                        at<void>(c, c.L.qkv), (size_t)R * QKV * a, s);
     if (l == cf.L - 1 && !head) break;  // nothing downstream reads the last layer's output
     AttnArgsHost ah{act, at<void>(c, c.L.qkv), QKV, kv->k[l], kv->v[l], kv->cap, nullptr, nullptr,
-                    B, T, cf.Hq, cf.Hkv, cf.hd, 1, lens, at<void>(c, c.L.o), at<float>(c, c.L.po),
+                    B, T, cf.Hq, cf.Hkv, cf.hd, 1, lens, at<void>(c, c.L.o), at<void>(c, c.L.po),
                     at<float>(c, c.L.pml), c.L.part_cap};
     stage_event(taps, l, DG_STAGE_ATTN, 0, s);
     launch_attention(ah, s);
@@ -572,7 +574,7 @@ static dg_status denoise(const dg_model* m, const dg_kv* kv, const int32_t* canv
                        at<void>(c, c.L.qkv), (size_t)R * QKV * a, s);
     const char* qkv = at<char>(c, c.L.qkv);
     AttnArgsHost ah{act, qkv, QKV, kv->k[l], kv->v[l], kv->cap, qkv + QD * a, qkv + (QD + KD) * a,
-                    B, N, cf.Hq, cf.Hkv, cf.hd, 0, lens, at<void>(c, c.L.o), at<float>(c, c.L.po),
+                    B, N, cf.Hq, cf.Hkv, cf.hd, 0, lens, at<void>(c, c.L.o), at<void>(c, c.L.po),
                     at<float>(c, c.L.pml), c.L.part_cap};
     stage_event(taps, l, DG_STAGE_ATTN, 0, s);
     launch_attention(ah, s);

@@ -43,7 +43,7 @@ struct AttnArgs {
   Lens len;
   float scale_log2;
   void* out;
-  float* po;      // [nsplit][rows*Hq][hd]
+  void* po;       // [nsplit][rows*Hq][hd], elements of the activation type
   float* pml;     // [nsplit][rows*Hq][2]
   int rows;       // B*T
   int nqt, groups;   // query tiles; (request, kv head, split) groups
@@ -395,7 +395,7 @@ __global__ __launch_bounds__(256) void attn_k(AttnArgs a) {
   // ---- key splits: unnormalised partials (O, m, l), merged by attn_merge_k ----
   if (!qvalid) return;
   const size_t e = split * (size_t)a.rows * a.Hq + row * a.Hq + head;
-  float* po = a.po + e * HD;
+  float* po = static_cast<float*>(a.po) + e * HD;
 #pragma unroll
   for (int ht = 0; ht < HD / 16; ht++)
 #pragma unroll
@@ -787,12 +787,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_k(AttnArgs a) {
         *reinterpret_cast<uint2*>(out + 16 * ht) =
             make_uint2(f2bf2(o[j][ht][0] * inv, o[j][ht][1] * inv), f2bf2(o[j][ht][2] * inv, o[j][ht][3] * inv));
     } else {
-      // key splits: unnormalised partials (O, m, l), merged by attn_merge_k
+      // key splits: unnormalised partials (O rounded to bf16, m, l in fp32),
+      // merged by attn_merge_k
       const size_t e = split * (size_t)a.rows * a.Hq + row * a.Hq + head[j];
-      float* po = a.po + e * HD + 4 * g4;
+      uint16_t* po = static_cast<uint16_t*>(a.po) + e * HD + 4 * g4;
 #pragma unroll
       for (int ht = 0; ht < NHT; ht++)
-        *reinterpret_cast<float4*>(po + 16 * ht) = make_float4(o[j][ht][0], o[j][ht][1], o[j][ht][2], o[j][ht][3]);
+        *reinterpret_cast<uint2*>(po + 16 * ht) =
+            make_uint2(f2bf2(o[j][ht][0], o[j][ht][1]), f2bf2(o[j][ht][2], o[j][ht][3]));
       if (g4 == 0) {
         a.pml[2 * e] = mrow[j];
         a.pml[2 * e + 1] = l;
@@ -804,11 +806,19 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_bf16_k(AttnArgs a) {
 // combine key splits in split order: o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
 // A thread owns 4 consecutive head-dimension elements of one (row, head)
 // entry and has the loads of every split in flight at once (the merge is a
-// short latency chain over 2 + nsplit loads).
+// short latency chain over 2 + nsplit loads).  The partial O_s are fp32 (fp32
+// attention) or bf16 (bf16 attention: half the partial traffic; the rounding
+// is one more bf16 step before the output's own, on a weighted average).
 constexpr int ATTN_MAX_SPLIT = 16;
 template <typename T> struct TypeTag { using type = T; };
+__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4(const uint16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
 template <typename TA, int HD, int NS>
-__global__ __launch_bounds__(256) void attn_merge_k(const float* __restrict__ po,
+__global__ __launch_bounds__(256) void attn_merge_k(const TA* __restrict__ po,
                                                     const float* __restrict__ pml, int nsplit,
                                                     int entries, TA* __restrict__ out) {
   constexpr int TPE = HD / 4;   // threads per entry
@@ -824,7 +834,7 @@ __global__ __launch_bounds__(256) void attn_merge_k(const float* __restrict__ po
     const size_t ee = (size_t)(j < nsplit ? j : 0) * entries + e;
     m[j] = pml[2 * ee];
     l[j] = pml[2 * ee + 1];
-    v[j] = *reinterpret_cast<const float4*>(po + ee * HD + d0);
+    v[j] = load4(po + ee * HD + d0);
   }
   float M = -INFINITY;
 #pragma unroll
@@ -962,8 +972,9 @@ void launch_attention(const AttnArgsHost& h, hipStream_t s) {
     auto merge = [&](auto tac, auto nsc) {
       using TA = typename decltype(tac)::type;
       constexpr int NS = decltype(nsc)::value;
-      if (h.hd == 128) attn_merge_k<TA, 128, NS><<<blocks, 256, 0, s>>>(h.po, h.pml, p.nsplit, entries, (TA*)h.out);
-      else attn_merge_k<TA, 64, NS><<<blocks, 256, 0, s>>>(h.po, h.pml, p.nsplit, entries, (TA*)h.out);
+      const TA* po = static_cast<const TA*>(h.po);   // partials of the attention's own type
+      if (h.hd == 128) attn_merge_k<TA, 128, NS><<<blocks, 256, 0, s>>>(po, h.pml, p.nsplit, entries, (TA*)h.out);
+      else attn_merge_k<TA, 64, NS><<<blocks, 256, 0, s>>>(po, h.pml, p.nsplit, entries, (TA*)h.out);
     };
     auto by_splits = [&](auto tac) {
       if (p.nsplit <= 4) merge(tac, std::integral_constant<int, 4>());

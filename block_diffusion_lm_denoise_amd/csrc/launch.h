@@ -177,7 +177,7 @@ struct AttnArgsHost {
   int mode;        // 0 = canvas (bidirectional over cache + canvas), 1 = causal over cache
   Lens len;
   void* out;       // [B*T][Hq*hd]
-  float* po;       // split partials
+  void* po;        // split partials O (activation type: bf16 or fp32)
   float* pml;
   long part_cap;   // capacity of the partial buffers in (row, head) entries
 };
