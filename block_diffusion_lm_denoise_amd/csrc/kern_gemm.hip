@@ -288,20 +288,26 @@ struct MainloopD {
 };
 
 // Main loop of the LDS-tiled GEMMs: bf16 activations take MainloopD with NWM
-// waves along the rows (2: 64-column wave tiles from BN = 128 on; 1: BN/32
-// waves of 32 columns side by side), fp32 activations Mainloop (2 x 2 waves).
+// waves along the rows (2: 64-column wave tiles from BN = 128 on; 1: waves of
+// group_wn columns side by side), fp32 activations Mainloop (2 x 2 waves).
 // Register rings: GROUP_P k-tiles for one wave along the rows, GEMM_P for
-// two.  Expert tiles of 64 rows keep a block under 128 VGPRs, so two blocks
-// share a CU and one block's barrier waits are filled by the other's MFMAs
-// (batch-8 fp8 gate/up: 176 us at 128-row tiles with one block per CU, 143 at
-// 64).
+// two.  Expert tiles of 64 rows keep a block small enough that two or three
+// blocks share a CU and one block's barrier waits are filled by the others'
+// MFMAs (batch-8 fp8 gate/up: 176 us at 128-row tiles with one block per CU,
+// 143 at 64).
 constexpr int GROUP_P = 2;
 constexpr int GROUP_BM = 64;   // rows of a bf16-activation expert tile
 constexpr int DENSE_WIDE = 1;  // dense bf16 GEMMs from 1024 rows: 64-row tiles, waves side by side
+// columns per wave with one wave along the rows: 64 for fp8 weights (each
+// wave reads the block's activation tile from LDS once per 64 columns: batch-8
+// gate/up 133 -> 127 us, down unchanged), 32 for bf16 weights (64 made the
+// dense projections at 2048 rows ~10 us slower in all)
+template <typename TW>
+constexpr int group_wn() { return sizeof(TW) == 1 ? 64 : 32; }
 template <typename TA, typename TW, int BM, int BN, int NWM>
 using GemmML = typename std::conditional<
     sizeof(TA) == 2,
-    typename std::conditional<NWM == 1, MainloopD<TW, BM, BN, GROUP_P, 1, 32>,
+    typename std::conditional<NWM == 1, MainloopD<TW, BM, BN, GROUP_P, 1, group_wn<TW>()>,
                               MainloopD<TW, BM, BN, GEMM_P, 2, (BN >= 128 ? 64 : BN / 2)>>::type,
     Mainloop<TA, TW, BM, BN, GEMM_P>>::type;
 template <typename TA, typename TW, int BM, int BN, int NWM>
