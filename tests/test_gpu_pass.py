@@ -96,6 +96,17 @@ def test_tiled_expert_path_narrow_column_blocks(expert, D, F):
     _run(pair, 2, [30, 5], 100, 17)
 
 
+def test_wide_lm_head_many_rows_ragged_vocab():
+    """Over 1024 rows the bf16 LM head takes 512-column vocabulary tiles of
+    64 columns per wave.  Five requests of 230 canvas tokens (1150 rows: the
+    last 128-row tile holds 126) and a vocabulary of 1000 (a second tile of 488
+    columns) reach its masked epilogue and its rows past the end; with the
+    oracle's final-norm rows injected the argmax bar is asserted."""
+    cfg = _cfg(V=1000)
+    pair = Pair(cfg, 19, scale_lm=10.0)
+    _run(pair, 5, [30, 5, 0, 12, 7], 230, 19)
+
+
 def test_ragged_prefixes_with_key_splits_full_width():
     """Two requests at the 1024-prefix layer's width, one with a 2048-token
     prefix and one with none: the attention splits the keys four ways, so the
