@@ -50,9 +50,8 @@ size_t router_floats(const dg_config& c, int rows) {
   return (size_t)rows * c.E * router_split(c, rows);
 }
 
-// bytes of one (row, head) entry of the attention split partials: O and (m, l)
-// bytes of one (row, head) entry of the split partials: O in the activation
-// type, then (m, l) in fp32
+// bytes of one (row, head) entry of the attention split partials: O in the
+// activation type, then (m, l) in fp32
 size_t part_entry_bytes(const dg_config& c) { return (size_t)c.hd * esize(c.act_dtype) + 2 * 4; }
 
 // Workspace carve for `rows` token rows with room for `part_entries` (row,
