@@ -560,9 +560,9 @@ __global__ __launch_bounds__((gemm_threads<TA, TW, BM, BN, NWM>())) void down_ld
 }
 
 // ---------------------------------------------------------------------------
-// LM head: logits tile [BM rows x 128 vocabulary], reduced per row to
-// (max, lowest index attaining it, sum exp(l - max)); logits never stored
-// unless the debug tap asks for them.
+// LM head for fp32 activations: logits tile [BM rows x 128 vocabulary],
+// reduced per row to (max, lowest index attaining it, sum exp(l - max));
+// logits never stored unless the debug tap asks for them.
 // ---------------------------------------------------------------------------
 struct HeadArgs {
   const void* A;
@@ -801,13 +801,14 @@ __device__ __forceinline__ void head_tile_epilogue(const f32x4_t (&acc)[RT][CT],
 }
 
 // ---------------------------------------------------------------------------
-// LM head for bf16 activations and more than 64 rows.  Block tile: 128 rows x
-// 256 vocabulary entries; the 4 waves sit side by side (128 x 64 each).  Every
-// weight byte is used by exactly one wave, so the weight rows stream from HBM
-// straight into MFMA fragments; only the activation tile, which all 4 waves
-// share, goes through LDS (a ring of P contraction tiles in flight in
-// registers, LDS double buffer).  Staging both operands through LDS would make
-// the LDS write port the bottleneck.
+// LM head for bf16 activations below 1024 rows.  Block tile: 128 rows x BN
+// vocabulary entries; the NW waves sit side by side (128 x BN/NW each: 8
+// waves of 32 columns).  Every weight byte is used by exactly one wave, so the
+// weight rows stream from HBM straight into MFMA fragments (P contraction
+// tiles in flight in registers); only the activation tile, which all waves
+// share, goes through LDS (a 3-buffer ring, stored from registers loaded two
+// steps earlier).  Staging both operands through LDS would make the LDS write
+// port the bottleneck.
 // ---------------------------------------------------------------------------
 template <int P, int NW, int BN, int MINB>
 __global__ __launch_bounds__(NW * 64, MINB) void lmhead_direct_k(HeadArgs a) {
@@ -1140,23 +1141,22 @@ int launch_lmhead(int act, const void* uf, int M, int D, const void* lm, int V, 
         <<<((nt + 7) / 8) * 8 * a.mtiles, LMHEAD_NW * 64, 0, s>>>(a);
     return nt;
   }
-  if (act == ACT_BF16 && M > 64) {
+  if (act == ACT_BF16) {
+    // any smaller row count, down to the one row of a decoding step (rows
+    // past M are masked; one row: 97 against 104 us per decoding step with
+    // the LDS-tiled head)
     const int nt = (V + LMHEAD_BN - 1) / LMHEAD_BN;
     HeadArgs a{uf, M, D, lm, V, pmax, pidx, psum, logits, nt, (M + 127) / 128};
     lmhead_direct_k<LMHEAD_P, LMHEAD_NW, LMHEAD_BN, LMHEAD_MINB>
         <<<((nt + 7) / 8) * 8 * a.mtiles, LMHEAD_NW * 64, 0, s>>>(a);
     return nt;
   }
+  // fp32 activations
   const int nt = (V + 127) / 128, bm = M > 64 ? 128 : 64;
   HeadArgs a{uf, M, D, lm, V, pmax, pidx, psum, logits, nt, (M + bm - 1) / bm};
   const dim3 grid(((nt + 7) / 8) * 8 * a.mtiles);
-  if (bm == 128) {
-    if (act == ACT_BF16) lmhead_k<uint16_t, 128, 1><<<grid, 256, 0, s>>>(a);
-    else lmhead_k<float, 128, 1><<<grid, 256, 0, s>>>(a);
-  } else {
-    if (act == ACT_BF16) lmhead_k<uint16_t, 64, 1><<<grid, 256, 0, s>>>(a);
-    else lmhead_k<float, 64, 1><<<grid, 256, 0, s>>>(a);
-  }
+  if (bm == 128) lmhead_k<float, 128, 1><<<grid, 256, 0, s>>>(a);
+  else lmhead_k<float, 64, 1><<<grid, 256, 0, s>>>(a);
   return nt;
 }
 
