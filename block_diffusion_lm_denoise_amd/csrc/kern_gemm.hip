@@ -1127,6 +1127,10 @@ constexpr int LMHEAD_P = 4;
 constexpr int LMHEAD_NW = 8;
 constexpr int LMHEAD_BN = 256;
 constexpr int LMHEAD_MINB = 1;
+// up to this many rows: 4-wave blocks of 128 vocabulary entries
+constexpr int LMHEAD_FEW_ROWS = 64;
+constexpr int LMHEAD_FEW_BN = 128;
+constexpr int LMHEAD_FEW_P = 3;
 // from this many rows: 64 vocabulary columns per wave, 512 per block
 constexpr int LMHEAD_WIDE_MIN_ROWS = 1024;
 constexpr int LMHEAD_WIDE_P = 2;
@@ -1141,10 +1145,17 @@ int launch_lmhead(int act, const void* uf, int M, int D, const void* lm, int V, 
         <<<((nt + 7) / 8) * 8 * a.mtiles, LMHEAD_NW * 64, 0, s>>>(a);
     return nt;
   }
-  if (act == ACT_BF16) {
-    // any smaller row count, down to the one row of a decoding step (rows
-    // past M are masked; one row: 97 against 104 us per decoding step with
-    // the LDS-tiled head)
+  if (act == ACT_BF16 && M <= LMHEAD_FEW_ROWS) {
+    // a few rows (decoding steps): 128 vocabulary entries per block of 4
+    // waves, so one row tile still makes a block per CU (one row: 94.6 against
+    // 97.3 us per decoding step with 256-entry blocks, 104 with the LDS-tiled
+    // head); 3 register stages keep it within 256 VGPRs
+    const int nt = (V + LMHEAD_FEW_BN - 1) / LMHEAD_FEW_BN;
+    HeadArgs a{uf, M, D, lm, V, pmax, pidx, psum, logits, nt, (M + 127) / 128};
+    lmhead_direct_k<LMHEAD_FEW_P, 4, LMHEAD_FEW_BN, 2><<<((nt + 7) / 8) * 8 * a.mtiles, 4 * 64, 0, s>>>(a);
+    return nt;
+  }
+  if (act == ACT_BF16) {   // rows past M are masked
     const int nt = (V + LMHEAD_BN - 1) / LMHEAD_BN;
     HeadArgs a{uf, M, D, lm, V, pmax, pidx, psum, logits, nt, (M + 127) / 128};
     lmhead_direct_k<LMHEAD_P, LMHEAD_NW, LMHEAD_BN, LMHEAD_MINB>
