@@ -36,6 +36,14 @@ __device__ __forceinline__ void stx(uint16_t* p, size_t i, float v) { p[i] = f2b
 __device__ __forceinline__ float rnd(float v, const float*) { return v; }
 __device__ __forceinline__ float rnd(float v, const uint16_t*) { return bf2f(f2bf(v)); }
 
+// SwiGLU of one (gate, up) pair: silu(g) * u = g / (1 + e^-g) * u, with the
+// hardware base-2 exponential and reciprocal (a few fp32 ulps, below the
+// rounding of the stored result).  Very negative g: e^-g is +inf, its
+// reciprocal 0, and the result a signed zero.
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f)) * u;
+}
+
 // ---------------------------------------------------------------------------
 // MFMA fragments.  A fragment is 8 consecutive contraction-dim elements of one
 // matrix row held by one lane.  For a 16x16 output tile, lane l holds row

@@ -502,7 +502,7 @@ __global__ __launch_bounds__((gemm_threads<TA, TW, BM, BN, NWM>())) void gateup_
         if (r >= nrows) continue;
         const float gv = acc[rt][2 * p][i] * sg, uv = acc[rt][2 * p + 1][i] * su;
         const int f = f0 + wn * (ML::WN / 2) + 16 * p + l16;
-        stx((TA*)a.out, (size_t)(row0 + r) * a.ldo + f, gv / (1.f + expf(-gv)) * uv);
+        stx((TA*)a.out, (size_t)(row0 + r) * a.ldo + f, swiglu(gv, uv));
       }
 }
 

@@ -394,7 +394,7 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
           const int r = rt * 16 + 4 * g + i;
           if (r < nrows)
             stx((TA*)a.out, (size_t)(row0 + r) * a.ldo + (chunk * CWG + grp) * 32 + 16 * pp + l16,
-                gv / (1.f + expf(-gv)) * uv);
+                swiglu(gv, uv));
         }
       }
     } else {
