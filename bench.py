@@ -143,6 +143,7 @@ def main():
                     masked_left=counts[1] if args.early_exit else None)
         dgpass.canvas_update(canvas, None, None, dict(base, pass_tag=0), cfg.V)
         ran = S
+        carry = False   # the workspace holds the first layer's input of `canvas`
         for p in range(S):
             # one mid-canvas pass of each timed step carries the stage events of
             # the dominant kernel (an event record costs a few us of GPU time)
@@ -150,10 +151,15 @@ def main():
             # coverage and the update for the next pass run in the pass's last
             # kernel (uniform: none after the last pass; masked: the last update
             # fills every masked slot)
+            # (and the embedding of the updated canvas, when the next pass
+            # takes an update: that pass then skips its own embedding)
             last = p == S - 1
-            nxt = None if (last and not masked) else dict(base, pass_tag=p + 1, final_pass=last)
+            ahead = p + 1 < S and (masked or p + 1 < S - 1)
+            nxt = None if (last and not masked) else dict(base, pass_tag=p + 1, final_pass=last,
+                                                          embed_next=ahead, input_embedded=carry)
             model.denoise_pass_next(kv, canvas, argmax, conf, ws, touched=touched[c, p], renoise=nxt,
                                     stage_events=se)
+            carry = nxt is not None and nxt["embed_next"]
             if args.early_exit and not last:
                 torch.cuda.synchronize()
                 if int(counts[1 if masked else 0].max()) == 0:
@@ -206,13 +212,23 @@ def main():
     if chained:   # the pass-only figures use a cache holding the prompt
         model.kv_prefill(kv, prompt, ws)
     pass_lens = kv.lens.copy()
-    model.denoise_pass(kv, canvas, argmax, conf, ws)
+    # a pass as it runs inside a canvas: the fused tail (coverage, update,
+    # embedding of the updated canvas) included, its own embedding skipped
+    inner = dict(sampler=args.sampler, mask_id=cfg.V - 1, tau=wl.tau, seed=wl.seed,
+                 pos0=pass_lens.copy(), pass_tag=1, embed_next=True, input_embedded=False)
+    cov_scratch = torch.zeros(cfg.L, dtype=torch.int32, device=dev)
+
+    def inner_pass():
+        model.denoise_pass_next(kv, canvas, argmax, conf, ws, touched=cov_scratch, renoise=inner)
+        inner["input_embedded"] = True
+
+    inner_pass()
     torch.cuda.synchronize()
     npass = max(8, args.steps)
     p0, p1 = ev_pair()
     p0.record()
     for _ in range(npass):
-        model.denoise_pass(kv, canvas, argmax, conf, ws)
+        inner_pass()
     p1.record()
     torch.cuda.synchronize()
     pass_us = p0.elapsed_time(p1) / npass * 1e3
@@ -223,7 +239,7 @@ def main():
         scratch.fill_(1)
         a, b = ev_pair()
         a.record()
-        model.denoise_pass(kv, canvas, argmax, conf, ws)
+        inner_pass()
         b.record()
         torch.cuda.synchronize()
         cold.append(a.elapsed_time(b) * 1e3)

@@ -155,6 +155,9 @@ struct Ctx {
   const dg_taps* taps;
   hipStream_t s;
   bool pass;      // denoising pass (writes coverage counts)
+  int32_t* zero0 = nullptr;   // [nzero] counters the pass's last kernel adds to,
+  int32_t* zero1 = nullptr;   // cleared by the last layer's combine
+  int nzero = 0;
 };
 
 template <typename T>
@@ -251,31 +254,38 @@ void moe_block(const Ctx& c, int l, const float* gnext) {
   // fused RMSNorm + router + top-k on 16-token tiles (bf16): only with many
   // tiles, since each tile is a serial chain (with few, the unfused kernels
   // spread the work over more of the chip)
-  if (c.R < ROUTE_MIN_ROWS || !launch_route(act, ra, s)) {
-    launch_rmsnorm(act, at<void>(c, c.L.x1), w.g2, c.R, cf.D, cf.eps, at<void>(c, c.L.u2), s);
+  if (c.R <= STREAM_MAX_ROWS) {
+    // the RMSNorm rides on the router and top-k launches (one dependent launch
+    // fewer): the streamed router multiplies x1 by g2 in flight, and top-k
+    // takes the row's rsqrt, scales the summed logits by it and writes u2
+    const bool inj = t && t->inject_router;
     int S = 1;
-    if (!(t && t->inject_router)) {
-      if (c.R <= STREAM_MAX_ROWS) {
-        // weight streaming with contraction splits; top-k sums the partials
-        S = router_split(cf, c.R);
-        StreamGemm g{};
-        g.A = at<void>(c, c.L.u2);
-        g.M = c.R;
-        g.K = cf.D;
-        g.W0 = w.wr;
-        g.n1 = cf.E;
-        g.N = cf.E;
-        g.nchunks = (cf.E + 63) / 64;
-        g.ksplit = S;
-        g.out = at<void>(c, c.L.rl);
-        g.ldo = cf.E;
-        launch_stream_gemm(act, cf.act_dtype, SG_F32, 4, g, 0, s);
-      } else {
-        dense_gemm(c, GEMM_F32, at<void>(c, c.L.u2), c.R, cf.D, w.wr, cf.E, nullptr, 0, nullptr, cf.E,
-                   at<void>(c, c.L.rl), cf.E, nullptr, nullptr);
-      }
+    if (!inj) {
+      // weight streaming with contraction splits; top-k sums the partials
+      S = router_split(cf, c.R);
+      StreamGemm g{};
+      g.A = at<void>(c, c.L.x1);
+      g.M = c.R;
+      g.K = cf.D;
+      g.W0 = w.wr;
+      g.n1 = cf.E;
+      g.N = cf.E;
+      g.nchunks = (cf.E + 63) / 64;
+      g.ksplit = S;
+      g.gs = w.g2;
+      g.out = at<void>(c, c.L.rl);
+      g.ldo = cf.E;
+      launch_stream_gemm(act, cf.act_dtype, SG_F32, 4, g, 0, s);
     }
-    launch_topk(const_cast<float*>(rl), S, c.R, cf.E, cf.k, at<int32_t>(c, c.L.ids),
+    TopkNorm tn{at<void>(c, c.L.x1), w.g2, cf.D, cf.eps, at<void>(c, c.L.u2), inj ? 0 : 1};
+    launch_topk_norm(act, const_cast<float*>(rl), S, c.R, cf.E, cf.k, at<int32_t>(c, c.L.ids),
+                     at<float>(c, c.L.gates), tn, s);
+  } else if (c.R < ROUTE_MIN_ROWS || !launch_route(act, ra, s)) {
+    launch_rmsnorm(act, at<void>(c, c.L.x1), w.g2, c.R, cf.D, cf.eps, at<void>(c, c.L.u2), s);
+    if (!(t && t->inject_router))
+      dense_gemm(c, GEMM_F32, at<void>(c, c.L.u2), c.R, cf.D, w.wr, cf.E, nullptr, 0, nullptr, cf.E,
+                 at<void>(c, c.L.rl), cf.E, nullptr, nullptr);
+    launch_topk(const_cast<float*>(rl), 1, c.R, cf.E, cf.k, at<int32_t>(c, c.L.ids),
                 at<float>(c, c.L.gates), s);
   }
   if (t) {
@@ -360,7 +370,8 @@ void moe_block(const Ctx& c, int l, const float* gnext) {
   // x = x1 + sum_j g_j y_j; u = next norm
   launch_combine_norm(act, at<void>(c, c.L.x1), at<void>(c, c.L.Y), at<float>(c, c.L.gates),
                       at<int32_t>(c, c.L.inv), c.R, cf.k, cf.D, gnext, cf.eps, at<void>(c, c.L.x),
-                      at<void>(c, c.L.u), s);
+                      at<void>(c, c.L.u), s, l + 1 == cf.L ? c.zero0 : nullptr,
+                      l + 1 == cf.L ? c.zero1 : nullptr, c.nzero);
   if (t) tap_copy(t->xout ? (char*)t->xout + l * R * D * a : nullptr, at<void>(c, c.L.x), R * D * a, s);
 }
 
@@ -535,7 +546,8 @@ dg_status dg_decode_step(const dg_model* m, dg_kv* kv, const int32_t* tokens, in
 // one pass; nx carries the between-pass work its last kernel takes over
 static dg_status denoise(const dg_model* m, const dg_kv* kv, const int32_t* canvas, int32_t B,
                          int32_t N, int32_t* argmax, float* conf, const dg_taps* taps, void* ws,
-                         size_t ws_bytes, void* stream, MergeNext nx) {
+                         size_t ws_bytes, void* stream, MergeNext nx, bool embed_next = false,
+                         bool input_embedded = false) {
   if (!model_ok(m) || !kv || !kv->len || !canvas || !argmax || !conf || !ws) return DG_ERR_INVALID;
   if (B < 1 || B > DG_MAX_BATCH || N < 1) return DG_ERR_INVALID;
   const dg_config& cf = m->cfg;
@@ -561,9 +573,16 @@ static dg_status denoise(const dg_model* m, const dg_kv* kv, const int32_t* canv
   const size_t a = esize(cf.act_dtype);
   const int QD = cf.Hq * cf.hd, KD = cf.Hkv * cf.hd, QKV = QD + 2 * KD;
   hipStream_t s = c.s;
-  launch_embed_norm(act, canvas, m->w.emb, m->w.layers[0].g1, R, cf.D, cf.V, cf.eps, at<void>(c, c.L.x),
-                    at<void>(c, c.L.u), s, nx.rn.canvas ? nx.rn.changed : nullptr, B,
-                    nx.rn.canvas ? nx.rn.masked_left : nullptr, B);
+  if (nx.rn.canvas) {
+    c.zero0 = nx.rn.changed;
+    c.zero1 = nx.rn.masked_left;
+    c.nzero = B;
+  }
+  // the first layer's input: embedded here, or (input_embedded) written into
+  // the workspace by the previous pass's last kernel
+  if (!(nx.rn.canvas && input_embedded))
+    launch_embed_norm(act, canvas, m->w.emb, m->w.layers[0].g1, R, cf.D, cf.V, cf.eps,
+                      at<void>(c, c.L.x), at<void>(c, c.L.u), s);
   for (int l = 0; l < cf.L; l++) {
     const dg_layer_weights& w = m->w.layers[l];
     inject_layer_input(c, l);
@@ -598,6 +617,15 @@ static dg_status denoise(const dg_model* m, const dg_kv* kv, const int32_t* canv
   nx.rn.B = B;
   nx.rn.N = N;
   nx.rn.V = (uint32_t)cf.V;
+  if (nx.rn.canvas && embed_next) {
+    nx.act = act;
+    nx.emb = m->w.emb;
+    nx.g1 = m->w.layers[0].g1;
+    nx.D = cf.D;
+    nx.eps = cf.eps;
+    nx.ex = at<void>(c, c.L.x);
+    nx.eu = at<void>(c, c.L.u);
+  }
   launch_lm_merge(at<float>(c, c.L.lpm), at<int32_t>(c, c.L.lpi), at<float>(c, c.L.lps), R, nparts,
                   argmax, conf, nx, s);
   return check_hip();
@@ -636,7 +664,8 @@ dg_status dg_denoise_pass_next(const dg_model* m, const dg_kv* kv, int32_t* canv
     nx.rn.changed = next->changed;
     nx.rn.masked_left = next->masked_left;
   }
-  return denoise(m, kv, canvas, B, N, argmax, conf, taps, ws, ws_bytes, stream, nx);
+  return denoise(m, kv, canvas, B, N, argmax, conf, taps, ws, ws_bytes, stream, nx,
+                 next && next->embed_next, next && next->input_embedded);
 }
 
 dg_status dg_denoise_pass_next_noalloc(const dg_model* m, const dg_kv* kv, int32_t* canvas, int32_t B,

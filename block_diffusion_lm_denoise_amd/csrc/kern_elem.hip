@@ -13,24 +13,13 @@ namespace dg {
 // 256 * 8 * ROWC elements); all loads of a phase are issued together.
 constexpr int ROWC = 2;
 
-// x[row] = emb[tok[row]] (copied), u[row] = round(x * rsqrt(mean(x^2)+eps) * g)
-// (token ids outside [0, V) are clamped into range rather than read out of bounds)
+// x[row] = emb[tk] (copied), u[row] = round(x * rsqrt(mean(x^2)+eps) * g) by
+// the 256 threads of a block
 template <typename TA>
-__global__ __launch_bounds__(256) void embed_norm_k(const int32_t* __restrict__ tok,
-                                                    const TA* __restrict__ emb,
-                                                    const float* __restrict__ g, int D, int V,
-                                                    float eps, TA* __restrict__ x,
-                                                    TA* __restrict__ u, int32_t* zero0, int nzero0,
-                                                    int32_t* zero1, int nzero1) {
-  __shared__ float red[4];
-  const size_t row = blockIdx.x;
-  // counters the pass's last kernel adds to start at zero: cleared here, by
-  // the pass's first kernel
-  if (row == 0) {
-    if (zero0 && (int)threadIdx.x < nzero0) zero0[threadIdx.x] = 0;
-    if (zero1 && (int)threadIdx.x < nzero1) zero1[threadIdx.x] = 0;
-  }
-  const int tk = min(max(tok[row], 0), V - 1);
+__device__ __forceinline__ void embed_norm_row(int tk, const TA* __restrict__ emb,
+                                               const float* __restrict__ g, int D, float eps,
+                                               TA* __restrict__ x, TA* __restrict__ u, size_t row,
+                                               float* red) {
   const TA* src = emb + (size_t)tk * D;
   float v[ROWC][8], gv[ROWC][8];
   float ss = 0.f;
@@ -75,6 +64,19 @@ __global__ __launch_bounds__(256) void embed_norm_k(const int32_t* __restrict__ 
     for (int i = 0; i < 8; i++) w[i] = w[i] * r * g[c + i];
     st8(u + row * D + c, w);
   }
+}
+
+// one block per token row (token ids outside [0, V) are clamped into range
+// rather than read out of bounds)
+template <typename TA>
+__global__ __launch_bounds__(256) void embed_norm_k(const int32_t* __restrict__ tok,
+                                                    const TA* __restrict__ emb,
+                                                    const float* __restrict__ g, int D, int V,
+                                                    float eps, TA* __restrict__ x,
+                                                    TA* __restrict__ u) {
+  __shared__ float red[4];
+  const int tk = min(max(tok[blockIdx.x], 0), V - 1);
+  embed_norm_row<TA>(tk, emb, g, D, eps, x, u, blockIdx.x, red);
 }
 
 template <typename TA>
@@ -131,9 +133,16 @@ __global__ __launch_bounds__(256) void combine_norm_k(const TA* __restrict__ x1,
                                                       const float* __restrict__ gates,
                                                       const int32_t* __restrict__ inv, int k, int D,
                                                       const float* __restrict__ gnext, float eps,
-                                                      TA* __restrict__ x, TA* __restrict__ u) {
+                                                      TA* __restrict__ x, TA* __restrict__ u,
+                                                      int32_t* zero0, int32_t* zero1, int nzero) {
   __shared__ float red[4];
   const size_t row = blockIdx.x;
+  // counters the pass's last kernel adds to start at zero: cleared here, by
+  // the last layer's combine (the kernel before the head)
+  if (row == 0 && (int)threadIdx.x < nzero) {
+    if (zero0) zero0[threadIdx.x] = 0;
+    if (zero1) zero1[threadIdx.x] = 0;
+  }
   float gs[8];
   int32_t rs[8];
 #pragma unroll
@@ -352,6 +361,7 @@ __global__ __launch_bounds__(256) void lm_merge_k(const float* __restrict__ pmax
                                                   float* __restrict__ conf, MergeNext nx) {
   __shared__ float sm[4], ss[4];
   __shared__ int si[4];
+  __shared__ int stok;
   if ((int)blockIdx.x >= rows) {
     coverage_block(nx.counts, nx.E, blockIdx.x - rows, nx.touched, nullptr, si);
     return;
@@ -391,7 +401,20 @@ __global__ __launch_bounds__(256) void lm_merge_k(const float* __restrict__ pmax
       if (nx.rn.changed && t != old) atomicAdd(nx.rn.changed + b, 1);
       if (nx.rn.masked_left && nx.rn.mode == DG_SAMPLER_MASKED && t == nx.rn.mask_id)
         atomicAdd(nx.rn.masked_left + b, 1);
+      stok = t;
     }
+  }
+  // the first layer's input of the updated slot for the next pass (what
+  // embed_norm_k would write from the new canvas)
+  if (nx.ex) {
+    __syncthreads();
+    const int tk = min(max(stok, 0), (int)nx.rn.V - 1);
+    if (nx.act == ACT_BF16)
+      embed_norm_row<uint16_t>(tk, (const uint16_t*)nx.emb, nx.g1, nx.D, nx.eps, (uint16_t*)nx.ex,
+                               (uint16_t*)nx.eu, row, sm);
+    else
+      embed_norm_row<float>(tk, (const float*)nx.emb, nx.g1, nx.D, nx.eps, (float*)nx.ex,
+                            (float*)nx.eu, row, sm);
   }
 }
 
@@ -437,15 +460,13 @@ __global__ __launch_bounds__(256) void pack_mx_k(const uint8_t* __restrict__ src
 
 // ---------------------------------------------------------------------------
 void launch_embed_norm(int act, const int32_t* tok, const void* emb, const float* g, int rows, int D,
-                       int V, float eps, void* x, void* u, hipStream_t s, int32_t* zero0, int nzero0,
-                       int32_t* zero1, int nzero1) {
+                       int V, float eps, void* x, void* u, hipStream_t s) {
   if (act == ACT_BF16)
     embed_norm_k<uint16_t><<<rows, 256, 0, s>>>(tok, (const uint16_t*)emb, g, D, V, eps,
-                                                 (uint16_t*)x, (uint16_t*)u, zero0, nzero0, zero1,
-                                                 nzero1);
+                                                 (uint16_t*)x, (uint16_t*)u);
   else
     embed_norm_k<float><<<rows, 256, 0, s>>>(tok, (const float*)emb, g, D, V, eps, (float*)x,
-                                              (float*)u, zero0, nzero0, zero1, nzero1);
+                                              (float*)u);
 }
 
 void launch_rmsnorm(int act, const void* x, const float* g, int rows, int D, float eps, void* u,
@@ -458,13 +479,14 @@ void launch_rmsnorm(int act, const void* x, const float* g, int rows, int D, flo
 
 void launch_combine_norm(int act, const void* x1, const void* Y, const float* gates,
                          const int32_t* inv, int rows, int k, int D, const float* gnext, float eps,
-                         void* x, void* u, hipStream_t s) {
+                         void* x, void* u, hipStream_t s, int32_t* zero0, int32_t* zero1, int nzero) {
   if (act == ACT_BF16)
     combine_norm_k<uint16_t><<<rows, 256, 0, s>>>((const uint16_t*)x1, (const uint16_t*)Y, gates,
-                                                   inv, k, D, gnext, eps, (uint16_t*)x, (uint16_t*)u);
+                                                   inv, k, D, gnext, eps, (uint16_t*)x, (uint16_t*)u,
+                                                   zero0, zero1, nzero);
   else
     combine_norm_k<float><<<rows, 256, 0, s>>>((const float*)x1, (const float*)Y, gates, inv, k, D,
-                                                gnext, eps, (float*)x, (float*)u);
+                                                gnext, eps, (float*)x, (float*)u, zero0, zero1, nzero);
 }
 
 void launch_renoise(int32_t* canvas, const int32_t* argmax, const float* conf, float tau,

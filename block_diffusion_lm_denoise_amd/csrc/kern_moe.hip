@@ -107,6 +107,91 @@ __global__ __launch_bounds__(64) void topk_k(float* __restrict__ logits, int nsp
   select_topk<1>(v, valid, E, k, idp, gp);
 }
 
+// Top-k with the RMSNorm in front of the router folded in (one wave per
+// row).  The row's x1 and g2 loads go out first, beside the router partials:
+// none of them depends on the others.  The wave sums the squares of its row
+// (8 consecutive elements per lane and 512-element chunk), writes
+// u2 = round(x1 * r * g2) with r = rsqrt(mean(x1^2) + eps), and ranks the
+// logits: the split sums times r when the router ran on round(x1 * g2)
+// (scale set), else the logits as given (injected).
+template <typename TA>
+__global__ __launch_bounds__(64) void topk_norm_k(float* __restrict__ logits, int nsplit, int rows,
+                                                  int E, int k, int32_t* __restrict__ ids,
+                                                  float* __restrict__ gates, const TA* __restrict__ x1,
+                                                  const float* __restrict__ g2, int D, float eps,
+                                                  TA* __restrict__ u2, int scale) {
+  constexpr int NC = 4;   // 512-element chunks held in registers (rows up to 2048)
+  const int lane = threadIdx.x;
+  const int row = blockIdx.x;
+  const TA* xr = x1 + (size_t)row * D;
+  float xv[NC][8], gv[NC][8];
+#pragma unroll
+  for (int c = 0; c < NC; c++) {   // chunks past the row re-read element 0 (never used): no branches
+    const int i = lane * 8 + 512 * c, ii = i < D ? i : 0;
+    ld8(xr + ii, xv[c]);
+    ld8(g2 + ii, gv[c]);
+  }
+  const size_t stride = (size_t)rows * E;
+  float p[4][ROUTER_MAX_SPLIT];
+#pragma unroll
+  for (int c = 0; c < 4; c++) {
+    const int e = lane + 64 * c;
+    const size_t o = (size_t)row * E + (e < E ? e : 0);
+#pragma unroll
+    for (int sp = 0; sp < ROUTER_MAX_SPLIT; sp++)
+      p[c][sp] = logits[(sp < nsplit ? sp : 0) * stride + o];
+  }
+  __builtin_amdgcn_sched_barrier(0);   // every load above is issued before the first use
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; c++)
+    if (lane * 8 + 512 * c < D)
+#pragma unroll
+      for (int i = 0; i < 8; i++) ss += xv[c][i] * xv[c][i];
+  for (int i0 = lane * 8 + 512 * NC; i0 < D; i0 += 512) {   // longer rows
+    float w[8];
+    ld8(xr + i0, w);
+#pragma unroll
+    for (int i = 0; i < 8; i++) ss += w[i] * w[i];
+  }
+  ss = wave_sum(ss);
+  const float r = rsqrtf(ss / (float)D + eps);
+  TA* ur = u2 + (size_t)row * D;
+#pragma unroll
+  for (int c = 0; c < NC; c++) {
+    const int i0 = lane * 8 + 512 * c;
+    if (i0 < D) {
+#pragma unroll
+      for (int i = 0; i < 8; i++) xv[c][i] = xv[c][i] * r * gv[c][i];
+      st8(ur + i0, xv[c]);
+    }
+  }
+  for (int i0 = lane * 8 + 512 * NC; i0 < D; i0 += 512) {
+    float w[8], h[8];
+    ld8(xr + i0, w);
+    ld8(g2 + i0, h);
+#pragma unroll
+    for (int i = 0; i < 8; i++) w[i] = w[i] * r * h[i];
+    st8(ur + i0, w);
+  }
+  float v[1][4];
+#pragma unroll
+  for (int c = 0; c < 4; c++) {
+    const int e = lane + 64 * c;
+    float x = p[c][0];
+#pragma unroll
+    for (int sp = 1; sp < ROUTER_MAX_SPLIT; sp++) x = sp < nsplit ? x + p[c][sp] : x;
+    if (scale) x *= r;
+    // the logits routing used (the router tap reads them back)
+    if (e < E && (nsplit > 1 || scale)) logits[(size_t)row * E + e] = x;
+    v[0][c] = x != x ? -INFINITY : x;  // a NaN logit ranks with -inf (ids stay in range)
+  }
+  const bool valid[1] = {true};
+  int32_t* const idp[1] = {ids + (size_t)row * k};
+  float* const gp[1] = {gates + (size_t)row * k};
+  select_topk<1>(v, valid, E, k, idp, gp);
+}
+
 // ---------------------------------------------------------------------------
 // plan: one block per expert.  Every block builds the expert histogram of all
 // (token, slot) entries in LDS and scans it; block e then lists its entries in
@@ -456,6 +541,18 @@ bool launch_route(int act, const RouteArgs& a, hipStream_t s) {
 void launch_topk(float* logits, int nsplit, int rows, int E, int k, int32_t* ids, float* gates,
                  hipStream_t s) {
   topk_k<<<rows, 64, 0, s>>>(logits, nsplit, rows, E, k, ids, gates);
+}
+
+void launch_topk_norm(int act, float* logits, int nsplit, int rows, int E, int k, int32_t* ids,
+                      float* gates, const TopkNorm& tn, hipStream_t s) {
+  if (act == ACT_BF16)
+    topk_norm_k<uint16_t><<<rows, 64, 0, s>>>(logits, nsplit, rows, E, k, ids, gates,
+                                               (const uint16_t*)tn.x1, tn.g2, tn.D, tn.eps,
+                                               (uint16_t*)tn.u2, tn.scale);
+  else
+    topk_norm_k<float><<<rows, 64, 0, s>>>(logits, nsplit, rows, E, k, ids, gates,
+                                            (const float*)tn.x1, tn.g2, tn.D, tn.eps, (float*)tn.u2,
+                                            tn.scale);
 }
 
 void launch_plan(const int32_t* ids, int rows, int k, int E, int tile_rows, int32_t* counts,

@@ -285,12 +285,58 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
       for (int rt = 0; rt < RT; rt++)
         ar[rt][j] = *reinterpret_cast<const u32x4*>(arow[rt] + c * PC::EP + PC::a_off(j, g));
   };
+  // router (SG_F32) with a.gs: each activation element times gs[element],
+  // rounded to the activation type, before the MFMAs (the RMSNorm weight in
+  // front of the router; the row's rsqrt is applied to the summed logits).
+  // A 16-byte register holds 16 / sizeof(TA) consecutive elements, whose
+  // scales come in two 16-byte loads (one for fp32).
+  constexpr bool GSC = MODE == SG_F32;
+  const bool gsc = GSC && a.gs != nullptr;
+  float4 gbuf[GSC ? NB : 1][GSC ? NA : 1][2];
+  auto load_g = [&](int b, int c) {
+    if constexpr (GSC) {
+      if (gsc) {
+#pragma unroll
+        for (int j = 0; j < NA; j++) {
+          const float* gp = a.gs + c * PC::EP + PC::a_off(j, g);
+          gbuf[b][j][0] = *reinterpret_cast<const float4*>(gp);
+          if constexpr (sizeof(TA) == 2) gbuf[b][j][1] = *reinterpret_cast<const float4*>(gp + 4);
+        }
+      }
+    }
+  };
+  auto scale_a = [&](int b) {
+    if constexpr (GSC) {
+      if (gsc) {
+#pragma unroll
+        for (int j = 0; j < NA; j++) {
+          const float gj[8] = {gbuf[b][j][0].x, gbuf[b][j][0].y, gbuf[b][j][0].z, gbuf[b][j][0].w,
+                               gbuf[b][j][1].x, gbuf[b][j][1].y, gbuf[b][j][1].z, gbuf[b][j][1].w};
+#pragma unroll
+          for (int rt = 0; rt < RT; rt++) {
+            u32x4 u = abuf[b][rt][j];
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+              if constexpr (sizeof(TA) == 2)
+                u[q] = f2bf2(__uint_as_float(u[q] << 16) * gj[2 * q],
+                             __uint_as_float(u[q] & 0xffff0000u) * gj[2 * q + 1]);
+              else
+                u[q] = __float_as_uint(__uint_as_float(u[q]) * gj[q]);
+            }
+            abuf[b][rt][j] = u;
+          }
+        }
+      }
+    }
+  };
   auto load = [&](int b, int c) {
     load_w(wbuf[b], c);
     load_s(sbuf[b], c);
     load_a(abuf[b], c);
+    load_g(b, c);
   };
   auto comp = [&](int b) {
+    scale_a(b);
     if constexpr (MX) piece_mma_mx<RT>(acc, wbuf[b], abuf[b], sbuf[b], nrt);
     else piece_mma<RT>(acc, wbuf[b], abuf[b], nrt, (TA*)nullptr, (TW*)nullptr);
   };
@@ -338,6 +384,7 @@ __global__ __launch_bounds__(256, 2) void wstream_k(StreamGemm a) {
   for (int rt = 0; rt < RT; rt++)
     arow[rt] = (const TA*)a.A + (size_t)(MODE == SG_GATEUP ? src[rt] / a.k : src[rt]) * K;
   load_a(abuf[0], cidx(0));
+  load_g(0, cidx(0));
 #pragma unroll
   for (int b = 1; b < NB; b++) load(b, cidx(b));
   int ib = 0;

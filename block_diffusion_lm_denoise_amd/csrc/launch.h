@@ -21,13 +21,13 @@ struct ReqIds {
 // ---- elementwise / reductions (kern_elem.hip) ----
 // zero: optional device ints cleared by the same launch (n <= 256 each)
 void launch_embed_norm(int act, const int32_t* tok, const void* emb, const float* g, int rows, int D,
-                       int V, float eps, void* x, void* u, hipStream_t s, int32_t* zero0 = nullptr,
-                       int nzero0 = 0, int32_t* zero1 = nullptr, int nzero1 = 0);
+                       int V, float eps, void* x, void* u, hipStream_t s);
 void launch_rmsnorm(int act, const void* x, const float* g, int rows, int D, float eps, void* u,
                     hipStream_t s);
 void launch_combine_norm(int act, const void* x1, const void* Y, const float* gates,
                          const int32_t* inv, int rows, int k, int D, const float* gnext, float eps,
-                         void* x, void* u, hipStream_t s);
+                         void* x, void* u, hipStream_t s, int32_t* zero0 = nullptr,
+                         int32_t* zero1 = nullptr, int nzero = 0);
 void launch_renoise(int32_t* canvas, const int32_t* argmax, const float* conf, float tau,
                     uint64_t seed, uint32_t tag, const Lens& pos0, const ReqIds& req, int B, int N,
                     int V, hipStream_t s);
@@ -64,6 +64,15 @@ struct MergeNext {
   const int32_t* counts;
   int L, E;
   int32_t* touched;
+  // with ex set (and rn.canvas): each row block also writes the first layer's
+  // input of its updated slot, x = emb[token] and u = its RMSNorm with g1
+  int act;
+  const void* emb;
+  const float* g1;
+  int D;
+  float eps;
+  void* ex;
+  void* eu;
 };
 void launch_lm_merge(const float* pmax, const int32_t* pidx, const float* psum, int rows,
                      int ntiles, int32_t* argmax, float* conf, const MergeNext& nx, hipStream_t s);
@@ -74,6 +83,20 @@ void launch_lm_merge(const float* pmax, const int32_t* pidx, const float* psum, 
 constexpr int ROUTER_MAX_SPLIT = 16;
 void launch_topk(float* logits, int nsplit, int rows, int E, int k, int32_t* ids, float* gates,
                  hipStream_t s);
+// top-k that also takes the RMSNorm in front of the router: it writes
+// u2 = round(x1 * rsqrt(mean(x1^2) + eps) * g2) for its row and, with
+// scale set, multiplies the summed logits by the same rsqrt (the router GEMM
+// then ran on round(x1 * g2)); with scale clear the logits are used as given
+struct TopkNorm {
+  const void* x1;
+  const float* g2;
+  int D;
+  float eps;
+  void* u2;
+  int scale;
+};
+void launch_topk_norm(int act, float* logits, int nsplit, int rows, int E, int k, int32_t* ids,
+                      float* gates, const TopkNorm& tn, hipStream_t s);
 // fused RMSNorm + router logits + top-k (false if D does not fit the LDS tile)
 struct RouteArgs {
   const void* x1;
@@ -154,6 +177,8 @@ struct StreamGemm {
   int nchunks;            // 64-weight-row chunks per row tile (gate/up: F/32)
   int ksplit;             // SG_F32: contraction splits (0 or 1 = none); split s writes
                           // its partial sums to out + s * M * ldo
+  const float* gs;        // SG_F32: optional [K] scale of the activations (each element
+                          // multiplied, then rounded to the activation type, before the MFMAs)
   void* out;
   int ldo;
   const void* R;          // residual (SG_RESID)

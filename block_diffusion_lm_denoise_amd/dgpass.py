@@ -72,7 +72,8 @@ class dg_renoise_args(C.Structure):
     _fields_ = [("tau", C.c_float), ("seed", C.c_uint64), ("pass_tag", C.c_uint32),
                 ("pos0", C.c_void_p), ("req_id", C.c_void_p), ("mode", C.c_int32),
                 ("mask_id", C.c_int32), ("final_pass", C.c_int32), ("changed", C.c_void_p),
-                ("masked_left", C.c_void_p)]
+                ("masked_left", C.c_void_p), ("embed_next", C.c_int32),
+                ("input_embedded", C.c_int32)]
 
 
 SAMPLER_UNIFORM, SAMPLER_MASKED = 0, 1
@@ -220,9 +221,11 @@ def _taps_struct(taps, inject_router=None, inject_x=None, inject_uf=None, stage_
 
 def _renoise_struct(renoise):
     """dg_renoise_args for dict(tau, seed, pass_tag, pos0[, req_id, sampler,
-    mask_id, final_pass, changed, masked_left]) (or None), with the host
-    arrays it points to (kept alive by the caller).  sampler: "uniform" or
-    "masked"; changed / masked_left: device int32 tensors [B] or None."""
+    mask_id, final_pass, changed, masked_left, embed_next, input_embedded])
+    (or None), with the host arrays it points to (kept alive by the caller).
+    sampler: "uniform" or "masked"; changed / masked_left: device int32
+    tensors [B] or None; embed_next / input_embedded: booleans (the carry of
+    the first layer's input between consecutive passes, see dgpass.h)."""
     if renoise is None:
         return None, None
     p0 = renoise.get("pos0")
@@ -235,7 +238,9 @@ def _renoise_struct(renoise):
                          None if rq is None else rq.ctypes.data_as(C.c_void_p),
                          _SAMPLER[renoise.get("sampler", "uniform")], int(renoise.get("mask_id", 0)),
                          int(bool(renoise.get("final_pass", False))), _ptr(renoise.get("changed")),
-                         _ptr(renoise.get("masked_left")))
+                         _ptr(renoise.get("masked_left")),
+                         int(bool(renoise.get("embed_next", False))),
+                         int(bool(renoise.get("input_embedded", False))))
     return nx, (p0, rq)
 
 

@@ -84,6 +84,7 @@ def generate(model: dgpass.Model, kv: dgpass.KVCache, prompt: torch.Tensor, n_ca
         else:
             dgpass.canvas_update(canvas, None, None, dict(base, pass_tag=0), cfg.V, stream=stream)
         ran = S
+        carry = False   # the workspace holds the first layer's input of `canvas`
         for p in range(p0, S):
             if stop is not None and (c, p) == tuple(stop):
                 state = dict(canvas_index=c, pass_index=p, canvas=canvas.clone())
@@ -95,10 +96,14 @@ def generate(model: dgpass.Model, kv: dgpass.KVCache, prompt: torch.Tensor, n_ca
             if sampler == "uniform" and last:
                 nxt = None
             else:
+                # the pass's last kernel also embeds the updated canvas when the
+                # next pass takes an update (it then skips its own embedding)
+                ahead = p + 1 < S and not (sampler == "uniform" and p + 1 == S - 1)
                 nxt = dict(base, pass_tag=p + 1, final_pass=last, changed=changed,
-                           masked_left=masked_left)
+                           masked_left=masked_left, embed_next=ahead, input_embedded=carry)
             model.denoise_pass_next(kv, canvas, argmax, conf, ws, touched=touched[c, p], renoise=nxt,
                                     stream=stream)
+            carry = nxt is not None and nxt["embed_next"]
             if early_exit and not last:
                 left = masked_left if sampler == "masked" else changed
                 if stream is not None:

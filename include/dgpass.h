@@ -268,7 +268,18 @@ dg_status dg_renoise(int32_t* canvas, const int32_t* argmax, const float* conf, 
  * and (masked mode) the number still holding mask_id afterwards -- the canvas
  * has converged when nothing changed (uniform) or nothing is masked (masked;
  * explainer, "Uniform State Diffusion": after several passes the canvas
- * converges). */
+ * converges).
+ * Two flags let consecutive passes of one canvas skip the canvas embedding
+ * (both are read by dg_denoise_pass_next only; 0 = off):
+ *  - embed_next: the pass's last kernel also writes the first layer's input
+ *    of the updated canvas (its embedding rows and their RMSNorm) into the
+ *    workspace;
+ *  - input_embedded: this pass does not embed `canvas`; it reads the first
+ *    layer's input from the workspace.  Set it only when the previous call on
+ *    this workspace (and stream) was a dg_denoise_pass_next with embed_next
+ *    for this canvas, B and N, and the canvas has not changed since: the
+ *    library cannot check this, and any other use gives the pass the wrong
+ *    input. */
 typedef struct dg_renoise_args {
   float tau;
   uint64_t seed;
@@ -280,6 +291,8 @@ typedef struct dg_renoise_args {
   int32_t final_pass;
   int32_t* changed;
   int32_t* masked_left;
+  int32_t embed_next;
+  int32_t input_embedded;
 } dg_renoise_args;
 
 /* The between-pass update of device canvases [B][N] in place as its own call:

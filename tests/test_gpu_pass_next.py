@@ -103,3 +103,55 @@ def test_pass_next_without_renoise_leaves_the_canvas():
     gm.expert_coverage(ws, tt2)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(tt), host(tt2))
+
+
+@pytest.mark.parametrize("name,sampler,B,N,lens", [("bf16", "uniform", 2, 16, (5, 9)),
+                                                   ("bf16", "masked", 1, 300, (33,)),
+                                                   ("f32", "uniform", 3, 7, (0, 4, 1))])
+def test_embedding_carry_equals_embedding_each_pass(name, sampler, B, N, lens):
+    """A chain of passes whose last kernel also embeds the updated canvas for
+    the next pass (embed_next), the next pass skipping its own embedding
+    (input_embedded), gives bit for bit the canvases, argmax, conf, coverage and
+    change counts of the same chain embedding the canvas in every pass."""
+    cfg = CFGS[name]
+    # masked rows see nearly the same context under random weights, so they
+    # share one confidence: tau 0 fills them all on the first pass
+    seed, tau, S = 9, (0.0 if sampler == "masked" else 0.5), 4
+    pair = Pair(cfg, seed, scale_lm=12.0)   # uniform: confidences straddle tau
+    gm = pair.gm
+    cap = max(lens) + N
+    _, _, _, kv = pair.caches(B, cap, list(lens), seed, synthetic=True)
+    ws = gm.workspace(B * max(max(lens), N), cap, device=DEV)
+    pos0 = np.array(lens, np.int32)
+    mask_id = cfg.V - 1
+    canvas0 = synth.tokens(cfg.V - 1, (B, N), seed, name="canvas")
+    if sampler == "masked":   # every other slot masked: rows differ, so confidences do
+        canvas0[:, ::2] = mask_id
+    canvas0 = canvas0.to(DEV)
+
+    def chain(carry):
+        cv = canvas0.clone()
+        ch = torch.full((B,), -1, dtype=torch.int32, device=DEV)
+        ml = torch.full((B,), -1, dtype=torch.int32, device=DEV)
+        outs, have = [], False
+        for p in range(S):
+            am = torch.full((B, N), -1, dtype=torch.int32, device=DEV)
+            cf = torch.full((B, N), -1.0, dtype=torch.float32, device=DEV)
+            tt = torch.full((cfg.L,), -1, dtype=torch.int32, device=DEV)
+            ahead = carry and p + 1 < S
+            rn = dict(tau=tau, seed=seed, pass_tag=p + 1, pos0=pos0, sampler=sampler, mask_id=mask_id,
+                      final_pass=p == S - 1, changed=ch, masked_left=ml, embed_next=ahead,
+                      input_embedded=have)
+            gm.denoise_pass_next(kv, cv, am, cf, ws, touched=tt, renoise=rn)
+            have = ahead
+            torch.cuda.synchronize()
+            outs.append((host(cv).copy(), host(am).copy(), host(cf).view(np.uint32).copy(),
+                         host(tt).copy(), host(ch).copy(), host(ml).copy()))
+        return outs
+
+    plain, carried = chain(False), chain(True)
+    for p, (a, b) in enumerate(zip(plain, carried)):
+        for what, x, y in zip(("canvas", "argmax", "conf", "touched", "changed", "masked_left"), a, b):
+            np.testing.assert_array_equal(y, x, err_msg=f"pass {p}: {what}")
+    # the chain did change the canvas between passes (the carry had work to do)
+    assert any(int(o[4].sum()) > 0 for o in plain[:-1])
