@@ -73,6 +73,18 @@ def test_single_slot_canvas_and_empty_prefix():
     _run(pair, 2, [1, 0], 1, 13)
 
 
+@pytest.mark.parametrize("act", ["bf16", "f32"])
+def test_rows_longer_than_2048(act):
+    # D 2560: the row kernels' loop over elements past the 2048 held in
+    # registers (embedding, the RMSNorm folded into top-k, combine), with the
+    # streamed projections at 40 (bf16) or 80 (fp32) pieces per weight row
+    cfg = _cfg(L=2, D=2560, Hq=4, Hkv=2, hd=128, E=8, k=2, F=128, V=512, act=act, expert=act)
+    # head scale 3: logits grow with sqrt(D), so this keeps the spread of the
+    # D 256 tests' scale 10
+    pair = Pair(cfg, 18, scale_lm=3.0)
+    _run(pair, 2, [20, 7], 19, 18)
+
+
 def test_fp8_experts_small():
     pair = Pair(_cfg(expert="fp8", L=2), 14, scale_lm=10.0)
     _run(pair, 2, [20, 9], 33, 14)

@@ -20,6 +20,8 @@ pytestmark = pytest.mark.gpu
 CFGS = {
     "bf16": ModelConfig(L=2, D=256, Hq=4, Hkv=2, hd=64, E=16, k=4, F=128, V=1000, act="bf16", expert="bf16"),
     "f32": ModelConfig(L=1, D=128, Hq=2, Hkv=1, hd=64, E=8, k=2, F=128, V=512, act="f32", expert="f32"),
+    # rows longer than the 2048 elements the row kernels hold in registers
+    "wide": ModelConfig(L=1, D=2560, Hq=4, Hkv=2, hd=128, E=8, k=2, F=128, V=512, act="bf16", expert="bf16"),
 }
 
 
@@ -107,7 +109,8 @@ def test_pass_next_without_renoise_leaves_the_canvas():
 
 @pytest.mark.parametrize("name,sampler,B,N,lens", [("bf16", "uniform", 2, 16, (5, 9)),
                                                    ("bf16", "masked", 1, 300, (33,)),
-                                                   ("f32", "uniform", 3, 7, (0, 4, 1))])
+                                                   ("f32", "uniform", 3, 7, (0, 4, 1)),
+                                                   ("wide", "uniform", 1, 24, (11,))])
 def test_embedding_carry_equals_embedding_each_pass(name, sampler, B, N, lens):
     """A chain of passes whose last kernel also embeds the updated canvas for
     the next pass (embed_next), the next pass skipping its own embedding
