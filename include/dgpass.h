@@ -279,7 +279,8 @@ dg_status dg_renoise(int32_t* canvas, const int32_t* argmax, const float* conf, 
  *    this workspace (and stream) was a dg_denoise_pass_next with embed_next
  *    for this canvas, B and N, and the canvas has not changed since: the
  *    library cannot check this, and any other use gives the pass the wrong
- *    input. */
+ *    input.  For dg_denoise_pass_next_noalloc the workspace is the GPU's
+ *    scratch, so the previous call is the previous one on that GPU. */
 typedef struct dg_renoise_args {
   float tau;
   uint64_t seed;
