@@ -68,3 +68,40 @@ def test_noalloc_rejects_a_pass_beyond_the_scratch():
     with pytest.raises(dgpass.DgError) as e:
         model.denoise_pass_next_noalloc(kv, canvas, am, cf)
     assert e.value.status == -4
+
+
+def test_noalloc_embedding_carry_equals_workspace_form():
+    """Three passes of one canvas where each pass's last kernel embeds the
+    updated canvas for the next (embed_next) and the next pass reads it
+    (input_embedded): on the static scratch the same canvases, argmax, conf
+    and coverage bit for bit as with a caller workspace."""
+    cfg = ModelConfig(L=2, D=256, Hq=4, Hkv=2, hd=64, E=16, k=4, F=128, V=1000, act="bf16", expert="bf16")
+    model = dgpass.Model(cfg, synth.make_weights(cfg, 44, device=DEV))
+    B, N, P, S = 2, 40, 24, 3
+    kv = model.kv_cache(B, P + N, device=DEV)
+    ws0 = model.workspace(B * P, P + N, device=DEV)
+    model.kv_prefill(kv, synth.tokens(cfg.V, (B, P), 44, device=DEV), ws0)
+    torch.cuda.synchronize()
+    canvas = synth.tokens(cfg.V, (B, N), 44, "canvas", device=DEV)
+
+    def chain(noalloc):
+        cv = canvas.clone()
+        ws = None if noalloc else model.workspace(B * N, P + N, device=DEV)
+        outs = []
+        for p in range(S):
+            am = torch.full((B, N), -1, dtype=torch.int32, device=DEV)
+            cf = torch.full((B, N), -1.0, dtype=torch.float32, device=DEV)
+            tch = torch.full((cfg.L,), -1, dtype=torch.int32, device=DEV)
+            nxt = dict(tau=0.5, seed=44, pass_tag=p + 1, pos0=kv.lens.copy(), embed_next=p + 1 < S,
+                       input_embedded=p > 0)
+            if noalloc:
+                model.denoise_pass_next_noalloc(kv, cv, am, cf, touched=tch, renoise=nxt)
+            else:
+                model.denoise_pass_next(kv, cv, am, cf, ws, touched=tch, renoise=nxt)
+            torch.cuda.synchronize()
+            outs.append((am.cpu(), cf.cpu(), tch.cpu(), cv.cpu()))
+        return outs
+
+    for a, b in zip(chain(False), chain(True)):
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
