@@ -397,7 +397,7 @@ __global__ __launch_bounds__(256) void lm_merge_k(const float* __restrict__ pmax
       const int32_t old = nx.rn.canvas[row];
       const int32_t t = update_token(nx.rn, b, p, old, i, cf);
       nx.rn.canvas[row] = t;
-      // the counters were cleared by the pass's first kernel
+      // the counters were cleared by the last layer's combine
       if (nx.rn.changed && t != old) atomicAdd(nx.rn.changed + b, 1);
       if (nx.rn.masked_left && nx.rn.mode == DG_SAMPLER_MASKED && t == nx.rn.mask_id)
         atomicAdd(nx.rn.masked_left + b, 1);

@@ -19,7 +19,6 @@ struct ReqIds {
 };
 
 // ---- elementwise / reductions (kern_elem.hip) ----
-// zero: optional device ints cleared by the same launch (n <= 256 each)
 void launch_embed_norm(int act, const int32_t* tok, const void* emb, const float* g, int rows, int D,
                        int V, float eps, void* x, void* u, hipStream_t s);
 void launch_rmsnorm(int act, const void* x, const float* g, int rows, int D, float eps, void* u,
@@ -27,7 +26,8 @@ void launch_rmsnorm(int act, const void* x, const float* g, int rows, int D, flo
 void launch_combine_norm(int act, const void* x1, const void* Y, const float* gates,
                          const int32_t* inv, int rows, int k, int D, const float* gnext, float eps,
                          void* x, void* u, hipStream_t s, int32_t* zero0 = nullptr,
-                         int32_t* zero1 = nullptr, int nzero = 0);
+                         int32_t* zero1 = nullptr, int nzero = 0);   // zero0/1: [nzero <= 256]
+                                                                    // ints cleared by block 0
 void launch_renoise(int32_t* canvas, const int32_t* argmax, const float* conf, float tau,
                     uint64_t seed, uint32_t tag, const Lens& pos0, const ReqIds& req, int B, int N,
                     int V, hipStream_t s);
